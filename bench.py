@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Bench of the KDA mixer hot path on one MI355X.
+
+Headline (``value``): decode state bandwidth, GB/s, of ``kda_decode_step`` on 64
+sequences x 96 heads (head dim 128, fp32 states), one token per sequence per step.
+Beside it, in the same JSON line: the prefill's tokens/s on one 8192-token sequence x 96
+heads (bf16 inputs, chunk 64), each with its roofline fraction, and the fp64 CPU oracle
+timed on this host on a bounded sample of the same work.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Decode timing rotates three copies of the resident state (3 x 403 MB) so that the
+256 MB last-level cache cannot serve a step from the previous one.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+D = 128
+
+
+def decode_bytes(B: int, H: int) -> int:
+    """Algorithmic HBM bytes of one decode step: every byte the step must move once."""
+    HD = H * D
+    state = 2 * B * H * D * D * 4            # read + write
+    conv = 2 * B * 3 * HD * 3 * 4            # read + write
+    tok = (3 * B * HD + 2 * B * HD + B * H) * 4  # q, k, v, z, g, b
+    out = B * HD * 4
+    params = (3 * HD * 4 + HD + H + D) * 4   # conv_w, dt_bias, A_log, norm_w
+    return state + conv + tok + out + params
+
+
+def chunk_flops(L: int, d: int = D) -> int:
+    """Algorithmic FLOPs of one chunk of L tokens for one head (multiply-add = 2;
+    masked triangles not counted): A, P, the UT inverse, W and U', the three state
+    products, and P.U."""
+    return (d * L * (L - 1) + d * L * (L + 1) + (L - 1) * L * (L + 1) // 3 + 2 * d * L * (L + 1) +
+            6 * L * d * d + d * L * (L + 1))
+
+
+def prefill_flops(lengths, H: int, chunk: int = 64) -> int:
+    tot = 0
+    for n in lengths:
+        full, rem = divmod(int(n), chunk)
+        tot += full * chunk_flops(chunk) + (chunk_flops(rem) if rem else 0)
+    return tot * H
+
+
+def prefill_bytes(N: int, B: int, H: int, initial: bool) -> int:
+    HD = H * D
+    tok = (5 * N * HD + N * H) * 2              # bf16 q, k, v, z, g, b
+    out = N * HD * 4                             # fp32 out
+    states = B * H * D * D * 4 * (2 if initial else 1)
+    conv = B * 3 * HD * 3 * 4 * (2 if initial else 1)
+    params = (3 * HD * 4 + HD + H + D) * 4
+    return tok + out + states + conv + params
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def bench_decode(args, dev):
+    import torch
+
+    import kda_inputs as ki
+    import gated_delta_rule_31_amd as kda
+
+    case = ki.case1_decode()
+    B, H = case.B, case.H
+    cfg = kda.KdaConfig(num_heads=H)
+    p = case.params
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    conv_w, A_log, dt_bias, norm_w = tt(p.conv_w), tt(p.A_log), tt(p.dt_bias), tt(p.norm_w)
+    n_sets = 3
+    states = [tt(case.state) for _ in range(n_sets)]
+    convs = [tt(case.conv_state) for _ in range(n_sets)]
+    x = case.step(0)
+    xs = [tt(getattr(x, n)) for n in "qkvzbg"]
+    out = torch.empty((B, H * D), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        kda.kda_decode_step(cfg, *xs, conv_w, A_log, dt_bias, norm_w, states[i % n_sets], convs[i % n_sets],
+                            out=out)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    alg = decode_bytes(B, H)
+    state_b = 2 * B * H * D * D * 4
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    return dict(
+        B=B, H=H, ms_per_step=ms_step, kernel_ms=kern_ms,
+        state_gbs=state_b / (ms_step * 1e-3) / 1e9,
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": "decode_kernel", "alg_bytes_per_launch": alg,
+                  "kernel_avg_us": round(kern_ms * 1e3, 2),
+                  "state_only_frac": round(state_b / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    )
+
+
+def bench_prefill(args, dev):
+    import torch
+
+    import kda_inputs as ki
+    import gated_delta_rule_31_amd as kda
+
+    case = ki.case2_prefill()
+    H = case.H
+    cfg = kda.KdaConfig(num_heads=H)
+    p = case.params
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    cu = tt(case.cu_seqlens.astype(np.int32))
+    xs = [bf(getattr(case.x, n)) for n in "qkvzbg"]
+    prm = [tt(p.conv_w), tt(p.A_log), tt(p.dt_bias), tt(p.norm_w)]
+    N = case.N
+    out = torch.empty((N, H * D), dtype=torch.float32, device=dev)
+    fs = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    fcs = torch.empty((1, 3 * H * D, 3), dtype=torch.float32, device=dev)
+
+    def launch():
+        kda.kda_prefill(cfg, cu, *xs, *prm, None, None, out=out, final_state=fs, final_conv_state=fcs)
+
+    for _ in range(max(1, args.warmup // 2)):
+        launch()
+    torch.cuda.synchronize()
+    n = args.prefill_steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    t0 = time.perf_counter()
+    for i in range(n):
+        ev[i][0].record()
+        launch()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / n
+    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    flops = prefill_flops([N], H)
+    byts = prefill_bytes(N, 1, H, initial=False)
+    tf = flops / (kern_ms * 1e-3) / 1e12
+    gbs = byts / (kern_ms * 1e-3) / 1e9
+    mf, hf = tf / BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS
+    return {"workload": "kda-prefill-1x8192tok-96head", "tokens_per_s": round(N / (ms * 1e-3), 1),
+            "ms_per_call": round(ms, 4), "kernel_avg_us": round(kern_ms * 1e3, 2),
+            "mfma_frac": round(mf, 4), "hbm_frac": round(hf, 4), "roofline_frac": round(max(mf, hf), 4),
+            "alg_flops": flops, "alg_bytes": byts, "achieved_tflops": round(tf, 2), "achieved_gbs": round(gbs, 1)}
+
+
+def cpu_baseline():
+    """The fp64 oracle on this host: one decode step of all 64 x 96 (sequence, head) pairs."""
+    import kda_inputs as ki
+    import oracle
+
+    case = ki.case1_decode()
+    x = case.step(0)
+    p = case.params
+    cores = len(os.sched_getaffinity(0))
+    pairs = [(b, h) for b in range(case.B) for h in range(case.H)]
+    cu = np.arange(case.B + 1)
+    t0 = time.perf_counter()
+    oracle.forward(oracle.MixerConfig(), cu, x.q, x.k, x.v, x.z, x.b, x.g, p.conv_w, p.A_log, p.dt_bias, p.norm_w,
+                   case.state, case.conv_state, pairs=pairs, threads=cores)
+    dt = time.perf_counter() - t0
+    state_b = 2 * len(pairs) * D * D * 4
+    return {"value": round(state_b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"one decode step of all {case.B}x{case.H} (sequence, head) pairs (fp64), {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the KDA decode and prefill paths here run on a single MI355X "
+              "and have no multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    log(f"device {torch.cuda.get_device_name(0)}")
+    log("decode: 64 seq x 96 heads")
+    dec = bench_decode(args, dev)
+    log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")
+    pre = None
+    if not args.skip_prefill:
+        log("prefill: 1 x 8192 tokens x 96 heads")
+        try:
+            pre = bench_prefill(args, dev)
+        except Exception as e:  # a prefill failure must not hide the decode line
+            pre = {"error": str(e)}
+        log(f"prefill: {pre}")
+    cpu = None
+    if not args.skip_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline()
+        log(f"cpu baseline: {cpu}")
+    line = {
+        "metric": "KDA decode state GB/s (% HBM peak) + prefill tokens/s (% MFMA), 96 heads",
+        "value": round(dec["state_gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "kda-decode-64seq-96head", "batch": dec["B"], "heads": dec["H"], "head_dim": D,
+                   "state_dtype": "f32", "state_sets_rotated": 3},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+"""Kimi Delta Attention (KDA) mixer hot path for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libkda.so`` (C ABI declared in ``include/kda.h``).  The
+functions here only marshal torch tensors into pointers and sizes; every step of the
+mixer runs in the library's HIP kernels.  PyTorch provides device memory and streams.
+There is no CPU fallback: if the library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = ["KdaConfig", "kda_decode_step", "kda_prefill", "kda_prefill_workspace_bytes", "KdaError",
+           "lib", "LIB_PATH", "EXPORTED_SYMBOLS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_prefill", "kda_prefill_workspace_bytes",
+                    "kda_status_str", "kda_abi_version")
+ABI_VERSION = 1
+HEAD_DIM = 128
+CONV = 4
+
+
+class _CConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("conv_size", ctypes.c_int32),
+        ("gate_lower_bound", ctypes.c_float),
+        ("l2_eps", ctypes.c_float),
+        ("rms_eps", ctypes.c_float),
+        ("q_scale", ctypes.c_float),
+    ]
+
+
+@dataclass
+class KdaConfig:
+    num_heads: int = 96
+    head_dim: int = HEAD_DIM
+    conv_size: int = CONV
+    gate_lower_bound: float = -5.0
+    l2_eps: float = 1e-6
+    rms_eps: float = 1e-5
+    q_scale: float = 0.0  # <= 0 selects head_dim ** -0.5
+
+    def _c(self) -> _CConfig:
+        return _CConfig(self.num_heads, self.head_dim, self.conv_size, self.gate_lower_bound, self.l2_eps,
+                        self.rms_eps, self.q_scale)
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_lib.kda_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m gated_delta_rule_31_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, fp = ctypes.c_void_p, ctypes.c_void_p
+    L.kda_config_default.restype = _CConfig
+    L.kda_config_default.argtypes = []
+    L.kda_decode_step.restype = ctypes.c_int
+    L.kda_decode_step.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32] + [fp] * 13 + [vp]
+    L.kda_prefill.restype = ctypes.c_int
+    L.kda_prefill.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 6 +
+                              [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp, ctypes.c_size_t, vp])
+    L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32]
+    L.kda_status_str.restype = ctypes.c_char_p
+    L.kda_status_str.argtypes = [ctypes.c_int]
+    L.kda_abi_version.restype = ctypes.c_int32
+    L.kda_abi_version.argtypes = []
+    if L.kda_abi_version() != ABI_VERSION:
+        raise ImportError(f"libkda.so ABI {L.kda_abi_version()} != binding ABI {ABI_VERSION}")
+    return L
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(t: torch.Tensor | None, dtype: torch.dtype, shape: tuple, name: str):
+    """Pointer of a dense device tensor of the given dtype and shape (None -> NULL)."""
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def kda_decode_step(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state, conv_state,
+                    out=None, stream=None) -> torch.Tensor:
+    """One token per sequence.  q,k,v,z,g: [B, H*D] fp32; b: [B, H]; state [B,H,D,D] and
+    conv_state [B,3*H*D,3] are updated in place.  Returns out [B, H*D] fp32."""
+    H, D = cfg.num_heads, cfg.head_dim
+    B = q.shape[0]
+    HD = H * D
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty((B, HD), dtype=f32, device=q.device)
+    args = [
+        _ptr(q, f32, (B, HD), "q"), _ptr(k, f32, (B, HD), "k"), _ptr(v, f32, (B, HD), "v"),
+        _ptr(z, f32, (B, HD), "z"), _ptr(b, f32, (B, H), "b"), _ptr(g, f32, (B, HD), "g"),
+        _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
+        _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
+        _ptr(state, f32, (B, H, D, D), "state"), _ptr(conv_state, f32, (B, 3 * HD, CONV - 1), "conv_state"),
+        _ptr(out, f32, (B, HD), "out"),
+    ]
+    c = cfg._c()
+    st = _lib.kda_decode_step(ctypes.byref(c), B, *args, _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step")
+    return out
+
+
+def kda_prefill_workspace_bytes(cfg: KdaConfig, num_seqs: int, total_tokens: int) -> int:
+    c = cfg._c()
+    return int(_lib.kda_prefill_workspace_bytes(ctypes.byref(c), num_seqs, total_tokens))
+
+
+def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
+                initial_state=None, initial_conv_state=None, out=None, final_state=None,
+                final_conv_state=None, workspace=None, stream=None):
+    """Varlen prefill.  cu_seqlens: int32 [B+1] on the GPU; q,k,v,z,g: [N, H*D] bf16;
+    b: [N, H] bf16.  Returns (out [N, H*D] fp32, final_state, final_conv_state).
+    ``final_state`` may be ``initial_state`` (in-place carry)."""
+    H, D = cfg.num_heads, cfg.head_dim
+    B = cu_seqlens.shape[0] - 1
+    N = q.shape[0]
+    HD = H * D
+    f32, bf = torch.float32, torch.bfloat16
+    dev = q.device
+    if out is None:
+        out = torch.empty((N, HD), dtype=f32, device=dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, D, D), dtype=f32, device=dev)
+    if final_conv_state is None:
+        final_conv_state = torch.empty((B, 3 * HD, CONV - 1), dtype=f32, device=dev)
+    ws_bytes = kda_prefill_workspace_bytes(cfg, B, N)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    args = [
+        _ptr(cu_seqlens, torch.int32, (B + 1,), "cu_seqlens"),
+        _ptr(q, bf, (N, HD), "q"), _ptr(k, bf, (N, HD), "k"), _ptr(v, bf, (N, HD), "v"),
+        _ptr(z, bf, (N, HD), "z"), _ptr(b, bf, (N, H), "b"), _ptr(g, bf, (N, HD), "g"),
+        _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
+        _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
+        _ptr(initial_state, f32, (B, H, D, D), "initial_state"),
+        _ptr(initial_conv_state, f32, (B, 3 * HD, CONV - 1), "initial_conv_state"),
+        _ptr(out, f32, (N, HD), "out"), _ptr(final_state, f32, (B, H, D, D), "final_state"),
+        _ptr(final_conv_state, f32, (B, 3 * HD, CONV - 1), "final_conv_state"),
+    ]
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    c = cfg._c()
+    st = _lib.kda_prefill(ctypes.byref(c), B, N, *args, ws, ctypes.c_size_t(ws_bytes), _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_prefill")
+    return out, final_state, final_conv_state

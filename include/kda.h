@@ -1,0 +1,166 @@
+/*
+ * kda.h -- C ABI of libkda.so: the Kimi Delta Attention (KDA) mixer's hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "colibri/c/kimi_k3.c", file header comment "KDA per-head
+ * recurrence"), per sequence and head, head dim D = 128:
+ *
+ *   q,k,v = SiLU(ShortConv4(x))        depthwise causal conv, 4 taps, oldest tap first,
+ *                                      no bias; x_{t<0} taken from the carried conv state
+ *   q,k   L2-normalised over the head's D channels, eps added inside the sqrt;
+ *         q *= q_scale (D^-0.5)
+ *   gk    = gate_lower_bound * sigmoid(exp(A_log[h]) * (z + dt_bias)),  alpha = exp(gk)
+ *   beta  = sigmoid(b)
+ *   S     = (I - beta k k^T) Diag(alpha) S + beta k v^T       S[key][value], fp32
+ *   o     = S^T q                                             with the updated S
+ *   out   = sigmoid(g) * RMSNorm(o)                           RMSNorm weight norm_w[D],
+ *                                                             shared by all heads
+ *
+ * The projections that produce the pre-conv q/k/v and the z/b/g logits, and the output
+ * projection, are not part of this library.
+ *
+ * Layouts (row-major, every array dense):
+ *   per-token activations q, k, v, z, g   [tokens, H*D]   channel h*D+i of head h
+ *   beta logits b                         [tokens, H]
+ *   conv_w                                [3*H*D, 4]      rows: the q block (H*D), then
+ *                                                         k, then v; taps oldest first
+ *   A_log [H], dt_bias [H*D], norm_w [D]
+ *   state                                 [B, H, D, D]    S[key][value], fp32
+ *   conv_state                            [B, 3*H*D, 3]   the 3 previous pre-conv inputs
+ *                                                         of each channel, oldest first
+ *   out                                   [tokens, H*D]   fp32
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers (HIP) unless stated; the caller owns every buffer.
+ *     The library allocates and frees nothing and never synchronises: all work is
+ *     queued on the given HIP stream (NULL = the default stream), so a call may be
+ *     captured into a HIP graph.
+ *   - Arguments are checked on the host before anything is queued; a rejected call
+ *     queues nothing and leaves every buffer untouched.  Values inside device buffers
+ *     (e.g. cu_seqlens) cannot be checked on the host; the kernels clamp them so that
+ *     no access leaves the buffers the sizes describe.
+ *   - The library never exits or aborts.  A device fault surfaces at the caller's next
+ *     synchronisation.
+ *   - Calls on different streams that touch different buffers may run concurrently;
+ *     calls that write the same state buffer must be ordered by the caller.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
+    KDA_ERR_BAD_CONFIG = 2, /* head_dim != 128, conv_size != 4, num_heads < 1, bad eps */
+    KDA_ERR_BAD_SHAPE = 3,  /* negative or inconsistent sizes, or sizes past the limits */
+    KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned */
+    KDA_ERR_WORKSPACE = 5,  /* workspace smaller than kda_prefill_workspace_bytes() */
+    KDA_ERR_LAUNCH = 6      /* the HIP runtime refused a kernel launch */
+} kda_status;
+
+/* Mixer constants.  Fill with kda_config_default() and set num_heads. */
+typedef struct {
+    int32_t num_heads;      /* H >= 1 */
+    int32_t head_dim;       /* D; must be 128 (the pages' KDA head dim) */
+    int32_t conv_size;      /* ShortConv taps; must be 4 */
+    float gate_lower_bound; /* gmin of the decay gate; the pages' value is -5 */
+    float l2_eps;           /* added to sum(x^2) inside the sqrt of the q/k L2 norm; 1e-6 */
+    float rms_eps;          /* eps of the per-head RMSNorm of o; the loader's rms default 1e-5 */
+    float q_scale;          /* scale of the normalised q; <= 0 selects D^-0.5 */
+} kda_config;
+
+/* Defaults: H = 96, D = 128, conv 4, gmin -5, l2_eps 1e-6, rms_eps 1e-5, q_scale D^-0.5
+ * (page "colibri/c/kimi_k3.c": header comment "KDA per-head recurrence" and the
+ * config loader's rms_norm_eps default). */
+kda_config kda_config_default(void);
+
+/*
+ * kda_decode_step -- one new token for each of B sequences against resident states.
+ *
+ * Follows the header comment "KDA per-head recurrence" (page "colibri/c/kimi_k3.c")
+ * for a single token: the conv window of every channel is advanced by one input, the
+ * state is decayed, corrected and written, and the gated, normalised readout is
+ * returned.  The state is streamed once: each 64 KiB head state is read and written
+ * exactly once per call.
+ *
+ *   batch                  B >= 0 (0: nothing queued, KDA_OK)
+ *   q, k, v                [B, H*D] fp32 pre-conv inputs of the new token
+ *   z                      [B, H*D] fp32 decay logits, before dt_bias
+ *   b                      [B, H]   fp32 beta logits
+ *   g                      [B, H*D] fp32 output-gate logits
+ *   conv_w, A_log, dt_bias, norm_w   fp32 parameters (layouts above)
+ *   state                  [B, H, D, D] fp32, read and overwritten in place
+ *   conv_state             [B, 3*H*D, 3] fp32, read and overwritten in place
+ *   out                    [B, H*D] fp32, written; must not overlap any input
+ *   stream                 hipStream_t or NULL
+ * Alignment: every pointer 16-byte aligned.  Limits: B*H <= 2^31-1.
+ */
+kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
+                           const float *q, const float *k, const float *v,
+                           const float *z, const float *b, const float *g,
+                           const float *conv_w, const float *A_log, const float *dt_bias,
+                           const float *norm_w,
+                           float *state, float *conv_state, float *out,
+                           void *stream);
+
+/*
+ * kda_prefill -- a packed batch of whole sequences (varlen), processed in chunks of
+ * 64 tokens with the chunked (WY / UT-transform) form of the same recurrence; returns
+ * every token's output and each sequence's final state and conv state.
+ *
+ * Follows the header comment "KDA per-head recurrence" (page "colibri/c/kimi_k3.c");
+ * the engine's prefill also runs in token chunks (same page, ENV K3_CHUNK).  The
+ * chunked form gives the token recurrence's result up to rounding.
+ *
+ *   num_seqs               B >= 0 (0: nothing queued)
+ *   total_tokens           N >= 0, the packed token count
+ *   cu_seqlens             device int32 [B+1]: sequence s holds tokens
+ *                          cu_seqlens[s] .. cu_seqlens[s+1]-1; must start at 0, be
+ *                          non-decreasing and end at N (values are clamped to [0, N])
+ *   q, k, v, z, g          [N, H*D] bf16 (raw bit patterns)
+ *   b                      [N, H]   bf16
+ *   conv_w, A_log, dt_bias, norm_w   fp32 parameters
+ *   initial_state          [B, H, D, D] fp32, or NULL for zeros
+ *   initial_conv_state     [B, 3*H*D, 3] fp32, or NULL for zeros
+ *   out                    [N, H*D] fp32, written
+ *   final_state            [B, H, D, D] fp32, written; may be the same pointer as
+ *                          initial_state (in-place carry), must not partially overlap it
+ *   final_conv_state       [B, 3*H*D, 3] fp32, written; may equal initial_conv_state
+ *   workspace              device scratch of workspace_bytes (may be NULL when
+ *                          kda_prefill_workspace_bytes() returns 0)
+ *   stream                 hipStream_t or NULL
+ * A sequence of length 0 copies its initial state and conv state to the final ones.
+ * Alignment: every fp32/bf16 array pointer 16-byte aligned, cu_seqlens 4-byte aligned.
+ * Limits: N <= 2^31-1, B*H <= 2^31-1.
+ */
+kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
+                       const int32_t *cu_seqlens,
+                       const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *z, const uint16_t *b, const uint16_t *g,
+                       const float *conv_w, const float *A_log, const float *dt_bias,
+                       const float *norm_w,
+                       const float *initial_state, const float *initial_conv_state,
+                       float *out, float *final_state, float *final_conv_state,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device scratch kda_prefill needs for these sizes (0 when it needs none). */
+size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_status_str(kda_status s);
+
+/* KDA_ABI_VERSION of the built library. */
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,116 @@
+"""Shared helpers of the GPU parity tests: upload seeded cases, run the oracle on the
+same inputs, and the error metrics the tolerances are stated in.
+
+Metrics (per (sequence, head) slice):
+  rel  = max|x - r| / max|r|          -- "max relative error" (decode: 1e-4; prefill states: 5e-3)
+  abs  = max|x - r|                   -- "max abs error" (prefill outputs: 2e-2)
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import kda_inputs as ki
+import oracle
+
+D = 128
+
+DECODE_REL_TOL = 1e-4        # fp32 decode: outputs and states
+PREFILL_OUT_ABS_TOL = 2e-2   # bf16-input chunked prefill: gated RMS-normalised outputs
+PREFILL_STATE_REL_TOL = 5e-3  # bf16-input chunked prefill: final states
+
+
+def slice_rel(x: np.ndarray, r: np.ndarray) -> float:
+    x = np.asarray(x, np.float64)
+    r = np.asarray(r, np.float64)
+    den = np.max(np.abs(r))
+    return float(np.max(np.abs(x - r)) / den) if den > 0 else float(np.max(np.abs(x)))
+
+
+def t(a, dev, dtype=None):
+    """numpy -> device tensor (uint16 arrays become bf16)."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    x = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return x if dtype is None else x.to(dtype)
+
+
+def oracle_cfg() -> oracle.MixerConfig:
+    return oracle.MixerConfig(head_dim=D, conv_size=4, gate_lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-5)
+
+
+# ------------------------------------------------------------------------------- decode
+
+def decode_oracle(case: ki.DecodeCase, pairs, n_steps: int | None = None):
+    """The oracle over ``n_steps`` decode steps for the given (sequence, head) pairs:
+    each sequence's steps form a token sequence.  Returns {(b, h): PairResult}."""
+    n = case.n_steps if n_steps is None else n_steps
+    seqs = sorted({b for b, _ in pairs})
+    H = case.H
+    # gather, per needed sequence, its n tokens: rows ordered [seq][step]
+    rows = {name: [] for name in "qkvzbg"}
+    for i in range(n):
+        x = case.step(i)
+        for name in "qkvzbg":
+            rows[name].append(getattr(x, name)[seqs])
+    stacked = {name: np.stack(rows[name], axis=1).reshape(len(seqs) * n, -1) for name in rows}
+    cu = np.arange(len(seqs) + 1) * n
+    idx = {b: j for j, b in enumerate(seqs)}
+    sub_pairs = [(idx[b], h) for b, h in pairs]
+    p = case.params
+    res = oracle.forward(oracle_cfg(), cu, stacked["q"], stacked["k"], stacked["v"], stacked["z"],
+                         stacked["b"], stacked["g"], p.conv_w, p.A_log, p.dt_bias, p.norm_w,
+                         case.state[seqs], case.conv_state[seqs], pairs=sub_pairs)
+    return {(b, h): res[(idx[b], h)] for b, h in pairs}
+
+
+class DecodeRun:
+    """A decode case resident on the GPU."""
+
+    def __init__(self, case: ki.DecodeCase, dev):
+        import gated_delta_rule_31_amd as kda
+        self.kda = kda
+        self.case = case
+        self.dev = dev
+        self.cfg = kda.KdaConfig(num_heads=case.H)
+        p = case.params
+        self.conv_w, self.A_log = t(p.conv_w, dev), t(p.A_log, dev)
+        self.dt_bias, self.norm_w = t(p.dt_bias, dev), t(p.norm_w, dev)
+        self.state = t(case.state, dev)
+        self.conv_state = t(case.conv_state, dev)
+
+    def inputs(self, i: int):
+        x = self.case.step(i)
+        return [t(getattr(x, n), self.dev) for n in "qkvzbg"]
+
+    def step(self, xs, out=None, stream=None):
+        return self.kda.kda_decode_step(self.cfg, *xs, self.conv_w, self.A_log, self.dt_bias, self.norm_w,
+                                        self.state, self.conv_state, out=out, stream=stream)
+
+
+# ------------------------------------------------------------------------------- prefill
+
+def prefill_oracle(case: ki.PrefillCase, pairs=None):
+    x = case.x.as_f32()
+    p = case.params
+    return oracle.forward(oracle_cfg(), case.cu_seqlens, x.q, x.k, x.v, x.z, x.b, x.g, p.conv_w, p.A_log,
+                          p.dt_bias, p.norm_w, case.initial_state, case.initial_conv_state, pairs=pairs)
+
+
+def prefill_gpu(case: ki.PrefillCase, dev, in_place: bool = False):
+    import gated_delta_rule_31_amd as kda
+    cfg = kda.KdaConfig(num_heads=case.H)
+    p = case.params
+    cu = t(case.cu_seqlens.astype(np.int32), dev)
+    xs = [t(getattr(case.x, n), dev) for n in "qkvzbg"]
+    st = t(case.initial_state, dev)
+    cst = t(case.initial_conv_state, dev)
+    kw = {}
+    if in_place:
+        kw = dict(final_state=st, final_conv_state=cst)
+    out, fs, fcs = kda.kda_prefill(cfg, cu, *xs, t(p.conv_w, dev), t(p.A_log, dev), t(p.dt_bias, dev),
+                                   t(p.norm_w, dev), st, cst, **kw)
+    torch.cuda.synchronize()
+    return out, fs, fcs

@@ -1,0 +1,116 @@
+"""GPU parity of kda_decode_step against the fp64 oracle (fp32 path: max relative
+error 1e-4 per (sequence, head) slice on outputs, states and conv states)."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+from tests.parity import DECODE_REL_TOL, DecodeRun, decode_oracle, slice_rel
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _check_final(run: DecodeRun, ref, pairs):
+    st = run.state.cpu().numpy()
+    cst = run.conv_state.cpu().numpy()
+    H = run.case.H
+    worst = 0.0
+    for (b, h) in pairs:
+        r = ref[(b, h)]
+        worst = max(worst, slice_rel(st[b, h], r.state))
+        got_c = np.stack([cst[b, blk * H * D + h * D: blk * H * D + (h + 1) * D] for blk in range(3)])
+        np.testing.assert_array_equal(got_c, r.conv_state)  # the window shift is exact
+    assert worst <= DECODE_REL_TOL, worst
+
+
+def _run_steps(case, dev, pairs, n_steps=None):
+    run = DecodeRun(case, dev)
+    n = case.n_steps if n_steps is None else n_steps
+    outs = []
+    for i in range(n):
+        out = run.step(run.inputs(i))
+        outs.append(out.cpu().numpy().reshape(case.B, case.H, D))
+    torch.cuda.synchronize()
+    ref = decode_oracle(case, pairs, n)
+    worst = 0.0
+    for (b, h) in pairs:
+        for i in range(n):
+            worst = max(worst, slice_rel(outs[i][b, h], ref[(b, h)].out[i]))
+    assert worst <= DECODE_REL_TOL, worst
+    _check_final(run, ref, pairs)
+    return run, ref
+
+
+def test_cfg0_sixty_four_steps_from_zero(device):
+    case = ki.case0_decode()
+    print(f"[decode] {case.name} B={case.B} H={case.H} steps={case.n_steps}", flush=True)
+    _run_steps(case, device, [(0, h) for h in range(case.H)])
+
+
+def test_cfg1_k3_shape_one_step_all_heads(device):
+    case = ki.case1_decode()
+    print(f"[decode] {case.name} B={case.B} H={case.H}", flush=True)
+    _run_steps(case, device, [(b, h) for b in range(case.B) for h in range(case.H)])
+
+
+def test_cfg4_large_batch_32_chained_steps_sampled(device):
+    case = ki.case4_decode()
+    print(f"[decode] {case.name} B={case.B} H={case.H} steps={case.n_steps}", flush=True)
+    rng = np.random.default_rng(404)
+    bs = [0, case.B - 1] + list(rng.choice(np.arange(1, case.B - 1), 10, replace=False))
+    hs = [0, case.H - 1] + list(rng.choice(np.arange(1, case.H - 1), 4, replace=False))
+    pairs = [(int(b), int(h)) for b in bs for h in hs]
+    _run_steps(case, device, pairs)
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (3, 5), (7, 16)])
+def test_odd_shapes_multi_step(device, B, H):
+    case = ki.decode_case(50 + B * 10 + H, B, H, 5, f"odd-{B}x{H}")
+    _run_steps(case, device, [(b, h) for b in range(B) for h in range(H)])
+
+
+def test_saturated_gates(device):
+    """Logits far in the tails: sigmoid saturates (beta -> 0 or 1, alpha -> 1 or e^-5)."""
+    case = ki.decode_case(61, 2, 4, 3, "saturated")
+    steps = []
+    for i in range(3):
+        x = case.step(i)
+        x.z[0] = 40.0
+        x.z[1] = -40.0
+        x.b[0] = 30.0
+        x.b[1] = -30.0
+        x.g[:, :64] = 25.0
+        steps.append(x)
+    case._steps = steps
+    _run_steps(case, device, [(b, h) for b in range(2) for h in range(4)])
+
+
+def test_empty_batch_is_a_no_op(device):
+    import gated_delta_rule_31_amd as kda
+    case = ki.decode_case(70, 1, 2, 1, "empty")
+    run = DecodeRun(case, device)
+    xs = [x[:0] for x in run.inputs(0)]
+    before = run.state.clone()
+    out = kda.kda_decode_step(run.cfg, *xs, run.conv_w, run.A_log, run.dt_bias, run.norm_w,
+                              run.state[:0], run.conv_state[:0])
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2 * D)
+    assert torch.equal(before, run.state)
+
+
+def test_decode_on_a_side_stream_and_repeatable(device):
+    """Same inputs on a non-default stream give bit-identical results."""
+    case = ki.decode_case(71, 4, 8, 1, "stream")
+    r1 = DecodeRun(case, device)
+    o1 = r1.step(r1.inputs(0))
+    r2 = DecodeRun(case, device)
+    s = torch.cuda.Stream()
+    xs = r2.inputs(0)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        o2 = r2.step(xs, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(r1.state, r2.state)

@@ -6,9 +6,10 @@ none of the mixer's arithmetic.
 
 Recipe (every case):
 
-* Each named tensor has its own numpy ``default_rng`` stream, seeded with
-  ``[case_seed, stream_id]`` where ``stream_id`` is a fixed number per tensor (and per
-  decode step), so any tensor can be regenerated on its own.
+* Each named tensor has its own numpy ``default_rng`` streams, seeded with
+  ``[case_seed, stream_id, block]`` where ``stream_id`` is a fixed number per tensor
+  (and per decode step) and ``block`` numbers blocks of about 2^18 elements (whole rows
+  of the last dimension), so any tensor can be regenerated on its own, in parallel.
 * ``N(0, s)`` means mean 0 and *standard deviation* s; draws are float32.
 * ``U(a, b)``: float32 uniform on [a, b).
 * Pre-conv q/k/v, decay logits z, beta logits b and output-gate logits g are N(0, 1);
@@ -23,6 +24,8 @@ states ``[B, H, D, D]``, conv states ``[B, 3*H*D, 3]``.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -35,23 +38,42 @@ _S_STATE, _S_CONV_STATE, _S_CONV_W, _S_DT_BIAS, _S_A_LOG, _S_LENS = 1, 2, 3, 4, 
 _S_Q, _S_K, _S_V, _S_Z, _S_B, _S_G = 10, 11, 12, 13, 14, 15
 _STEP_STRIDE = 100  # decode step i uses stream id  base + STEP_STRIDE * (i + 1)
 
-_ROW_BLOCK = 1024  # large tensors are drawn this many rows at a time (fixed, so the stream is too)
+_BLOCK_ELEMS = 1 << 18  # large tensors are drawn in blocks of about this many elements
 
 
-def _rng(seed: int, stream: int) -> np.random.Generator:
-    return np.random.default_rng([int(seed), int(stream)])
+def _rng(seed: int, stream: int, block: int | None = None) -> np.random.Generator:
+    key = [int(seed), int(stream)] if block is None else [int(seed), int(stream), int(block)]
+    return np.random.default_rng(key)
 
 
-def normal(seed: int, stream: int, shape, std: float) -> np.ndarray:
+def _threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def normal(seed: int, stream: int, shape, std: float, bf16: bool = False) -> np.ndarray:
+    """N(0, std) float32 draws (or their bf16 bit patterns).  The array is cut into rows
+    of its last dimension and blocks of ``max(1, 2^18 // last_dim)`` rows; block b comes
+    from its own stream [seed, stream, b].  So the result does not depend on how many
+    threads draw it, and a prefix of leading rows does not depend on the row count."""
     shape = tuple(int(s) for s in shape)
-    r = _rng(seed, stream)
-    out = np.empty(shape, dtype=np.float32)
-    flat = out.reshape(shape[0], -1) if len(shape) > 1 else out.reshape(-1, 1)
-    for r0 in range(0, flat.shape[0], _ROW_BLOCK):
-        blk = flat[r0:r0 + _ROW_BLOCK]
-        blk[...] = r.standard_normal(blk.shape, dtype=np.float32)
-    if std != 1.0:
-        out *= np.float32(std)
+    out = np.empty(shape, dtype=np.uint16 if bf16 else np.float32)
+    flat = out.reshape(-1, shape[-1])
+    rows = max(1, _BLOCK_ELEMS // shape[-1])
+    nblk = (flat.shape[0] + rows - 1) // rows
+
+    def draw(b):
+        blk = flat[b * rows:(b + 1) * rows]
+        x = _rng(seed, stream, b).standard_normal(blk.shape, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        blk[...] = to_bf16_bits(x) if bf16 else x
+
+    if nblk <= 2:
+        for b in range(nblk):
+            draw(b)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(draw, range(nblk)))
     return out
 
 
@@ -115,15 +137,17 @@ class TokenInputs:
         return TokenInputs(*(cv(a) for a in (self.q, self.k, self.v, self.z, self.b, self.g)))
 
 
-def token_inputs(seed: int, N: int, H: int, step: int | None = None) -> TokenInputs:
+def token_inputs(seed: int, N: int, H: int, step: int | None = None, bf16: bool = False) -> TokenInputs:
+    """Per-token activations; with bf16=True, their bf16 roundings (bit patterns), which
+    equal ``token_inputs(...).as_bf16()``."""
     off = 0 if step is None else _STEP_STRIDE * (step + 1)
     return TokenInputs(
-        q=normal(seed, _S_Q + off, (N, H * D), 1.0),
-        k=normal(seed, _S_K + off, (N, H * D), 1.0),
-        v=normal(seed, _S_V + off, (N, H * D), 1.0),
-        z=normal(seed, _S_Z + off, (N, H * D), 1.0),
-        b=normal(seed, _S_B + off, (N, H), 1.0),
-        g=normal(seed, _S_G + off, (N, H * D), 1.0),
+        q=normal(seed, _S_Q + off, (N, H * D), 1.0, bf16),
+        k=normal(seed, _S_K + off, (N, H * D), 1.0, bf16),
+        v=normal(seed, _S_V + off, (N, H * D), 1.0, bf16),
+        z=normal(seed, _S_Z + off, (N, H * D), 1.0, bf16),
+        b=normal(seed, _S_B + off, (N, H), 1.0, bf16),
+        g=normal(seed, _S_G + off, (N, H * D), 1.0, bf16),
     )
 
 
@@ -212,7 +236,7 @@ def prefill_case(seed: int, H: int, lengths, with_initial: bool, name: str) -> P
     B, N = len(lengths), int(cu[-1])
     st = normal(seed, _S_STATE, (B, H, D, D), 0.05) if with_initial else None
     cst = normal(seed, _S_CONV_STATE, (B, 3 * H * D, K - 1), 1.0) if with_initial else None
-    return PrefillCase(name, seed, H, cu, params(seed, H), token_inputs(seed, N, H).as_bf16(), st, cst)
+    return PrefillCase(name, seed, H, cu, params(seed, H), token_inputs(seed, N, H, bf16=True), st, cst)
 
 
 def case2_prefill(T: int = 8192, H: int = 96) -> PrefillCase:

@@ -169,14 +169,15 @@ class PairResult:
 
 
 def forward(cfg: MixerConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
-            state=None, conv_state=None, pairs=None, threads: int | None = None):
+            state=None, conv_state=None, pairs=None, threads: int | None = None, decode=None):
     """Run the oracle for every (sequence, head) in ``pairs`` (default: all).
 
-    Arrays may be any float dtype (bf16 inputs are passed as their exact float32
-    values); only the slices the pairs touch are converted to fp64.  ``state`` is
-    ``[B, H, D, D]`` or None (zeros); ``conv_state`` ``[B, 3*H*D, K-1]`` or None (zeros).
-    Returns ``{(s, h): PairResult}``.
+    Activations may be any float dtype, or an encoding that ``decode`` turns into exact
+    float values slice by slice (e.g. bf16 bit patterns); only the slices the pairs touch
+    are converted to fp64.  ``state`` is ``[B, H, D, D]`` or None (zeros); ``conv_state``
+    ``[B, 3*H*D, K-1]`` or None (zeros).  Returns ``{(s, h): PairResult}``.
     """
+    dec = decode if decode is not None else (lambda x: x)
     D, K = cfg.head_dim, cfg.conv_size
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     B = len(cu) - 1
@@ -194,9 +195,9 @@ def forward(cfg: MixerConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bi
     for j, (s, h) in enumerate(pairs):
         t0, t1 = int(cu[s]), int(cu[s + 1])
         cs = slice(h * D, (h + 1) * D)
-        xq, xk, xv = _f64(q[t0:t1, cs]), _f64(k[t0:t1, cs]), _f64(v[t0:t1, cs])
-        zz, gg = _f64(z[t0:t1, cs]), _f64(g[t0:t1, cs])
-        bb = _f64(b[t0:t1, h])
+        xq, xk, xv = _f64(dec(q[t0:t1, cs])), _f64(dec(k[t0:t1, cs])), _f64(dec(v[t0:t1, cs]))
+        zz, gg = _f64(dec(z[t0:t1, cs])), _f64(dec(g[t0:t1, cs]))
+        bb = _f64(dec(b[t0:t1, h]))
         wq = _f64(conv_w[0 * HD + h * D:0 * HD + (h + 1) * D])
         wk = _f64(conv_w[1 * HD + h * D:1 * HD + (h + 1) * D])
         wv = _f64(conv_w[2 * HD + h * D:2 * HD + (h + 1) * D])

@@ -93,10 +93,33 @@ class DecodeRun:
 # ------------------------------------------------------------------------------- prefill
 
 def prefill_oracle(case: ki.PrefillCase, pairs=None):
-    x = case.x.as_f32()
+    """The oracle on the case's bf16 activations (their exact values) for the pairs."""
+    x = case.x
     p = case.params
     return oracle.forward(oracle_cfg(), case.cu_seqlens, x.q, x.k, x.v, x.z, x.b, x.g, p.conv_w, p.A_log,
-                          p.dt_bias, p.norm_w, case.initial_state, case.initial_conv_state, pairs=pairs)
+                          p.dt_bias, p.norm_w, case.initial_state, case.initial_conv_state, pairs=pairs,
+                          decode=ki.bf16_bits_to_f32)
+
+
+def check_prefill(case: ki.PrefillCase, out, fs, fcs, pairs):
+    """Compare GPU prefill results with the oracle on (sequence, head) pairs.  Returns
+    (max output abs error, max state rel error)."""
+    ref = prefill_oracle(case, pairs)
+    cu = case.cu_seqlens
+    H = case.H
+    out_np = out.cpu().numpy() if hasattr(out, "cpu") else out
+    fs_np = fs.cpu().numpy() if hasattr(fs, "cpu") else fs
+    fcs_np = fcs.cpu().numpy() if hasattr(fcs, "cpu") else fcs
+    worst_o, worst_s = 0.0, 0.0
+    for (s, h) in pairs:
+        r = ref[(s, h)]
+        o = out_np[cu[s]:cu[s + 1], h * D:(h + 1) * D]
+        if o.size:
+            worst_o = max(worst_o, float(np.max(np.abs(o - r.out))))
+        worst_s = max(worst_s, slice_rel(fs_np[s, h], r.state))
+        got_c = np.stack([fcs_np[s, blk * H * D + h * D: blk * H * D + (h + 1) * D] for blk in range(3)])
+        np.testing.assert_array_equal(got_c, r.conv_state)  # the window is copied, exact
+    return worst_o, worst_s
 
 
 def prefill_gpu(case: ki.PrefillCase, dev, in_place: bool = False):

@@ -64,6 +64,34 @@ def prefill_bytes(N: int, B: int, H: int, initial: bool) -> int:
     return tok + out + states + conv + params
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_31_amd", "csrc", "kda_decode.hip")
+DECODE_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_64seq_96head.md")
+
+
+def measured_decode_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None
+    if the summary is missing or was taken on a different decode kernel source."""
+    import hashlib
+
+    if not os.path.exists(DECODE_PROFILE):
+        return None
+    vals = {}
+    with open(DECODE_PROFILE) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    with open(DECODE_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if vals.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -167,24 +195,79 @@ def bench_prefill(args, dev):
             "alg_flops": flops, "alg_bytes": byts, "achieved_tflops": round(tf, 2), "achieved_gbs": round(gbs, 1)}
 
 
-def cpu_baseline():
-    """The fp64 oracle on this host: one decode step of all 64 x 96 (sequence, head) pairs."""
+def cpu_baseline(n_steps: int = 16, min_seconds: float = 10.0):
+    """The fp64 oracle on this host: ``n_steps`` chained decode steps of all 64 x 96
+    (sequence, head) pairs of the decode workload, repeated from the same initial state
+    until ``min_seconds`` of work have run."""
     import kda_inputs as ki
     import oracle
 
     case = ki.case1_decode()
-    x = case.step(0)
     p = case.params
     cores = len(os.sched_getaffinity(0))
-    pairs = [(b, h) for b in range(case.B) for h in range(case.H)]
-    cu = np.arange(case.B + 1)
+    steps = [case.step(i) if i == 0 else ki.token_inputs(case.seed, case.B, case.H, step=i) for i in range(n_steps)]
+    # tokens of sequence b are rows b*n .. b*n+n-1
+    tok = {n: np.stack([getattr(x, n) for x in steps], axis=1).reshape(case.B * n_steps, -1) for n in "qkvzbg"}
+    cu = np.arange(case.B + 1) * n_steps
+    reps = 0
     t0 = time.perf_counter()
-    oracle.forward(oracle.MixerConfig(), cu, x.q, x.k, x.v, x.z, x.b, x.g, p.conv_w, p.A_log, p.dt_bias, p.norm_w,
-                   case.state, case.conv_state, pairs=pairs, threads=cores)
-    dt = time.perf_counter() - t0
-    state_b = 2 * len(pairs) * D * D * 4
+    while True:
+        oracle.forward(oracle.MixerConfig(), cu, tok["q"], tok["k"], tok["v"], tok["z"], tok["b"], tok["g"],
+                       p.conv_w, p.A_log, p.dt_bias, p.norm_w, case.state, case.conv_state, threads=cores)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    state_b = 2 * case.B * case.H * D * D * 4 * n_steps * reps
     return {"value": round(state_b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"one decode step of all {case.B}x{case.H} (sequence, head) pairs (fp64), {dt:.2f} s"}
+            "sample": f"{reps} x {n_steps} chained decode steps of all {case.B}x{case.H} (sequence, head) pairs, "
+                      f"fp64, {dt:.2f} s"}
+
+
+def cpu_baseline_prefill(heads_per_batch: int = 4, min_seconds: float = 5.0):
+    """The fp64 oracle on this host: batches of heads of the 8192-token prefill until
+    ``min_seconds`` of work have run; scaled to 96 heads."""
+    import kda_inputs as ki
+    import oracle
+
+    case = ki.case2_prefill()
+    p = case.params
+    cores = len(os.sched_getaffinity(0))
+    x = case.x
+    done = 0
+    t0 = time.perf_counter()
+    while done < case.H:
+        pairs = [(0, h) for h in range(done, min(case.H, done + heads_per_batch))]
+        oracle.forward(oracle.MixerConfig(), case.cu_seqlens, x.q, x.k, x.v, x.z, x.b, x.g, p.conv_w, p.A_log,
+                       p.dt_bias, p.norm_w, pairs=pairs, threads=cores, decode=ki.bf16_bits_to_f32)
+        done += len(pairs)
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(case.N * done / case.H / dt, 1), "unit": "tokens/s (96 heads)", "cores": cores,
+            "kind": "oracle", "sample": f"{done} of 96 heads x {case.N} tokens, fp64, {dt:.2f} s; scaled to 96 heads"}
+
+
+def bench_copy(args, dev):
+    """A plain device-to-device copy of one decode state (402.7 MB read + written): the
+    reference for HBM counter readings and achievable bandwidth."""
+    import torch
+
+    n = 64 * 96 * D * D
+    src = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        dst.copy_(src)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return {"bytes_per_copy": 2 * n * 4, "kernel_avg_us": round(ms * 1e3, 2),
+            "gbs": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}
 
 
 def main():
@@ -193,6 +276,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "decode", "prefill", "copy"], default="all",
+                    help="run one part only (counter runs under rocprofv3 use this)")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -207,11 +292,18 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     log(f"device {torch.cuda.get_device_name(0)}")
+    if args.only == "copy":
+        print(json.dumps({"copy": bench_copy(args, dev)}), flush=True)
+        return
+    if args.only == "prefill":
+        print(json.dumps({"prefill": bench_prefill(args, dev)}), flush=True)
+        return
     log("decode: 64 seq x 96 heads")
     dec = bench_decode(args, dev)
     log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")
+    dec["roofline"]["traffic"] = measured_decode_traffic()
     pre = None
-    if not args.skip_prefill:
+    if args.only == "all" and not args.skip_prefill:
         log("prefill: 1 x 8192 tokens x 96 heads")
         try:
             pre = bench_prefill(args, dev)
@@ -219,10 +311,13 @@ def main():
             pre = {"error": str(e)}
         log(f"prefill: {pre}")
     cpu = None
-    if not args.skip_cpu_baseline:
+    if args.only == "all" and not args.skip_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline()
         log(f"cpu baseline: {cpu}")
+        if pre is not None and "error" not in pre:
+            pre["cpu_baseline"] = cpu_baseline_prefill()
+            log(f"cpu baseline prefill: {pre['cpu_baseline']}")
     line = {
         "metric": "KDA decode state GB/s (% HBM peak) + prefill tokens/s (% MFMA), 96 heads",
         "value": round(dec["state_gbs"], 1),

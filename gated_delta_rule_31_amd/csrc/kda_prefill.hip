@@ -54,7 +54,8 @@ constexpr int OFF_R6 = 117760;   // sT fp32 [64][68]            -> sQe bf16 [64]
 constexpr int OFF_R7 = 135168;   // sTb bf16 [64][64]
 constexpr int OFF_TAB = 143360;  // small fp32 tables
 constexpr int kTabFloats = 512 + 640 + 768 + 512 + 512 + 128 + 64;
-constexpr int kLdsBytes = OFF_TAB + kTabFloats * 4;
+constexpr int OFF_CW = OFF_TAB + kTabFloats * 4;  // conv taps of this head, fp32 [3][128][4]
+constexpr int kLdsBytes = OFF_CW + 3 * 128 * 4 * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 constexpr int CB_LD = 132;  // fp32 row pitch of sCB
@@ -158,6 +159,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     float *sEndRef = sExpRef + 512;                            // [4][128] e^{G_end - r_I}
     float *sExpEnd = sEndRef + 512;                            // [128]    e^{G_end}
     float *sBeta = sExpEnd + 128;                              // [64]
+    float *sConvW = reinterpret_cast<float *>(smem + OFF_CW);  // [3][128][4] taps, oldest first
 
     const int H = a.c.H;
     const int N = a.N;
@@ -196,6 +198,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     }
     }
 
+    for (int i = threadIdx.x; i < 3 * kD; i += kThreads) {
+        const int blk = i >> 7, c = i & 127;
+        *reinterpret_cast<float4 *>(sConvW + i * 4) =
+            *reinterpret_cast<const float4 *>(a.conv_w + ((size_t)blk * HD + (size_t)h * kD + c) * 4);
+    }
+    __syncthreads();
+
     for (int c0 = 0; c0 < T; c0 += kChunk) {
         const int L = min(kChunk, T - c0);
 
@@ -206,33 +215,61 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             KDA_LANE_IDS();
             const bool valid = t < L;
             const int tau = t0 + c0 + t;  // packed row of the token
-            const float beta = valid ? sigm(bf2f(a.b[(size_t)tau * H + h])) : 0.0f;
+            // All raw loads first, branch-free so that they are all in flight together: rows
+            // tau-3 .. tau of this lane's 32 channels of q, k, v and its z row.  Rows are
+            // clamped into the sequence so every address is valid; rows before the sequence
+            // start are replaced by the carried window below, padding tokens are zeroed.
+            const int tauc = valid ? tau : t0;
+            uint4 raw[3][4][4];  // [block q,k,v][piece][row tau-3+r]
+            uint4 zraw[4];
+#pragma unroll
+            for (int blk = 0; blk < 3; ++blk)
+#pragma unroll
+                for (int pc = 0; pc < 4; ++pc)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int tok = max(tauc - 3 + r, t0);
+                        raw[blk][pc][r] = *reinterpret_cast<const uint4 *>(X[blk] + (size_t)tok * HD +
+                                                                            (size_t)h * kD + 32 * lg + 8 * pc);
+                    }
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc)
+                zraw[pc] = *reinterpret_cast<const uint4 *>(a.z + (size_t)tauc * HD + (size_t)h * kD + 32 * lg + 8 * pc);
+            const float braw = bf2f(a.b[(size_t)tauc * H + h]);
+            const float beta = valid ? sigm(braw) : 0.0f;
+            const bool head_of_seq = c0 == 0 && t < 3;  // rows before the sequence start
             // SiLU(ShortConv4(x)) of the 8 channels 32lg + 8pc .. +7 of block blk (0 q, 1 k, 2 v)
             auto conv_piece = [&](const int blk, const int pc, float *u) {
                 const int cb0 = 32 * lg + 8 * pc;
                 float xr[4][8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int tok = tau - 3 + r;
-                    if (!valid) {
+                    const uint32_t wv[4] = {raw[blk][pc][r].x, raw[blk][pc][r].y, raw[blk][pc][r].z,
+                                            raw[blk][pc][r].w};
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) xr[r][j] = 0.f;
-                    } else if (tok >= t0) {
-                        load8_bf16(X[blk] + (size_t)tok * HD + (size_t)h * kD + cb0, xr[r]);
-                    } else {
-                        const int p = tok - t0 + 3;  // slot of the carried window, 0..2
+                    for (int j = 0; j < 4; ++j) {
+                        xr[r][2 * j] = __uint_as_float(wv[j] << 16);
+                        xr[r][2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
+                    }
+                }
+                if (head_of_seq) {
 #pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            xr[r][j] = a.initial_conv_state
-                                           ? a.initial_conv_state[conv_seq +
-                                                                  ((size_t)blk * HD + (size_t)h * kD + cb0 + j) * 3 + p]
-                                           : 0.f;
+                    for (int r = 0; r < 3; ++r) {
+                        const int tok = tau - 3 + r;
+                        if (tok < t0) {
+                            const int p = tok - t0 + 3;  // slot of the carried window, 0..2
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                                xr[r][j] = a.initial_conv_state
+                                               ? a.initial_conv_state[conv_seq +
+                                                                      ((size_t)blk * HD + (size_t)h * kD + cb0 + j) * 3 + p]
+                                               : 0.f;
+                        }
                     }
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float4 cw = *reinterpret_cast<const float4 *>(
-                        a.conv_w + ((size_t)blk * HD + (size_t)h * kD + cb0 + j) * 4);
+                    const float4 cw = *reinterpret_cast<const float4 *>(sConvW + (blk * kD + cb0 + j) * 4);
                     const float y = cw.x * xr[0][j] + cw.y * xr[1][j] + cw.z * xr[2][j] + cw.w * xr[3][j];
                     u[j] = valid ? y * sigm(y) : 0.f;
                 }
@@ -249,7 +286,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     sVtHi[sw64(32 * lg + 8 * pc + j, t)] = hi;
                     sVtLo[sw64(32 * lg + 8 * pc + j, t)] = (__bf16)(bv - (float)hi);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
             // q, k parked in LDS until their norms are known (each lane reads back only what
             // it wrote), and their sums of squares
@@ -269,7 +305,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 for (int j = 0; j < 8; ++j) ssk += u[j] * u[j];
                 *reinterpret_cast<float4 *>(dk) = make_float4(u[0], u[1], u[2], u[3]);
                 *reinterpret_cast<float4 *>(dk + 4) = make_float4(u[4], u[5], u[6], u[7]);
-                __builtin_amdgcn_sched_barrier(0);
             }
             // L2 norms over the 4 lanes that hold this token's 128 channels
             ssq += __shfl_xor(ssq, 16, 64);
@@ -283,8 +318,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc) {
                 const int cb0 = 32 * lg + 8 * pc;
-                float zz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (valid) load8_bf16(a.z + (size_t)tau * HD + (size_t)h * kD + cb0, zz);
+                const uint32_t zw[4] = {zraw[pc].x, zraw[pc].y, zraw[pc].z, zraw[pc].w};
+                float zz[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    zz[2 * j] = __uint_as_float(zw[j] << 16);
+                    zz[2 * j + 1] = __uint_as_float(zw[j] & 0xffff0000u);
+                }
                 float cbv[8], uq8[8], uk8[8];
                 lds_read8(sUq + t * CB_LD + cb0, uq8);
                 lds_read8(sUk + t * CB_LD + cb0, uk8);
@@ -304,7 +344,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 float *dst = sCB + t * CB_LD + cb0;  // overwrites this lane's own q slot
                 *reinterpret_cast<float4 *>(dst) = make_float4(cbv[0], cbv[1], cbv[2], cbv[3]);
                 *reinterpret_cast<float4 *>(dst + 4) = make_float4(cbv[4], cbv[5], cbv[6], cbv[7]);
-                __builtin_amdgcn_sched_barrier(0);
             }
             if (lg == 0) sBeta[t] = beta;
         }
@@ -534,6 +573,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ================= phase 5: state side =================
+        // (the epilogue's output-gate logits are loaded now, to arrive during the MFMAs)
+        uint4 graw[4];
+        {
+            int tid_ = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid_));
+            const int tok = min(tid_ >> 2, L - 1);
+            const uint16_t *gp = a.g + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + 32 * (tid_ & 3);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) graw[j] = *reinterpret_cast<const uint4 *>(gp + 8 * j);
+        }
         {
             KDA_LANE_IDS();
             bf16x8 Sh[4][2];  // S0 as the B operand of key contractions (hi part)
@@ -655,7 +704,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int j = 0; j < 32; j += 8) {
                     float g8[8];
-                    load8_bf16(a.g + row + j, g8);
+                    const uint32_t gw[4] = {graw[j / 8].x, graw[j / 8].y, graw[j / 8].z, graw[j / 8].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        g8[2 * e] = __uint_as_float(gw[e] << 16);
+                        g8[2 * e + 1] = __uint_as_float(gw[e] & 0xffff0000u);
+                    }
                     const float4 w0 = *reinterpret_cast<const float4 *>(a.norm_w + v0 + j);
                     const float4 w1 = *reinterpret_cast<const float4 *>(a.norm_w + v0 + j + 4);
                     float4 y0, y1;

@@ -30,6 +30,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 // sum over groups of W consecutive lanes (W a power of two <= 64)
@@ -53,11 +55,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const size_t HD = (size_t)H * kD;
 
     // ---- 1. issue the state reads (64 floats per lane) ----
+    // (nontemporal: the state is streamed once per step and must not evict the small,
+    //  reused per-head parameters from the caches)
     float *S = a.state + (size_t)bh * kD * kD;
-    float4 s[16];
+    f32x4 s[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-        s[j] = *reinterpret_cast<const float4 *>(S + (rg + 8 * j) * kD + 4 * cg);
+        s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (rg + 8 * j) * kD + 4 * cg));
 
     __shared__ float sh_kh[kD];     // normalised k
     __shared__ float sh_ak[kD];     // alpha * k
@@ -166,12 +170,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int j = 0; j < 16; ++j) {
         const int r = rg + 8 * j;
         const float al = sh_alpha[r], kr = sh_kh[r];
-        float4 n;
+        f32x4 n;
         n.x = al * s[j].x + kr * u[0];
         n.y = al * s[j].y + kr * u[1];
         n.z = al * s[j].z + kr * u[2];
         n.w = al * s[j].w + kr * u[3];
-        *reinterpret_cast<float4 *>(S + r * kD + 4 * cg) = n;
+        __builtin_nontemporal_store(n, reinterpret_cast<f32x4 *>(S + r * kD + 4 * cg));
     }
 
     // ---- 5. out = sigmoid(g) * RMSNorm(o) (lanes 0..31 of wave 0 hold all 128 columns) ----

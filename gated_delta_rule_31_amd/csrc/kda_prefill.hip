@@ -77,7 +77,8 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
 }
 
 __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
-__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// sigmoid with the hardware reciprocal (about 1 ulp) instead of an IEEE division
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
 #pragma unroll
@@ -198,10 +199,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     }
     }
 
+    // the conv taps of this head's 384 channels, and its initial conv windows (zeros if
+    // none): these sit in sPair/sExpRef, which the first chunk's tables step overwrites
+    // only after the last read of the windows (phase 1 of chunk 0)
+    float *sWin0 = sPair;  // [3*128][3]
     for (int i = threadIdx.x; i < 3 * kD; i += kThreads) {
         const int blk = i >> 7, c = i & 127;
-        *reinterpret_cast<float4 *>(sConvW + i * 4) =
-            *reinterpret_cast<const float4 *>(a.conv_w + ((size_t)blk * HD + (size_t)h * kD + c) * 4);
+        const size_t ch = (size_t)blk * HD + (size_t)h * kD + c;
+        *reinterpret_cast<float4 *>(sConvW + i * 4) = *reinterpret_cast<const float4 *>(a.conv_w + ch * 4);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            sWin0[i * 3 + j] = a.initial_conv_state ? a.initial_conv_state[conv_seq + ch * 3 + j] : 0.f;
     }
     __syncthreads();
 
@@ -219,22 +227,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             // tau-3 .. tau of this lane's 32 channels of q, k, v and its z row.  Rows are
             // clamped into the sequence so every address is valid; rows before the sequence
             // start are replaced by the carried window below, padding tokens are zeroed.
-            const int tauc = valid ? tau : t0;
+            const int tauc = valid ? tau : t0 + c0;  // a padding lane reads the chunk's first row
+            // uniform base of the rows this chunk may touch; lane offsets stay 32-bit
+            const int rbase = max(t0 + c0 - 3, t0);
+            const size_t ebase = (size_t)rbase * HD + (size_t)h * kD;
             uint4 raw[3][4][4];  // [block q,k,v][piece][row tau-3+r]
             uint4 zraw[4];
 #pragma unroll
-            for (int blk = 0; blk < 3; ++blk)
+            for (int blk = 0; blk < 3; ++blk) {
+                const uint16_t *base = X[blk] + ebase;
 #pragma unroll
                 for (int pc = 0; pc < 4; ++pc)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int tok = max(tauc - 3 + r, t0);
-                        raw[blk][pc][r] = *reinterpret_cast<const uint4 *>(X[blk] + (size_t)tok * HD +
-                                                                            (size_t)h * kD + 32 * lg + 8 * pc);
+                        const uint32_t tok = (uint32_t)(max(tauc - 3 + r, t0) - rbase);
+                        raw[blk][pc][r] =
+                            *reinterpret_cast<const uint4 *>(base + (tok * (uint32_t)HD + 32u * lg + 8u * pc));
                     }
+            }
+            {
+                const uint16_t *base = a.z + ebase;
+                const uint32_t tok = (uint32_t)(tauc - rbase);
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc)
-                zraw[pc] = *reinterpret_cast<const uint4 *>(a.z + (size_t)tauc * HD + (size_t)h * kD + 32 * lg + 8 * pc);
+                for (int pc = 0; pc < 4; ++pc)
+                    zraw[pc] = *reinterpret_cast<const uint4 *>(base + (tok * (uint32_t)HD + 32u * lg + 8u * pc));
+            }
             const float braw = bf2f(a.b[(size_t)tauc * H + h]);
             const float beta = valid ? sigm(braw) : 0.0f;
             const bool head_of_seq = c0 == 0 && t < 3;  // rows before the sequence start
@@ -259,11 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                         if (tok < t0) {
                             const int p = tok - t0 + 3;  // slot of the carried window, 0..2
 #pragma unroll
-                            for (int j = 0; j < 8; ++j)
-                                xr[r][j] = a.initial_conv_state
-                                               ? a.initial_conv_state[conv_seq +
-                                                                      ((size_t)blk * HD + (size_t)h * kD + cb0 + j) * 3 + p]
-                                               : 0.f;
+                            for (int j = 0; j < 8; ++j) xr[r][j] = sWin0[(blk * kD + cb0 + j) * 3 + p];
                         }
                     }
                 }

@@ -1,10 +1,10 @@
 // kda_prefill.hip -- chunked varlen KDA prefill on gfx950 (bf16 MFMA, fp32 state).
 //
-// One workgroup (4 waves) per (sequence, head) walks the sequence in chunks of 64 tokens
-// and carries the 128x128 fp32 state in MFMA accumulator registers.  Every step of the
-// header comment "KDA per-head recurrence" (page "colibri/c/kimi_k3.c") is fused: conv
-// with the carried window, SiLU, L2 norms, gates, the chunked state update and readout,
-// the gated RMSNorm and the final state / conv window write.
+// One workgroup (8 waves, two per SIMD) per (sequence, head) walks the sequence in
+// chunks of 64 tokens and carries the 128x128 fp32 state in MFMA accumulator registers.
+// Every step of the header comment "KDA per-head recurrence" (page "colibri/c/kimi_k3.c")
+// is fused: conv with the carried window, SiLU, L2 norms, gates, the chunked state update
+// and readout, the gated RMSNorm and the final state / conv window write.
 //
 // Chunk algebra (exact rewrite of the token recurrence; G_t = sum_{s<=t} gk_s per key
 // channel, chunk-local):
@@ -19,20 +19,22 @@
 // |gk| < 5), so no factor leaves the fp32 / bf16 exponent range.
 //
 // Precision: bf16 MFMA operands with fp32 accumulation; T is computed in fp32.  The
-// products whose operands were measured to decide the error of the fp32 state and of
-// the normalised output use a hi+lo bf16 split of those operands (3 MFMAs instead of
-// 1): P (both operands), beta*v in U', U in P.U and K_end^T U, and K_end.
+// products whose operands decide the error of the fp32 state and of the normalised
+// output use a hi+lo bf16 split of those operands (3 MFMAs instead of 1): P (both
+// operands), beta*v in U', U in P.U and K_end^T U, and K_end.
 //
-// Layout tricks.  Wave w owns value columns 32w..32w+31 of the state for all 128 keys:
-// 16 accumulator tiles.  Inside each 32-key block the two 16-row tiles interleave their
-// rows (tile x, row m -> key 32P + 8(m/4) + 4x + m%4), so that a lane's 8 accumulator
-// values of one column are 8 consecutive keys: exactly the B-operand layout of a
+// Work split.  Wave w (0..7) owns value columns 16w..16w+15 of the state for all 128
+// keys (8 accumulator tiles).  Inside each 32-key block the two 16-row tiles interleave
+// their rows (tile x, row m -> key 32P + 8(m/4) + 4x + m%4), so that a lane's 8
+// accumulator values of one column are 8 consecutive keys: the B-operand layout of a
 // K = 32 MFMA.  The state therefore feeds W S0 and (q e^G) S0 straight from registers.
 // U uses the same interleave over tokens, so it feeds P U and K_end^T U the same way.
 //
-// In the prologue, lane (wave w, lane l) owns token 16w + l%16 and the 32 channels
-// 32(l/16) .. 32(l/16)+31: these are also the A-operand rows/K-slices of block row w of
-// A and P, which wave w therefore computes from its own registers.
+// In the prologue wave w handles sub-chunk I = w % 4 (tokens 16I..16I+15) and channel
+// half w / 4; lane l owns token 16I + l%16 and 16 channels 64(w/4) + 16(l/16) + 0..15.
+// Those are also the A-operand rows and K-slices of block row I of A and P over that
+// channel half, so each wave computes its half of block row I from its own registers;
+// the two halves are added through LDS.
 
 #include "kda_internal.hpp"
 
@@ -42,18 +44,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 // ---- LDS map (bytes).  Regions are reused once their first tenant is dead. ----
 constexpr int OFF_R1 = 0;        // sCB fp32 [64][132]          -> sKe hi/lo bf16 [128][64] x2
-constexpr int OFF_R2 = 33792;    // sVt hi/lo bf16 [128][64] x2 (beta*v, transposed)
+constexpr int OFF_R2 = 33792;    // sVt hi/lo bf16 [128][64] x2 -> sO fp32 [64][128]
 constexpr int OFF_R3 = 66560;    // sWr bf16 [128][64]          (beta k e^G, transposed)
 constexpr int OFF_R4 = 82944;    // sA fp32 [64][68]            -> sW bf16 [64][128]
 constexpr int OFF_R5 = 100352;   // sP fp32 [64][68]
 constexpr int OFF_R6 = 117760;   // sT fp32 [64][68]            -> sQe bf16 [64][128]
 constexpr int OFF_R7 = 135168;   // sTb bf16 [64][64]
 constexpr int OFF_TAB = 143360;  // small fp32 tables
-constexpr int kTabFloats = 512 + 640 + 768 + 512 + 512 + 128 + 64;
+constexpr int kTabFloats = 512 + 640 + 768 + 512 + 512 + 128 + 64 + 256;
 constexpr int OFF_CW = OFF_TAB + kTabFloats * 4;  // conv taps of this head, fp32 [3][128][4]
 constexpr int kLdsBytes = OFF_CW + 3 * 128 * 4 * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
@@ -94,8 +96,7 @@ __device__ __forceinline__ bf16x8 to_bf8(const float *x) {
     for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
     return r;
 }
-__device__ __forceinline__ void load8_bf16(const uint16_t *p, float *x) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+__device__ __forceinline__ void unpack8(const uint4 &u, float *x) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -108,6 +109,10 @@ __device__ __forceinline__ void lds_read8(const float *p, float *x) {
     const float4 b = *reinterpret_cast<const float4 *>(p + 4);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void lds_write8(float *p, const float *x) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 // inclusive prefix sum over the 16 lanes of a DPP row (lanes 16g .. 16g+15)
 // (DPP row_shr:n moves lane i-n of the same 16-lane row into lane i; lanes without a
@@ -124,23 +129,27 @@ __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2
 // Lane coordinates, re-derived at the start of every phase from an opaque copy of the
 // thread id.  Without this the compiler hoists every lane-dependent LDS address of the
 // chunk loop out of the loop and keeps (or spills) hundreds of them across it.
+//   w: wave (uniform), lr: lane % 16, lg: lane / 16, sub: sub-chunk of the wave's
+//   prologue tokens, half: its channel half, t: its prologue token.
 #define KDA_LANE_IDS()                                         \
     int tid_ = (int)threadIdx.x;                               \
     asm volatile("" : "+v"(tid_));                             \
     const int w = __builtin_amdgcn_readfirstlane(tid_ >> 6);   \
     const int lr = tid_ & 15;                                  \
     const int lg = (tid_ >> 4) & 3;                            \
-    const int t = 16 * w + lr;                                 \
+    const int sub = w & 3;                                     \
+    const int half = w >> 2;                                   \
+    const int t = 16 * sub + lr;                               \
     (void)w;                                                   \
     (void)lr;                                                  \
     (void)lg;                                                  \
+    (void)sub;                                                 \
+    (void)half;                                                \
     (void)t
 
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     float *sCB = reinterpret_cast<float *>(smem + OFF_R1);              // [64][132] k e^{r - G}
-    float *sUq = sCB;                                                    // [64][132] q before norm
-    float *sUk = reinterpret_cast<float *>(smem + OFF_R4);              // [64][132] k before norm
     __bf16 *sKeHi = reinterpret_cast<__bf16 *>(smem + OFF_R1);          // [128][64] K_end^T
     __bf16 *sKeLo = sKeHi + 128 * 64;
     __bf16 *sVtHi = reinterpret_cast<__bf16 *>(smem + OFF_R2);          // [128][64] (beta v)^T
@@ -153,13 +162,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     float *sT = reinterpret_cast<float *>(smem + OFF_R6);               // [64][68]
     __bf16 *sQe = reinterpret_cast<__bf16 *>(smem + OFF_R6);            // [64][128] q e^G
     __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + OFF_R7);            // [64][64]
-    float *sTot = reinterpret_cast<float *>(smem + OFF_TAB);  // [4][128] per-wave gk sums
+    float *sTot = reinterpret_cast<float *>(smem + OFF_TAB);  // [4][128] per-sub-chunk gk sums
     float *sRef = sTot + 512;                                  // [5][128] r_0..r_3, G_end
     float *sPair = sRef + 640;                                 // [6][128] e^{r_I - r_J}, J < I
     float *sExpRef = sPair + 768;                              // [4][128] e^{r_I}
     float *sEndRef = sExpRef + 512;                            // [4][128] e^{G_end - r_I}
     float *sExpEnd = sEndRef + 512;                            // [128]    e^{G_end}
     float *sBeta = sExpEnd + 128;                              // [64]
+    float *sNorm = sBeta + 64;                                 // [2 halves][q,k][64] sums of squares
     float *sConvW = reinterpret_cast<float *>(smem + OFF_CW);  // [3][128][4] taps, oldest first
 
     const int H = a.c.H;
@@ -180,8 +190,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const size_t conv_seq = (size_t)seq * 3 * HD * 3;  // this sequence's conv windows
     const uint16_t *X[3] = {a.q, a.k, a.v};
 
-    // ---- the state: S[P][x][nt][i] = S[key 32P + 8lg + 4x + i][value 32w + 16nt + lr] ----
-    f32x4 S[4][2][2];
+    // ---- the state: S[P][x][i] = S[key 32P + 8lg + 4x + i][value 16w + lr] ----
+    f32x4 S[4][2];
     {
         KDA_LANE_IDS();
         const float *S0 = a.initial_state ? a.initial_state + ((size_t)seq * H + h) * kD * kD : nullptr;
@@ -190,13 +200,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = 32 * P + 8 * lg + 4 * x + i;
-                        const int val = 32 * w + 16 * nt + lr;
-                        S[P][x][nt][i] = S0 ? S0[key * kD + val] : 0.0f;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 32 * P + 8 * lg + 4 * x + i;
+                    S[P][x][i] = S0 ? S0[key * kD + 16 * w + lr] : 0.0f;
+                }
     }
 
     // the conv taps of this head's 384 channels, and its initial conv windows (zeros if
@@ -216,59 +223,52 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     for (int c0 = 0; c0 < T; c0 += kChunk) {
         const int L = min(kChunk, T - c0);
 
-        // ================= phase 1: conv, SiLU, norms, gates =================
-        // lane: token t = 16w + lr of the chunk, channels 32lg .. 32lg+31
-        float qr[32], kr[32], cbk[32];  // q e^{G-r_w}, k e^{G-r_w}, k e^{r_w-G} (normalised q, k)
+        // ================= phase 1: conv, SiLU, partial norms, gates =================
+        float uq[16], uk[16], gs[16];  // q, k before the norm; G_t - r_sub of the 16 channels
+        float beta;
         {
             KDA_LANE_IDS();
             const bool valid = t < L;
-            const int tau = t0 + c0 + t;  // packed row of the token
-            // All raw loads first, branch-free so that they are all in flight together: rows
-            // tau-3 .. tau of this lane's 32 channels of q, k, v and its z row.  Rows are
-            // clamped into the sequence so every address is valid; rows before the sequence
-            // start are replaced by the carried window below, padding tokens are zeroed.
-            const int tauc = valid ? tau : t0 + c0;  // a padding lane reads the chunk's first row
+            const int tau = t0 + c0 + t;                // packed row of the token
+            const int tauc = valid ? tau : t0 + c0;     // a padding lane reads the chunk's first row
+            const int cbase = 64 * half + 16 * lg;      // first of this lane's 16 channels
             // uniform base of the rows this chunk may touch; lane offsets stay 32-bit
             const int rbase = max(t0 + c0 - 3, t0);
             const size_t ebase = (size_t)rbase * HD + (size_t)h * kD;
-            uint4 raw[3][4][4];  // [block q,k,v][piece][row tau-3+r]
-            uint4 zraw[4];
+            // all raw loads first, branch-free, so that they are in flight together: rows
+            // tau-3 .. tau of q, k, v (clamped into the sequence; earlier rows come from the
+            // carried window below) and the z row
+            uint4 raw[3][2][4];  // [block q,k,v][piece][row tau-3+r]
+            uint4 zraw[2];
 #pragma unroll
             for (int blk = 0; blk < 3; ++blk) {
                 const uint16_t *base = X[blk] + ebase;
 #pragma unroll
-                for (int pc = 0; pc < 4; ++pc)
+                for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const uint32_t tok = (uint32_t)(max(tauc - 3 + r, t0) - rbase);
                         raw[blk][pc][r] =
-                            *reinterpret_cast<const uint4 *>(base + (tok * (uint32_t)HD + 32u * lg + 8u * pc));
+                            *reinterpret_cast<const uint4 *>(base + (tok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
                     }
             }
             {
                 const uint16_t *base = a.z + ebase;
                 const uint32_t tok = (uint32_t)(tauc - rbase);
 #pragma unroll
-                for (int pc = 0; pc < 4; ++pc)
-                    zraw[pc] = *reinterpret_cast<const uint4 *>(base + (tok * (uint32_t)HD + 32u * lg + 8u * pc));
+                for (int pc = 0; pc < 2; ++pc)
+                    zraw[pc] = *reinterpret_cast<const uint4 *>(base + (tok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
             }
             const float braw = bf2f(a.b[(size_t)tauc * H + h]);
-            const float beta = valid ? sigm(braw) : 0.0f;
+            beta = valid ? sigm(braw) : 0.0f;
             const bool head_of_seq = c0 == 0 && t < 3;  // rows before the sequence start
-            // SiLU(ShortConv4(x)) of the 8 channels 32lg + 8pc .. +7 of block blk (0 q, 1 k, 2 v)
+
+            // SiLU(ShortConv4(x)) of the 8 channels cbase + 8pc .. +7 of block blk
             auto conv_piece = [&](const int blk, const int pc, float *u) {
-                const int cb0 = 32 * lg + 8 * pc;
+                const int cb0 = cbase + 8 * pc;
                 float xr[4][8];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t wv[4] = {raw[blk][pc][r].x, raw[blk][pc][r].y, raw[blk][pc][r].z,
-                                            raw[blk][pc][r].w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        xr[r][2 * j] = __uint_as_float(wv[j] << 16);
-                        xr[r][2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
-                    }
-                }
+                for (int r = 0; r < 4; ++r) unpack8(raw[blk][pc][r], xr[r]);
                 if (head_of_seq) {
 #pragma unroll
                     for (int r = 0; r < 3; ++r) {
@@ -289,123 +289,122 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             };
             // v: beta * v, hi/lo, transposed into sVt
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
+            for (int pc = 0; pc < 2; ++pc) {
                 float u[8];
                 conv_piece(2, pc, u);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float bv = beta * u[j];
                     const __bf16 hi = (__bf16)bv;
-                    sVtHi[sw64(32 * lg + 8 * pc + j, t)] = hi;
-                    sVtLo[sw64(32 * lg + 8 * pc + j, t)] = (__bf16)(bv - (float)hi);
+                    sVtHi[sw64(cbase + 8 * pc + j, t)] = hi;
+                    sVtLo[sw64(cbase + 8 * pc + j, t)] = (__bf16)(bv - (float)hi);
                 }
             }
-            // q, k parked in LDS until their norms are known (each lane reads back only what
-            // it wrote), and their sums of squares
+            // q, k and their partial sums of squares over this wave's 64 channels
             float ssq = 0.f, ssk = 0.f;
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                float u[8];
-                float *dq = sUq + t * CB_LD + 32 * lg + 8 * pc;
-                float *dk = sUk + t * CB_LD + 32 * lg + 8 * pc;
-                conv_piece(0, pc, u);
+            for (int pc = 0; pc < 2; ++pc) {
+                conv_piece(0, pc, uq + 8 * pc);
+                conv_piece(1, pc, uk + 8 * pc);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) ssq += u[j] * u[j];
-                *reinterpret_cast<float4 *>(dq) = make_float4(u[0], u[1], u[2], u[3]);
-                *reinterpret_cast<float4 *>(dq + 4) = make_float4(u[4], u[5], u[6], u[7]);
-                conv_piece(1, pc, u);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ssk += u[j] * u[j];
-                *reinterpret_cast<float4 *>(dk) = make_float4(u[0], u[1], u[2], u[3]);
-                *reinterpret_cast<float4 *>(dk + 4) = make_float4(u[4], u[5], u[6], u[7]);
+                for (int j = 0; j < 8; ++j) {
+                    ssq += uq[8 * pc + j] * uq[8 * pc + j];
+                    ssk += uk[8 * pc + j] * uk[8 * pc + j];
+                }
             }
-            // L2 norms over the 4 lanes that hold this token's 128 channels
             ssq += __shfl_xor(ssq, 16, 64);
             ssq += __shfl_xor(ssq, 32, 64);
             ssk += __shfl_xor(ssk, 16, 64);
             ssk += __shfl_xor(ssk, 32, 64);
-            const float inv_q = qscale / sqrtf(ssq + l2eps);
-            const float inv_k = 1.0f / sqrtf(ssk + l2eps);
-            // decay gate gk = gmin * sigmoid(exp(A_log) * (z + dt_bias)) and its cumulative sum
-            // over the wave's 16 tokens (G_t - r_w); the operand rows built from it
+            if (lg == 0) {
+                sNorm[half * 128 + t] = ssq;
+                sNorm[half * 128 + 64 + t] = ssk;
+            }
+            // decay gate gk = gmin * sigmoid(exp(A_log) * (z + dt_bias)) and its cumulative
+            // sum over the sub-chunk's 16 tokens (= G_t - r_sub)
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                const int cb0 = 32 * lg + 8 * pc;
-                const uint32_t zw[4] = {zraw[pc].x, zraw[pc].y, zraw[pc].z, zraw[pc].w};
+            for (int pc = 0; pc < 2; ++pc) {
                 float zz[8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    zz[2 * j] = __uint_as_float(zw[j] << 16);
-                    zz[2 * j + 1] = __uint_as_float(zw[j] & 0xffff0000u);
-                }
-                float cbv[8], uq8[8], uk8[8];
-                lds_read8(sUq + t * CB_LD + cb0, uq8);
-                lds_read8(sUk + t * CB_LD + cb0, uk8);
+                unpack8(zraw[pc], zz);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    float g = valid ? gmin * sigm(rate * (zz[j] + a.dt_bias[(size_t)h * kD + cb0 + j])) : 0.f;
+                    const int c = cbase + 8 * pc + j;
+                    float g = valid ? gmin * sigm(rate * (zz[j] + a.dt_bias[(size_t)h * kD + c])) : 0.f;
                     g = row_scan16(g);
-                    if (lr == 15) sTot[w * 128 + cb0 + j] = g;
-                    const float rf = __expf(g);
-                    const float cf = __expf(-g);
-                    const float kh = uk8[j] * inv_k;
-                    qr[8 * pc + j] = uq8[j] * inv_q * rf;
-                    kr[8 * pc + j] = kh * rf;
-                    cbv[j] = kh * cf;
-                    cbk[8 * pc + j] = cbv[j];
+                    if (lr == 15) sTot[sub * 128 + c] = g;
+                    gs[8 * pc + j] = g;
                 }
-                float *dst = sCB + t * CB_LD + cb0;  // overwrites this lane's own q slot
-                *reinterpret_cast<float4 *>(dst) = make_float4(cbv[0], cbv[1], cbv[2], cbv[3]);
-                *reinterpret_cast<float4 *>(dst + 4) = make_float4(cbv[4], cbv[5], cbv[6], cbv[7]);
             }
-            if (lg == 0) sBeta[t] = beta;
+            if (lg == 0 && half == 0) sBeta[t] = beta;
         }
         __syncthreads();
 
-        // ---- per-chunk channel tables: sub-chunk references and their exponentials ----
+        // ---- per-chunk channel tables (threads 0..255), and this lane's operand rows ----
+        float qr[16], kr[16], cbk[16];  // q e^{G-r}, k e^{G-r}, k e^{r-G} of the normalised q, k
         {
             const int tid = threadIdx.x;
-            const int c = tid & 127;
-            float r[5];
-            r[0] = 0.f;
-            r[1] = sTot[c];
-            r[2] = r[1] + sTot[128 + c];
-            r[3] = r[2] + sTot[256 + c];
-            r[4] = r[3] + sTot[384 + c];
-            if (tid < 128) {
+            if (tid < 256) {
+                const int c = tid & 127;
+                float r[5];
+                r[0] = 0.f;
+                r[1] = sTot[c];
+                r[2] = r[1] + sTot[128 + c];
+                r[3] = r[2] + sTot[256 + c];
+                r[4] = r[3] + sTot[384 + c];
+                if (tid < 128) {
 #pragma unroll
-                for (int I = 0; I < 5; ++I) sRef[I * 128 + c] = r[I];
+                    for (int I = 0; I < 5; ++I) sRef[I * 128 + c] = r[I];
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    sExpRef[I * 128 + c] = __expf(r[I]);
-                    sEndRef[I * 128 + c] = __expf(r[4] - r[I]);
+                    for (int I = 0; I < 4; ++I) {
+                        sExpRef[I * 128 + c] = __expf(r[I]);
+                        sEndRef[I * 128 + c] = __expf(r[4] - r[I]);
+                    }
+                    sExpEnd[c] = __expf(r[4]);
+                } else {
+#pragma unroll
+                    for (int I = 1; I < 4; ++I)
+#pragma unroll
+                        for (int J = 0; J < I; ++J) sPair[pair_index(I, J) * 128 + c] = __expf(r[I] - r[J]);
                 }
-                sExpEnd[c] = __expf(r[4]);
-            } else {
-#pragma unroll
-                for (int I = 1; I < 4; ++I)
-#pragma unroll
-                    for (int J = 0; J < I; ++J) sPair[pair_index(I, J) * 128 + c] = __expf(r[I] - r[J]);
             }
+        }
+        {
+            KDA_LANE_IDS();
+            const int cbase = 64 * half + 16 * lg;
+            const float ssq = sNorm[t] + sNorm[128 + t];
+            const float ssk = sNorm[64 + t] + sNorm[192 + t];
+            const float inv_q = qscale / sqrtf(ssq + l2eps);
+            const float inv_k = 1.0f / sqrtf(ssk + l2eps);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float rf = __expf(gs[j]);
+                const float cf = __expf(-gs[j]);
+                const float kh = uk[j] * inv_k;
+                qr[j] = uq[j] * inv_q * rf;
+                kr[j] = kh * rf;
+                cbk[j] = kh * cf;
+            }
+            lds_write8(sCB + t * CB_LD + cbase, cbk);
+            lds_write8(sCB + t * CB_LD + cbase + 8, cbk + 8);
         }
         __syncthreads();
 
-        // ---- rows that need the tables; MFMA operands of block row w ----
-        bf16x8 ak[4], aqh[4], aql[4], qe8[4];  // k e^{G-r}, q e^{G-r} (hi/lo), q e^G
-        float ke[32];                            // K_end = k e^{G_end - G}
+        // ---- rows that need the tables; MFMA operands of block row `sub` ----
+        bf16x8 ak[2], aqh[2], aql[2], qe8[2];  // k e^{G-r}, q e^{G-r} (hi/lo), q e^G
+        float ke[16];                            // K_end = k e^{G_end - G}
         {
             KDA_LANE_IDS();
-            const float beta = sBeta[t];
+            const int cbase = 64 * half + 16 * lg;
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                const int cb0 = 32 * lg + 8 * pc;
+            for (int pc = 0; pc < 2; ++pc) {
                 float qe[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float er = sExpRef[w * 128 + cb0 + j];
-                    sWr[sw64(cb0 + j, t)] = (__bf16)(beta * kr[8 * pc + j] * er);
+                    const int c = cbase + 8 * pc + j;
+                    const float er = sExpRef[sub * 128 + c];
+                    sWr[sw64(c, t)] = (__bf16)(beta * kr[8 * pc + j] * er);
                     qe[j] = qr[8 * pc + j] * er;
-                    ke[8 * pc + j] = cbk[8 * pc + j] * sEndRef[w * 128 + cb0 + j];
+                    ke[8 * pc + j] = cbk[8 * pc + j] * sEndRef[sub * 128 + c];
                 }
                 qe8[pc] = to_bf8(qe);
                 ak[pc] = to_bf8(kr + 8 * pc);
@@ -413,66 +412,90 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             }
         }
 
-        // ================= phase 2: blocks (w, J <= w) of A and P =================
+        // ================= phase 2: block row `sub` of A and P over this channel half =====
+        // K-step ks is the lane's piece ks: channels 64 half + 16 lg + 8 ks .. +7 (both
+        // operands use the same channel order, so the contraction is over the half).  The
+        // channel-half-1 waves park their partial tiles in regions 6-7 (free until phase 3);
+        // the half-0 waves add them after the barrier (LDS float atomics are far slower).
+        float *sPart = reinterpret_cast<float *>(smem + OFF_R6);  // [10 blocks][A,P][64 lanes][4]
+        f32x4 accA[4], accP[4];
         {
             KDA_LANE_IDS();
+            const int lane = tid_ & 63;
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
-                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-                if (J <= w) {
+                accA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (J > sub) continue;
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const int cb0 = 32 * lg + 8 * ks;
-                        float col[8];
-                        lds_read8(sCB + (16 * J + lr) * CB_LD + cb0, col);
-                        if (J < w) {
-                            float pf[8];
-                            lds_read8(sPair + pair_index(w, J) * 128 + cb0, pf);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int cb0 = 64 * half + 16 * lg + 8 * ks;
+                    float col[8];
+                    lds_read8(sCB + (16 * J + lr) * CB_LD + cb0, col);
+                    if (J < sub) {
+                        float pf[8];
+                        lds_read8(sPair + pair_index(sub, J) * 128 + cb0, pf);
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) col[j] *= pf[j];
-                        }
-                        bf16x8 ch, cl;
-                        split8(col, ch, cl);
-                        accA = mma(ak[ks], ch, accA);
-                        accP = mma(aqh[ks], ch, accP);
-                        accP = mma(aql[ks], ch, accP);
-                        accP = mma(aqh[ks], cl, accP);
+                        for (int j = 0; j < 8; ++j) col[j] *= pf[j];
                     }
+                    bf16x8 ch, cl;
+                    split8(col, ch, cl);
+                    accA[J] = mma(ak[ks], ch, accA[J]);
+                    accP[J] = mma(aqh[ks], ch, accP[J]);
+                    accP[J] = mma(aql[ks], ch, accP[J]);
+                    accP[J] = mma(aqh[ks], cl, accP[J]);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tr = 4 * lg + i;  // row inside the 16x16 block
-                    const int trow = 16 * w + tr;
-                    float va = accA[i] * sBeta[trow];
-                    float vp = accP[i];
-                    if (J == w) {
-                        if (lr >= tr) va = 0.f;
-                        if (lr > tr) vp = 0.f;
-                    }
-                    sA[trow * F_LD + 16 * J + lr] = va;
-                    sP[trow * F_LD + 16 * J + lr] = vp;
+                if (half == 1) {
+                    const int bi = sub * (sub + 1) / 2 + J;  // block (sub, J), 0..9
+                    *reinterpret_cast<f32x4 *>(sPart + ((bi * 2 + 0) * 64 + lane) * 4) = accA[J];
+                    *reinterpret_cast<f32x4 *>(sPart + ((bi * 2 + 1) * 64 + lane) * 4) = accP[J];
                 }
             }
         }
         __syncthreads();
-
-        // sCB is dead: K_end^T, hi/lo, into region 1
         {
             KDA_LANE_IDS();
+            const int lane = tid_ & 63;
+            if (half == 0) {
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const int c = 32 * lg + j;
+                for (int J = 0; J < 4; ++J) {
+                    f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+                    if (J <= sub) {
+                        const int bi = sub * (sub + 1) / 2 + J;
+                        pa = accA[J] + *reinterpret_cast<const f32x4 *>(sPart + ((bi * 2 + 0) * 64 + lane) * 4);
+                        pp = accP[J] + *reinterpret_cast<const f32x4 *>(sPart + ((bi * 2 + 1) * 64 + lane) * 4);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tr = 4 * lg + i;  // row inside the 16x16 block
+                        const int trow = 16 * sub + tr;
+                        float va = pa[i] * sBeta[trow];
+                        float vp = pp[i];
+                        if (J == sub) {
+                            if (lr >= tr) va = 0.f;
+                            if (lr > tr) vp = 0.f;
+                        }
+                        sA[trow * F_LD + 16 * J + lr] = va;
+                        sP[trow * F_LD + 16 * J + lr] = vp;
+                    }
+                }
+            }
+            // sCB is dead: K_end^T, hi/lo, into region 1
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int c = 64 * half + 16 * lg + j;
                 const __bf16 hi = (__bf16)ke[j];
                 sKeHi[sw64(c, t)] = hi;
                 sKeLo[sw64(c, t)] = (__bf16)(ke[j] - (float)hi);
             }
         }
+        __syncthreads();
 
         // ================= phase 3: T = (I + A)^-1 in fp32 =================
-        // diagonal 16x16 blocks by forward substitution: wave w, lanes 0..15 own columns
+        // diagonal 16x16 blocks by forward substitution: waves 0..3, lanes 0..15 own columns
         {
             KDA_LANE_IDS();
-            if (lg == 0) {
+            if (w < 4 && lg == 0) {
                 float xcol[16];
 #pragma unroll
                 for (int tt = 0; tt < 16; ++tt) {
@@ -524,10 +547,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         {
             int tid_ = (int)threadIdx.x;
             asm volatile("" : "+v"(tid_));
-            const int r = tid_ >> 2;
+            const int r = tid_ >> 3;
 #pragma unroll
-            for (int cc = 0; cc < 16; ++cc) {
-                const int c = 16 * (tid_ & 3) + cc;
+            for (int cc = 0; cc < 8; ++cc) {
+                const int c = 8 * (tid_ & 7) + cc;
                 const float v = ((c >> 4) <= (r >> 4)) ? sT[r * F_LD + c] : 0.0f;
                 sTb[sw64(r, c)] = (__bf16)v;
             }
@@ -537,132 +560,111 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         {
             KDA_LANE_IDS();
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) *reinterpret_cast<bf16x8 *>(sQe + sw128(t, 32 * lg + 8 * pc)) = qe8[pc];
+            for (int pc = 0; pc < 2; ++pc)
+                *reinterpret_cast<bf16x8 *>(sQe + sw128(t, 64 * half + 16 * lg + 8 * pc)) = qe8[pc];
         }
 
         // ================= phase 4: W = T (beta k e^G) -> LDS;  U' = T (beta v) -> regs ====
-        f32x4 U[2][2][2];  // [tp][x][nt]: U[token 32tp + 8lg + 4x + i][value 32w + 16nt + lr]
+        f32x4 U[2][2];  // [tp][x]: U[token 32tp + 8lg + 4x + i][value 16w + lr]
         {
             KDA_LANE_IDS();
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
+            for (int tt = 0; tt < 4; ++tt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        if (ks == 1 && tt < 2) continue;  // T is lower triangular
-                        const bf16x8 A8 =
-                            *reinterpret_cast<const bf16x8 *>(sTb + sw64(16 * tt + lr, 32 * ks + 8 * lg));
-                        const bf16x8 B8 =
-                            *reinterpret_cast<const bf16x8 *>(sWr + sw64(32 * w + 16 * nt + lr, 32 * ks + 8 * lg));
-                        acc = mma(A8, B8, acc);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sW[sw128(16 * tt + 4 * lg + i, 32 * w + 16 * nt + lr)] = (__bf16)acc[i];
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks == 1 && tt < 2) continue;  // T is lower triangular
+                    const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sTb + sw64(16 * tt + lr, 32 * ks + 8 * lg));
+                    const bf16x8 B8 = *reinterpret_cast<const bf16x8 *>(sWr + sw64(16 * w + lr, 32 * ks + 8 * lg));
+                    acc = mma(A8, B8, acc);
                 }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sW[sw128(16 * tt + 4 * lg + i, 16 * w + lr)] = (__bf16)acc[i];
+            }
+            const int vrow = 16 * w + lr;
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-                for (int x = 0; x < 2; ++x)
+                for (int x = 0; x < 2; ++x) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const int trow = 32 * tp + 8 * (lr >> 2) + 4 * x + (lr & 3);
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                        const int trow = 32 * tp + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                        const int vrow = 32 * w + 16 * nt + lr;
-#pragma unroll
-                        for (int ks = 0; ks < 2; ++ks) {
-                            if (ks > tp) continue;
-                            const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sTb + sw64(trow, 32 * ks + 8 * lg));
-                            const bf16x8 Bh = *reinterpret_cast<const bf16x8 *>(sVtHi + sw64(vrow, 32 * ks + 8 * lg));
-                            const bf16x8 Bl = *reinterpret_cast<const bf16x8 *>(sVtLo + sw64(vrow, 32 * ks + 8 * lg));
-                            acc = mma(A8, Bh, acc);
-                            acc = mma(A8, Bl, acc);
-                        }
-                        U[tp][x][nt] = acc;
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if (ks > tp) continue;
+                        const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sTb + sw64(trow, 32 * ks + 8 * lg));
+                        const bf16x8 Bh = *reinterpret_cast<const bf16x8 *>(sVtHi + sw64(vrow, 32 * ks + 8 * lg));
+                        const bf16x8 Bl = *reinterpret_cast<const bf16x8 *>(sVtLo + sw64(vrow, 32 * ks + 8 * lg));
+                        acc = mma(A8, Bh, acc);
+                        acc = mma(A8, Bl, acc);
                     }
+                    U[tp][x] = acc;
+                }
         }
         __syncthreads();
 
         // ================= phase 5: state side =================
         // (the epilogue's output-gate logits are loaded now, to arrive during the MFMAs)
-        uint4 graw[4];
+        uint4 graw[2];
         {
             int tid_ = (int)threadIdx.x;
             asm volatile("" : "+v"(tid_));
-            const int tok = min(tid_ >> 2, L - 1);
-            const uint16_t *gp = a.g + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + 32 * (tid_ & 3);
+            const int tok = min(tid_ >> 3, L - 1);
+            const uint16_t *gp = a.g + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + 16 * (tid_ & 7);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) graw[j] = *reinterpret_cast<const uint4 *>(gp + 8 * j);
+            for (int j = 0; j < 2; ++j) graw[j] = *reinterpret_cast<const uint4 *>(gp + 8 * j);
         }
         {
             KDA_LANE_IDS();
-            bf16x8 Sh[4][2];  // S0 as the B operand of key contractions (hi part)
+            bf16x8 Sh[4];  // S0 as the B operand of key contractions (hi part)
 #pragma unroll
-            for (int P = 0; P < 4; ++P)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    float v8[8] = {S[P][0][nt][0], S[P][0][nt][1], S[P][0][nt][2], S[P][0][nt][3],
-                                   S[P][1][nt][0], S[P][1][nt][1], S[P][1][nt][2], S[P][1][nt][3]};
-                    Sh[P][nt] = to_bf8(v8);
-                }
+            for (int P = 0; P < 4; ++P) {
+                float v8[8] = {S[P][0][0], S[P][0][1], S[P][0][2], S[P][0][3],
+                               S[P][1][0], S[P][1][1], S[P][1][2], S[P][1][3]};
+                Sh[P] = to_bf8(v8);
+            }
             // U = U' - W S0
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int trow = 32 * tp + 8 * (lr >> 2) + 4 * x + (lr & 3);
+                    f32x4 ws = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        f32x4 ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int P = 0; P < 4; ++P) {
-                            const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + sw128(trow, 32 * P + 8 * lg));
-                            ws = mma(A8, Sh[P][nt], ws);
-                        }
-                        U[tp][x][nt] -= ws;
+                    for (int P = 0; P < 4; ++P) {
+                        const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + sw128(trow, 32 * P + 8 * lg));
+                        ws = mma(A8, Sh[P], ws);
                     }
+                    U[tp][x] -= ws;
                 }
-            bf16x8 Uh[2][2], Ul[2][2];  // [tp][nt]
+            bf16x8 Uh[2], Ul[2];  // [tp]
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    float v8[8] = {U[tp][0][nt][0], U[tp][0][nt][1], U[tp][0][nt][2], U[tp][0][nt][3],
-                                   U[tp][1][nt][0], U[tp][1][nt][1], U[tp][1][nt][2], U[tp][1][nt][3]};
-                    split8(v8, Uh[tp][nt], Ul[tp][nt]);
-                }
+            for (int tp = 0; tp < 2; ++tp) {
+                float v8[8] = {U[tp][0][0], U[tp][0][1], U[tp][0][2], U[tp][0][3],
+                               U[tp][1][0], U[tp][1][1], U[tp][1][2], U[tp][1][3]};
+                split8(v8, Uh[tp], Ul[tp]);
+            }
             // O = Q~ S0 + P U   (rows: token 16tt + 4lg + i), parked in region 2 (beta v is dead)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                bf16x8 Ph[2], Pl[2];
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int P = 0; P < 4; ++P) {
+                    const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sQe + sw128(16 * tt + lr, 32 * P + 8 * lg));
+                    acc = mma(A8, Sh[P], acc);
+                }
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
-                    if (tp > (tt >> 1)) continue;
+                    if (tp > (tt >> 1)) continue;  // P is lower triangular
                     float p8[8];
                     lds_read8(sP + (16 * tt + lr) * F_LD + 32 * tp + 8 * lg, p8);
-                    split8(p8, Ph[tp], Pl[tp]);
+                    bf16x8 Ph, Pl;
+                    split8(p8, Ph, Pl);
+                    acc = mma(Ph, Uh[tp], acc);
+                    acc = mma(Pl, Uh[tp], acc);
+                    acc = mma(Ph, Ul[tp], acc);
                 }
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int P = 0; P < 4; ++P) {
-                        const bf16x8 A8 =
-                            *reinterpret_cast<const bf16x8 *>(sQe + sw128(16 * tt + lr, 32 * P + 8 * lg));
-                        acc = mma(A8, Sh[P][nt], acc);
-                    }
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp) {
-                        if (tp > (tt >> 1)) continue;  // P is lower triangular
-                        acc = mma(Ph[tp], Uh[tp][nt], acc);
-                        acc = mma(Pl[tp], Uh[tp][nt], acc);
-                        acc = mma(Ph[tp], Ul[tp][nt], acc);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sO[(16 * tt + 4 * lg + i) * kD + 32 * w + 16 * nt + lr] = acc[i];
-                }
+                for (int i = 0; i < 4; ++i) sO[(16 * tt + 4 * lg + i) * kD + 16 * w + lr] = acc[i];
             }
             // S = Diag(e^{G_end}) S0 + K_end^T U
 #pragma unroll
@@ -670,72 +672,49 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int krow = 32 * P + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                    float dec[4];
+                    f32x4 acc = S[P][x];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dec[i] = sExpEnd[32 * P + 8 * lg + 4 * x + i];
-                    bf16x8 Kh[2], Kl[2];
+                    for (int i = 0; i < 4; ++i) acc[i] *= sExpEnd[32 * P + 8 * lg + 4 * x + i];
 #pragma unroll
                     for (int tp = 0; tp < 2; ++tp) {
-                        Kh[tp] = *reinterpret_cast<const bf16x8 *>(sKeHi + sw64(krow, 32 * tp + 8 * lg));
-                        Kl[tp] = *reinterpret_cast<const bf16x8 *>(sKeLo + sw64(krow, 32 * tp + 8 * lg));
+                        const bf16x8 Kh = *reinterpret_cast<const bf16x8 *>(sKeHi + sw64(krow, 32 * tp + 8 * lg));
+                        const bf16x8 Kl = *reinterpret_cast<const bf16x8 *>(sKeLo + sw64(krow, 32 * tp + 8 * lg));
+                        acc = mma(Kh, Uh[tp], acc);
+                        acc = mma(Kl, Uh[tp], acc);
+                        acc = mma(Kh, Ul[tp], acc);
                     }
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        f32x4 acc = S[P][x][nt];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i] *= dec[i];
-#pragma unroll
-                        for (int tp = 0; tp < 2; ++tp) {
-                            acc = mma(Kh[tp], Uh[tp][nt], acc);
-                            acc = mma(Kl[tp], Uh[tp][nt], acc);
-                            acc = mma(Kh[tp], Ul[tp][nt], acc);
-                        }
-                        S[P][x][nt] = acc;
-                    }
+                    S[P][x] = acc;
                 }
         }
         __syncthreads();
 
         // ================= epilogue: out = sigmoid(g) * RMSNorm(o) =================
-        // four adjacent lanes own one token row: 32 values each, 16-byte loads and stores
+        // eight adjacent lanes own one token row: 16 values each, 16-byte loads and stores
         {
             int tid_ = (int)threadIdx.x;
             asm volatile("" : "+v"(tid_));
-            const int tok = tid_ >> 2;
-            const int v0 = 32 * (tid_ & 3);
-            float o[32];
-#pragma unroll
-            for (int j = 0; j < 32; j += 8) lds_read8(sO + tok * kD + v0 + j, o + j);
+            const int tok = tid_ >> 3;
+            const int v0 = 16 * (tid_ & 7);
+            float o[16];
+            lds_read8(sO + tok * kD + v0, o);
+            lds_read8(sO + tok * kD + v0 + 8, o + 8);
             float ss = 0.f;
 #pragma unroll
-            for (int j = 0; j < 32; ++j) ss += o[j] * o[j];
+            for (int j = 0; j < 16; ++j) ss += o[j] * o[j];
             ss += __shfl_xor(ss, 1, 64);
             ss += __shfl_xor(ss, 2, 64);
+            ss += __shfl_xor(ss, 4, 64);
             if (tok < L) {
                 const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
-                const size_t row = (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
+                float *orow = a.out + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
 #pragma unroll
-                for (int j = 0; j < 32; j += 8) {
-                    float g8[8];
-                    const uint32_t gw[4] = {graw[j / 8].x, graw[j / 8].y, graw[j / 8].z, graw[j / 8].w};
+                for (int j = 0; j < 16; j += 8) {
+                    float g8[8], y[8];
+                    unpack8(graw[j / 8], g8);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        g8[2 * e] = __uint_as_float(gw[e] << 16);
-                        g8[2 * e + 1] = __uint_as_float(gw[e] & 0xffff0000u);
-                    }
-                    const float4 w0 = *reinterpret_cast<const float4 *>(a.norm_w + v0 + j);
-                    const float4 w1 = *reinterpret_cast<const float4 *>(a.norm_w + v0 + j + 4);
-                    float4 y0, y1;
-                    y0.x = sigm(g8[0]) * (o[j + 0] * rinv * w0.x);
-                    y0.y = sigm(g8[1]) * (o[j + 1] * rinv * w0.y);
-                    y0.z = sigm(g8[2]) * (o[j + 2] * rinv * w0.z);
-                    y0.w = sigm(g8[3]) * (o[j + 3] * rinv * w0.w);
-                    y1.x = sigm(g8[4]) * (o[j + 4] * rinv * w1.x);
-                    y1.y = sigm(g8[5]) * (o[j + 5] * rinv * w1.y);
-                    y1.z = sigm(g8[6]) * (o[j + 6] * rinv * w1.z);
-                    y1.w = sigm(g8[7]) * (o[j + 7] * rinv * w1.w);
-                    *reinterpret_cast<float4 *>(a.out + row + j) = y0;
-                    *reinterpret_cast<float4 *>(a.out + row + j + 4) = y1;
+                    for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[j + e] * rinv * a.norm_w[v0 + j + e]);
+                    *reinterpret_cast<float4 *>(orow + j) = make_float4(y[0], y[1], y[2], y[3]);
+                    *reinterpret_cast<float4 *>(orow + j + 4) = make_float4(y[4], y[5], y[6], y[7]);
                 }
             }
         }
@@ -751,13 +730,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = 32 * P + 8 * lg + 4 * x + i;
-                        const int val = 32 * w + 16 * nt + lr;
-                        Sf[key * kD + val] = S[P][x][nt][i];
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 32 * P + 8 * lg + 4 * x + i;
+                    Sf[key * kD + 16 * w + lr] = S[P][x][i];
+                }
     }
     // ---- final conv windows: the last 3 pre-conv inputs (from the initial window if T < 3) ----
     for (int q = threadIdx.x; q < 3 * kD; q += kThreads) {

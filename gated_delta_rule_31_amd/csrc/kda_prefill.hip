@@ -43,6 +43,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 
@@ -59,6 +60,23 @@ constexpr int kTabFloats = 512 + 640 + 768 + 512 + 512 + 128 + 64 + 256;
 constexpr int OFF_CW = OFF_TAB + kTabFloats * 4;  // conv taps of this head, fp32 [3][128][4]
 constexpr int kLdsBytes = OFF_CW + 3 * 128 * 4 * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+// raw q, k, v rows of a chunk, staged once per chunk in regions 4-7 (free until phase 2):
+// [3 blocks][67 rows = the chunk's 64 tokens and the 3 before][136 bf16], the row pitch
+// padded by 16 bytes so that 16 lanes reading 16 consecutive rows hit different banks
+constexpr int STG_ROWS = kChunk + 3;
+constexpr int STG_LD = 136;
+static_assert(OFF_R4 + 3 * STG_ROWS * STG_LD * 2 <= OFF_TAB, "staging fits regions 4-7");
+
+// One chunk's raw inputs as this lane loads them: the chunk's 64 rows of q, k, v as 16-byte
+// pieces (lane l loads piece l%16 of rows l/16 and l/16 + 32 of each block), one piece of
+// the 3 rows before the chunk (lanes < 144), and the lane's own z row and beta logit.
+struct ChunkLoads {
+    u32x4 row[3][2];
+    u32x4 hist;
+    u32x4 z[2];
+    float b;
+};
 
 constexpr int CB_LD = 132;  // fp32 row pitch of sCB
 constexpr int F_LD = 68;    // fp32 row pitch of sA, sP, sT
@@ -96,7 +114,7 @@ __device__ __forceinline__ bf16x8 to_bf8(const float *x) {
     for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
     return r;
 }
-__device__ __forceinline__ void unpack8(const uint4 &u, float *x) {
+__device__ __forceinline__ void unpack8(const u32x4 &u, float *x) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -147,6 +165,43 @@ __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2
     (void)half;                                                \
     (void)t
 
+// Rows are clamped into the sequence [t0, t1): rows before its start are replaced by the
+// carried window later, rows past its end belong to padding tokens and are never used.
+// The base row is uniform, so lane offsets stay 32-bit.
+__device__ __forceinline__ ChunkLoads load_chunk(const PrefillArgs &a, int tid, int h, int t0, int t1, int c0) {
+    ChunkLoads r;
+    const size_t HD = (size_t)a.c.H * kD;
+    // every row below lies in [rbase, t1 - 1] (t1 > t0), also when c0 is past the end
+    const int rbase = min(max(t0 + c0 - 3, t0), t1 - 1);
+    const size_t ebase = (size_t)rbase * HD + (size_t)h * kD;
+    const uint16_t *X[3] = {a.q, a.k, a.v};
+    const uint32_t piece = 8u * (uint32_t)(tid & 15);
+#pragma unroll
+    for (int blk = 0; blk < 3; ++blk)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int row = (tid >> 4) + 32 * k;  // chunk row 0..63
+            const uint32_t tok = (uint32_t)(min(max(t0 + c0 + row, t0), t1 - 1) - rbase);
+            r.row[blk][k] = *reinterpret_cast<const u32x4 *>(X[blk] + ebase + (tok * (uint32_t)HD + piece));
+        }
+    {
+        const int i = min(tid, 143);  // 3 blocks x 3 rows x 16 pieces
+        const int blk = i / 48, row = (i % 48) >> 4;  // history row 0..2 = token c0 - 3 + row
+        const uint16_t *src = blk == 0 ? a.q : (blk == 1 ? a.k : a.v);
+        const uint32_t tok = (uint32_t)(min(max(t0 + c0 - 3 + row, t0), t1 - 1) - rbase);
+        r.hist = *reinterpret_cast<const u32x4 *>(src + ebase + (tok * (uint32_t)HD + piece));
+    }
+    const int lane_t = 16 * ((tid >> 6) & 3) + (tid & 15);     // the prologue token of this lane
+    const int cbase = 64 * (tid >> 8) + 16 * ((tid >> 4) & 3);  // and its 16 channels
+    const int tauc = min(max(t0 + c0 + lane_t, t0), t1 - 1);
+    const uint32_t ztok = (uint32_t)(tauc - rbase);
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc)
+        r.z[pc] = *reinterpret_cast<const u32x4 *>(a.z + ebase + (ztok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
+    r.b = bf2f(a.b[(size_t)tauc * a.c.H + h]);
+    return r;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     float *sCB = reinterpret_cast<float *>(smem + OFF_R1);              // [64][132] k e^{r - G}
@@ -188,7 +243,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const float qscale = a.c.q_scale;
     const float l2eps = a.c.l2_eps;
     const size_t conv_seq = (size_t)seq * 3 * HD * 3;  // this sequence's conv windows
-    const uint16_t *X[3] = {a.q, a.k, a.v};
 
     // ---- the state: S[P][x][i] = S[key 32P + 8lg + 4x + i][value 16w + lr] ----
     f32x4 S[4][2];
@@ -220,8 +274,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
+    // Raw inputs of a chunk are loaded one chunk ahead (issued before the previous chunk's
+    // state-side MFMAs, so that their latency is hidden) and the q, k, v rows are staged
+    // in LDS at the chunk's start, each 16-byte piece once.
+    uint16_t *sStage = reinterpret_cast<uint16_t *>(smem + OFF_R4);
+    ChunkLoads ld = {};
+    if (T > 0) {
+        int tid_ = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid_));
+        ld = load_chunk(a, tid_, h, t0, t1, 0);
+    }
+
     for (int c0 = 0; c0 < T; c0 += kChunk) {
         const int L = min(kChunk, T - c0);
+
+        // stage this chunk's raw rows (regions 4-7 are dead since the last chunk's phase 5);
+        // staging row r holds token c0 - 3 + r
+        {
+            int tid_ = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid_));
+            const int piece = 8 * (tid_ & 15);
+#pragma unroll
+            for (int blk = 0; blk < 3; ++blk)
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    *reinterpret_cast<u32x4 *>(sStage + (blk * STG_ROWS + 3 + (tid_ >> 4) + 32 * k) * STG_LD + piece) =
+                        ld.row[blk][k];
+            if (tid_ < 144) {
+                const int blk = tid_ / 48, row = (tid_ % 48) >> 4;
+                *reinterpret_cast<u32x4 *>(sStage + (blk * STG_ROWS + row) * STG_LD + piece) = ld.hist;
+            }
+        }
+        __syncthreads();
 
         // ================= phase 1: conv, SiLU, partial norms, gates =================
         float uq[16], uk[16], gs[16];  // q, k before the norm; G_t - r_sub of the 16 channels
@@ -230,45 +314,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             KDA_LANE_IDS();
             const bool valid = t < L;
             const int tau = t0 + c0 + t;                // packed row of the token
-            const int tauc = valid ? tau : t0 + c0;     // a padding lane reads the chunk's first row
             const int cbase = 64 * half + 16 * lg;      // first of this lane's 16 channels
-            // uniform base of the rows this chunk may touch; lane offsets stay 32-bit
-            const int rbase = max(t0 + c0 - 3, t0);
-            const size_t ebase = (size_t)rbase * HD + (size_t)h * kD;
-            // all raw loads first, branch-free, so that they are in flight together: rows
-            // tau-3 .. tau of q, k, v (clamped into the sequence; earlier rows come from the
-            // carried window below) and the z row
-            uint4 raw[3][2][4];  // [block q,k,v][piece][row tau-3+r]
-            uint4 zraw[2];
-#pragma unroll
-            for (int blk = 0; blk < 3; ++blk) {
-                const uint16_t *base = X[blk] + ebase;
-#pragma unroll
-                for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t tok = (uint32_t)(max(tauc - 3 + r, t0) - rbase);
-                        raw[blk][pc][r] =
-                            *reinterpret_cast<const uint4 *>(base + (tok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
-                    }
-            }
-            {
-                const uint16_t *base = a.z + ebase;
-                const uint32_t tok = (uint32_t)(tauc - rbase);
-#pragma unroll
-                for (int pc = 0; pc < 2; ++pc)
-                    zraw[pc] = *reinterpret_cast<const uint4 *>(base + (tok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
-            }
-            const float braw = bf2f(a.b[(size_t)tauc * H + h]);
-            beta = valid ? sigm(braw) : 0.0f;
+            beta = valid ? sigm(ld.b) : 0.0f;
             const bool head_of_seq = c0 == 0 && t < 3;  // rows before the sequence start
 
             // SiLU(ShortConv4(x)) of the 8 channels cbase + 8pc .. +7 of block blk
             auto conv_piece = [&](const int blk, const int pc, float *u) {
                 const int cb0 = cbase + 8 * pc;
-                float xr[4][8];
+                float xr[4][8];  // rows tau-3 .. tau = staging rows t .. t+3
 #pragma unroll
-                for (int r = 0; r < 4; ++r) unpack8(raw[blk][pc][r], xr[r]);
+                for (int r = 0; r < 4; ++r)
+                    unpack8(*reinterpret_cast<const u32x4 *>(sStage + (blk * STG_ROWS + t + r) * STG_LD + cb0), xr[r]);
                 if (head_of_seq) {
 #pragma unroll
                     for (int r = 0; r < 3; ++r) {
@@ -325,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 float zz[8];
-                unpack8(zraw[pc], zz);
+                unpack8(ld.z[pc], zz);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int c = cbase + 8 * pc + j;
@@ -603,15 +659,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ================= phase 5: state side =================
-        // (the epilogue's output-gate logits are loaded now, to arrive during the MFMAs)
-        uint4 graw[2];
+        // (the epilogue's output-gate logits and the next chunk's raw inputs are loaded
+        //  now, to arrive during the MFMAs)
+        {
+            // (past the last chunk this reloads clamped rows that are never used)
+            int tid_ = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid_));
+            ld = load_chunk(a, tid_, h, t0, t1, c0 + kChunk);
+        }
+        u32x4 graw[2];
         {
             int tid_ = (int)threadIdx.x;
             asm volatile("" : "+v"(tid_));
             const int tok = min(tid_ >> 3, L - 1);
             const uint16_t *gp = a.g + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + 16 * (tid_ & 7);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) graw[j] = *reinterpret_cast<const uint4 *>(gp + 8 * j);
+            for (int j = 0; j < 2; ++j) graw[j] = *reinterpret_cast<const u32x4 *>(gp + 8 * j);
         }
         {
             KDA_LANE_IDS();
@@ -743,8 +806,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const int tok = t1 - 3 + j;
+            const uint16_t *src = blk == 0 ? a.q : (blk == 1 ? a.k : a.v);
             if (tok >= t0)
-                win[j] = bf2f(X[blk][(size_t)tok * HD + (size_t)h * kD + cc]);
+                win[j] = bf2f(src[(size_t)tok * HD + (size_t)h * kD + cc]);
             else
                 win[j] = a.initial_conv_state ? a.initial_conv_state[conv_seq + ch * 3 + (tok - t0 + 3)] : 0.f;
         }

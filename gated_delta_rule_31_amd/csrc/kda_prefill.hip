@@ -52,7 +52,7 @@ constexpr int OFF_R1 = 0;        // sCB fp32 [64][132]          -> sKe hi/lo bf1
 constexpr int OFF_R2 = 33792;    // sVt hi/lo bf16 [128][64] x2 -> sO fp32 [64][128]
 constexpr int OFF_R3 = 66560;    // sWr bf16 [128][64]          (beta k e^G, transposed)
 constexpr int OFF_R4 = 82944;    // sA fp32 [64][68]            -> sW bf16 [64][128]
-constexpr int OFF_R5 = 100352;   // sP fp32 [64][68]
+constexpr int OFF_R5 = 100352;   // sPh, sPl bf16 [64][64] (P split hi/lo)
 constexpr int OFF_R6 = 117760;   // sT fp32 [64][68]            -> sQe bf16 [64][128]
 constexpr int OFF_R7 = 135168;   // sTb bf16 [64][64]
 constexpr int OFF_TAB = 143360;  // small fp32 tables
@@ -79,7 +79,7 @@ struct ChunkLoads {
 };
 
 constexpr int CB_LD = 132;  // fp32 row pitch of sCB
-constexpr int F_LD = 68;    // fp32 row pitch of sA, sP, sT
+constexpr int F_LD = 68;    // fp32 row pitch of sA, sT
 
 // bf16 [rows][64] and [rows][128] tiles, 16-byte chunks XOR-swizzled by row
 __device__ __forceinline__ int sw64(int row, int col) {
@@ -213,7 +213,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     __bf16 *sWr = reinterpret_cast<__bf16 *>(smem + OFF_R3);            // [128][64] (beta k e^G)^T
     float *sA = reinterpret_cast<float *>(smem + OFF_R4);               // [64][68]
     __bf16 *sW = reinterpret_cast<__bf16 *>(smem + OFF_R4);             // [64][128]
-    float *sP = reinterpret_cast<float *>(smem + OFF_R5);               // [64][68]
+    __bf16 *sPh = reinterpret_cast<__bf16 *>(smem + OFF_R5);           // [64][64] P, hi part
+    __bf16 *sPl = sPh + 64 * 64;                                        // [64][64] P, lo part
     float *sT = reinterpret_cast<float *>(smem + OFF_R6);               // [64][68]
     __bf16 *sQe = reinterpret_cast<__bf16 *>(smem + OFF_R6);            // [64][128] q e^G
     __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + OFF_R7);            // [64][64]
@@ -277,6 +278,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // Raw inputs of a chunk are loaded one chunk ahead (issued before the previous chunk's
     // state-side MFMAs, so that their latency is hidden) and the q, k, v rows are staged
     // in LDS at the chunk's start, each 16-byte piece once.
+    // dt_bias of this lane's 16 prologue channels (the same in every chunk)
+    float dtb[16];
+    {
+        KDA_LANE_IDS();
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dtb[j] = a.dt_bias[(size_t)h * kD + 64 * half + 16 * lg + j];
+    }
     uint16_t *sStage = reinterpret_cast<uint16_t *>(smem + OFF_R4);
     ChunkLoads ld = {};
     if (T > 0) {
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int c = cbase + 8 * pc + j;
-                    float g = valid ? gmin * sigm(rate * (zz[j] + a.dt_bias[(size_t)h * kD + c])) : 0.f;
+                    float g = valid ? gmin * sigm(rate * (zz[j] + dtb[8 * pc + j])) : 0.f;
                     g = row_scan16(g);
                     if (lr == 15) sTot[sub * 128 + c] = g;
                     gs[8 * pc + j] = g;
@@ -532,7 +540,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                             if (lr > tr) vp = 0.f;
                         }
                         sA[trow * F_LD + 16 * J + lr] = va;
-                        sP[trow * F_LD + 16 * J + lr] = vp;
+                        const __bf16 ph = (__bf16)vp;
+                        sPh[sw64(trow, 16 * J + lr)] = ph;
+                        sPl[sw64(trow, 16 * J + lr)] = (__bf16)(vp - (float)ph);
                     }
                 }
             }
@@ -548,6 +558,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ================= phase 3: T = (I + A)^-1 in fp32 =================
+        // (first the next chunk's raw inputs are requested, to arrive during phases 3-5;
+        //  past the last chunk this reloads clamped rows that are never used)
+        {
+            int tid_ = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid_));
+            ld = load_chunk(a, tid_, h, t0, t1, c0 + kChunk);
+        }
         // diagonal 16x16 blocks by forward substitution: waves 0..3, lanes 0..15 own columns
         {
             KDA_LANE_IDS();
@@ -565,14 +582,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             }
         }
         __syncthreads();
-        // off-diagonal blocks, by distance d = I - J:  T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
-        // (fp32 MFMA; the sum M is parked in the unused upper block (J, I) of sT)
-#pragma unroll
-        for (int d = 1; d < 4; ++d) {
-            {
-                KDA_LANE_IDS();
-                if (w < 4 - d) {
-                    const int J = w, I = w + d;
+        // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ: wave J walks column J
+        // downward, so every T_KJ it needs is its own earlier result and only the diagonal
+        // blocks come from other waves (fp32 MFMA; the sum M is parked in the unused upper
+        // block (J, I) of sT; this wave's LDS accesses complete in order, so no barrier)
+        {
+            KDA_LANE_IDS();
+            if (w < 3) {
+                const int J = w;
+                for (int I = J + 1; I < 4; ++I) {
                     f32x4 M = {0.f, 0.f, 0.f, 0.f};
                     for (int K = J; K < I; ++K)
 #pragma unroll
@@ -581,13 +599,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                                         sT[(16 * K + 4 * kk + lg) * F_LD + 16 * J + lr], M);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sT[(16 * J + 4 * lg + i) * F_LD + 16 * I + lr] = M[i];
-                }
-            }
-            __syncthreads();
-            {
-                KDA_LANE_IDS();
-                if (w < 4 - d) {
-                    const int J = w, I = w + d;
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                     f32x4 R = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
@@ -595,10 +608,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                                     sT[(16 * J + 4 * kk + lg) * F_LD + 16 * I + lr], R);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sT[(16 * I + 4 * lg + i) * F_LD + 16 * J + lr] = R[i];
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();
         // T -> bf16 (upper blocks, which held scratch, become zero)
         {
             int tid_ = (int)threadIdx.x;
@@ -659,14 +674,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ================= phase 5: state side =================
-        // (the epilogue's output-gate logits and the next chunk's raw inputs are loaded
-        //  now, to arrive during the MFMAs)
-        {
-            // (past the last chunk this reloads clamped rows that are never used)
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
-            ld = load_chunk(a, tid_, h, t0, t1, c0 + kChunk);
-        }
+        // (the epilogue's output-gate logits are loaded now, to arrive during the MFMAs)
         u32x4 graw[2];
         {
             int tid_ = (int)threadIdx.x;
@@ -718,10 +726,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
                     if (tp > (tt >> 1)) continue;  // P is lower triangular
-                    float p8[8];
-                    lds_read8(sP + (16 * tt + lr) * F_LD + 32 * tp + 8 * lg, p8);
-                    bf16x8 Ph, Pl;
-                    split8(p8, Ph, Pl);
+                    const bf16x8 Ph = *reinterpret_cast<const bf16x8 *>(sPh + sw64(16 * tt + lr, 32 * tp + 8 * lg));
+                    const bf16x8 Pl = *reinterpret_cast<const bf16x8 *>(sPl + sw64(16 * tt + lr, 32 * tp + 8 * lg));
                     acc = mma(Ph, Uh[tp], acc);
                     acc = mma(Pl, Uh[tp], acc);
                     acc = mma(Ph, Ul[tp], acc);

@@ -546,13 +546,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     }
                 }
             }
-            // sCB is dead: K_end^T, hi/lo, into region 1
+            // sCB is dead: K_end^T, hi/lo, into region 1 (channel half 1 now, half 0 while
+            // the diagonal blocks of T are inverted)
+            if (half == 1) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int c = 64 * half + 16 * lg + j;
-                const __bf16 hi = (__bf16)ke[j];
-                sKeHi[sw64(c, t)] = hi;
-                sKeLo[sw64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                for (int j = 0; j < 16; ++j) {
+                    const int c = 64 * half + 16 * lg + j;
+                    const __bf16 hi = (__bf16)ke[j];
+                    sKeHi[sw64(c, t)] = hi;
+                    sKeLo[sw64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                }
             }
         }
         __syncthreads();
@@ -566,19 +569,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             ld = load_chunk(a, tid_, h, t0, t1, c0 + kChunk);
         }
         // diagonal 16x16 blocks by forward substitution: waves 0..3, lanes 0..15 own columns
+        // (every block of T is also written as bf16 into sTb for the MFMAs of phase 4; the
+        //  waves 4..7 clear sTb's upper blocks meanwhile)
         {
             KDA_LANE_IDS();
-            if (w < 4 && lg == 0) {
-                float xcol[16];
+            if (w < 4) {
+                if (lg == 0) {
+                    float xcol[16];
 #pragma unroll
-                for (int tt = 0; tt < 16; ++tt) {
-                    float acc = (tt == lr) ? 1.0f : 0.0f;
+                    for (int tt = 0; tt < 16; ++tt) {
+                        float acc = (tt == lr) ? 1.0f : 0.0f;
 #pragma unroll
-                    for (int j = 0; j < tt; ++j) acc -= sA[(16 * w + tt) * F_LD + 16 * w + j] * xcol[j];
-                    xcol[tt] = acc;
+                        for (int j = 0; j < tt; ++j) acc -= sA[(16 * w + tt) * F_LD + 16 * w + j] * xcol[j];
+                        xcol[tt] = acc;
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < 16; ++tt) {
+                        sT[(16 * w + tt) * F_LD + 16 * w + lr] = xcol[tt];
+                        sTb[sw64(16 * w + tt, 16 * w + lr)] = (__bf16)xcol[tt];
+                    }
                 }
+                // K_end^T of channel half 0
 #pragma unroll
-                for (int tt = 0; tt < 16; ++tt) sT[(16 * w + tt) * F_LD + 16 * w + lr] = xcol[tt];
+                for (int j = 0; j < 16; ++j) {
+                    const int c = 16 * lg + j;
+                    const __bf16 hi = (__bf16)ke[j];
+                    sKeHi[sw64(c, t)] = hi;
+                    sKeLo[sw64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                }
+            } else {
+                // upper blocks (I < J) of sTb: 6 blocks x 256 values over 256 lanes
+                const int lane = tid_ & 255;
+#pragma unroll
+                for (int b = 0; b < 6; ++b) {
+                    const int I = b < 3 ? 0 : (b < 5 ? 1 : 2);
+                    const int J = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3);
+                    sTb[sw64(16 * I + (lane >> 4), 16 * J + (lane & 15))] = (__bf16)0.0f;
+                }
             }
         }
         __syncthreads();
@@ -607,23 +634,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                         R = mma_f32(-sT[(16 * I + lr) * F_LD + 16 * I + 4 * kk + lg],
                                     sT[(16 * J + 4 * kk + lg) * F_LD + 16 * I + lr], R);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sT[(16 * I + 4 * lg + i) * F_LD + 16 * J + lr] = R[i];
+                    for (int i = 0; i < 4; ++i) {
+                        sT[(16 * I + 4 * lg + i) * F_LD + 16 * J + lr] = R[i];
+                        sTb[sw64(16 * I + 4 * lg + i, 16 * J + lr)] = (__bf16)R[i];
+                    }
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 }
-            }
-        }
-        __syncthreads();
-        // T -> bf16 (upper blocks, which held scratch, become zero)
-        {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
-            const int r = tid_ >> 3;
-#pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                const int c = 8 * (tid_ & 7) + cc;
-                const float v = ((c >> 4) <= (r >> 4)) ? sT[r * F_LD + c] : 0.0f;
-                sTb[sw64(r, c)] = (__bf16)v;
             }
         }
         __syncthreads();

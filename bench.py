@@ -155,7 +155,8 @@ def bench_prefill(args, dev):
 
     case = ki.case2_prefill()
     H = case.H
-    cfg = kda.KdaConfig(num_heads=H)
+    path = {"auto": kda.PREFILL_AUTO, "fused": kda.PREFILL_FUSED, "chunked": kda.PREFILL_CHUNKED}[args.prefill_path]
+    cfg = kda.KdaConfig(num_heads=H, prefill_path=path)
     p = case.params
     tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -166,9 +167,12 @@ def bench_prefill(args, dev):
     out = torch.empty((N, H * D), dtype=torch.float32, device=dev)
     fs = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
     fcs = torch.empty((1, 3 * H * D, 3), dtype=torch.float32, device=dev)
+    ws_bytes = kda.kda_prefill_workspace_bytes(cfg, 1, N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def launch():
-        kda.kda_prefill(cfg, cu, *xs, *prm, None, None, out=out, final_state=fs, final_conv_state=fcs)
+        kda.kda_prefill(cfg, cu, *xs, *prm, None, None, out=out, final_state=fs, final_conv_state=fcs,
+                        workspace=ws)
 
     for _ in range(max(1, args.warmup // 2)):
         launch()
@@ -189,7 +193,9 @@ def bench_prefill(args, dev):
     tf = flops / (kern_ms * 1e-3) / 1e12
     gbs = byts / (kern_ms * 1e-3) / 1e9
     mf, hf = tf / BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS
-    return {"workload": "kda-prefill-1x8192tok-96head", "tokens_per_s": round(N / (ms * 1e-3), 1),
+    return {"workload": "kda-prefill-1x8192tok-96head", "layout": args.prefill_path if path else
+            ("chunked" if ws_bytes else "fused"), "workspace_bytes": ws_bytes,
+            "tokens_per_s": round(N / (ms * 1e-3), 1),
             "ms_per_call": round(ms, 4), "kernel_avg_us": round(kern_ms * 1e3, 2),
             "mfma_frac": round(mf, 4), "hbm_frac": round(hf, 4), "roofline_frac": round(max(mf, hf), 4),
             "alg_flops": flops, "alg_bytes": byts, "achieved_tflops": round(tf, 2), "achieved_gbs": round(gbs, 1)}
@@ -276,6 +282,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-path", choices=["auto", "fused", "chunked"], default="auto",
+                    help="prefill work layout (auto: chunked below 512 (sequence, head) units)")
     ap.add_argument("--only", choices=["all", "decode", "prefill", "copy"], default="all",
                     help="run one part only (counter runs under rocprofv3 use this)")
     ap.add_argument("--skip-prefill", action="store_true")

@@ -14,12 +14,12 @@ from dataclasses import dataclass
 import torch
 
 __all__ = ["KdaConfig", "kda_decode_step", "kda_prefill", "kda_prefill_workspace_bytes", "KdaError",
-           "lib", "LIB_PATH", "EXPORTED_SYMBOLS"]
+           "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_prefill", "kda_prefill_workspace_bytes",
                     "kda_status_str", "kda_abi_version")
-ABI_VERSION = 1
+ABI_VERSION = 2
 HEAD_DIM = 128
 CONV = 4
 
@@ -33,7 +33,13 @@ class _CConfig(ctypes.Structure):
         ("l2_eps", ctypes.c_float),
         ("rms_eps", ctypes.c_float),
         ("q_scale", ctypes.c_float),
+        ("prefill_path", ctypes.c_int32),
     ]
+
+# kda_config.prefill_path values
+PREFILL_AUTO = 0     # chunked below 512 (sequence, head) units, fused otherwise
+PREFILL_FUSED = 1    # one workgroup per (sequence, head) over all chunks; no workspace
+PREFILL_CHUNKED = 2  # chunk records in parallel, then the carry; needs a workspace
 
 
 @dataclass
@@ -45,10 +51,11 @@ class KdaConfig:
     l2_eps: float = 1e-6
     rms_eps: float = 1e-5
     q_scale: float = 0.0  # <= 0 selects head_dim ** -0.5
+    prefill_path: int = PREFILL_AUTO
 
     def _c(self) -> _CConfig:
         return _CConfig(self.num_heads, self.head_dim, self.conv_size, self.gate_lower_bound, self.l2_eps,
-                        self.rms_eps, self.q_scale)
+                        self.rms_eps, self.q_scale, self.prefill_path)
 
 
 class KdaError(RuntimeError):
@@ -157,8 +164,11 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
     if final_conv_state is None:
         final_conv_state = torch.empty((B, 3 * HD, CONV - 1), dtype=f32, device=dev)
     ws_bytes = kda_prefill_workspace_bytes(cfg, B, N)
-    if ws_bytes and workspace is None:
+    own_ws = bool(ws_bytes) and workspace is None
+    if own_ws:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
     args = [
         _ptr(cu_seqlens, torch.int32, (B + 1,), "cu_seqlens"),
         _ptr(q, bf, (N, HD), "q"), _ptr(k, bf, (N, HD), "k"), _ptr(v, bf, (N, HD), "v"),
@@ -175,4 +185,8 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
     st = _lib.kda_prefill(ctypes.byref(c), B, N, *args, ws, ctypes.c_size_t(ws_bytes), _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_prefill")
+    if own_ws and stream is not None:
+        # the workspace is released when this returns: keep the allocator from handing it
+        # out again before the kernels queued on ``stream`` are done with it
+        workspace.record_stream(stream)
     return out, final_state, final_conv_state

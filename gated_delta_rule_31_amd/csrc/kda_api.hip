@@ -1,5 +1,5 @@
 // kda_api.hip -- the C-ABI entry points of libkda.so: host-side argument checks, then
-// one kernel launch on the caller's stream.  Declarations and contracts: include/kda.h.
+// the kernel launches on the caller's stream.  Declarations and contracts: include/kda.h.
 //
 // Every check runs before the first HIP call, so a rejected call touches neither the
 // device nor the HIP runtime's error state (and the checks run on a machine without a
@@ -33,7 +33,34 @@ kda_status check_config(const kda_config *cfg, kda::MixerConsts *out) {
 }
 
 // [B*H] units must fit the 1-D grid; [B or N, H*D] extents must fit size_t arithmetic.
-bool units_fit(int64_t rows, int64_t H) { return rows >= 0 && rows * H <= INT32_MAX; }
+bool units_fit(int64_t rows, int64_t H, int64_t max_units) { return rows >= 0 && rows * H <= max_units; }
+
+// The prefill layout for these sizes, and the workspace it needs; false for sizes
+// kda_prefill rejects.
+struct PrefillPlan {
+    int path;
+    int64_t nchunk_cap, nseg_cap;
+    size_t table_bytes, workspace_bytes;
+};
+bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan) {
+    const int64_t H = cfg->num_heads;
+    if (B < 0 || N < 0 || N > INT32_MAX || !units_fit(B, H, kda::kMaxPrefillUnits)) return false;
+    const int64_t cap = kda::chunk_cap(B, N);
+    const int64_t segs = kda::seg_cap(B, cap);
+    const bool chunked_fits = cap * H <= kda::kMaxPrefillUnits && segs * H <= kda::kMaxPrefillUnits;
+    int path = cfg->prefill_path;
+    if (path == kda::kPathAuto)
+        path = (B * H < kda::kChunkedBelowUnits && chunked_fits) ? kda::kPathChunked : kda::kPathFused;
+    if (path != kda::kPathFused && path != kda::kPathChunked) return false;
+    if (path == kda::kPathChunked && !chunked_fits) return false;
+    plan->path = path;
+    plan->nchunk_cap = cap;
+    plan->nseg_cap = segs;
+    plan->table_bytes = (size_t)((8 * (B + 1) + 255) / 256 * 256);  // chunk_start, seg_start
+    plan->workspace_bytes =
+        path == kda::kPathFused ? 0 : plan->table_bytes + (size_t)cap * (size_t)H * (size_t)kda::kRecBytes;
+    return true;
+}
 
 }  // namespace
 
@@ -48,6 +75,7 @@ kda_config kda_config_default(void) {
     c.l2_eps = 1e-6f;
     c.rms_eps = 1e-5f;
     c.q_scale = 0.0f;
+    c.prefill_path = KDA_PREFILL_AUTO;
     return c;
 }
 
@@ -59,7 +87,7 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch, const float *q,
     kda::DecodeArgs a;
     kda_status st = check_config(cfg, &a.c);
     if (st != KDA_OK) return st;
-    if (batch < 0 || !units_fit(batch, a.c.H)) return KDA_ERR_BAD_SHAPE;
+    if (batch < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits)) return KDA_ERR_BAD_SHAPE;
     if (batch == 0) return KDA_OK;
     const void *ptrs[] = {q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state, conv_state, out};
     for (const void *p : ptrs)
@@ -74,10 +102,10 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch, const float *q,
 }
 
 size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens) {
-    (void)cfg;
-    (void)num_seqs;
-    (void)total_tokens;
-    return 0;  // the fused chunk kernel keeps every intermediate on chip
+    kda::MixerConsts c;
+    PrefillPlan plan;
+    if (check_config(cfg, &c) != KDA_OK || !plan_prefill(cfg, num_seqs, total_tokens, &plan)) return 0;
+    return plan.workspace_bytes;
 }
 
 kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
@@ -90,10 +118,9 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
     kda::PrefillArgs a;
     kda_status st = check_config(cfg, &a.c);
     if (st != KDA_OK) return st;
-    if (num_seqs < 0 || total_tokens < 0 || !units_fit(num_seqs, a.c.H) || !units_fit(total_tokens, 1))
-        return KDA_ERR_BAD_SHAPE;
-    if (workspace_bytes < kda_prefill_workspace_bytes(cfg, num_seqs, total_tokens)) return KDA_ERR_WORKSPACE;
-    (void)workspace;
+    if (cfg->prefill_path < kda::kPathAuto || cfg->prefill_path > kda::kPathChunked) return KDA_ERR_BAD_CONFIG;
+    PrefillPlan plan;
+    if (!plan_prefill(cfg, num_seqs, total_tokens, &plan)) return KDA_ERR_BAD_SHAPE;
     if (num_seqs == 0) return total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
     const void *req[] = {cu_seqlens, conv_w, A_log, dt_bias, norm_w, final_state, final_conv_state};
     for (const void *p : req)
@@ -110,8 +137,17 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
     for (const void *p : al)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_MISALIGNED;
+    if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace)) return KDA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
     a.B = num_seqs;
     a.N = total_tokens;
+    a.path = plan.path;
+    a.nchunk_cap = (int)plan.nchunk_cap;
+    a.nseg_cap = (int)plan.nseg_cap;
+    const bool chunked = plan.path == kda::kPathChunked;
+    a.chunk_start = chunked ? static_cast<int32_t *>(workspace) : nullptr;
+    a.seg_start = chunked ? static_cast<int32_t *>(workspace) + (num_seqs + 1) : nullptr;
+    a.records = chunked ? static_cast<unsigned char *>(workspace) + plan.table_bytes : nullptr;
     a.cu_seqlens = cu_seqlens;
     a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
     a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
@@ -127,7 +163,7 @@ const char *kda_status_str(kda_status s) {
     switch (s) {
         case KDA_OK: return "ok";
         case KDA_ERR_NULL_ARG: return "a required pointer is NULL";
-        case KDA_ERR_BAD_CONFIG: return "unsupported config (head_dim must be 128, conv_size 4, num_heads >= 1, finite eps >= 0)";
+        case KDA_ERR_BAD_CONFIG: return "unsupported config (head_dim must be 128, conv_size 4, num_heads >= 1, finite eps >= 0, prefill_path 0..2)";
         case KDA_ERR_BAD_SHAPE: return "negative, inconsistent or too large sizes";
         case KDA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
         case KDA_ERR_WORKSPACE: return "workspace too small";

@@ -1,5 +1,6 @@
-// kda_internal.hpp -- launch descriptors shared by the entry points (kda_api.cpp) and
-// the kernels (kda_decode.hip, kda_prefill.hip).  Not part of the public ABI.
+// kda_internal.hpp -- launch descriptors shared by the entry points (kda_api.hip) and
+// the kernels (kda_decode.hip, kda_prefill.hip, kda_carry.hip).  Not part of the public
+// ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,9 +28,44 @@ struct DecodeArgs {
     float *state, *conv_state, *out;
 };
 
+// Prefill launch plans (kda_config.prefill_path):
+//   kPathFused   one workgroup per (sequence, head) walks the sequence chunk by chunk;
+//                every intermediate stays on chip
+//   kPathChunked a workgroup per (chunk, head) computes each chunk's state-independent
+//                products into the workspace (chunk records), then one workgroup per
+//                (sequence, head) carries the state across the records
+enum PrefillPath { kPathAuto = 0, kPathFused = 1, kPathChunked = 2 };
+
+// Launch-size limits: a dispatch holds fewer than 2^32 work-items per grid dimension.
+constexpr int64_t kMaxPrefillUnits = (int64_t)0xFFFFFFFF / 512;  // workgroups of 512 lanes
+constexpr int64_t kMaxDecodeUnits = (int64_t)0xFFFFFFFF / 256;   // workgroups of 256 lanes
+
+// Below this many (sequence, head) units the fused plan leaves most compute units idle
+// and the chunked plan is chosen.
+constexpr int64_t kChunkedBelowUnits = 512;
+
+// Bytes of one chunk record (the layout is in kda_device.hpp); a multiple of 256.
+constexpr int kRecBytes = 115200;
+
+// Chunk records that a batch of B sequences and N tokens can need at most:
+// sum_s ceil(len_s / 64) <= floor(N / 64) + B.
+inline int64_t chunk_cap(int64_t B, int64_t N) { return N / kChunk + B; }
+
+// The chunk kernel gives each workgroup a segment of up to kSegChunks consecutive chunks
+// of one sequence (it loads a chunk's inputs while it finishes the one before).  A batch
+// whose sequences hold n_s records in total has at most floor(sum n_s / 4) + B segments.
+constexpr int kSegChunks = 4;
+inline int64_t seg_cap(int64_t B, int64_t nchunk_cap) { return nchunk_cap / kSegChunks + B; }
+
 struct PrefillArgs {
     MixerConsts c;
     int B, N;
+    int path;            // kPathFused or kPathChunked (resolved)
+    int nchunk_cap;      // chunked plan: records available in the workspace
+    int nseg_cap;        // chunked plan: chunk-kernel workgroups per head
+    int32_t *chunk_start;     // chunked plan: [B+1] first record row of each sequence
+    int32_t *seg_start;       // chunked plan: [B+1] first segment of each sequence
+    unsigned char *records;   // chunked plan: [nchunk_cap][H] records
     const int32_t *cu_seqlens;
     const uint16_t *q, *k, *v, *z, *b, *g;
     const float *conv_w, *A_log, *dt_bias, *norm_w;
@@ -39,5 +75,10 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+// the chunked plan's kernels (kda_prefill.hip: chunk table, chunk records; kda_carry.hip:
+// the carry)
+hipError_t launch_chunk_table(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_chunk_records(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_carry(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace kda

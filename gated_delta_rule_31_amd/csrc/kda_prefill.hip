@@ -36,14 +36,10 @@
 // channel half, so each wave computes its half of block row I from its own registers;
 // the two halves are added through LDS.
 
-#include "kda_internal.hpp"
+#include "kda_device.hpp"
 
 namespace kda {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 
@@ -58,7 +54,8 @@ constexpr int OFF_R7 = 135168;   // sTb bf16 [64][64]
 constexpr int OFF_TAB = 143360;  // small fp32 tables
 constexpr int kTabFloats = 512 + 640 + 768 + 512 + 512 + 128 + 64 + 256;
 constexpr int OFF_CW = OFF_TAB + kTabFloats * 4;  // conv taps of this head, fp32 [3][128][4]
-constexpr int kLdsBytes = OFF_CW + 3 * 128 * 4 * 4;
+constexpr int OFF_DTB = OFF_CW + 3 * 128 * 4 * 4;  // dt_bias of this head, fp32 [128]
+constexpr int kLdsBytes = OFF_DTB + 128 * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 // raw q, k, v rows of a chunk, staged once per chunk in regions 4-7 (free until phase 2):
@@ -81,57 +78,6 @@ struct ChunkLoads {
 constexpr int CB_LD = 132;  // fp32 row pitch of sCB
 constexpr int F_LD = 68;    // fp32 row pitch of sA, sT
 
-// bf16 [rows][64] and [rows][128] tiles, 16-byte chunks XOR-swizzled by row
-__device__ __forceinline__ int sw64(int row, int col) {
-    return row * 64 + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
-}
-__device__ __forceinline__ int sw128(int row, int col) {
-    return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
-}
-
-__device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
-// sigmoid with the hardware reciprocal (about 1 ulp) instead of an IEEE division
-__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
-
-__device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const __bf16 h = (__bf16)x[j];
-        hi[j] = h;
-        lo[j] = (__bf16)(x[j] - (float)h);
-    }
-}
-__device__ __forceinline__ bf16x8 to_bf8(const float *x) {
-    bf16x8 r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
-    return r;
-}
-__device__ __forceinline__ void unpack8(const u32x4 &u, float *x) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        x[2 * j] = __uint_as_float(w[j] << 16);
-        x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-    }
-}
-__device__ __forceinline__ void lds_read8(const float *p, float *x) {
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ void lds_write8(float *p, const float *x) {
-    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
-}
 // inclusive prefix sum over the 16 lanes of a DPP row (lanes 16g .. 16g+15)
 // (DPP row_shr:n moves lane i-n of the same 16-lane row into lane i; lanes without a
 //  source receive 0)
@@ -202,6 +148,11 @@ __device__ __forceinline__ ChunkLoads load_chunk(const PrefillArgs &a, int tid, 
     return r;
 }
 
+// kChunked = false: the fused plan, one workgroup per (sequence, head) over all chunks.
+// kChunked = true: one workgroup per (segment, head) computes up to kSegChunks
+// consecutive chunks of one sequence up to U' and stores each chunk's record instead of
+// carrying the state.
+template <bool kChunked>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     float *sCB = reinterpret_cast<float *>(smem + OFF_R1);              // [64][132] k e^{r - G}
@@ -227,11 +178,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     float *sBeta = sExpEnd + 128;                              // [64]
     float *sNorm = sBeta + 64;                                 // [2 halves][q,k][64] sums of squares
     float *sConvW = reinterpret_cast<float *>(smem + OFF_CW);  // [3][128][4] taps, oldest first
+    float *sDtb = reinterpret_cast<float *>(smem + OFF_DTB);   // [128] dt_bias
 
     const int H = a.c.H;
     const int N = a.N;
-    const int seq = blockIdx.x / H;
-    const int h = blockIdx.x - seq * H;
+    // cbeg, cend: token offsets (in the sequence) of the chunks this workgroup walks;
+    // rec0: record row of the sequence's first chunk (chunked plan)
+    int seq, h, cbeg, nrec = 0, rec0 = 0;
+    if constexpr (kChunked) {
+        const int sg = blockIdx.x / H;
+        h = blockIdx.x - sg * H;
+        if (sg >= a.seg_start[a.B]) return;  // past the batch's last segment (uniform)
+        // the sequence owning segment sg: seg_start[lo] <= sg < seg_start[hi]
+        int lo = 0, hi = a.B;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.seg_start[mid] <= sg) lo = mid; else hi = mid;
+        }
+        seq = lo;
+        rec0 = a.chunk_start[seq];
+        nrec = a.chunk_start[seq + 1] - rec0;  // ceil(T / 64) for a valid batch
+        cbeg = (sg - a.seg_start[seq]) * kSegChunks * kChunk;
+    } else {
+        seq = blockIdx.x / H;
+        h = blockIdx.x - seq * H;
+        cbeg = 0;
+    }
     const size_t HD = (size_t)H * kD;
     int t0 = a.cu_seqlens[seq];
     int t1 = a.cu_seqlens[seq + 1];
@@ -247,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 
     // ---- the state: S[P][x][i] = S[key 32P + 8lg + 4x + i][value 16w + lr] ----
     f32x4 S[4][2];
-    {
+    if constexpr (!kChunked) {
         KDA_LANE_IDS();
         const float *S0 = a.initial_state ? a.initial_state + ((size_t)seq * H + h) * kD * kD : nullptr;
 #pragma unroll
@@ -262,38 +234,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
 
     // the conv taps of this head's 384 channels, and its initial conv windows (zeros if
-    // none): these sit in sPair/sExpRef, which the first chunk's tables step overwrites
-    // only after the last read of the windows (phase 1 of chunk 0)
+    // none; read only by the sequence's first chunk): these sit in sPair/sExpRef, which
+    // the first chunk's tables step overwrites only after the last read of the windows
+    // (phase 1 of chunk 0)
     float *sWin0 = sPair;  // [3*128][3]
     for (int i = threadIdx.x; i < 3 * kD; i += kThreads) {
         const int blk = i >> 7, c = i & 127;
         const size_t ch = (size_t)blk * HD + (size_t)h * kD + c;
         *reinterpret_cast<float4 *>(sConvW + i * 4) = *reinterpret_cast<const float4 *>(a.conv_w + ch * 4);
+        if (i < kD) sDtb[i] = a.dt_bias[(size_t)h * kD + i];
+        if (cbeg == 0) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
-            sWin0[i * 3 + j] = a.initial_conv_state ? a.initial_conv_state[conv_seq + ch * 3 + j] : 0.f;
+            for (int j = 0; j < 3; ++j)
+                sWin0[i * 3 + j] = a.initial_conv_state ? a.initial_conv_state[conv_seq + ch * 3 + j] : 0.f;
+        }
     }
     __syncthreads();
 
     // Raw inputs of a chunk are loaded one chunk ahead (issued before the previous chunk's
     // state-side MFMAs, so that their latency is hidden) and the q, k, v rows are staged
     // in LDS at the chunk's start, each 16-byte piece once.
-    // dt_bias of this lane's 16 prologue channels (the same in every chunk)
-    float dtb[16];
-    {
-        KDA_LANE_IDS();
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dtb[j] = a.dt_bias[(size_t)h * kD + 64 * half + 16 * lg + j];
-    }
     uint16_t *sStage = reinterpret_cast<uint16_t *>(smem + OFF_R4);
     ChunkLoads ld = {};
     if (T > 0) {
         int tid_ = (int)threadIdx.x;
         asm volatile("" : "+v"(tid_));
-        ld = load_chunk(a, tid_, h, t0, t1, 0);
+        ld = load_chunk(a, tid_, h, t0, t1, cbeg);
     }
 
-    for (int c0 = 0; c0 < T; c0 += kChunk) {
+    const int cend = kChunked ? min(min(cbeg + kSegChunks * kChunk, nrec * kChunk), T) : T;
+    for (int c0 = cbeg; c0 < cend; c0 += kChunk) {
         const int L = min(kChunk, T - c0);
 
         // stage this chunk's raw rows (regions 4-7 are dead since the last chunk's phase 5);
@@ -322,9 +292,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             KDA_LANE_IDS();
             const bool valid = t < L;
             const int tau = t0 + c0 + t;                // packed row of the token
+            const bool head_of_seq = c0 == 0 && t < 3;  // rows before the sequence start
             const int cbase = 64 * half + 16 * lg;      // first of this lane's 16 channels
             beta = valid ? sigm(ld.b) : 0.0f;
-            const bool head_of_seq = c0 == 0 && t < 3;  // rows before the sequence start
 
             // SiLU(ShortConv4(x)) of the 8 channels cbase + 8pc .. +7 of block blk
             auto conv_piece = [&](const int blk, const int pc, float *u) {
@@ -388,12 +358,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             // sum over the sub-chunk's 16 tokens (= G_t - r_sub)
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
-                float zz[8];
+                float zz[8], dtb[8];
                 unpack8(ld.z[pc], zz);
+                lds_read8(sDtb + cbase + 8 * pc, dtb);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int c = cbase + 8 * pc + j;
-                    float g = valid ? gmin * sigm(rate * (zz[j] + dtb[8 * pc + j])) : 0.f;
+                    float g = valid ? gmin * sigm(rate * (zz[j] + dtb[j])) : 0.f;
                     g = row_scan16(g);
                     if (lr == 15) sTot[sub * 128 + c] = g;
                     gs[8 * pc + j] = g;
@@ -406,7 +377,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         // ---- per-chunk channel tables (threads 0..255), and this lane's operand rows ----
         float qr[16], kr[16], cbk[16];  // q e^{G-r}, k e^{G-r}, k e^{r-G} of the normalised q, k
         {
-            const int tid = threadIdx.x;
+            int tid = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid));
             if (tid < 256) {
                 const int c = tid & 127;
                 float r[5];
@@ -690,6 +662,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
         __syncthreads();
 
+        if constexpr (kChunked) {
+            // ================= the chunk record (layout in kda_device.hpp) =================
+            KDA_LANE_IDS();
+            const int lane = tid_ & 63;
+            unsigned char *rec = a.records + ((size_t)(rec0 + c0 / kChunk) * H + h) * kRecBytes;
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+                    *reinterpret_cast<f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16) = U[tp][x];
+            // the operand images, copied as they sit in LDS: W (region 4), Q~ (region 6),
+            // P hi/lo (region 5), K_end^T hi/lo (region 1); 10 pieces of 16 bytes per lane
+#pragma unroll
+            for (int j = 0; j < REC_IMG / 16 / kThreads; ++j) {
+                const int off = (tid_ + kThreads * j) * 16;
+                const int src = j < 2 ? OFF_R4 + off
+                              : j < 4 ? OFF_R6 + (off - REC_Q)
+                              : j < 6 ? OFF_R5 + (off - REC_PH)
+                                      : OFF_R1 + (off - REC_KH);
+                *reinterpret_cast<u32x4 *>(rec + off) = *reinterpret_cast<const u32x4 *>(smem + src);
+            }
+            if (tid_ < 32)
+                *reinterpret_cast<u32x4 *>(rec + REC_E + tid_ * 16) = *reinterpret_cast<const u32x4 *>(sExpEnd + 4 * tid_);
+            __syncthreads();  // LDS is rewritten by the next chunk
+            continue;
+        }
+
         // ================= phase 5: state side =================
         // (the epilogue's output-gate logits are loaded now, to arrive during the MFMAs)
         u32x4 graw[2];
@@ -807,6 +806,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         __syncthreads();  // LDS is rewritten by the next chunk
     }
 
+    if constexpr (kChunked) return;  // the carry kernel writes the final state and windows
+
     // ---- final state ----
     {
         KDA_LANE_IDS();
@@ -842,15 +843,84 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 
 #undef KDA_LANE_IDS
 
+// ---- the chunked plan's tables ----
+// Sequence s owns record rows chunk_start[s] .. chunk_start[s+1]-1, one per chunk of 64
+// tokens (a partial last chunk included), in order, and chunk-kernel segments
+// seg_start[s] .. seg_start[s+1]-1 of up to kSegChunks of those rows each.  The running
+// record count is capped at nchunk_cap, so no record lies past the workspace even for a
+// cu_seqlens that breaks its contract (such a batch then loses its trailing chunks,
+// never memory safety); the segment count then stays within nseg_cap.
+constexpr int kTableThreads = 256;
+
+// inclusive prefix sum of v over the workgroup's lanes (Hillis-Steele through LDS)
+__device__ long long block_scan(long long *part, long long v) {
+    const int tid = threadIdx.x;
+    part[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kTableThreads; off <<= 1) {
+        const long long x = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += x;
+        __syncthreads();
+    }
+    return part[tid];
+}
+
+__global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs a) {
+    __shared__ long long part[kTableThreads];
+    const int tid = threadIdx.x;
+    const long long cap = a.nchunk_cap;
+    long long carry_c = 0, carry_s = 0;  // records and segments of the tiles before
+    for (int base = 0; base < a.B; base += kTableThreads) {
+        const int s = base + tid;
+        long long n = 0;
+        if (s < a.B) {
+            const int t0 = min(max(a.cu_seqlens[s], 0), a.N);
+            const int t1 = min(max(a.cu_seqlens[s + 1], t0), a.N);
+            n = (t1 - t0 + kChunk - 1) / kChunk;
+        }
+        const long long incl = block_scan(part, n);
+        const long long tile = part[kTableThreads - 1];
+        const long long lo = min(carry_c + incl - n, cap), hi = min(carry_c + incl, cap);
+        const long long nseg = (hi - lo + kSegChunks - 1) / kSegChunks;
+        __syncthreads();
+        const long long incl_s = block_scan(part, nseg);
+        const long long tile_s = part[kTableThreads - 1];
+        if (s < a.B) {
+            a.chunk_start[s] = (int)lo;
+            a.seg_start[s] = (int)(carry_s + incl_s - nseg);
+        }
+        carry_c += tile;
+        carry_s += tile_s;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.chunk_start[a.B] = (int)min(carry_c, cap);
+        a.seg_start[a.B] = (int)carry_s;
+    }
+}
+
+template <bool kChunked>
+hipError_t launch_prefill_kernel(const PrefillArgs &a, size_t blocks, hipStream_t stream) {
+    const void *fn = reinterpret_cast<const void *>(&prefill_kernel<kChunked>);
+    static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (attr != hipSuccess) return attr;
+    dim3 grid((unsigned)blocks), block(kThreads);
+    void *args[] = {const_cast<PrefillArgs *>(&a)};
+    return hipLaunchKernel(fn, grid, block, args, kLdsBytes, stream);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (attr != hipSuccess) return attr;
-    dim3 grid((unsigned)((size_t)a.B * a.c.H)), block(kThreads);
+    if (a.path == kPathFused) return launch_prefill_kernel<false>(a, (size_t)a.B * a.c.H, stream);
     void *args[] = {const_cast<PrefillArgs *>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_kernel), grid, block, args, kLdsBytes, stream);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&chunk_table_kernel), dim3(1), dim3(kTableThreads),
+                                   args, 0, stream);
+    if (e != hipSuccess) return e;
+    e = launch_prefill_kernel<true>(a, (size_t)a.nseg_cap * a.c.H, stream);
+    if (e != hipSuccess) return e;
+    return launch_carry(a, stream);
 }
 
 }  // namespace kda

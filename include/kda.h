@@ -54,14 +54,15 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
-    KDA_ERR_BAD_CONFIG = 2, /* head_dim != 128, conv_size != 4, num_heads < 1, bad eps */
+    KDA_ERR_BAD_CONFIG = 2, /* head_dim != 128, conv_size != 4, num_heads < 1, bad eps,
+                               prefill_path outside 0..2 (kda_prefill) */
     KDA_ERR_BAD_SHAPE = 3,  /* negative or inconsistent sizes, or sizes past the limits */
-    KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned */
+    KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned (workspace: 256-byte) */
     KDA_ERR_WORKSPACE = 5,  /* workspace smaller than kda_prefill_workspace_bytes() */
     KDA_ERR_LAUNCH = 6      /* the HIP runtime refused a kernel launch */
 } kda_status;
@@ -75,11 +76,24 @@ typedef struct {
     float l2_eps;           /* added to sum(x^2) inside the sqrt of the q/k L2 norm; 1e-6 */
     float rms_eps;          /* eps of the per-head RMSNorm of o; the loader's rms default 1e-5 */
     float q_scale;          /* scale of the normalised q; <= 0 selects D^-0.5 */
+    int32_t prefill_path;   /* KDA_PREFILL_AUTO, _FUSED or _CHUNKED (kda_prefill only) */
 } kda_config;
+
+/* How kda_prefill lays out its work (the result is the same up to rounding order):
+ *   KDA_PREFILL_FUSED    one workgroup per (sequence, head) walks the sequence chunk by
+ *                        chunk; no workspace.  Fills the GPU when B*H is large.
+ *   KDA_PREFILL_CHUNKED  one workgroup per (64-token chunk, head) computes the chunk's
+ *                        state-independent products into the workspace, then one
+ *                        workgroup per (sequence, head) carries the state through them.
+ *                        Fills the GPU when B*H is small (a few long sequences).
+ *   KDA_PREFILL_AUTO     CHUNKED when B*H < 512, else FUSED. */
+#define KDA_PREFILL_AUTO 0
+#define KDA_PREFILL_FUSED 1
+#define KDA_PREFILL_CHUNKED 2
 
 /* Defaults: H = 96, D = 128, conv 4, gmin -5, l2_eps 1e-6, rms_eps 1e-5, q_scale D^-0.5
  * (page "colibri/c/kimi_k3.c": header comment "KDA per-head recurrence" and the
- * config loader's rms_norm_eps default). */
+ * config loader's rms_norm_eps default), prefill_path KDA_PREFILL_AUTO. */
 kda_config kda_config_default(void);
 
 /*
@@ -101,7 +115,8 @@ kda_config kda_config_default(void);
  *   conv_state             [B, 3*H*D, 3] fp32, read and overwritten in place
  *   out                    [B, H*D] fp32, written; must not overlap any input
  *   stream                 hipStream_t or NULL
- * Alignment: every pointer 16-byte aligned.  Limits: B*H <= 2^31-1.
+ * Alignment: every pointer 16-byte aligned.  Limits: B*H <= 16,777,215 (one
+ * workgroup of 256 lanes per (sequence, head) in one dispatch).
  */
 kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
                            const float *q, const float *k, const float *v,
@@ -114,7 +129,8 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
 /*
  * kda_prefill -- a packed batch of whole sequences (varlen), processed in chunks of
  * 64 tokens with the chunked (WY / UT-transform) form of the same recurrence; returns
- * every token's output and each sequence's final state and conv state.
+ * every token's output and each sequence's final state and conv state.  The work
+ * layout follows cfg->prefill_path (see KDA_PREFILL_*).
  *
  * Follows the header comment "KDA per-head recurrence" (page "colibri/c/kimi_k3.c");
  * the engine's prefill also runs in token chunks (same page, ENV K3_CHUNK).  The
@@ -134,12 +150,19 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
  *   final_state            [B, H, D, D] fp32, written; may be the same pointer as
  *                          initial_state (in-place carry), must not partially overlap it
  *   final_conv_state       [B, 3*H*D, 3] fp32, written; may equal initial_conv_state
- *   workspace              device scratch of workspace_bytes (may be NULL when
- *                          kda_prefill_workspace_bytes() returns 0)
+ *   workspace              device scratch of workspace_bytes >=
+ *                          kda_prefill_workspace_bytes(cfg, B, N), 256-byte aligned;
+ *                          may be NULL when that is 0.  Contents on entry are ignored
+ *                          and on return are unspecified; two calls that overlap in
+ *                          time must not share it.
  *   stream                 hipStream_t or NULL
  * A sequence of length 0 copies its initial state and conv state to the final ones.
  * Alignment: every fp32/bf16 array pointer 16-byte aligned, cu_seqlens 4-byte aligned.
- * Limits: N <= 2^31-1, B*H <= 2^31-1.
+ * Limits: N <= 2^31-1; B*H <= 8,388,607 (one workgroup of 512 lanes per (sequence,
+ * head) in one dispatch); for the chunked layout also (floor(N/64) + B)*H <= 8,388,607
+ * and (floor((floor(N/64) + B)/4) + B)*H <= 8,388,607
+ * (KDA_PREFILL_AUTO falls back to FUSED past it; an explicit CHUNKED returns
+ * KDA_ERR_BAD_SHAPE).
  */
 kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
                        const int32_t *cu_seqlens,
@@ -151,7 +174,11 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
                        float *out, float *final_state, float *final_conv_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
-/* Device scratch kda_prefill needs for these sizes (0 when it needs none). */
+/* Device scratch kda_prefill needs for these sizes with cfg->prefill_path: 0 for the
+ * fused layout; for the chunked one a table of 2(B+1) int32 (padded to 256 bytes) and one
+ * 115,200-byte record per (chunk, head) for floor(N/64) + B chunks (the most that B
+ * sequences of N tokens in total can need).  Returns 0 for arguments kda_prefill would
+ * reject. */
 size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens);
 
 /* Static, NUL-terminated description of a status code. */

@@ -92,8 +92,19 @@ class DecodeRun:
 
 # ------------------------------------------------------------------------------- prefill
 
+_ORACLE_CACHE: dict = {}
+
+
 def prefill_oracle(case: ki.PrefillCase, pairs=None):
-    """The oracle on the case's bf16 activations (their exact values) for the pairs."""
+    """The oracle on the case's bf16 activations (their exact values) for the pairs
+    (memoised per case name, seed and pairs: the tests run each case on both layouts)."""
+    key = (case.name, case.seed, case.H, tuple(case.cu_seqlens.tolist()), None if pairs is None else tuple(pairs))
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE[key] = _prefill_oracle(case, pairs)
+    return _ORACLE_CACHE[key]
+
+
+def _prefill_oracle(case: ki.PrefillCase, pairs=None):
     x = case.x
     p = case.params
     return oracle.forward(oracle_cfg(), case.cu_seqlens, x.q, x.k, x.v, x.z, x.b, x.g, p.conv_w, p.A_log,
@@ -122,9 +133,14 @@ def check_prefill(case: ki.PrefillCase, out, fs, fcs, pairs):
     return worst_o, worst_s
 
 
-def prefill_gpu(case: ki.PrefillCase, dev, in_place: bool = False):
+# kda_config.prefill_path values (kda.PREFILL_*), spelled out so that collecting the
+# tests does not need the library
+PATH_AUTO, PATH_FUSED, PATH_CHUNKED = 0, 1, 2
+
+
+def prefill_gpu(case: ki.PrefillCase, dev, in_place: bool = False, path: int = PATH_AUTO):
     import gated_delta_rule_31_amd as kda
-    cfg = kda.KdaConfig(num_heads=case.H)
+    cfg = kda.KdaConfig(num_heads=case.H, prefill_path=path)
     p = case.params
     cu = t(case.cu_seqlens.astype(np.int32), dev)
     xs = [t(getattr(case.x, n), dev) for n in "qkvzbg"]

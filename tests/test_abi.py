@@ -106,3 +106,54 @@ def test_prefill_rejects_bad_arguments():
 
 def test_workspace_query_is_host_only():
     assert kda.kda_prefill_workspace_bytes(kda.KdaConfig(), 16, 40000) >= 0
+
+
+REC_BYTES = 115200  # one chunk record
+
+
+def _ws(cfg, B, N):
+    return kda.lib().kda_prefill_workspace_bytes(ctypes.byref(cfg), B, N)
+
+
+def test_prefill_path_selection_and_workspace_size():
+    # fused: no workspace
+    assert _ws(_cfg(prefill_path=1), 1, 8192) == 0
+    # chunked: 2(B+1) int32 padded to 256 bytes, then floor(N/64) + B records per head
+    assert _ws(_cfg(prefill_path=2, num_heads=96), 1, 8192) == 256 + (128 + 1) * 96 * REC_BYTES
+    assert _ws(_cfg(prefill_path=2, num_heads=4), 100, 1000) == 1024 + (15 + 100) * 4 * REC_BYTES
+    # auto: chunked below 512 (sequence, head) units, fused from there on
+    assert _ws(_cfg(num_heads=96), 5, 8192) == _ws(_cfg(prefill_path=2, num_heads=96), 5, 8192)
+    assert _ws(_cfg(num_heads=96), 6, 8192) == 0
+    # sizes the call would reject
+    assert _ws(_cfg(prefill_path=2), -1, 10) == 0
+    assert _ws(_cfg(prefill_path=7), 1, 10) == 0
+
+
+def test_prefill_rejects_bad_path_and_small_or_misaligned_workspace():
+    assert _prefill(_cfg(prefill_path=3), 1, 8) == BAD_CONFIG
+    assert _prefill(_cfg(prefill_path=-1), 1, 8) == BAD_CONFIG
+    need = _ws(_cfg(prefill_path=2), 2, 100)
+    p = [ctypes.c_void_p(FAKE)] * 16
+    lib = kda.lib()
+
+    def call(ws, nbytes, path=2):
+        c = _cfg(prefill_path=path)
+        return lib.kda_prefill(ctypes.byref(c), 2, 100, *p, ws, nbytes, None)
+
+    assert call(None, 0) == WORKSPACE
+    assert call(ctypes.c_void_p(FAKE), need - 1) == WORKSPACE
+    assert call(None, need) == WORKSPACE
+    assert call(ctypes.c_void_p(FAKE + 16), need) == MISALIGNED
+    # the fused layout takes no workspace, so none is checked
+    assert _ws(_cfg(prefill_path=1), 2, 100) == 0
+
+
+def test_launch_size_limits():
+    # one workgroup per (sequence, head); a dispatch holds < 2^32 work-items
+    assert _decode(_cfg(num_heads=1), 16_777_216) == BAD_SHAPE
+    assert _prefill(_cfg(num_heads=1, prefill_path=1), 8_388_608, 0) == BAD_SHAPE
+    # chunked: (floor(N/64) + B) * H workgroups; auto falls back to fused past the limit
+    big_n = 64 * 8_388_608
+    assert _ws(_cfg(num_heads=1, prefill_path=2), 1, big_n) == 0
+    assert _prefill(_cfg(num_heads=1, prefill_path=2), 1, big_n) == BAD_SHAPE
+    assert _ws(_cfg(num_heads=1), 1, big_n) == 0

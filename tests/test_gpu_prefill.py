@@ -1,92 +1,126 @@
 """GPU parity of kda_prefill (bf16 inputs, chunk 64, fp32 state) against the fp64 oracle:
 max abs error 2e-2 on the gated RMS-normalised outputs, max relative error 5e-3 per
-(sequence, head) on final states, exact final conv windows."""
+(sequence, head) on final states, exact final conv windows.  Every case runs on both
+work layouts (fused; chunk records + carry), which must also agree with each other
+bit for bit."""
+import functools
+
 import numpy as np
 import pytest
 import torch
 
 import kda_inputs as ki
-from tests.parity import (PREFILL_OUT_ABS_TOL, PREFILL_STATE_REL_TOL, DecodeRun, check_prefill, prefill_gpu,
-                          slice_rel, t)
+from tests.parity import (PATH_CHUNKED, PATH_FUSED, PREFILL_OUT_ABS_TOL, PREFILL_STATE_REL_TOL, DecodeRun,
+                          check_prefill, prefill_gpu, slice_rel, t)
 
 pytestmark = pytest.mark.gpu
 
 D = 128
 
+PATHS = [pytest.param(PATH_FUSED, id="fused"), pytest.param(PATH_CHUNKED, id="chunked")]
 
-def _run_and_check(case, dev, pairs=None, in_place=False):
+
+def _run_and_check(case, dev, path, pairs=None, in_place=False):
     if pairs is None:
         pairs = [(s, h) for s in range(case.B) for h in range(case.H)]
-    print(f"[prefill] {case.name} B={case.B} N={case.N} H={case.H} pairs={len(pairs)}", flush=True)
-    out, fs, fcs = prefill_gpu(case, dev, in_place=in_place)
+    print(f"[prefill] {case.name} path={path} B={case.B} N={case.N} H={case.H} pairs={len(pairs)}", flush=True)
+    out, fs, fcs = prefill_gpu(case, dev, in_place=in_place, path=path)
     eo, es = check_prefill(case, out, fs, fcs, pairs)
-    print(f"[prefill] {case.name}: out abs err {eo:.3e}, state rel err {es:.3e}", flush=True)
+    print(f"[prefill] {case.name} path={path}: out abs err {eo:.3e}, state rel err {es:.3e}", flush=True)
     assert eo <= PREFILL_OUT_ABS_TOL, eo
     assert es <= PREFILL_STATE_REL_TOL, es
     return out, fs, fcs
 
 
-def test_cfg0_single_chunk(device):
-    _run_and_check(ki.case0_prefill(), device)
+@functools.lru_cache(maxsize=None)
+def _case2():
+    return ki.case2_prefill()
 
 
+@functools.lru_cache(maxsize=None)
+def _case3():
+    return ki.case3_prefill()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_cfg0_single_chunk(device, path):
+    _run_and_check(ki.case0_prefill(), device, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("T", [1, 3, 17, 63, 64, 65, 200])
-def test_ragged_lengths_with_initial_state(device, T):
+def test_ragged_lengths_with_initial_state(device, T, path):
     case = ki.prefill_case(100 + T, 3, [T], True, f"ragged-{T}")
-    _run_and_check(case, device)
+    _run_and_check(case, device, path)
 
 
-def test_varlen_small_with_empty_and_short_sequences(device):
+@pytest.mark.parametrize("path", PATHS)
+def test_varlen_small_with_empty_and_short_sequences(device, path):
     case = ki.prefill_case(120, 2, [5, 0, 1, 2, 70, 64, 129, 3, 300], True, "varlen-small")
-    _run_and_check(case, device)
+    _run_and_check(case, device, path)
 
 
-def test_zero_initial_state_multi_chunk(device):
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_initial_state_multi_chunk(device, path):
     case = ki.prefill_case(121, 4, [333, 190], False, "zero-init")
-    _run_and_check(case, device)
+    _run_and_check(case, device, path)
 
 
-def test_in_place_state_carry(device):
+@pytest.mark.parametrize("path", PATHS)
+def test_in_place_state_carry(device, path):
     case = ki.prefill_case(122, 2, [150, 77], True, "in-place")
-    _run_and_check(case, device, in_place=True)
+    _run_and_check(case, device, path, in_place=True)
 
 
-def test_cfg2_long_sequence_sampled_heads(device):
-    case = ki.case2_prefill()
+@pytest.mark.parametrize("path", PATHS)
+def test_cfg2_long_sequence_sampled_heads(device, path):
     pairs = [(0, h) for h in (0, 17, 41, 63, 80, 95)]
-    _run_and_check(case, device, pairs)
+    _run_and_check(_case2(), device, path, pairs)
 
 
-def test_cfg3_varlen_sampled(device):
-    case = ki.case3_prefill()
+@pytest.mark.parametrize("path", PATHS)
+def test_cfg3_varlen_sampled(device, path):
+    case = _case3()
     rng = np.random.default_rng(303)
     pairs = [(0, 0), (case.B - 1, case.H - 1)]
     pairs += [(int(s), int(h)) for s, h in zip(rng.integers(0, case.B, 10), rng.integers(0, case.H, 10))]
-    _run_and_check(case, device, pairs)
+    _run_and_check(case, device, path, pairs)
 
 
-def test_packing_invariance(device):
+def test_layouts_agree_bitwise(device):
+    """The chunked layout performs the fused kernel's arithmetic in the same order, so
+    the two give identical bits (outputs, final states, final windows)."""
+    case = ki.prefill_case(126, 3, [1, 64, 130, 0, 257], True, "layouts")
+    a = prefill_gpu(case, device, path=PATH_FUSED)
+    b = prefill_gpu(case, device, path=PATH_CHUNKED)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_packing_invariance(device, path):
     """Each sequence of a packed batch gives what it gives alone."""
     case = ki.prefill_case(123, 2, [90, 31, 200], True, "packed")
-    out, fs, fcs = prefill_gpu(case, device)
+    out, fs, fcs = prefill_gpu(case, device, path=path)
     cu = case.cu_seqlens
     for s in range(case.B):
         alone = ki.PrefillCase(f"alone-{s}", case.seed, case.H, np.array([0, cu[s + 1] - cu[s]], np.int32),
                                case.params,
                                ki.TokenInputs(*(getattr(case.x, n)[cu[s]:cu[s + 1]] for n in "qkvzbg")),
                                case.initial_state[s:s + 1], case.initial_conv_state[s:s + 1])
-        o1, f1, c1 = prefill_gpu(alone, device)
+        o1, f1, c1 = prefill_gpu(alone, device, path=path)
         assert torch.equal(o1, out[cu[s]:cu[s + 1]])
         assert torch.equal(f1[0], fs[s])
         assert torch.equal(c1[0], fcs[s])
 
 
-def test_prefill_matches_decode_steps(device):
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_matches_decode_steps(device, path):
     """32 decode steps on the bf16-rounded tokens give the 32-token prefill's result
     (fp32 decode vs chunked bf16-MFMA prefill, within the prefill tolerances)."""
     H, T = 4, 32
     case = ki.prefill_case(124, H, [T], True, "decode-vs-prefill")
-    out, fs, fcs = prefill_gpu(case, device)
+    out, fs, fcs = prefill_gpu(case, device, path=path)
     x = case.x.as_f32()
     steps = [ki.TokenInputs(*(getattr(x, n)[i:i + 1] for n in "qkvzbg")) for i in range(T)]
     dcase = ki.DecodeCase("dec", case.seed, 1, H, T, case.params, case.initial_state, case.initial_conv_state,
@@ -101,11 +135,12 @@ def test_prefill_matches_decode_steps(device):
     assert torch.equal(fcs, run.conv_state)
 
 
-def test_empty_batch_and_stream(device):
+@pytest.mark.parametrize("path", PATHS)
+def test_empty_batch_and_stream(device, path):
     import gated_delta_rule_31_amd as kda
     case = ki.prefill_case(125, 2, [40], True, "stream")
-    o1, f1, _ = prefill_gpu(case, device)
-    cfg = kda.KdaConfig(num_heads=2)
+    o1, f1, _ = prefill_gpu(case, device, path=path)
+    cfg = kda.KdaConfig(num_heads=2, prefill_path=path)
     p = case.params
     s = torch.cuda.Stream()
     args = [t(getattr(case.x, n), device) for n in "qkvzbg"]

@@ -13,8 +13,13 @@
 // owns value columns 16w .. 16w+15 for all 128 keys.  Inside each 32-key block the rows
 // of the two 16-row accumulator tiles interleave (tile x, row m -> key 32P + 8(m/4) + 4x
 // + m%4), so a lane's 8 accumulator values of one column are 8 consecutive keys, the
-// B-operand layout of a K = 32 MFMA; U interleaves its tokens the same way.  The record
-// of the next chunk is loaded into registers while the current one is used.
+// B-operand layout of a K = 32 MFMA; U interleaves its tokens the same way.
+//
+// Overlap: the next chunk's record is loaded into registers in three parts, issued
+// between the phases of the current chunk (a record is 115 KB per workgroup, about 2K
+// cycles of the compute unit's load path, so issuing it at once would stall every wave
+// behind it), and a chunk's epilogue runs after the next chunk's first barrier, beside
+// that chunk's MFMAs, from a second O tile.
 
 #include "kda_device.hpp"
 
@@ -26,9 +31,10 @@ constexpr int kCarryThreads = 512;
 // ---- LDS map (bytes) ----
 constexpr int C_E = REC_IMG;                         // e^{G_end} fp32 [128]
 constexpr int C_NW = C_E + 512;                      // norm_w fp32 [128]
-constexpr int C_O = C_NW + 512;                      // O fp32 [64][CO_LD]
+constexpr int C_O = C_NW + 512;                      // O fp32 [2 tiles][64][CO_LD]
 constexpr int CO_LD = 132;                           // padded row pitch of O
-constexpr int kCarryLds = C_O + kChunk * CO_LD * 4;  // the operand images sit at 0
+constexpr int kOTile = kChunk * CO_LD;               // floats of one O tile
+constexpr int kCarryLds = C_O + 2 * kOTile * 4;      // the operand images sit at 0
 static_assert(kCarryLds <= 160 * 1024, "LDS budget");
 static_assert(REC_IMG % (16 * kCarryThreads) == 0, "image pieces split evenly over the lanes");
 constexpr int kImgPieces = REC_IMG / 16 / kCarryThreads;  // 10
@@ -41,19 +47,21 @@ struct RecordLoads {
     f32x4 u[2][2];  // [tp][x]
 };
 
-__device__ __forceinline__ RecordLoads load_record(const unsigned char *rec, int tid) {
-    RecordLoads r;
-    const int w = tid >> 6, lane = tid & 63;
+// image pieces J0 .. J1-1 of a record
+template <int J0, int J1>
+__device__ __forceinline__ void load_images(RecordLoads &r, const unsigned char *rec, int tid) {
 #pragma unroll
-    for (int j = 0; j < kImgPieces; ++j)
-        r.img[j] = *reinterpret_cast<const u32x4 *>(rec + (tid + kCarryThreads * j) * 16);
+    for (int j = J0; j < J1; ++j) r.img[j] = *reinterpret_cast<const u32x4 *>(rec + (tid + kCarryThreads * j) * 16);
+}
+// e^{G_end} and U' of a record
+__device__ __forceinline__ void load_tail(RecordLoads &r, const unsigned char *rec, int tid) {
+    const int w = tid >> 6, lane = tid & 63;
     r.e = *reinterpret_cast<const u32x4 *>(rec + REC_E + min(tid, 31) * 16);
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
         for (int x = 0; x < 2; ++x)
             r.u[tp][x] = *reinterpret_cast<const f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
-    return r;
 }
 
 // Lane coordinates from an opaque copy of the thread id, re-derived in every phase so
@@ -112,16 +120,53 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         if (tid_ < kD) sNw[tid_] = a.norm_w[tid_];
     }
 
+    // out = sigmoid(g) * RMSNorm(O) for the L tokens from c0 of an O tile: eight adjacent
+    // lanes own one token row (16 values each), 16-byte loads and stores
+    auto epilogue = [&](const float *tile, const u32x4 *graw, int c0, int L) {
+        int tid_ = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid_));
+        const int tok = tid_ >> 3;
+        const int v0 = 16 * (tid_ & 7);
+        float o[16];
+        lds_read8(tile + tok * CO_LD + v0, o);
+        lds_read8(tile + tok * CO_LD + v0 + 8, o + 8);
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ss += o[j] * o[j];
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        ss += __shfl_xor(ss, 4, 64);
+        if (tok < L) {
+            const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
+            float *orow = a.out + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float g8[8], nw[8], y[8];
+                unpack8(graw[j], g8);
+                lds_read8(sNw + v0 + 8 * j, nw);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[8 * j + e] * rinv * nw[e]);
+                *reinterpret_cast<float4 *>(orow + 8 * j) = make_float4(y[0], y[1], y[2], y[3]);
+                *reinterpret_cast<float4 *>(orow + 8 * j + 4) = make_float4(y[4], y[5], y[6], y[7]);
+            }
+        }
+    };
+
     RecordLoads ld = {};
     if (nrec > 0) {
         int tid_ = (int)threadIdx.x;
         asm volatile("" : "+v"(tid_));
-        ld = load_record(rec0, tid_);
+        load_images<0, kImgPieces>(ld, rec0, tid_);
+        load_tail(ld, rec0, tid_);
     }
+    u32x4 gprev[2] = {};  // output-gate logits of the previous chunk
 
     for (int c = 0; c < nrec; ++c) {
         const int c0 = c * kChunk;
         const int L = min(kChunk, T - c0);
+        const bool more = c + 1 < nrec;
+        const unsigned char *next = rec0 + (size_t)(c + 1) * rec_stride;
+        float *tile = sO + (c & 1) * kOTile;
 
         // ---- this chunk's operand images and e^{G_end} into LDS; U' into registers ----
         f32x4 U[2][2];
@@ -137,26 +182,26 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
 #pragma unroll
                 for (int x = 0; x < 2; ++x) U[tp][x] = ld.u[tp][x];
         }
-        __syncthreads();
+        lds_barrier();
 
-        // the next record, and this chunk's output-gate logits, are requested now to
-        // arrive during the MFMAs
-        u32x4 graw[2];
+        // the previous chunk's epilogue (a full chunk: only the last can be partial)
+        if (c > 0) epilogue(sO + ((c - 1) & 1) * kOTile, gprev, c0 - kChunk, kChunk);
+        // this chunk's output-gate logits, used by its epilogue one chunk later
+        u32x4 gcur[2];
         {
             int tid_ = (int)threadIdx.x;
             asm volatile("" : "+v"(tid_));
-            // (the logits first: the epilogue's wait for them then does not include the
-            //  record, which is only needed at the next chunk's start)
             const int tok = min(tid_ >> 3, L - 1);
             const uint16_t *gp = a.g + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + 16 * (tid_ & 7);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) graw[j] = *reinterpret_cast<const u32x4 *>(gp + 8 * j);
-            if (c + 1 < nrec) ld = load_record(rec0 + (size_t)(c + 1) * rec_stride, tid_);
+            for (int j = 0; j < 2; ++j) gcur[j] = *reinterpret_cast<const u32x4 *>(gp + 8 * j);
+            if (more) load_images<0, 4>(ld, next, tid_);
         }
 
+        bf16x8 Sh[4];  // S0 as the B operand of key contractions
+        bf16x8 Uh[2], Ul[2];  // U as the B operand of token contractions, hi/lo [tp]
         {
             CARRY_LANE_IDS();
-            bf16x8 Sh[4];  // S0 as the B operand of key contractions
 #pragma unroll
             for (int P = 0; P < 4; ++P) {
                 const float v8[8] = {S[P][0][0], S[P][0][1], S[P][0][2], S[P][0][3],
@@ -172,18 +217,25 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                     f32x4 ws = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int P = 0; P < 4; ++P) {
-                        const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + sw128(trow, 32 * P + 8 * lg));
+                        const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + swi128(trow, 32 * P + 8 * lg));
                         ws = mma(A8, Sh[P], ws);
                     }
                     U[tp][x] -= ws;
                 }
-            bf16x8 Uh[2], Ul[2];  // [tp]
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp) {
                 const float v8[8] = {U[tp][0][0], U[tp][0][1], U[tp][0][2], U[tp][0][3],
                                      U[tp][1][0], U[tp][1][1], U[tp][1][2], U[tp][1][3]};
                 split8(v8, Uh[tp], Ul[tp]);
             }
+        }
+        {
+            int tid_ = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid_));
+            if (more) load_images<4, 7>(ld, next, tid_);
+        }
+        {
+            CARRY_LANE_IDS();
             // O = Q~ S0 + P U   (rows: token 16tt + 4lg + i)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
@@ -203,8 +255,19 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                     acc = mma(Ph, Ul[tp], acc);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sO[(16 * tt + 4 * lg + i) * CO_LD + 16 * w + lr] = acc[i];
+                for (int i = 0; i < 4; ++i) tile[(16 * tt + 4 * lg + i) * CO_LD + 16 * w + lr] = acc[i];
             }
+        }
+        {
+            int tid_ = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid_));
+            if (more) {
+                load_images<7, kImgPieces>(ld, next, tid_);
+                load_tail(ld, next, tid_);
+            }
+        }
+        {
+            CARRY_LANE_IDS();
             // S = Diag(e^{G_end}) S0 + K_end^T U
 #pragma unroll
             for (int P = 0; P < 4; ++P)
@@ -214,8 +277,8 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                     f32x4 acc = S[P][x] * *reinterpret_cast<const f32x4 *>(sE + 32 * P + 8 * lg + 4 * x);
 #pragma unroll
                     for (int tp = 0; tp < 2; ++tp) {
-                        const bf16x8 Kh = *reinterpret_cast<const bf16x8 *>(sKh + sw64(krow, 32 * tp + 8 * lg));
-                        const bf16x8 Kl = *reinterpret_cast<const bf16x8 *>(sKl + sw64(krow, 32 * tp + 8 * lg));
+                        const bf16x8 Kh = *reinterpret_cast<const bf16x8 *>(sKh + swi64(krow, 32 * tp + 8 * lg));
+                        const bf16x8 Kl = *reinterpret_cast<const bf16x8 *>(sKl + swi64(krow, 32 * tp + 8 * lg));
                         acc = mma(Kh, Uh[tp], acc);
                         acc = mma(Kl, Uh[tp], acc);
                         acc = mma(Kh, Ul[tp], acc);
@@ -223,41 +286,12 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                     S[P][x] = acc;
                 }
         }
-        __syncthreads();
-
-        // ---- out = sigmoid(g) * RMSNorm(O): eight adjacent lanes own one token row ----
-        // (the next chunk's image writes go to other LDS and its O writes follow its
-        //  first barrier, so no barrier closes this step)
-        {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
-            const int tok = tid_ >> 3;
-            const int v0 = 16 * (tid_ & 7);
-            float o[16];
-            lds_read8(sO + tok * CO_LD + v0, o);
-            lds_read8(sO + tok * CO_LD + v0 + 8, o + 8);
-            float ss = 0.f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) ss += o[j] * o[j];
-            ss += __shfl_xor(ss, 1, 64);
-            ss += __shfl_xor(ss, 2, 64);
-            ss += __shfl_xor(ss, 4, 64);
-            if (tok < L) {
-                const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
-                float *orow = a.out + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float g8[8], nw[8], y[8];
-                    unpack8(graw[j], g8);
-                    lds_read8(sNw + v0 + 8 * j, nw);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[8 * j + e] * rinv * nw[e]);
-                    *reinterpret_cast<float4 *>(orow + 8 * j) = make_float4(y[0], y[1], y[2], y[3]);
-                    *reinterpret_cast<float4 *>(orow + 8 * j + 4) = make_float4(y[4], y[5], y[6], y[7]);
-                }
-            }
-        }
+        gprev[0] = gcur[0];
+        gprev[1] = gcur[1];
+        lds_barrier();  // the operand images are rewritten by the next chunk
     }
+    if (nrec > 0)
+        epilogue(sO + ((nrec - 1) & 1) * kOTile, gprev, (nrec - 1) * kChunk, min(kChunk, T - (nrec - 1) * kChunk));
 
     // ---- final state ----
     {

@@ -20,6 +20,18 @@ __device__ __forceinline__ int sw64(int row, int col) {
 __device__ __forceinline__ int sw128(int row, int col) {
     return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
 }
+// The same tiles for A operands read with the accumulator row interleave (lane l reads
+// row 32p + 8(l/4) + 4x + l%4): the chunk index is XORed with a row function that is
+// distinct over the rows 8 consecutive lanes read (row & 7 repeats after 4 of them,
+// which costs a 2-way bank conflict on every read).
+__device__ __forceinline__ int swi64(int row, int col) {
+    const int f = (row & 3) | ((row >> 1) & 4);
+    return row * 64 + (((col >> 3) ^ f) << 3) + (col & 7);
+}
+__device__ __forceinline__ int swi128(int row, int col) {
+    const int f = (row & 3) | ((row >> 1) & 12);
+    return row * 128 + (((col >> 3) ^ f) << 3) + (col & 7);
+}
 
 // D += A B on one 16x16 tile.  bf16, K = 32: lane l holds A[l%16][8(l/16)+j] and
 // B[8(l/16)+j][l%16] (j < 8) and receives D[4(l/16)+i][l%16] (i < 4).
@@ -30,6 +42,14 @@ __device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, f32x4 c) 
 __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+
+// Workgroup barrier for LDS traffic.  __syncthreads() also waits for all of the wave's
+// outstanding global loads and stores (this GPU counts both on one counter), which would
+// expose the latency of prefetches and output stores meant to run across it; this one
+// waits for the wave's LDS operations only.  Use it where every cross-wave dependency
+// goes through LDS.  The memory clobber keeps the compiler from moving any memory
+// access across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 // sigmoid with the hardware reciprocal (about 1 ulp) instead of an IEEE division
@@ -76,11 +96,11 @@ __device__ __forceinline__ void lds_write8(float *p, const float *x) {
 // the state-side products, U' is stored in the register order of the consumer (value
 // column group cg of 16, token pair tp, interleave x, lane: 16 bytes each, the
 // accumulator rows of token 32tp + 8(l/16) + 4x + i, column 16cg + l%16).
-constexpr int REC_W = 0;           // W = T (beta k e^G)        bf16 sw128 [64 tok][128 key]
+constexpr int REC_W = 0;           // W = T (beta k e^G)        bf16 swi128 [64 tok][128 key]
 constexpr int REC_Q = 16384;       // Q~ = q e^G                 bf16 sw128 [64 tok][128 key]
 constexpr int REC_PH = 32768;      // P, hi part                 bf16 sw64  [64 tok][64 tok]
 constexpr int REC_PL = 40960;      // P, lo part
-constexpr int REC_KH = 49152;      // K_end^T = (k e^{G_end-G})^T, hi   bf16 sw64 [128 key][64 tok]
+constexpr int REC_KH = 49152;      // K_end^T = (k e^{G_end-G})^T, hi   bf16 swi64 [128 key][64 tok]
 constexpr int REC_KL = 65536;      // K_end^T, lo part
 constexpr int REC_IMG = 81920;     // bytes of the five operand images
 constexpr int REC_U = 81920;       // U' = T (beta v)            fp32 [8 cg][2 tp][2 x][64 lanes][4]

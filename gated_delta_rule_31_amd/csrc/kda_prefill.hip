@@ -263,6 +263,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
 
     const int cend = kChunked ? min(min(cbeg + kSegChunks * kChunk, nrec * kChunk), T) : T;
+    // (inside the chunk loop every cross-wave dependency goes through LDS, so its
+    //  barriers wait for LDS traffic only: the next chunk's loads and this chunk's output
+    //  stores stay in flight across them)
     for (int c0 = cbeg; c0 < cend; c0 += kChunk) {
         const int L = min(kChunk, T - c0);
 
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 *reinterpret_cast<u32x4 *>(sStage + (blk * STG_ROWS + row) * STG_LD + piece) = ld.hist;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ================= phase 1: conv, SiLU, partial norms, gates =================
         float uq[16], uk[16], gs[16];  // q, k before the norm; G_t - r_sub of the 16 channels
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             }
             if (lg == 0 && half == 0) sBeta[t] = beta;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- per-chunk channel tables (threads 0..255), and this lane's operand rows ----
         float qr[16], kr[16], cbk[16];  // q e^{G-r}, k e^{G-r}, k e^{r-G} of the normalised q, k
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             lds_write8(sCB + t * CB_LD + cbase, cbk);
             lds_write8(sCB + t * CB_LD + cbase + 8, cbk + 8);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- rows that need the tables; MFMA operands of block row `sub` ----
         bf16x8 ak[2], aqh[2], aql[2], qe8[2];  // k e^{G-r}, q e^{G-r} (hi/lo), q e^G
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         {
             KDA_LANE_IDS();
             const int lane = tid_ & 63;
@@ -525,12 +528,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 for (int j = 0; j < 16; ++j) {
                     const int c = 64 * half + 16 * lg + j;
                     const __bf16 hi = (__bf16)ke[j];
-                    sKeHi[sw64(c, t)] = hi;
-                    sKeLo[sw64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                    sKeHi[swi64(c, t)] = hi;
+                    sKeLo[swi64(c, t)] = (__bf16)(ke[j] - (float)hi);
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ================= phase 3: T = (I + A)^-1 in fp32 =================
         // (first the next chunk's raw inputs are requested, to arrive during phases 3-5;
@@ -566,8 +569,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 for (int j = 0; j < 16; ++j) {
                     const int c = 16 * lg + j;
                     const __bf16 hi = (__bf16)ke[j];
-                    sKeHi[sw64(c, t)] = hi;
-                    sKeLo[sw64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                    sKeHi[swi64(c, t)] = hi;
+                    sKeLo[swi64(c, t)] = (__bf16)(ke[j] - (float)hi);
                 }
             } else {
                 // upper blocks (I < J) of sTb: 6 blocks x 256 values over 256 lanes
@@ -580,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ: wave J walks column J
         // downward, so every T_KJ it needs is its own earlier result and only the diagonal
         // blocks come from other waves (fp32 MFMA; the sum M is parked in the unused upper
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // sT is dead: Q~ = q e^G into region 6
         {
             KDA_LANE_IDS();
@@ -639,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     acc = mma(A8, B8, acc);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sW[sw128(16 * tt + 4 * lg + i, 16 * w + lr)] = (__bf16)acc[i];
+                for (int i = 0; i < 4; ++i) sW[swi128(16 * tt + 4 * lg + i, 16 * w + lr)] = (__bf16)acc[i];
             }
             const int vrow = 16 * w + lr;
 #pragma unroll
@@ -660,7 +663,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     U[tp][x] = acc;
                 }
         }
-        __syncthreads();
+        lds_barrier();
 
         if constexpr (kChunked) {
             // ================= the chunk record (layout in kda_device.hpp) =================
@@ -685,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             }
             if (tid_ < 32)
                 *reinterpret_cast<u32x4 *>(rec + REC_E + tid_ * 16) = *reinterpret_cast<const u32x4 *>(sExpEnd + 4 * tid_);
-            __syncthreads();  // LDS is rewritten by the next chunk
+            lds_barrier();  // LDS is rewritten by the next chunk
             continue;
         }
 
@@ -718,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     f32x4 ws = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int P = 0; P < 4; ++P) {
-                        const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + sw128(trow, 32 * P + 8 * lg));
+                        const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + swi128(trow, 32 * P + 8 * lg));
                         ws = mma(A8, Sh[P], ws);
                     }
                     U[tp][x] -= ws;
@@ -762,8 +765,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     for (int i = 0; i < 4; ++i) acc[i] *= sExpEnd[32 * P + 8 * lg + 4 * x + i];
 #pragma unroll
                     for (int tp = 0; tp < 2; ++tp) {
-                        const bf16x8 Kh = *reinterpret_cast<const bf16x8 *>(sKeHi + sw64(krow, 32 * tp + 8 * lg));
-                        const bf16x8 Kl = *reinterpret_cast<const bf16x8 *>(sKeLo + sw64(krow, 32 * tp + 8 * lg));
+                        const bf16x8 Kh = *reinterpret_cast<const bf16x8 *>(sKeHi + swi64(krow, 32 * tp + 8 * lg));
+                        const bf16x8 Kl = *reinterpret_cast<const bf16x8 *>(sKeLo + swi64(krow, 32 * tp + 8 * lg));
                         acc = mma(Kh, Uh[tp], acc);
                         acc = mma(Kl, Uh[tp], acc);
                         acc = mma(Kh, Ul[tp], acc);
@@ -771,7 +774,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     S[P][x] = acc;
                 }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ================= epilogue: out = sigmoid(g) * RMSNorm(o) =================
         // eight adjacent lanes own one token row: 16 values each, 16-byte loads and stores
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 }
             }
         }
-        __syncthreads();  // LDS is rewritten by the next chunk
+        lds_barrier();  // LDS is rewritten by the next chunk
     }
 
     if constexpr (kChunked) return;  // the carry kernel writes the final state and windows

@@ -550,12 +550,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             KDA_LANE_IDS();
             if (w < 4) {
                 if (lg == 0) {
+                    // the block's strictly lower part is read up front (the same 120 values
+                    // in all 16 lanes), so that no step of the substitution waits for LDS
+                    float arow[16][16];
+#pragma unroll
+                    for (int tt = 1; tt < 16; ++tt)
+#pragma unroll
+                        for (int j = 0; j < tt; ++j) arow[tt][j] = sA[(16 * w + tt) * F_LD + 16 * w + j];
                     float xcol[16];
 #pragma unroll
                     for (int tt = 0; tt < 16; ++tt) {
                         float acc = (tt == lr) ? 1.0f : 0.0f;
 #pragma unroll
-                        for (int j = 0; j < tt; ++j) acc -= sA[(16 * w + tt) * F_LD + 16 * w + j] * xcol[j];
+                        for (int j = 0; j < tt; ++j) acc -= arow[tt][j] * xcol[j];
                         xcol[tt] = acc;
                     }
 #pragma unroll

@@ -1,6 +1,6 @@
 // kda_carry.hip -- the sequential half of the chunked prefill plan (gfx950).
 //
-// One workgroup of 4 waves per (sequence, head) walks the sequence's chunk records, which
+// One workgroup of 8 waves per (sequence, head) walks the sequence's chunk records, which
 // the chunk kernel (kda_prefill.hip) wrote, and carries the 128x128 fp32 state in MFMA
 // accumulator registers.  Per chunk, in the notation of the chunk algebra there,
 //   U = U' - W S0,   O = Q~ S0 + P U,   S_end = Diag(e^{G_end}) S0 + K_end^T U,

@@ -64,11 +64,11 @@ __device__ __forceinline__ void load_tail(RecordLoads &r, const unsigned char *r
             r.u[tp][x] = *reinterpret_cast<const f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
 }
 
-// Lane coordinates from an opaque copy of the thread id, re-derived in every phase so
-// that the compiler keeps no lane-dependent LDS address live across the chunk loop.
+// Lane coordinates.  (Unlike the chunk kernel, this one has the registers to keep its
+// lane-dependent LDS addresses across the chunk loop, so the compiler may hoist them: that
+// halves the loop's VALU work.)
 #define CARRY_LANE_IDS()                                       \
     int tid_ = (int)threadIdx.x;                               \
-    asm volatile("" : "+v"(tid_));                             \
     const int w = __builtin_amdgcn_readfirstlane(tid_ >> 6);   \
     const int lr = tid_ & 15;                                  \
     const int lg = (tid_ >> 4) & 3;                            \
@@ -123,8 +123,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
     // out = sigmoid(g) * RMSNorm(O) for the L tokens from c0 of an O tile: eight adjacent
     // lanes own one token row (16 values each), 16-byte loads and stores
     auto epilogue = [&](const float *tile, const u32x4 *graw, int c0, int L) {
-        int tid_ = (int)threadIdx.x;
-        asm volatile("" : "+v"(tid_));
+        const int tid_ = (int)threadIdx.x;
         const int tok = tid_ >> 3;
         const int v0 = 16 * (tid_ & 7);
         float o[16];
@@ -154,8 +153,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
 
     RecordLoads ld = {};
     if (nrec > 0) {
-        int tid_ = (int)threadIdx.x;
-        asm volatile("" : "+v"(tid_));
+        const int tid_ = (int)threadIdx.x;
         load_images<0, kImgPieces>(ld, rec0, tid_);
         load_tail(ld, rec0, tid_);
     }
@@ -171,8 +169,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         // ---- this chunk's operand images and e^{G_end} into LDS; U' into registers ----
         f32x4 U[2][2];
         {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
+            const int tid_ = (int)threadIdx.x;
 #pragma unroll
             for (int j = 0; j < kImgPieces; ++j)
                 *reinterpret_cast<u32x4 *>(smem + (tid_ + kCarryThreads * j) * 16) = ld.img[j];
@@ -189,8 +186,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         // this chunk's output-gate logits, used by its epilogue one chunk later
         u32x4 gcur[2];
         {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
+            const int tid_ = (int)threadIdx.x;
             const int tok = min(tid_ >> 3, L - 1);
             const uint16_t *gp = a.g + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + 16 * (tid_ & 7);
 #pragma unroll
@@ -230,8 +226,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
             }
         }
         {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
+            const int tid_ = (int)threadIdx.x;
             if (more) load_images<4, 7>(ld, next, tid_);
         }
         {
@@ -259,8 +254,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
             }
         }
         {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
+            const int tid_ = (int)threadIdx.x;
             if (more) {
                 load_images<7, kImgPieces>(ld, next, tid_);
                 load_tail(ld, next, tid_);

@@ -38,6 +38,18 @@ def decode_bytes(B: int, H: int) -> int:
     return state + conv + tok + out + params
 
 
+def decode_multi_bytes(B: int, H: int, T: int) -> int:
+    """Algorithmic HBM bytes of one T-token decode call: the state and windows move once,
+    the token inputs and outputs once per token."""
+    HD = H * D
+    state = 2 * B * H * D * D * 4
+    conv = 2 * B * 3 * HD * 3 * 4
+    tok = T * (3 * B * HD + 2 * B * HD + B * H) * 4
+    out = T * B * HD * 4
+    params = (3 * HD * 4 + HD + H + D) * 4
+    return state + conv + tok + out + params
+
+
 def chunk_flops(L: int, d: int = D) -> int:
     """Algorithmic FLOPs of one chunk of L tokens for one head (multiply-add = 2;
     masked triangles not counted): A, P, the UT inverse, W and U', the three state
@@ -145,6 +157,49 @@ def bench_decode(args, dev):
                   "kernel_avg_us": round(kern_ms * 1e3, 2),
                   "state_only_frac": round(state_b / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     )
+
+
+def bench_decode_multi(args, dev, T: int):
+    """T known tokens per sequence in one kda_decode_multi call, 64 sequences x 96 heads,
+    in place, three state sets rotated as in the one-token leg."""
+    import torch
+
+    import kda_inputs as ki
+    import gated_delta_rule_31_amd as kda
+
+    case = ki.case1_decode()
+    B, H = case.B, case.H
+    cfg = kda.KdaConfig(num_heads=H)
+    p = case.params
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    conv_w, A_log, dt_bias, norm_w = tt(p.conv_w), tt(p.A_log), tt(p.dt_bias), tt(p.norm_w)
+    n_sets = 3
+    states = [tt(case.state) for _ in range(n_sets)]
+    convs = [tt(case.conv_state) for _ in range(n_sets)]
+    steps = [ki.token_inputs(case.seed, B, H, step=i) for i in range(T)]
+    xs = [tt(np.stack([getattr(x, n) for x in steps], axis=1)) for n in "qkvzbg"]
+    out = torch.empty((B, T, H * D), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        kda.kda_decode_multi(cfg, *xs, conv_w, A_log, dt_bias, norm_w, states[i % n_sets], convs[i % n_sets],
+                             out=out)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 2)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    alg = decode_multi_bytes(B, H, T)
+    return {"workload": f"kda-decode-multi-64seq-96head-{T}tok", "tokens": T,
+            "kernel_avg_us": round(kern_ms * 1e3, 2), "us_per_token": round(kern_ms * 1e3 / T, 2),
+            "tokens_per_s": round(B * T / (kern_ms * 1e-3), 1), "alg_bytes_per_launch": alg,
+            "hbm_frac": round(alg / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def bench_prefill(args, dev):
@@ -284,7 +339,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--prefill-path", choices=["auto", "fused", "chunked"], default="auto",
                     help="prefill work layout (auto: chunked below 512 (sequence, head) units)")
-    ap.add_argument("--only", choices=["all", "decode", "prefill", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "decode", "decode-multi", "prefill", "copy"], default="all",
                     help="run one part only (counter runs under rocprofv3 use this)")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
@@ -306,10 +361,18 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"prefill": bench_prefill(args, dev)}), flush=True)
         return
+    if args.only == "decode-multi":
+        print(json.dumps({"decode_multi": [bench_decode_multi(args, dev, T) for T in (4, 8)]}), flush=True)
+        return
     log("decode: 64 seq x 96 heads")
     dec = bench_decode(args, dev)
     log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")
     dec["roofline"]["traffic"] = measured_decode_traffic()
+    multi = None
+    if args.only == "all":
+        log("decode_multi: 64 seq x 96 heads, 4 and 8 tokens per call")
+        multi = [bench_decode_multi(args, dev, T) for T in (4, 8)]
+        log(f"decode_multi: {multi}")
     pre = None
     if args.only == "all" and not args.skip_prefill:
         log("prefill: 1 x 8192 tokens x 96 heads")
@@ -343,6 +406,7 @@ def main():
                    "state_dtype": "f32", "state_sets_rotated": 3},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
+        "decode_multi": multi,
         "prefill": pre,
     }
     print(json.dumps(line), flush=True)

@@ -101,6 +101,37 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch, const float *q,
     return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
+                            const float *q, const float *k, const float *v, const float *z, const float *b,
+                            const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
+                            const float *norm_w, const float *state_in, float *state_out,
+                            const float *conv_state_in, float *conv_state_out, float *out, void *stream) {
+    kda::DecodeMultiArgs a;
+    kda_status st = check_config(cfg, &a.c);
+    if (st != KDA_OK) return st;
+    if (batch < 0 || tokens < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits) ||
+        !units_fit(batch, tokens, INT32_MAX))
+        return KDA_ERR_BAD_SHAPE;
+    if (batch == 0) return KDA_OK;
+    if (tokens == 0) return KDA_ERR_BAD_SHAPE;
+    const void *ptrs[] = {q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
+                          state_in, state_out, conv_state_in, conv_state_out, out};
+    for (const void *p : ptrs)
+        if (!p) return KDA_ERR_NULL_ARG;
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(n_tokens) & 3u) != 0) return KDA_ERR_MISALIGNED;
+    a.B = batch;
+    a.T = tokens;
+    a.n_tokens = n_tokens;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
+    a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
+    a.state_in = state_in; a.state_out = state_out;
+    a.conv_in = conv_state_in; a.conv_out = conv_state_out;
+    a.out = out;
+    return kda::launch_decode_multi(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens) {
     kda::MixerConsts c;
     PrefillPlan plan;

@@ -1,0 +1,224 @@
+// kda_decode_multi.hip -- several known tokens per sequence in one launch (gfx950).
+//
+// The one-token decode of kda_decode.hip, applied to up to T tokens of each sequence:
+// the 64 KiB head state is read once, carried in registers through the tokens, and
+// written once (to state_out, which may be state_in); the conv windows likewise stay in
+// registers.  Each token follows the header comment "KDA per-head recurrence" (page
+// "colibri/c/kimi_k3.c") with decode_kernel's arithmetic, expression for expression, so
+// n tokens here give the bits of n calls of decode_kernel.  Lanes < 128 own the q and k
+// channel of their index, lanes >= 128 the v channel; the state layout (lane (rg, cg):
+// rows rg + 8j of columns 4cg..4cg+3) and the two key reductions are decode_kernel's.
+// Outputs of tokens t >= n_tokens[b] are not written.
+
+#include "kda_device.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+
+// the same helpers as decode_kernel's, so that the roundings agree bit for bit
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs a) {
+    const int H = a.c.H;
+    const int T = a.T;
+    const int bh = blockIdx.x;  // sequence * H + head
+    const int bs = bh / H;
+    const int h = bh - bs * H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cg = tid & 31;
+    const int rg = tid >> 5;
+    const size_t HD = (size_t)H * kD;
+    const int n = a.n_tokens ? min(max(a.n_tokens[bs], 0), T) : T;
+
+    f32x4 s[16];
+    const float *Sin = a.state_in + (size_t)bh * kD * kD;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sin + (rg + 8 * j) * kD + 4 * cg));
+
+    __shared__ float sh_kh[kD];
+    __shared__ float sh_ak[kD];
+    __shared__ float sh_aq[kD];
+    __shared__ float sh_alpha[kD];
+    __shared__ float sh_v[kD];
+    __shared__ float sh_gate[kD];
+    __shared__ float sh_red[2][3];
+    __shared__ float sh_beta;
+    __shared__ float sh_part[4][2][kD];
+
+    // this lane's channels: their taps and carried windows (A: q or v, B: k)
+    const size_t conv_seq = (size_t)bs * 3 * HD * 3;
+    const int i = tid < kD ? tid : tid - kD;
+    const size_t chA = (tid < kD ? 0 : 2 * HD) + (size_t)h * kD + i;
+    const size_t chB = HD + (size_t)h * kD + i;
+    const float4 wA = *reinterpret_cast<const float4 *>(a.conv_w + chA * 4);
+    const float4 wB = *reinterpret_cast<const float4 *>(a.conv_w + chB * 4);
+    float winA[3], winB[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        winA[j] = a.conv_in[conv_seq + chA * 3 + j];
+        winB[j] = tid < kD ? a.conv_in[conv_seq + chB * 3 + j] : 0.f;
+    }
+    const float dtb = a.dt_bias[h * kD + i];
+    const float rate = expf(a.A_log[h]);
+
+    // This lane's inputs of a token (A: q or v, B: k or z, G: g, beta logit), loaded one
+    // token ahead.  The loop's barriers wait for LDS traffic only, so these loads stay in
+    // flight across them.
+    struct TokenLoads {
+        float A, B, G, b;
+    };
+    auto load_token = [&](int t) {
+        const size_t row = (size_t)bs * T + t;
+        const size_t tok = row * HD + (size_t)h * kD + i;
+        TokenLoads r;
+        r.A = tid < kD ? a.q[tok] : a.v[tok];
+        r.B = tid < kD ? a.k[tok] : a.z[tok];
+        r.G = a.g[tok];
+        r.b = a.b[row * H + h];
+        return r;
+    };
+    TokenLoads cur = {0.f, 0.f, 0.f, 0.f};
+    if (n > 0) cur = load_token(0);
+
+    for (int t = 0; t < n; ++t) {
+        const size_t row = (size_t)bs * T + t;
+        const size_t tok = row * HD + (size_t)h * kD;
+        const TokenLoads x = cur;
+        if (t + 1 < n) cur = load_token(t + 1);
+        // ---- prologue of token t ----
+        float uq = 0.f, uk = 0.f;
+        if (tid < kD) {
+            const float xq = x.A, xk = x.B;
+            const float yq = wA.x * winA[0] + wA.y * winA[1] + wA.z * winA[2] + wA.w * xq;
+            const float yk = wB.x * winB[0] + wB.y * winB[1] + wB.z * winB[2] + wB.w * xk;
+            winA[0] = winA[1]; winA[1] = winA[2]; winA[2] = xq;
+            winB[0] = winB[1]; winB[1] = winB[2]; winB[2] = xk;
+            uq = yq * sigmoid_f(yq);
+            uk = yk * sigmoid_f(yk);
+            const float sqq = group_sum<64>(uq * uq);
+            const float skk = group_sum<64>(uk * uk);
+            const float sqk = group_sum<64>(uq * uk);
+            if (lane == 0) {
+                sh_red[wave][0] = sqq;
+                sh_red[wave][1] = skk;
+                sh_red[wave][2] = sqk;
+            }
+        } else {
+            const float xv = x.A;
+            const float yv = wA.x * winA[0] + wA.y * winA[1] + wA.z * winA[2] + wA.w * xv;
+            winA[0] = winA[1]; winA[1] = winA[2]; winA[2] = xv;
+            sh_v[i] = yv * sigmoid_f(yv);
+            const float gk = a.c.gate_lower_bound * sigmoid_f(rate * (x.B + dtb));
+            sh_alpha[i] = expf(gk);
+            sh_gate[i] = sigmoid_f(x.G);
+            if (i == 0) sh_beta = sigmoid_f(x.b);
+        }
+        lds_barrier();
+
+        const float ssq = sh_red[0][0] + sh_red[1][0];
+        const float ssk = sh_red[0][1] + sh_red[1][1];
+        const float sqk = sh_red[0][2] + sh_red[1][2];
+        const float inv_q = a.c.q_scale / sqrtf(ssq + a.c.l2_eps);
+        const float inv_k = 1.0f / sqrtf(ssk + a.c.l2_eps);
+        const float kappa = sqk * inv_q * inv_k;
+        const float beta = sh_beta;
+        if (tid < kD) {
+            const float qh = uq * inv_q, kh = uk * inv_k, al = sh_alpha[tid];
+            sh_kh[tid] = kh;
+            sh_ak[tid] = al * kh;
+            sh_aq[tid] = al * qh;
+        }
+        lds_barrier();
+
+        // ---- a = S^T(alpha k), c = S^T(alpha q) ----
+        float pa[4] = {0.f, 0.f, 0.f, 0.f}, pc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = rg + 8 * j;
+            const float fk = sh_ak[r], fq = sh_aq[r];
+            pa[0] += s[j].x * fk; pa[1] += s[j].y * fk; pa[2] += s[j].z * fk; pa[3] += s[j].w * fk;
+            pc[0] += s[j].x * fq; pc[1] += s[j].y * fq; pc[2] += s[j].z * fq; pc[3] += s[j].w * fq;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pa[c] += __shfl_xor(pa[c], 32, 64);
+            pc[c] += __shfl_xor(pc[c], 32, 64);
+        }
+        if (lane < 32) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                sh_part[wave][0][4 * cg + c] = pa[c];
+                sh_part[wave][1][4 * cg + c] = pc[c];
+            }
+        }
+        lds_barrier();
+
+        // ---- u = beta (v - a), o = c + kappa u, S' = D_a S + k u^T ----
+        float u[4], o[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int col = 4 * cg + c;
+            const float av = sh_part[0][0][col] + sh_part[1][0][col] + sh_part[2][0][col] + sh_part[3][0][col];
+            const float cv = sh_part[0][1][col] + sh_part[1][1][col] + sh_part[2][1][col] + sh_part[3][1][col];
+            u[c] = beta * (sh_v[col] - av);
+            o[c] = cv + kappa * u[c];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = rg + 8 * j;
+            const float al = sh_alpha[r], kr = sh_kh[r];
+            f32x4 nw;
+            nw.x = al * s[j].x + kr * u[0];
+            nw.y = al * s[j].y + kr * u[1];
+            nw.z = al * s[j].z + kr * u[2];
+            nw.w = al * s[j].w + kr * u[3];
+            s[j] = nw;
+        }
+
+        // ---- out = sigmoid(g) * RMSNorm(o) ----
+        if (tid < 32) {
+            const float ss = group_sum<32>(o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3]);
+            const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
+            const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + 4 * cg);
+            float4 y;
+            y.x = sh_gate[4 * cg + 0] * (o[0] * rinv * w.x);
+            y.y = sh_gate[4 * cg + 1] * (o[1] * rinv * w.y);
+            y.z = sh_gate[4 * cg + 2] * (o[2] * rinv * w.z);
+            y.w = sh_gate[4 * cg + 3] * (o[3] * rinv * w.w);
+            *reinterpret_cast<float4 *>(a.out + tok + 4 * cg) = y;
+        }
+        lds_barrier();  // the next token rewrites the shared arrays
+    }
+
+    float *Sout = a.state_out + (size_t)bh * kD * kD;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        __builtin_nontemporal_store(s[j], reinterpret_cast<f32x4 *>(Sout + (rg + 8 * j) * kD + 4 * cg));
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        a.conv_out[conv_seq + chA * 3 + j] = winA[j];
+        if (tid < kD) a.conv_out[conv_seq + chB * 3 + j] = winB[j];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_multi(const DecodeMultiArgs &a, hipStream_t stream) {
+    dim3 grid((unsigned)((size_t)a.B * a.c.H)), block(kThreads);
+    void *args[] = {const_cast<DecodeMultiArgs *>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&decode_multi_kernel), grid, block, args, 0, stream);
+}
+
+}  // namespace kda

@@ -28,6 +28,18 @@ struct DecodeArgs {
     float *state, *conv_state, *out;
 };
 
+// Multi-token decode: up to T tokens per sequence ([B, T, ...] inputs), the state read
+// from state_in and written to state_out (which may be the same buffer).
+struct DecodeMultiArgs {
+    MixerConsts c;
+    int B, T;
+    const int32_t *n_tokens;  // device [B] tokens to apply per sequence, or null (= T)
+    const float *q, *k, *v, *z, *b, *g;
+    const float *conv_w, *A_log, *dt_bias, *norm_w;
+    const float *state_in, *conv_in;
+    float *state_out, *conv_out, *out;
+};
+
 // Prefill launch plans (kda_config.prefill_path):
 //   kPathFused   one workgroup per (sequence, head) walks the sequence chunk by chunk;
 //                every intermediate stays on chip
@@ -74,6 +86,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeMultiArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // the chunked plan's kernels (kda_prefill.hip: chunk table, chunk records; kda_carry.hip:
 // the carry)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -125,6 +125,46 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
                            const float *norm_w,
                            float *state, float *conv_state, float *out,
                            void *stream);
+
+/*
+ * kda_decode_multi -- up to `tokens` new tokens for each of B sequences in one call:
+ * the state is read once, carried through the tokens, and written once.  This is the
+ * decode step for several known tokens (speculative verification, or a short chunk of
+ * a prompt against a resident state); each token follows the header comment "KDA
+ * per-head recurrence" (page "colibri/c/kimi_k3.c") exactly as kda_decode_step does,
+ * and n tokens here give the bits of n kda_decode_step calls on the same tokens.
+ *
+ * Verify and roll back (the engine's multi-token verify and rollback are not
+ * implemented on the pages; this is this library's form of it): call with
+ * state_out != state_in, so that state_in keeps the state before the candidates; after
+ * accepting a prefix of a_s tokens of sequence s, call again from state_in with
+ * n_tokens = a to commit exactly the accepted prefix (state_out may then be state_in).
+ *
+ *   batch                  B >= 0 (0: nothing queued, KDA_OK)
+ *   tokens                 T >= 1 when B > 0: the token slots per sequence
+ *   n_tokens               device int32 [B]: tokens to apply to sequence s (clamped to
+ *                          [0, T]; the rest of its slots are ignored), or NULL for T each
+ *   q, k, v, z, g          [B, T, H*D] fp32 (row s*T + t is token t of sequence s)
+ *   b                      [B, T, H] fp32
+ *   conv_w, A_log, dt_bias, norm_w   fp32 parameters (layouts above)
+ *   state_in, state_out    [B, H, D, D] fp32; either the same buffer (update in place)
+ *                          or disjoint
+ *   conv_state_in, conv_state_out   [B, 3*H*D, 3] fp32; the same buffer or disjoint
+ *   out                    [B, T, H*D] fp32: rows of applied tokens are written, the
+ *                          others are left untouched; must not overlap any input
+ *   stream                 hipStream_t or NULL
+ * A sequence with n_tokens 0 copies its state and windows to the outputs.
+ * Alignment: every fp32 pointer 16-byte aligned, n_tokens 4-byte aligned.
+ * Limits: B*H <= 16,777,215; B*T <= 2^31-1.
+ */
+kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
+                            const float *q, const float *k, const float *v,
+                            const float *z, const float *b, const float *g,
+                            const float *conv_w, const float *A_log, const float *dt_bias,
+                            const float *norm_w,
+                            const float *state_in, float *state_out,
+                            const float *conv_state_in, float *conv_state_out,
+                            float *out, void *stream);
 
 /*
  * kda_prefill -- a packed batch of whole sequences (varlen), processed in chunks of

@@ -157,3 +157,27 @@ def test_launch_size_limits():
     assert _ws(_cfg(num_heads=1, prefill_path=2), 1, big_n) == 0
     assert _prefill(_cfg(num_heads=1, prefill_path=2), 1, big_n) == BAD_SHAPE
     assert _ws(_cfg(num_heads=1), 1, big_n) == 0
+
+
+def _multi(cfg, B, T, n_tokens=None, ptrs=None):
+    p = [ctypes.c_void_p(FAKE)] * 15 if ptrs is None else ptrs
+    return kda.lib().kda_decode_multi(ctypes.byref(cfg), B, T, n_tokens, *p, None)
+
+
+def test_decode_multi_rejects_bad_arguments():
+    assert _multi(_cfg(head_dim=64), 1, 2) == BAD_CONFIG
+    assert _multi(_cfg(), -1, 2) == BAD_SHAPE
+    assert _multi(_cfg(), 1, -2) == BAD_SHAPE
+    assert _multi(_cfg(), 0, 4) == OK       # empty batch: nothing queued
+    assert _multi(_cfg(), 2, 0) == BAD_SHAPE
+    assert _multi(_cfg(num_heads=1), 16_777_216, 1) == BAD_SHAPE
+    assert _multi(_cfg(num_heads=1), 65_536, 65_536) == BAD_SHAPE  # B*T rows past 2^31-1
+    # argument order: q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in, state_out,
+    # conv_in, conv_out, out -- all required
+    for i in range(15):
+        p = [ctypes.c_void_p(FAKE)] * 15
+        p[i] = None
+        assert _multi(_cfg(), 2, 3, ptrs=p) == NULL_ARG, i
+        p[i] = ctypes.c_void_p(FAKE + 4)
+        assert _multi(_cfg(), 2, 3, ptrs=p) == MISALIGNED, i
+    assert _multi(_cfg(), 2, 3, n_tokens=ctypes.c_void_p(FAKE + 2)) == MISALIGNED

@@ -1,0 +1,134 @@
+"""GPU parity of kda_decode_multi (several known tokens per sequence in one call) against
+the fp64 oracle (max relative error 1e-4 per (sequence, head) slice, as for one-token
+decode), bit-for-bit agreement with the same number of kda_decode_step calls, and the
+verify / roll-back use: out-of-place candidates, then an in-place commit of the
+accepted prefix."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_31_amd as kda
+import kda_inputs as ki
+from tests.parity import DECODE_REL_TOL, DecodeRun, decode_oracle, slice_rel, t
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+class MultiRun:
+    """A decode case's first T tokens as [B, T, ...] inputs on the GPU."""
+
+    def __init__(self, case: ki.DecodeCase, T: int, dev):
+        self.case, self.T, self.dev = case, T, dev
+        self.cfg = kda.KdaConfig(num_heads=case.H)
+        p = case.params
+        self.prm = [t(p.conv_w, dev), t(p.A_log, dev), t(p.dt_bias, dev), t(p.norm_w, dev)]
+        steps = [case.step(i) for i in range(T)]
+        self.xs = [t(np.ascontiguousarray(np.stack([getattr(s, n) for s in steps], axis=1)), dev) for n in "qkvzbg"]
+        self.state0 = t(case.state, dev)
+        self.conv0 = t(case.conv_state, dev)
+
+    def call(self, state_in, conv_in, state_out=None, conv_out=None, n_tokens=None):
+        B, H = self.case.B, self.case.H
+        out = torch.full((B, self.T, H * D), float("nan"), dtype=torch.float32, device=self.dev)
+        nt = None if n_tokens is None else torch.tensor(n_tokens, dtype=torch.int32, device=self.dev)
+        kda.kda_decode_multi(self.cfg, *self.xs, *self.prm, state_in, conv_in, state_out=state_out,
+                             conv_state_out=conv_out, n_tokens=nt, out=out)
+        torch.cuda.synchronize()
+        return out
+
+
+def _single_steps(case, n, dev):
+    """n kda_decode_step calls on the whole batch: outputs [n][B, H*D], final state, windows."""
+    run = DecodeRun(case, dev)
+    outs = [run.step(run.inputs(i)).clone() for i in range(n)]
+    torch.cuda.synchronize()
+    return outs, run.state, run.conv_state
+
+
+def _window(cst, b, h, H):
+    return np.stack([cst[b, blk * H * D + h * D: blk * H * D + (h + 1) * D] for blk in range(3)])
+
+
+def test_per_sequence_counts_against_oracle(device):
+    case = ki.decode_case(310, 4, 4, 8, "multi-counts")
+    n = [8, 3, 0, 1]
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=8 n={n}", flush=True)
+    mr = MultiRun(case, 8, device)
+    s_out, c_out = torch.empty_like(mr.state0), torch.empty_like(mr.conv0)
+    state_in, conv_in = mr.state0.clone(), mr.conv0.clone()
+    out = mr.call(state_in, conv_in, s_out, c_out, n_tokens=n).cpu().numpy().reshape(case.B, 8, case.H, D)
+    st, cst = s_out.cpu().numpy(), c_out.cpu().numpy()
+    # the inputs are left as they were (they are the pre-verify snapshot)
+    assert torch.equal(state_in, mr.state0) and torch.equal(conv_in, mr.conv0)
+    worst = 0.0
+    for b in range(case.B):
+        assert np.isnan(out[b, n[b]:]).all()  # rows past the count are not written
+        if n[b] == 0:
+            np.testing.assert_array_equal(st[b], case.state[b])
+            np.testing.assert_array_equal(cst[b], case.conv_state[b])
+            continue
+        ref = decode_oracle(case, [(b, h) for h in range(case.H)], n[b])
+        for h in range(case.H):
+            r = ref[(b, h)]
+            for i in range(n[b]):
+                worst = max(worst, slice_rel(out[b, i, h], r.out[i]))
+            worst = max(worst, slice_rel(st[b, h], r.state))
+            np.testing.assert_array_equal(_window(cst, b, h, case.H), r.conv_state)
+    print(f"[decode-multi] {case.name}: max rel err {worst:.3e}", flush=True)
+    assert worst <= DECODE_REL_TOL, worst
+
+
+def test_in_place_equals_single_steps_bitwise(device):
+    case = ki.decode_case(311, 5, 6, 6, "multi-vs-steps")
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=6", flush=True)
+    mr = MultiRun(case, 6, device)
+    state, conv = mr.state0.clone(), mr.conv0.clone()
+    out = mr.call(state, conv)
+    outs, st, cst = _single_steps(case, 6, device)
+    for i in range(6):
+        assert torch.equal(out[:, i], outs[i]), i
+    assert torch.equal(state, st) and torch.equal(conv, cst)
+
+
+def test_verify_then_commit_accepted_prefix(device):
+    case = ki.decode_case(312, 3, 4, 6, "multi-verify")
+    accepted = [6, 2, 0]
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=6 accepted={accepted}", flush=True)
+    mr = MultiRun(case, 6, device)
+    state, conv = mr.state0.clone(), mr.conv0.clone()
+    spec_s, spec_c = torch.empty_like(state), torch.empty_like(conv)
+    spec_out = mr.call(state, conv, spec_s, spec_c)  # candidates; `state` is the snapshot
+    assert torch.equal(state, mr.state0)
+    out = mr.call(state, conv, n_tokens=accepted)    # commit the accepted prefixes in place
+    for b, a in enumerate(accepted):
+        outs, st, cst = _single_steps(case, a, device) if a else ([], mr.state0, mr.conv0)
+        for i in range(a):
+            assert torch.equal(out[b, i], outs[i][b]) and torch.equal(spec_out[b, i], outs[i][b])
+        assert torch.equal(state[b], st[b]) and torch.equal(conv[b], cst[b])
+    # a fully accepted sequence ends where the candidates ended
+    assert torch.equal(state[0], spec_s[0]) and torch.equal(conv[0], spec_c[0])
+
+
+def test_k3_shape_four_tokens(device):
+    case = ki.decode_case(313, 64, 96, 4, "multi-k3")
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=4", flush=True)
+    mr = MultiRun(case, 4, device)
+    state, conv = mr.state0.clone(), mr.conv0.clone()
+    out = mr.call(state, conv)
+    outs, st, cst = _single_steps(case, 4, device)
+    assert torch.equal(state, st) and torch.equal(conv, cst)
+    for i in range(4):
+        assert torch.equal(out[:, i], outs[i])
+    rng = np.random.default_rng(313)
+    pairs = [(0, 0), (63, 95)] + [(int(b), int(h)) for b, h in zip(rng.integers(0, 64, 10), rng.integers(0, 96, 10))]
+    ref = decode_oracle(case, pairs, 4)
+    o = out.cpu().numpy().reshape(case.B, 4, case.H, D)
+    s = state.cpu().numpy()
+    worst = 0.0
+    for (b, h) in pairs:
+        for i in range(4):
+            worst = max(worst, slice_rel(o[b, i, h], ref[(b, h)].out[i]))
+        worst = max(worst, slice_rel(s[b, h], ref[(b, h)].state))
+    assert worst <= DECODE_REL_TOL, worst

@@ -202,6 +202,51 @@ def bench_decode_multi(args, dev, T: int):
             "hbm_frac": round(alg / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def bench_decode_cfg4(args, dev):
+    """512 sequences x 96 heads (3.2 GB of fp32 states): 32 chained kda_decode_step calls,
+    and the same 32 tokens as one kda_decode_multi call."""
+    import torch
+
+    import kda_inputs as ki
+    import gated_delta_rule_31_amd as kda
+
+    B, H, T = 512, 96, 32
+    case = ki.decode_case(4, B, H, T, "cfg4-decode")
+    cfg = kda.KdaConfig(num_heads=H)
+    p = case.params
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    conv_w, A_log, dt_bias, norm_w = tt(p.conv_w), tt(p.A_log), tt(p.dt_bias), tt(p.norm_w)
+    state, conv = tt(case.state), tt(case.conv_state)
+    xs = [[tt(getattr(case.step(i), n)) for n in "qkvzbg"] for i in range(T)]
+    out = torch.empty((B, H * D), dtype=torch.float32, device=dev)
+    # warm-up step, then the 32 chained steps
+    kda.kda_decode_step(cfg, *xs[0], conv_w, A_log, dt_bias, norm_w, state, conv, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(T):
+        kda.kda_decode_step(cfg, *xs[i], conv_w, A_log, dt_bias, norm_w, state, conv, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / T
+    alg = decode_bytes(B, H)
+    # the same tokens in one call
+    mx = [torch.stack([xs[i][j] for i in range(T)], dim=1).contiguous() for j in range(6)]
+    del xs
+    mout = torch.empty((B, T, H * D), dtype=torch.float32, device=dev)
+    kda.kda_decode_multi(cfg, *mx, conv_w, A_log, dt_bias, norm_w, state, conv, out=mout)
+    torch.cuda.synchronize()
+    e0.record()
+    kda.kda_decode_multi(cfg, *mx, conv_w, A_log, dt_bias, norm_w, state, conv, out=mout)
+    e1.record()
+    torch.cuda.synchronize()
+    multi_ms = e0.elapsed_time(e1)
+    return {"workload": "kda-decode-512seq-96head-32steps", "step_us": round(step_ms * 1e3, 2),
+            "step_hbm_frac": round(alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "state_gbs": round(2 * B * H * D * D * 4 / (step_ms * 1e-3) / 1e9, 1),
+            "multi_32tok_us": round(multi_ms * 1e3, 2), "multi_us_per_token": round(multi_ms * 1e3 / T, 2)}
+
+
 def bench_prefill(args, dev):
     import torch
 
@@ -339,7 +384,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--prefill-path", choices=["auto", "fused", "chunked"], default="auto",
                     help="prefill work layout (auto: chunked below 512 (sequence, head) units)")
-    ap.add_argument("--only", choices=["all", "decode", "decode-multi", "prefill", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "decode", "decode-multi", "decode-cfg4", "prefill", "copy"],
+                    default="all",
                     help="run one part only (counter runs under rocprofv3 use this)")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
@@ -360,6 +406,9 @@ def main():
         return
     if args.only == "prefill":
         print(json.dumps({"prefill": bench_prefill(args, dev)}), flush=True)
+        return
+    if args.only == "decode-cfg4":
+        print(json.dumps({"decode_cfg4": bench_decode_cfg4(args, dev)}), flush=True)
         return
     if args.only == "decode-multi":
         print(json.dumps({"decode_multi": [bench_decode_multi(args, dev, T) for T in (4, 8)]}), flush=True)

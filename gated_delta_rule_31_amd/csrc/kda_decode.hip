@@ -34,6 +34,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Workgroups are dealt to the 8 XCDs round-robin in id order.  This maps hardware id i
+// (XCD i % 8, its (i / 8)-th workgroup) to a logical id so that each XCD walks one
+// contiguous eighth of the (sequence, head) range in order: its L2, address translation
+// and DRAM pages then see one streaming region instead of every eighth 64 KiB state.
+// A bijection for any n, so the result does not depend on the dispatch order.
+__device__ __forceinline__ int xcd_contiguous(int i, int n) {
+    const int q = n >> 3, r = n & 7, x = i & 7;
+    return x * q + min(x, r) + (i >> 3);
+}
+
 // sum over groups of W consecutive lanes (W a power of two <= 64)
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
@@ -44,7 +54,7 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int H = a.c.H;
-    const int bh = blockIdx.x;  // sequence * H + head
+    const int bh = xcd_contiguous(blockIdx.x, gridDim.x);  // sequence * H + head
     const int bs = bh / H;
     const int h = bh - bs * H;
     const int tid = threadIdx.x;
@@ -195,8 +205,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-    // Workgroup id = sequence * H + head.  Workgroups are dealt round-robin to the 8
-    // XCDs, so with H a multiple of 8 a head's parameters stay in one XCD's L2.
+    // One workgroup per (sequence, head), ids remapped by xcd_contiguous.
     dim3 grid((unsigned)((size_t)a.B * a.c.H)), block(kThreads);
     void *args[] = {const_cast<DecodeArgs *>(&a)};
     return hipLaunchKernel(reinterpret_cast<const void *>(&decode_kernel), grid, block, args, 0, stream);

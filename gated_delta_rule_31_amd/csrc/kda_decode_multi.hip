@@ -20,6 +20,13 @@ constexpr int kThreads = 256;
 // the same helpers as decode_kernel's, so that the roundings agree bit for bit
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// decode_kernel's XCD-contiguous workgroup order (each XCD walks one contiguous eighth of
+// the (sequence, head) range)
+__device__ __forceinline__ int xcd_contiguous(int i, int n) {
+    const int q = n >> 3, r = n & 7, x = i & 7;
+    return x * q + min(x, r) + (i >> 3);
+}
+
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
@@ -30,7 +37,7 @@ __device__ __forceinline__ float group_sum(float x) {
 __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs a) {
     const int H = a.c.H;
     const int T = a.T;
-    const int bh = blockIdx.x;  // sequence * H + head
+    const int bh = xcd_contiguous(blockIdx.x, gridDim.x);  // sequence * H + head
     const int bs = bh / H;
     const int h = bh - bs * H;
     const int tid = threadIdx.x;

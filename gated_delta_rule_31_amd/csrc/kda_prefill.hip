@@ -521,8 +521,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     }
                 }
             }
-            // sCB is dead: K_end^T, hi/lo, into region 1 (channel half 1 now, half 0 while
-            // the diagonal blocks of T are inverted)
+            // sCB is dead: K_end^T, hi/lo, into region 1 (channel half 1 now, half 0 in
+            // phase 4)
             if (half == 1) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
@@ -570,14 +570,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                         sT[(16 * w + tt) * F_LD + 16 * w + lr] = xcol[tt];
                         sTb[sw64(16 * w + tt, 16 * w + lr)] = (__bf16)xcol[tt];
                     }
-                }
-                // K_end^T of channel half 0
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int c = 16 * lg + j;
-                    const __bf16 hi = (__bf16)ke[j];
-                    sKeHi[swi64(c, t)] = hi;
-                    sKeLo[swi64(c, t)] = (__bf16)(ke[j] - (float)hi);
                 }
             } else {
                 // upper blocks (I < J) of sTb: 6 blocks x 256 values over 256 lanes
@@ -638,6 +630,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         f32x4 U[2][2];  // [tp][x]: U[token 32tp + 8lg + 4x + i][value 16w + lr]
         {
             KDA_LANE_IDS();
+            // K_end^T of channel half 0 (its LDS writes issue beside this phase's MFMAs)
+            if (half == 0) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int c = 16 * lg + j;
+                    const __bf16 hi = (__bf16)ke[j];
+                    sKeHi[swi64(c, t)] = hi;
+                    sKeLo[swi64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                }
+            }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};

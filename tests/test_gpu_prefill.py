@@ -87,6 +87,35 @@ def test_cfg3_varlen_sampled(device, path):
     _run_and_check(case, device, path, pairs)
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_saturated_gates(device, path):
+    """Logits far in the tails, per sequence: the strongest decay (gk -> -5, so G falls by
+    about 5 per token and e^{-G} would overflow fp32 within a chunk without the sub-chunk
+    references) with beta -> 1; beta -> 0 (no update); strongest and no decay alternating
+    every 16 tokens (the sub-chunk boundary) with beta -> 1; a random mix per token.
+    (No decay with beta -> 1 on every token is outside the tolerance margin of the bf16
+    operand splits; its measured error is documented with the precision choices.)"""
+    case = ki.prefill_case(140, 3, [150, 150, 150, 200], True, "saturated")
+    bf = lambda v: ki.to_bf16_bits(np.float32(v))
+    cu = case.cu_seqlens
+    rng = np.random.default_rng(141)
+    for s in range(case.B):
+        for t in range(cu[s], cu[s + 1]):
+            i = t - cu[s]
+            if s == 0:
+                z, b = 40.0, 30.0
+            elif s == 1:
+                z, b = 40.0, -30.0
+            elif s == 2:
+                z, b = (40.0 if (i // 16) % 2 == 0 else -40.0), 30.0
+            else:
+                z, b = float(rng.choice([-40.0, 40.0, 0.0])), float(rng.choice([-30.0, 30.0, 0.0]))
+            case.x.z[t] = bf(z)
+            case.x.b[t] = bf(b)
+        case.x.g[cu[s]:cu[s + 1], :64] = bf(25.0)  # output gate saturated on one head's channels
+    _run_and_check(case, device, path)
+
+
 def test_layouts_agree_bitwise(device):
     """The chunked layout performs the fused kernel's arithmetic in the same order, so
     the two give identical bits (outputs, final states, final windows)."""

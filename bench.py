@@ -202,6 +202,52 @@ def bench_decode_multi(args, dev, T: int):
             "hbm_frac": round(alg / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def bench_decode_slots(args, dev):
+    """The one-token leg's 64 x 96 workload through kda_decode_step_slots: the 64 rows
+    update scattered entries of a 192-entry state pool, a different random set of 64
+    entries per launch (three sets rotated, as the dense leg rotates three state sets)."""
+    import torch
+
+    import kda_inputs as ki
+    import gated_delta_rule_31_amd as kda
+
+    case = ki.case1_decode()
+    B, H = case.B, case.H
+    P = 3 * B
+    cfg = kda.KdaConfig(num_heads=H)
+    p = case.params
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    conv_w, A_log, dt_bias, norm_w = tt(p.conv_w), tt(p.A_log), tt(p.dt_bias), tt(p.norm_w)
+    st, cs = tt(case.state), tt(case.conv_state)
+    pool = torch.cat([st, st, st])
+    conv_pool = torch.cat([cs, cs, cs])
+    del st, cs
+    perm = np.random.default_rng(7).permutation(P).astype(np.int32)
+    slot_sets = [tt(perm[j * B:(j + 1) * B]) for j in range(3)]
+    x = case.step(0)
+    xs = [tt(getattr(x, n)) for n in "qkvzbg"]
+    out = torch.empty((B, H * D), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        kda.kda_decode_step_slots(cfg, slot_sets[i % 3], *xs, conv_w, A_log, dt_bias, norm_w, pool, conv_pool,
+                                  out=out)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    alg = decode_bytes(B, H)
+    return {"workload": "kda-decode-slots-64rows-192pool-96head", "kernel_avg_us": round(kern_ms * 1e3, 2),
+            "hbm_frac": round(alg / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def bench_decode_cfg4(args, dev):
     """512 sequences x 96 heads (3.2 GB of fp32 states): 32 chained kda_decode_step calls,
     and the same 32 tokens as one kda_decode_multi call."""
@@ -384,7 +430,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--prefill-path", choices=["auto", "fused", "chunked"], default="auto",
                     help="prefill work layout (auto: chunked below 512 (sequence, head) units)")
-    ap.add_argument("--only", choices=["all", "decode", "decode-multi", "decode-cfg4", "prefill", "copy"],
+    ap.add_argument("--only", choices=["all", "decode", "decode-multi", "decode-slots", "decode-cfg4", "prefill",
+                                       "copy"],
                     default="all",
                     help="run one part only (counter runs under rocprofv3 use this)")
     ap.add_argument("--skip-prefill", action="store_true")
@@ -410,6 +457,9 @@ def main():
     if args.only == "decode-cfg4":
         print(json.dumps({"decode_cfg4": bench_decode_cfg4(args, dev)}), flush=True)
         return
+    if args.only == "decode-slots":
+        print(json.dumps({"decode_slots": bench_decode_slots(args, dev)}), flush=True)
+        return
     if args.only == "decode-multi":
         print(json.dumps({"decode_multi": [bench_decode_multi(args, dev, T) for T in (4, 8)]}), flush=True)
         return
@@ -417,11 +467,14 @@ def main():
     dec = bench_decode(args, dev)
     log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")
     dec["roofline"]["traffic"] = measured_decode_traffic()
-    multi = None
+    multi = slots = None
     if args.only == "all":
         log("decode_multi: 64 seq x 96 heads, 4 and 8 tokens per call")
         multi = [bench_decode_multi(args, dev, T) for T in (4, 8)]
         log(f"decode_multi: {multi}")
+        log("decode_slots: 64 rows of a 192-entry pool x 96 heads")
+        slots = bench_decode_slots(args, dev)
+        log(f"decode_slots: {slots}")
     pre = None
     if args.only == "all" and not args.skip_prefill:
         log("prefill: 1 x 8192 tokens x 96 heads")
@@ -456,6 +509,7 @@ def main():
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
         "decode_multi": multi,
+        "decode_slots": slots,
         "prefill": pre,
     }
     print(json.dumps(line), flush=True)

@@ -13,13 +13,13 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["KdaConfig", "kda_decode_step", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes", "KdaError",
+__all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes", "KdaError",
            "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
-EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes",
+EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes",
                     "kda_status_str", "kda_abi_version")
-ABI_VERSION = 3
+ABI_VERSION = 4
 HEAD_DIM = 128
 CONV = 4
 
@@ -73,6 +73,8 @@ def _load() -> ctypes.CDLL:
     L.kda_config_default.argtypes = []
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32] + [fp] * 13 + [vp]
+    L.kda_decode_step_slots.restype = ctypes.c_int
+    L.kda_decode_step_slots.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32, vp, ctypes.c_int32] + [fp] * 13 + [vp]
     L.kda_decode_multi.restype = ctypes.c_int
     L.kda_decode_multi.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [fp] * 15 +
                                    [vp])
@@ -140,6 +142,37 @@ def kda_decode_step(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, no
     st = _lib.kda_decode_step(ctypes.byref(c), B, *args, _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_decode_step")
+    return out
+
+
+def kda_decode_step_slots(cfg: KdaConfig, slots, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_pool,
+                          conv_pool, out=None, stream=None) -> torch.Tensor:
+    """One token per batch row against states held in a pool: row r advances pool entry
+    ``slots[r]`` (int32 [B] on the GPU) of state_pool [P,H,D,D] and conv_pool
+    [P,3*H*D,3], in place; rows whose slot lies outside [0, P) are skipped and their
+    output rows left as they were.  q,k,v,z,g: [B, H*D] fp32; b: [B, H].  Returns out
+    [B, H*D] fp32."""
+    H, D = cfg.num_heads, cfg.head_dim
+    B = q.shape[0]
+    P = state_pool.shape[0]
+    HD = H * D
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty((B, HD), dtype=f32, device=q.device)
+    args = [
+        _ptr(q, f32, (B, HD), "q"), _ptr(k, f32, (B, HD), "k"), _ptr(v, f32, (B, HD), "v"),
+        _ptr(z, f32, (B, HD), "z"), _ptr(b, f32, (B, H), "b"), _ptr(g, f32, (B, HD), "g"),
+        _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
+        _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
+        _ptr(state_pool, f32, (P, H, D, D), "state_pool"),
+        _ptr(conv_pool, f32, (P, 3 * HD, CONV - 1), "conv_pool"),
+        _ptr(out, f32, (B, HD), "out"),
+    ]
+    c = cfg._c()
+    st = _lib.kda_decode_step_slots(ctypes.byref(c), B, _ptr(slots, torch.int32, (B,), "slots"), P, *args,
+                                    _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step_slots")
     return out
 
 

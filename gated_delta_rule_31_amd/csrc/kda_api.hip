@@ -98,6 +98,34 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch, const float *q,
     a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
     a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
     a.state = state; a.conv_state = conv_state; a.out = out;
+    a.slots = nullptr;
+    a.pool = 0;
+    return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int32_t *slots, int32_t pool_size,
+                                 const float *q, const float *k, const float *v, const float *z, const float *b,
+                                 const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
+                                 const float *norm_w, float *state_pool, float *conv_pool, float *out,
+                                 void *stream) {
+    kda::DecodeArgs a;
+    kda_status st = check_config(cfg, &a.c);
+    if (st != KDA_OK) return st;
+    if (batch < 0 || pool_size < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits)) return KDA_ERR_BAD_SHAPE;
+    if (batch == 0 || pool_size == 0) return KDA_OK;  // every row would be skipped
+    const void *ptrs[] = {q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_pool, conv_pool, out};
+    if (!slots) return KDA_ERR_NULL_ARG;
+    for (const void *p : ptrs)
+        if (!p) return KDA_ERR_NULL_ARG;
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(slots) & 3u) != 0) return KDA_ERR_MISALIGNED;
+    a.B = batch;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
+    a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
+    a.state = state_pool; a.conv_state = conv_pool; a.out = out;
+    a.slots = slots;
+    a.pool = pool_size;
     return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

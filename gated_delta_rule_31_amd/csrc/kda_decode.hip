@@ -52,11 +52,19 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// kSlots: batch row bs updates pool entry a.slots[bs] of the state and conv-window
+// pools instead of entry bs; a row whose slot lies outside [0, a.pool) is skipped.
+template <bool kSlots>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int H = a.c.H;
-    const int bh = xcd_contiguous(blockIdx.x, gridDim.x);  // sequence * H + head
+    const int bh = xcd_contiguous(blockIdx.x, gridDim.x);  // batch row * H + head
     const int bs = bh / H;
     const int h = bh - bs * H;
+    int slot = bs;
+    if (kSlots) {
+        slot = a.slots[bs];                               // uniform over the workgroup
+        if (slot < 0 || slot >= a.pool) return;           // before any barrier
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -67,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // ---- 1. issue the state reads (64 floats per lane) ----
     // (nontemporal: the state is streamed once per step and must not evict the small,
     //  reused per-head parameters from the caches)
-    float *S = a.state + (size_t)bh * kD * kD;
+    float *S = a.state + ((size_t)slot * H + h) * kD * kD;
     f32x4 s[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     // ---- 2. prologue: conv + SiLU (+ sums for the L2 norms), gates ----
     const size_t tok = (size_t)bs * HD + (size_t)h * kD;  // this head's channels of the token row
-    float *cstate = a.conv_state + (size_t)bs * 3 * HD * 3;
+    float *cstate = a.conv_state + (size_t)slot * 3 * HD * 3;
     float uq = 0.f, uk = 0.f;
     if (tid < kD) {
         const int i = tid;
@@ -205,10 +213,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-    // One workgroup per (sequence, head), ids remapped by xcd_contiguous.
+    // One workgroup per (batch row, head), ids remapped by xcd_contiguous.
     dim3 grid((unsigned)((size_t)a.B * a.c.H)), block(kThreads);
     void *args[] = {const_cast<DecodeArgs *>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&decode_kernel), grid, block, args, 0, stream);
+    const void *fn = a.slots ? reinterpret_cast<const void *>(&decode_kernel<true>)
+                             : reinterpret_cast<const void *>(&decode_kernel<false>);
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 }  // namespace kda

@@ -26,6 +26,10 @@ struct DecodeArgs {
     const float *q, *k, *v, *z, *b, *g;
     const float *conv_w, *A_log, *dt_bias, *norm_w;
     float *state, *conv_state, *out;
+    // NULL: row b owns state[b] and conv_state[b].  Otherwise row b owns pool entry
+    // slots[b] of the `pool` entries of state / conv_state (rows outside are skipped).
+    const int32_t *slots;
+    int pool;
 };
 
 // Multi-token decode: up to T tokens per sequence ([B, T, ...] inputs), the state read

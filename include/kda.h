@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -125,6 +125,42 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
                            const float *norm_w,
                            float *state, float *conv_state, float *out,
                            void *stream);
+
+/*
+ * kda_decode_step_slots -- kda_decode_step for a batch whose states live in a pool:
+ * batch row r (its token inputs and output row r) advances pool entry slots[r] of
+ * state_pool and conv_pool.  The per-row step is exactly kda_decode_step's (the same
+ * kernel, so the same bits).  This is the multiplexed decode step of the serving
+ * engine, where each batch row is one token of one of several parked conversations and
+ * carries its own recurrent state (page "colibri/c/kimi_k3.c": the K3Seq / K3Row
+ * structures and the multiplexed step over them), with the states held in one device
+ * pool rather than a dense [B, ...] batch.
+ *
+ *   batch                  B >= 0 rows (0, or pool_size 0: nothing queued, KDA_OK)
+ *   slots                  device int32 [B]: the pool entry of row r.  A row whose slot
+ *                          lies outside [0, pool_size) is skipped: its pool entries are
+ *                          not touched and its output row is left as it was.  Two rows
+ *                          must not name the same slot (their updates race; the
+ *                          result for that slot is unspecified, every access still
+ *                          stays inside the pool)
+ *   pool_size              P >= 0 entries in state_pool and conv_pool
+ *   q, k, v, z, g          [B, H*D] fp32;  b [B, H] fp32 (row r is slot slots[r]'s token)
+ *   conv_w, A_log, dt_bias, norm_w   fp32 parameters (layouts above)
+ *   state_pool             [P, H, D, D] fp32, entries of valid slots read and
+ *                          overwritten in place
+ *   conv_pool              [P, 3*H*D, 3] fp32, likewise
+ *   out                    [B, H*D] fp32; must not overlap any input
+ *   stream                 hipStream_t or NULL
+ * Alignment: every fp32 pointer 16-byte aligned, slots 4-byte aligned.
+ * Limits: B*H <= 16,777,215.
+ */
+kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int32_t *slots, int32_t pool_size,
+                                 const float *q, const float *k, const float *v,
+                                 const float *z, const float *b, const float *g,
+                                 const float *conv_w, const float *A_log, const float *dt_bias,
+                                 const float *norm_w,
+                                 float *state_pool, float *conv_pool, float *out,
+                                 void *stream);
 
 /*
  * kda_decode_multi -- up to `tokens` new tokens for each of B sequences in one call:

@@ -181,3 +181,27 @@ def test_decode_multi_rejects_bad_arguments():
         p[i] = ctypes.c_void_p(FAKE + 4)
         assert _multi(_cfg(), 2, 3, ptrs=p) == MISALIGNED, i
     assert _multi(_cfg(), 2, 3, n_tokens=ctypes.c_void_p(FAKE + 2)) == MISALIGNED
+
+
+def _slots(cfg, B, P, slots=ctypes.c_void_p(FAKE), ptrs=None):
+    p = [ctypes.c_void_p(FAKE)] * 13 if ptrs is None else ptrs
+    return kda.lib().kda_decode_step_slots(ctypes.byref(cfg), B, slots, P, *p, None)
+
+
+def test_decode_slots_rejects_bad_arguments():
+    assert _slots(_cfg(head_dim=64), 1, 4) == BAD_CONFIG
+    assert _slots(_cfg(), -1, 4) == BAD_SHAPE
+    assert _slots(_cfg(), 1, -4) == BAD_SHAPE
+    assert _slots(_cfg(num_heads=1), 16_777_216, 4) == BAD_SHAPE
+    assert _slots(_cfg(), 0, 4) == OK   # empty batch: nothing queued
+    assert _slots(_cfg(), 3, 0) == OK   # empty pool: every row would be skipped
+    assert _slots(_cfg(), 3, 4, slots=None) == NULL_ARG
+    assert _slots(_cfg(), 3, 4, slots=ctypes.c_void_p(FAKE + 2)) == MISALIGNED
+    # argument order: q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_pool,
+    # conv_pool, out -- all required
+    for i in range(13):
+        p = [ctypes.c_void_p(FAKE)] * 13
+        p[i] = None
+        assert _slots(_cfg(), 3, 4, ptrs=p) == NULL_ARG, i
+        p[i] = ctypes.c_void_p(FAKE + 4)
+        assert _slots(_cfg(), 3, 4, ptrs=p) == MISALIGNED, i

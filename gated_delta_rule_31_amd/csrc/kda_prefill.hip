@@ -30,11 +30,13 @@
 // K = 32 MFMA.  The state therefore feeds W S0 and (q e^G) S0 straight from registers.
 // U uses the same interleave over tokens, so it feeds P U and K_end^T U the same way.
 //
-// In the prologue wave w handles sub-chunk I = w % 4 (tokens 16I..16I+15) and channel
-// half w / 4; lane l owns token 16I + l%16 and 16 channels 64(w/4) + 16(l/16) + 0..15.
-// Those are also the A-operand rows and K-slices of block row I of A and P over that
-// channel half, so each wave computes its half of block row I from its own registers;
-// the two halves are added through LDS.
+// In the prologue wave w handles channel half w / 4 of sub-chunk I (tokens 16I..16I+15),
+// I = w % 4 for half 0 and 3 - w % 4 for half 1; lane l owns token 16I + l%16 and 16
+// channels 64(w/4) + 16(l/16) + 0..15.  Those are also the operand rows and K-slices of
+// block row I of A and P over that channel half, so each wave computes its half of block
+// row I from its own registers; the two halves are added through LDS.  Block row I has
+// I + 1 blocks, and waves w and w + 4 share a SIMD: pairing sub-chunks I and 3 - I there
+// gives every SIMD the same 5 blocks.
 
 #include "kda_device.hpp"
 
@@ -52,7 +54,7 @@ constexpr int OFF_R5 = 100352;   // sPh, sPl bf16 [64][64] (P split hi/lo)
 constexpr int OFF_R6 = 117760;   // sT fp32 [64][68]            -> sQe bf16 [64][128]
 constexpr int OFF_R7 = 135168;   // sTb bf16 [64][64]
 constexpr int OFF_TAB = 143360;  // small fp32 tables
-constexpr int kTabFloats = 512 + 640 + 768 + 512 + 512 + 128 + 64 + 256;
+constexpr int kTabFloats = 512 + 640 + 768 + 512 + 512 + 128 + 256;
 constexpr int OFF_CW = OFF_TAB + kTabFloats * 4;  // conv taps of this head, fp32 [3][128][4]
 constexpr int OFF_DTB = OFF_CW + 3 * 128 * 4 * 4;  // dt_bias of this head, fp32 [128]
 constexpr int kLdsBytes = OFF_DTB + 128 * 4;
@@ -89,6 +91,10 @@ __device__ __forceinline__ float row_scan16(float v) {
     return v;
 }
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }  // J < I
+// the prologue sub-chunk of wave w (see the header)
+__device__ __forceinline__ int wave_sub(int w) { return (w >> 2) ? 3 - (w & 3) : (w & 3); }
+// 4 consecutive bf16 of one row of a swizzled tile (8 bytes, one LDS store)
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Lane coordinates, re-derived at the start of every phase from an opaque copy of the
 // thread id.  Without this the compiler hoists every lane-dependent LDS address of the
@@ -101,7 +107,7 @@ __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2
     const int w = __builtin_amdgcn_readfirstlane(tid_ >> 6);   \
     const int lr = tid_ & 15;                                  \
     const int lg = (tid_ >> 4) & 3;                            \
-    const int sub = w & 3;                                     \
+    const int sub = wave_sub(w);                               \
     const int half = w >> 2;                                   \
     const int t = 16 * sub + lr;                               \
     (void)w;                                                   \
@@ -137,7 +143,7 @@ __device__ __forceinline__ ChunkLoads load_chunk(const PrefillArgs &a, int tid, 
         const uint32_t tok = (uint32_t)(min(max(t0 + c0 - 3 + row, t0), t1 - 1) - rbase);
         r.hist = *reinterpret_cast<const u32x4 *>(src + ebase + (tok * (uint32_t)HD + piece));
     }
-    const int lane_t = 16 * ((tid >> 6) & 3) + (tid & 15);     // the prologue token of this lane
+    const int lane_t = 16 * wave_sub(tid >> 6) + (tid & 15);    // the prologue token of this lane
     const int cbase = 64 * (tid >> 8) + 16 * ((tid >> 4) & 3);  // and its 16 channels
     const int tauc = min(max(t0 + c0 + lane_t, t0), t1 - 1);
     const uint32_t ztok = (uint32_t)(tauc - rbase);
@@ -175,8 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     float *sExpRef = sPair + 768;                              // [4][128] e^{r_I}
     float *sEndRef = sExpRef + 512;                            // [4][128] e^{G_end - r_I}
     float *sExpEnd = sEndRef + 512;                            // [128]    e^{G_end}
-    float *sBeta = sExpEnd + 128;                              // [64]
-    float *sNorm = sBeta + 64;                                 // [2 halves][q,k][64] sums of squares
+    float *sNorm = sExpEnd + 128;                              // [2 halves][q,k][64] sums of squares
     float *sConvW = reinterpret_cast<float *>(smem + OFF_CW);  // [3][128][4] taps, oldest first
     float *sDtb = reinterpret_cast<float *>(smem + OFF_DTB);   // [128] dt_bias
 
@@ -373,7 +378,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     gs[8 * pc + j] = g;
                 }
             }
-            if (lg == 0 && half == 0) sBeta[t] = beta;
         }
         lds_barrier();
 
@@ -479,10 +483,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     }
                     bf16x8 ch, cl;
                     split8(col, ch, cl);
-                    accA[J] = mma(ak[ks], ch, accA[J]);
-                    accP[J] = mma(aqh[ks], ch, accP[J]);
-                    accP[J] = mma(aql[ks], ch, accP[J]);
-                    accP[J] = mma(aqh[ks], cl, accP[J]);
+                    // the transposed tiles: lane (lr, lg) receives the entries (t, s) of
+                    // token t = 16 sub + lr and the 4 tokens s = 16J + 4lg + i
+                    accA[J] = mma(ch, ak[ks], accA[J]);
+                    accP[J] = mma(ch, aqh[ks], accP[J]);
+                    accP[J] = mma(ch, aql[ks], accP[J]);
+                    accP[J] = mma(cl, aqh[ks], accP[J]);
                 }
                 if (half == 1) {
                     const int bi = sub * (sub + 1) / 2 + J;  // block (sub, J), 0..9
@@ -504,21 +510,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                         pa = accA[J] + *reinterpret_cast<const f32x4 *>(sPart + ((bi * 2 + 0) * 64 + lane) * 4);
                         pp = accP[J] + *reinterpret_cast<const f32x4 *>(sPart + ((bi * 2 + 1) * 64 + lane) * 4);
                     }
+                    // row t of A (scaled by beta_t) and of P, columns 16J + 4lg .. +3
+                    f32x4 va;
+                    bf16x4 ph, pl;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int tr = 4 * lg + i;  // row inside the 16x16 block
-                        const int trow = 16 * sub + tr;
-                        float va = pa[i] * sBeta[trow];
-                        float vp = pp[i];
+                        const int sr = 4 * lg + i;  // column inside the 16x16 block
+                        float x = pa[i] * beta;
+                        float y = pp[i];
                         if (J == sub) {
-                            if (lr >= tr) va = 0.f;
-                            if (lr > tr) vp = 0.f;
+                            if (sr >= lr) x = 0.f;
+                            if (sr > lr) y = 0.f;
                         }
-                        sA[trow * F_LD + 16 * J + lr] = va;
-                        const __bf16 ph = (__bf16)vp;
-                        sPh[sw64(trow, 16 * J + lr)] = ph;
-                        sPl[sw64(trow, 16 * J + lr)] = (__bf16)(vp - (float)ph);
+                        va[i] = x;
+                        ph[i] = (__bf16)y;
+                        pl[i] = (__bf16)(y - (float)ph[i]);
                     }
+                    *reinterpret_cast<f32x4 *>(sA + t * F_LD + 16 * J + 4 * lg) = va;
+                    *reinterpret_cast<bf16x4 *>(sPh + sw64(t, 16 * J + 4 * lg)) = ph;
+                    *reinterpret_cast<bf16x4 *>(sPl + sw64(t, 16 * J + 4 * lg)) = pl;
                 }
             }
             // sCB is dead: K_end^T, hi/lo, into region 1 (channel half 1 now, half 0 in
@@ -648,10 +658,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     if (ks == 1 && tt < 2) continue;  // T is lower triangular
                     const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sTb + sw64(16 * tt + lr, 32 * ks + 8 * lg));
                     const bf16x8 B8 = *reinterpret_cast<const bf16x8 *>(sWr + sw64(16 * w + lr, 32 * ks + 8 * lg));
-                    acc = mma(A8, B8, acc);
+                    acc = mma(B8, A8, acc);  // W^T tile: keys 16w + 4lg + i of token 16tt + lr
                 }
+                bf16x4 w4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sW[swi128(16 * tt + 4 * lg + i, 16 * w + lr)] = (__bf16)acc[i];
+                for (int i = 0; i < 4; ++i) w4[i] = (__bf16)acc[i];
+                *reinterpret_cast<bf16x4 *>(sW + swi128(16 * tt + lr, 16 * w + 4 * lg)) = w4;
             }
             const int vrow = 16 * w + lr;
 #pragma unroll

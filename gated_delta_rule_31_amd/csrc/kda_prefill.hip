@@ -38,6 +38,8 @@
 // I + 1 blocks, and waves w and w + 4 share a SIMD: pairing sub-chunks I and 3 - I there
 // gives every SIMD the same 5 blocks.
 
+#include <type_traits>
+
 #include "kda_device.hpp"
 
 namespace kda {
@@ -266,6 +268,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         asm volatile("" : "+v"(tid_));
         ld = load_chunk(a, tid_, h, t0, t1, cbeg);
     }
+    // (the prefetched z and b are marked consumed where no store is in flight: once here,
+    //  and in every chunk before its stores; without that the compiler cannot count the
+    //  stores issued after them across the loop's back edge and makes phase 1 wait for
+    //  every memory operation in flight, stores included)
+    asm volatile("" ::"v"(ld.z[0]), "v"(ld.z[1]), "v"(ld.b));
 
     const int cend = kChunked ? min(min(cbeg + kSegChunks * kChunk, nrec * kChunk), T) : T;
     // (inside the chunk loop every cross-wave dependency goes through LDS, so its
@@ -304,14 +311,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             const int cbase = 64 * half + 16 * lg;      // first of this lane's 16 channels
             beta = valid ? sigm(ld.b) : 0.0f;
 
-            // SiLU(ShortConv4(x)) of the 8 channels cbase + 8pc .. +7 of block blk
+            // SiLU(ShortConv4(x)) of the 8 channels cbase + 8pc .. +7 of block blk.  Tokens
+            // past the sequence end (t >= L) get finite values of no effect: their beta and
+            // decay gate are zero, so their rows of W, U' and U are exactly zero and their
+            // rows of A are masked; only their own output rows (never stored) see them.
             auto conv_piece = [&](const int blk, const int pc, float *u) {
                 const int cb0 = cbase + 8 * pc;
                 float xr[4][8];  // rows tau-3 .. tau = staging rows t .. t+3
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     unpack8(*reinterpret_cast<const u32x4 *>(sStage + (blk * STG_ROWS + t + r) * STG_LD + cb0), xr[r]);
+                float4 cw[8];
+                float y[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    cw[j] = *reinterpret_cast<const float4 *>(sConvW + (blk * kD + cb0 + j) * 4);
+                    y[j] = cw[j].x * xr[0][j] + cw[j].y * xr[1][j] + cw[j].z * xr[2][j] + cw[j].w * xr[3][j];
+                }
                 if (head_of_seq) {
+                    // the rows before the sequence start come from the carried window: the
+                    // same sum again with those rows replaced
 #pragma unroll
                     for (int r = 0; r < 3; ++r) {
                         const int tok = tau - 3 + r;
@@ -321,13 +340,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                             for (int j = 0; j < 8; ++j) xr[r][j] = sWin0[(blk * kD + cb0 + j) * 3 + p];
                         }
                     }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        y[j] = cw[j].x * xr[0][j] + cw[j].y * xr[1][j] + cw[j].z * xr[2][j] + cw[j].w * xr[3][j];
                 }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float4 cw = *reinterpret_cast<const float4 *>(sConvW + (blk * kD + cb0 + j) * 4);
-                    const float y = cw.x * xr[0][j] + cw.y * xr[1][j] + cw.z * xr[2][j] + cw.w * xr[3][j];
-                    u[j] = valid ? y * sigm(y) : 0.f;
-                }
+                for (int j = 0; j < 8; ++j) u[j] = y[j] * sigm(y[j]);
             };
             // v: beta * v, hi/lo, transposed into sVt
 #pragma unroll
@@ -593,39 +611,44 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             }
         }
         lds_barrier();
-        // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ: wave J walks column J
-        // downward, so every T_KJ it needs is its own earlier result and only the diagonal
-        // blocks come from other waves (fp32 MFMA; the sum M is parked in the unused upper
-        // block (J, I) of sT; this wave's LDS accesses complete in order, so no barrier)
+        // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ: wave J (< 3) walks
+        // column J downward (fp32 MFMA, K = 4 per step).  Step kk of a product takes lane
+        // group lg's contraction index as 4lg + kk, so the B operand of that step is element
+        // kk of the lane's own accumulator tile (rows 4lg + i): the wave's earlier results
+        // T_KJ and the sum M feed the next products from registers, and only the rows of
+        // A_IK and T_II (16-byte reads) and the diagonal block T_JJ come from LDS.
         {
             KDA_LANE_IDS();
-            if (w < 3) {
-                const int J = w;
+            auto column = [&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                f32x4 R[4];  // R[K] = T_KJ (K > J): rows 16K + 4lg + i, column 16J + lr
+                float tjj[4];  // T_JJ[4lg + kk][lr]
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) tjj[kk] = sT[(16 * J + 4 * lg + kk) * F_LD + 16 * J + lr];
+#pragma unroll
                 for (int I = J + 1; I < 4; ++I) {
                     f32x4 M = {0.f, 0.f, 0.f, 0.f};
-                    for (int K = J; K < I; ++K)
+                    const f32x4 aj = *reinterpret_cast<const f32x4 *>(sA + (16 * I + lr) * F_LD + 16 * J + 4 * lg);
 #pragma unroll
-                        for (int kk = 0; kk < 4; ++kk)
-                            M = mma_f32(sA[(16 * I + lr) * F_LD + 16 * K + 4 * kk + lg],
-                                        sT[(16 * K + 4 * kk + lg) * F_LD + 16 * J + lr], M);
+                    for (int kk = 0; kk < 4; ++kk) M = mma_f32(aj[kk], tjj[kk], M);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sT[(16 * J + 4 * lg + i) * F_LD + 16 * I + lr] = M[i];
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                    f32x4 R = {0.f, 0.f, 0.f, 0.f};
+                    for (int K = J + 1; K < I; ++K) {
+                        const f32x4 ak4 = *reinterpret_cast<const f32x4 *>(sA + (16 * I + lr) * F_LD + 16 * K + 4 * lg);
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        R = mma_f32(-sT[(16 * I + lr) * F_LD + 16 * I + 4 * kk + lg],
-                                    sT[(16 * J + 4 * kk + lg) * F_LD + 16 * I + lr], R);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sT[(16 * I + 4 * lg + i) * F_LD + 16 * J + lr] = R[i];
-                        sTb[sw64(16 * I + 4 * lg + i, 16 * J + lr)] = (__bf16)R[i];
+                        for (int kk = 0; kk < 4; ++kk) M = mma_f32(ak4[kk], R[K][kk], M);
                     }
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    const f32x4 tii = *reinterpret_cast<const f32x4 *>(sT + (16 * I + lr) * F_LD + 16 * I + 4 * lg);
+                    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) r = mma_f32(-tii[kk], M[kk], r);
+                    R[I] = r;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sTb[sw64(16 * I + 4 * lg + i, 16 * J + lr)] = (__bf16)r[i];
                 }
-            }
+            };
+            if (w == 0) column(std::integral_constant<int, 0>{});
+            else if (w == 1) column(std::integral_constant<int, 1>{});
+            else if (w == 2) column(std::integral_constant<int, 2>{});
         }
         lds_barrier();
         // sT is dead: Q~ = q e^G into region 6
@@ -684,6 +707,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     U[tp][x] = acc;
                 }
         }
+        asm volatile("" ::"v"(ld.z[0]), "v"(ld.z[1]), "v"(ld.b));  // (see before the loop)
         lds_barrier();
 
         if constexpr (kChunked) {

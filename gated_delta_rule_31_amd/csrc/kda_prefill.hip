@@ -564,42 +564,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         lds_barrier();
 
         // ================= phase 3: T = (I + A)^-1 in fp32 =================
-        // (first the next chunk's raw inputs are requested, to arrive during phases 3-5;
-        //  past the last chunk this reloads clamped rows that are never used)
-        {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
-            ld = load_chunk(a, tid_, h, t0, t1, c0 + kChunk);
-        }
-        // diagonal 16x16 blocks by forward substitution: waves 0..3, lanes 0..15 own columns
-        // (every block of T is also written as bf16 into sTb for the MFMAs of phase 4; the
-        //  waves 4..7 clear sTb's upper blocks meanwhile)
+        // diagonal 16x16 blocks: wave 3, lane group lg inverts block lg, lane lr its column lr,
+        // by forward substitution in right-looking order (once x[k] is final it is subtracted
+        // from every later row, so the updates of one step are independent).  Every block of
+        // T is also written as bf16 into sTb for the MFMAs of phase 4; waves 4..7 clear sTb's
+        // upper blocks meanwhile.
         {
             KDA_LANE_IDS();
-            if (w < 4) {
-                if (lg == 0) {
-                    // the block's strictly lower part is read up front (the same 120 values
-                    // in all 16 lanes), so that no step of the substitution waits for LDS
-                    float arow[16][16];
+            if (w == 3) {
+                const int d = 16 * lg;
+                // the block's strictly lower part is read up front (the same 120 values in
+                // all 16 lanes of the group), so that no step waits for LDS
+                float arow[16][16];
 #pragma unroll
-                    for (int tt = 1; tt < 16; ++tt)
+                for (int tt = 1; tt < 16; ++tt)
 #pragma unroll
-                        for (int j = 0; j < tt; ++j) arow[tt][j] = sA[(16 * w + tt) * F_LD + 16 * w + j];
-                    float xcol[16];
+                    for (int j = 0; j < tt; ++j) arow[tt][j] = sA[(d + tt) * F_LD + d + j];
+                float x[16];
 #pragma unroll
-                    for (int tt = 0; tt < 16; ++tt) {
-                        float acc = (tt == lr) ? 1.0f : 0.0f;
+                for (int tt = 0; tt < 16; ++tt) x[tt] = (tt == lr) ? 1.0f : 0.0f;
 #pragma unroll
-                        for (int j = 0; j < tt; ++j) acc -= arow[tt][j] * xcol[j];
-                        xcol[tt] = acc;
-                    }
+                for (int k = 0; k < 15; ++k)
 #pragma unroll
-                    for (int tt = 0; tt < 16; ++tt) {
-                        sT[(16 * w + tt) * F_LD + 16 * w + lr] = xcol[tt];
-                        sTb[sw64(16 * w + tt, 16 * w + lr)] = (__bf16)xcol[tt];
-                    }
+                    for (int tt = k + 1; tt < 16; ++tt) x[tt] -= arow[tt][k] * x[k];
+#pragma unroll
+                for (int tt = 0; tt < 16; ++tt) {
+                    sT[(d + tt) * F_LD + d + lr] = x[tt];
+                    sTb[sw64(d + tt, d + lr)] = (__bf16)x[tt];
                 }
-            } else {
+            } else if (w >= 4) {
                 // upper blocks (I < J) of sTb: 6 blocks x 256 values over 256 lanes
                 const int lane = tid_ & 255;
 #pragma unroll
@@ -609,6 +602,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     sTb[sw64(16 * I + (lane >> 4), 16 * J + (lane & 15))] = (__bf16)0.0f;
                 }
             }
+            // The next chunk's raw inputs are requested now, to arrive during phases 3-5
+            // (past the last chunk this reloads clamped rows that are never used).  Issuing
+            // all eight waves' loads occupies the CU's memory pipe for about 2K cycles: the
+            // other waves do it while wave 3 inverts, and wave 3 after its inverse.
+            ld = load_chunk(a, tid_, h, t0, t1, c0 + kChunk);
         }
         lds_barrier();
         // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ: wave J (< 3) walks

@@ -11,15 +11,16 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
-__all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes", "KdaError",
+__all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes", "kda_state_copy", "KdaError",
            "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes",
-                    "kda_status_str", "kda_abi_version")
-ABI_VERSION = 4
+                    "kda_state_copy", "kda_status_str", "kda_abi_version")
+ABI_VERSION = 5
 HEAD_DIM = 128
 CONV = 4
 
@@ -83,6 +84,9 @@ def _load() -> ctypes.CDLL:
                               [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp, ctypes.c_size_t, vp])
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32]
+    L.kda_state_copy.restype = ctypes.c_int
+    L.kda_state_copy.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp, vp,
+                                  ctypes.c_int32, vp, vp])
     L.kda_status_str.restype = ctypes.c_char_p
     L.kda_status_str.argtypes = [ctypes.c_int]
     L.kda_abi_version.restype = ctypes.c_int32
@@ -260,3 +264,41 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
         # out again before the kernels queued on ``stream`` are done with it
         workspace.record_stream(stream)
     return out, final_state, final_conv_state
+
+
+def kda_state_copy(cfg: KdaConfig, src_state, src_conv, src_slots, dst_state, dst_conv, dst_slots,
+                   stream=None) -> None:
+    """Copy entry src_slots[i] of (src_state [Ps,H,D,D], src_conv [Ps,3*H*D,3]) to entry
+    dst_slots[i] of (dst_state, dst_conv), in order.  The buffers are GPU tensors or host
+    tensors (pinned ones make the copies asynchronous on the stream); the slot lists are
+    host sequences of ints."""
+    H, D = cfg.num_heads, cfg.head_dim
+    f32 = torch.float32
+
+    def buf(t, shape, name):
+        if t.dtype != f32:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {f32}")
+        if tuple(t.shape[1:]) != shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected [entries, {', '.join(map(str, shape))}]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+    ss = np.ascontiguousarray(np.asarray(src_slots, dtype=np.int32).reshape(-1))
+    ds = np.ascontiguousarray(np.asarray(dst_slots, dtype=np.int32).reshape(-1))
+    if ss.shape != ds.shape:
+        raise ValueError(f"src_slots and dst_slots differ in length: {ss.shape[0]} vs {ds.shape[0]}")
+    if src_state.shape[0] != src_conv.shape[0] or dst_state.shape[0] != dst_conv.shape[0]:
+        raise ValueError("state and conv buffers of one side must hold the same number of entries")
+    if stream is None and (src_state.is_cuda or dst_state.is_cuda):
+        stream = torch.cuda.current_stream()
+    c = cfg._c()
+    st = _lib.kda_state_copy(ctypes.byref(c), int(ss.shape[0]),
+                             buf(src_state, (H, D, D), "src_state"), buf(src_conv, (3 * H * D, CONV - 1), "src_conv"),
+                             int(src_state.shape[0]), ss.ctypes.data_as(ctypes.c_void_p),
+                             buf(dst_state, (H, D, D), "dst_state"), buf(dst_conv, (3 * H * D, CONV - 1), "dst_conv"),
+                             int(dst_state.shape[0]), ds.ctypes.data_as(ctypes.c_void_p),
+                             ctypes.c_void_p(stream.cuda_stream) if stream is not None else None)
+    if st != 0:
+        raise KdaError(st, "kda_state_copy")
+

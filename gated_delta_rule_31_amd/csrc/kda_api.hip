@@ -218,6 +218,52 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
     return kda::launch_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status kda_state_copy(const kda_config *cfg, int32_t n, const float *src_state, const float *src_conv,
+                          int32_t src_entries, const int32_t *src_slots, float *dst_state, float *dst_conv,
+                          int32_t dst_entries, const int32_t *dst_slots, void *stream) {
+    kda::MixerConsts c;
+    kda_status st = check_config(cfg, &c);
+    if (st != KDA_OK) return st;
+    if (n < 0 || src_entries < 0 || dst_entries < 0) return KDA_ERR_BAD_SHAPE;
+    if (n == 0) return KDA_OK;
+    const void *ptrs[] = {src_state, src_conv, dst_state, dst_conv};
+    if (!src_slots || !dst_slots) return KDA_ERR_NULL_ARG;
+    for (const void *p : ptrs)
+        if (!p) return KDA_ERR_NULL_ARG;
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    for (int32_t i = 0; i < n; ++i)
+        if (src_slots[i] < 0 || src_slots[i] >= src_entries || dst_slots[i] < 0 || dst_slots[i] >= dst_entries)
+            return KDA_ERR_BAD_SHAPE;
+    const size_t state_bytes = (size_t)c.H * kda::kD * kda::kD * sizeof(float);
+    const size_t conv_bytes = (size_t)3 * c.H * kda::kD * (kda::kConv - 1) * sizeof(float);
+    // a source buffer and the destination buffer of the same kind are the same one or
+    // disjoint; a state buffer and a conv buffer are always disjoint
+    auto disjoint = [](const void *s, size_t sn, const void *d, size_t dn) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(s), b = reinterpret_cast<uintptr_t>(d);
+        return a + sn <= b || b + dn <= a;
+    };
+    const size_t ss_n = state_bytes * src_entries, sc_n = conv_bytes * src_entries;
+    const size_t ds_n = state_bytes * dst_entries, dc_n = conv_bytes * dst_entries;
+    if ((src_state != dst_state && !disjoint(src_state, ss_n, dst_state, ds_n)) ||
+        (src_conv != dst_conv && !disjoint(src_conv, sc_n, dst_conv, dc_n)) ||
+        !disjoint(src_state, ss_n, dst_conv, dc_n) || !disjoint(src_conv, sc_n, dst_state, ds_n))
+        return KDA_ERR_BAD_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t i = 0; i < n; ++i) {
+        const size_t si = (size_t)src_slots[i], di = (size_t)dst_slots[i];
+        const char *ss = reinterpret_cast<const char *>(src_state) + si * state_bytes;
+        char *ds = reinterpret_cast<char *>(dst_state) + di * state_bytes;
+        const char *sc = reinterpret_cast<const char *>(src_conv) + si * conv_bytes;
+        char *dc = reinterpret_cast<char *>(dst_conv) + di * conv_bytes;
+        if (ss == ds) continue;  // an entry onto itself
+        if (hipMemcpyAsync(ds, ss, state_bytes, hipMemcpyDefault, s) != hipSuccess ||
+            hipMemcpyAsync(dc, sc, conv_bytes, hipMemcpyDefault, s) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+    }
+    return KDA_OK;
+}
+
 const char *kda_status_str(kda_status s) {
     switch (s) {
         case KDA_OK: return "ok";
@@ -226,7 +272,7 @@ const char *kda_status_str(kda_status s) {
         case KDA_ERR_BAD_SHAPE: return "negative, inconsistent or too large sizes";
         case KDA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
         case KDA_ERR_WORKSPACE: return "workspace too small";
-        case KDA_ERR_LAUNCH: return "kernel launch failed";
+        case KDA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch or a copy";
     }
     return "unknown status";
 }

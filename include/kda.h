@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
     KDA_OK = 0,
@@ -64,7 +64,7 @@ typedef enum {
     KDA_ERR_BAD_SHAPE = 3,  /* negative or inconsistent sizes, or sizes past the limits */
     KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned (workspace: 256-byte) */
     KDA_ERR_WORKSPACE = 5,  /* workspace smaller than kda_prefill_workspace_bytes() */
-    KDA_ERR_LAUNCH = 6      /* the HIP runtime refused a kernel launch */
+    KDA_ERR_LAUNCH = 6      /* the HIP runtime refused a kernel launch or a copy */
 } kda_status;
 
 /* Mixer constants.  Fill with kda_config_default() and set num_heads. */
@@ -256,6 +256,40 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
  * sequences of N tokens in total can need).  Returns 0 for arguments kda_prefill would
  * reject. */
 size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens);
+
+/*
+ * kda_state_copy -- copy whole (sequence) entries of recurrent state and conv windows
+ * between two state buffers: entry src_slots[i] of (src_state, src_conv) to entry
+ * dst_slots[i] of (dst_state, dst_conv), for i = 0 .. n-1, in that order.
+ *
+ * The serving engine on page "colibri/c/kimi_k3.c" keeps "photos" of the KDA recurrent
+ * state and its three conv windows at turn boundaries (ENV COLI_K3_CKPT /
+ * COLI_K3_CKPT_DIR in the header comment) and resumes a divergent prompt from the
+ * deepest valid photo instead of prefilling again.  This call takes such a photo of pool
+ * entries into host memory, restores one into any pool entries, or copies entries
+ * inside the device (fork a sequence, compact a pool, keep a pre-verify snapshot).
+ *
+ *   n                      entries to copy, >= 0 (0: nothing queued)
+ *   src_state, src_conv    [src_entries, H, D, D] and [src_entries, 3*H*D, 3] fp32
+ *   src_entries            entries in the source buffers
+ *   src_slots              HOST int32 [n], each in [0, src_entries)
+ *   dst_state, dst_conv    [dst_entries, H, D, D] and [dst_entries, 3*H*D, 3] fp32
+ *   dst_entries, dst_slots the same for the destination
+ *   stream                 hipStream_t or NULL
+ * Each buffer is device memory or host memory; with pinned host memory (hipHostMalloc)
+ * the copies are asynchronous on the stream, with pageable host memory the runtime may
+ * complete them before returning.  A source and a destination buffer are either the same
+ * buffer or do not overlap (KDA_ERR_BAD_SHAPE otherwise); within one buffer the copies
+ * run in slot-list order.  Every slot is checked before anything is queued; a
+ * KDA_ERR_LAUNCH (the runtime refused a copy) can leave the entries before the failing
+ * one copied.
+ * Alignment: the four buffer pointers 16-byte aligned.
+ */
+kda_status kda_state_copy(const kda_config *cfg, int32_t n,
+                          const float *src_state, const float *src_conv, int32_t src_entries,
+                          const int32_t *src_slots,
+                          float *dst_state, float *dst_conv, int32_t dst_entries,
+                          const int32_t *dst_slots, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_str(kda_status s);

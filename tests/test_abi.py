@@ -205,3 +205,40 @@ def test_decode_slots_rejects_bad_arguments():
         assert _slots(_cfg(), 3, 4, ptrs=p) == NULL_ARG, i
         p[i] = ctypes.c_void_p(FAKE + 4)
         assert _slots(_cfg(), 3, 4, ptrs=p) == MISALIGNED, i
+
+
+def _copy(cfg, n, src=(FAKE, FAKE), src_entries=4, src_slots=None, dst=(FAKE, FAKE), dst_entries=4, dst_slots=None):
+    arr = lambda xs: (ctypes.c_int32 * len(xs))(*xs) if xs is not None else None
+    ss = arr(src_slots if src_slots is not None else [0] * max(n, 1))
+    ds = arr(dst_slots if dst_slots is not None else [0] * max(n, 1))
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return kda.lib().kda_state_copy(ctypes.byref(cfg), n, vp(src[0]), vp(src[1]), src_entries, ss,
+                                    vp(dst[0]), vp(dst[1]), dst_entries, ds, None)
+
+
+def test_state_copy_rejects_bad_arguments():
+    # every case below is rejected on the host before any copy is queued
+    H = 96
+    st, cv = H * 128 * 128 * 4, 3 * H * 128 * 3 * 4  # bytes of one entry
+    A, B = 0x100000000, 0x200000000  # two far-apart, 16-byte aligned addresses
+    src, dst = (A, A + 8 * st), (B, B + 8 * st)
+    assert _copy(_cfg(head_dim=64), 1, src, 4, [0], dst, 4, [0]) == BAD_CONFIG
+    assert _copy(_cfg(), -1, src, 4, [0], dst, 4, [0]) == BAD_SHAPE
+    assert _copy(_cfg(), 1, src, -1, [0], dst, 4, [0]) == BAD_SHAPE
+    assert _copy(_cfg(), 0, src, 4, [0], dst, 4, [0]) == OK  # nothing to copy
+    assert kda.lib().kda_state_copy(ctypes.byref(_cfg()), 1, ctypes.c_void_p(A), ctypes.c_void_p(A + 8 * st), 4,
+                                    None, ctypes.c_void_p(B), ctypes.c_void_p(B + 8 * st), 4,
+                                    (ctypes.c_int32 * 1)(0), None) == NULL_ARG
+    for i in range(4):
+        ptrs = [src[0], src[1], dst[0], dst[1]]
+        ptrs[i] = None
+        assert _copy(_cfg(), 1, (ptrs[0], ptrs[1]), 4, [0], (ptrs[2], ptrs[3]), 4, [0]) == NULL_ARG, i
+        ptrs[i] = [src[0], src[1], dst[0], dst[1]][i] + 4
+        assert _copy(_cfg(), 1, (ptrs[0], ptrs[1]), 4, [0], (ptrs[2], ptrs[3]), 4, [0]) == MISALIGNED, i
+    # slots outside the buffers, on either side, anywhere in the list
+    for ss, ds in (([4], [0]), ([-1], [0]), ([0], [4]), ([0], [-2]), ([0, 1, 9], [0, 1, 2])):
+        assert _copy(_cfg(), len(ss), src, 4, ss, dst, 4, ds) == BAD_SHAPE, (ss, ds)
+    # distinct source and destination buffers that overlap
+    assert _copy(_cfg(), 1, src, 4, [0], (A + st, B), 4, [0]) == BAD_SHAPE
+    assert _copy(_cfg(), 1, src, 4, [0], (B, A + 8 * st + 16), 4, [0]) == BAD_SHAPE
+    assert _copy(_cfg(), 1, src, 4, [0], (A + 8 * st, B), 4, [0]) == BAD_SHAPE  # dst state on src conv

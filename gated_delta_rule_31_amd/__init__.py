@@ -14,13 +14,14 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-__all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes", "kda_state_copy", "KdaError",
+__all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_decode_multi_slots", "kda_prefill", "kda_prefill_workspace_bytes", "kda_state_copy", "KdaError",
            "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
-EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_prefill", "kda_prefill_workspace_bytes",
+EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi",
+                    "kda_decode_multi_slots", "kda_prefill", "kda_prefill_workspace_bytes",
                     "kda_state_copy", "kda_status_str", "kda_abi_version")
-ABI_VERSION = 5
+ABI_VERSION = 6
 HEAD_DIM = 128
 CONV = 4
 
@@ -79,6 +80,9 @@ def _load() -> ctypes.CDLL:
     L.kda_decode_multi.restype = ctypes.c_int
     L.kda_decode_multi.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [fp] * 15 +
                                    [vp])
+    L.kda_decode_multi_slots.restype = ctypes.c_int
+    L.kda_decode_multi_slots.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                          ctypes.c_int32] + [fp] * 15 + [vp])
     L.kda_prefill.restype = ctypes.c_int
     L.kda_prefill.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 6 +
                               [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp, ctypes.c_size_t, vp])
@@ -180,14 +184,11 @@ def kda_decode_step_slots(cfg: KdaConfig, slots, q, k, v, z, b, g, conv_w, A_log
     return out
 
 
-def kda_decode_multi(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in, conv_state_in,
-                     state_out=None, conv_state_out=None, n_tokens=None, out=None, stream=None) -> torch.Tensor:
-    """Up to T tokens per sequence in one call.  q,k,v,z,g: [B, T, H*D] fp32; b: [B, T, H];
-    n_tokens: int32 [B] on the GPU or None (T each).  The states are written to
-    ``state_out`` / ``conv_state_out`` (default: in place).  Returns out [B, T, H*D] fp32
-    (rows of tokens past n_tokens[b] are left as they were)."""
+def _decode_multi(cfg, slots, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in, conv_state_in, state_out,
+                  conv_state_out, n_tokens, out, stream, where):
     H, D = cfg.num_heads, cfg.head_dim
     B, T = q.shape[0], q.shape[1]
+    P = B if slots is None else state_in.shape[0]
     HD = H * D
     f32 = torch.float32
     if state_out is None:
@@ -197,21 +198,46 @@ def kda_decode_multi(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, n
     if out is None:
         out = torch.empty((B, T, HD), dtype=f32, device=q.device)
     args = [
-        _ptr(n_tokens, torch.int32, (B,), "n_tokens"),
         _ptr(q, f32, (B, T, HD), "q"), _ptr(k, f32, (B, T, HD), "k"), _ptr(v, f32, (B, T, HD), "v"),
         _ptr(z, f32, (B, T, HD), "z"), _ptr(b, f32, (B, T, H), "b"), _ptr(g, f32, (B, T, HD), "g"),
         _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
         _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
-        _ptr(state_in, f32, (B, H, D, D), "state_in"), _ptr(state_out, f32, (B, H, D, D), "state_out"),
-        _ptr(conv_state_in, f32, (B, 3 * HD, CONV - 1), "conv_state_in"),
-        _ptr(conv_state_out, f32, (B, 3 * HD, CONV - 1), "conv_state_out"),
+        _ptr(state_in, f32, (P, H, D, D), "state_in"), _ptr(state_out, f32, (P, H, D, D), "state_out"),
+        _ptr(conv_state_in, f32, (P, 3 * HD, CONV - 1), "conv_state_in"),
+        _ptr(conv_state_out, f32, (P, 3 * HD, CONV - 1), "conv_state_out"),
         _ptr(out, f32, (B, T, HD), "out"),
     ]
     c = cfg._c()
-    st = _lib.kda_decode_multi(ctypes.byref(c), B, T, *args, _stream(stream))
+    nt = _ptr(n_tokens, torch.int32, (B,), "n_tokens")
+    if slots is None:
+        st = _lib.kda_decode_multi(ctypes.byref(c), B, T, nt, *args, _stream(stream))
+    else:
+        st = _lib.kda_decode_multi_slots(ctypes.byref(c), B, T, nt, _ptr(slots, torch.int32, (B,), "slots"), P,
+                                         *args, _stream(stream))
     if st != 0:
-        raise KdaError(st, "kda_decode_multi")
+        raise KdaError(st, where)
     return out
+
+
+def kda_decode_multi(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in, conv_state_in,
+                     state_out=None, conv_state_out=None, n_tokens=None, out=None, stream=None) -> torch.Tensor:
+    """Up to T tokens per sequence in one call.  q,k,v,z,g: [B, T, H*D] fp32; b: [B, T, H];
+    n_tokens: int32 [B] on the GPU or None (T each).  The states are written to
+    ``state_out`` / ``conv_state_out`` (default: in place).  Returns out [B, T, H*D] fp32
+    (rows of tokens past n_tokens[b] are left as they were)."""
+    return _decode_multi(cfg, None, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in, conv_state_in,
+                         state_out, conv_state_out, n_tokens, out, stream, "kda_decode_multi")
+
+
+def kda_decode_multi_slots(cfg: KdaConfig, slots, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in,
+                           conv_state_in, state_out=None, conv_state_out=None, n_tokens=None, out=None,
+                           stream=None) -> torch.Tensor:
+    """kda_decode_multi over state pools: batch row r works on pool entry ``slots[r]``
+    (int32 [B] on the GPU) of state_in [P,H,D,D] / conv_state_in [P,3*H*D,3] and writes it
+    to the same entry of state_out / conv_state_out (default: in place); rows whose slot
+    lies outside [0, P) are skipped."""
+    return _decode_multi(cfg, slots, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in, conv_state_in,
+                         state_out, conv_state_out, n_tokens, out, stream, "kda_decode_multi_slots")
 
 
 def kda_prefill_workspace_bytes(cfg: KdaConfig, num_seqs: int, total_tokens: int) -> int:

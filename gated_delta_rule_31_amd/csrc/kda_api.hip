@@ -129,26 +129,34 @@ kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int
     return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
-                            const float *q, const float *k, const float *v, const float *z, const float *b,
-                            const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
-                            const float *norm_w, const float *state_in, float *state_out,
-                            const float *conv_state_in, float *conv_state_out, float *out, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// pooled: the slot-indexed form (slots required)
+kda_status decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
+                        bool pooled, const int32_t *slots, int32_t pool_size, const float *q, const float *k, const float *v,
+                        const float *z, const float *b, const float *g, const float *conv_w, const float *A_log,
+                        const float *dt_bias, const float *norm_w, const float *state_in, float *state_out,
+                        const float *conv_state_in, float *conv_state_out, float *out, void *stream) {
     kda::DecodeMultiArgs a;
     kda_status st = check_config(cfg, &a.c);
     if (st != KDA_OK) return st;
-    if (batch < 0 || tokens < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits) ||
+    if (batch < 0 || tokens < 0 || pool_size < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits) ||
         !units_fit(batch, tokens, INT32_MAX))
         return KDA_ERR_BAD_SHAPE;
     if (batch == 0) return KDA_OK;
     if (tokens == 0) return KDA_ERR_BAD_SHAPE;
+    if (pooled && !slots) return KDA_ERR_NULL_ARG;
+    if (pooled && pool_size == 0) return KDA_OK;  // every row would be skipped
     const void *ptrs[] = {q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
                           state_in, state_out, conv_state_in, conv_state_out, out};
     for (const void *p : ptrs)
         if (!p) return KDA_ERR_NULL_ARG;
     for (const void *p : ptrs)
         if (!aligned16(p)) return KDA_ERR_MISALIGNED;
-    if ((reinterpret_cast<uintptr_t>(n_tokens) & 3u) != 0) return KDA_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(n_tokens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(slots) & 3u) != 0)
+        return KDA_ERR_MISALIGNED;
     a.B = batch;
     a.T = tokens;
     a.n_tokens = n_tokens;
@@ -157,7 +165,32 @@ kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens
     a.state_in = state_in; a.state_out = state_out;
     a.conv_in = conv_state_in; a.conv_out = conv_state_out;
     a.out = out;
+    a.slots = pooled ? slots : nullptr;
+    a.pool = pool_size;
     return kda::launch_decode_multi(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
+                            const float *q, const float *k, const float *v, const float *z, const float *b,
+                            const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
+                            const float *norm_w, const float *state_in, float *state_out,
+                            const float *conv_state_in, float *conv_state_out, float *out, void *stream) {
+    return decode_multi(cfg, batch, tokens, n_tokens, false, nullptr, 0, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
+                        state_in, state_out, conv_state_in, conv_state_out, out, stream);
+}
+
+kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
+                                  const int32_t *slots, int32_t pool_size, const float *q, const float *k,
+                                  const float *v, const float *z, const float *b, const float *g,
+                                  const float *conv_w, const float *A_log, const float *dt_bias,
+                                  const float *norm_w, const float *state_in, float *state_out,
+                                  const float *conv_state_in, float *conv_state_out, float *out, void *stream) {
+    return decode_multi(cfg, batch, tokens, n_tokens, true, slots, pool_size, q, k, v, z, b, g, conv_w, A_log, dt_bias,
+                        norm_w, state_in, state_out, conv_state_in, conv_state_out, out, stream);
 }
 
 size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens) {

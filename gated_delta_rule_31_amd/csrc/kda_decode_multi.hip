@@ -34,12 +34,21 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// kSlots: batch row bs reads and writes pool entry a.slots[bs] of the state and window
+// pools instead of entry bs; a row whose slot lies outside [0, a.pool) is skipped.
+template <bool kSlots>
 __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs a) {
     const int H = a.c.H;
     const int T = a.T;
-    const int bh = xcd_contiguous(blockIdx.x, gridDim.x);  // sequence * H + head
+    const int bh = xcd_contiguous(blockIdx.x, gridDim.x);  // batch row * H + head
     const int bs = bh / H;
     const int h = bh - bs * H;
+    int slot = bs;
+    if (kSlots) {
+        slot = a.slots[bs];                       // uniform over the workgroup
+        if (slot < 0 || slot >= a.pool) return;   // before any barrier
+    }
+    const size_t sofs = (size_t)slot * H + h;     // this head's state in the buffers
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -49,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
     const int n = a.n_tokens ? min(max(a.n_tokens[bs], 0), T) : T;
 
     f32x4 s[16];
-    const float *Sin = a.state_in + (size_t)bh * kD * kD;
+    const float *Sin = a.state_in + sofs * kD * kD;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sin + (rg + 8 * j) * kD + 4 * cg));
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
     __shared__ float sh_part[4][2][kD];
 
     // this lane's channels: their taps and carried windows (A: q or v, B: k)
-    const size_t conv_seq = (size_t)bs * 3 * HD * 3;
+    const size_t conv_seq = (size_t)slot * 3 * HD * 3;
     const int i = tid < kD ? tid : tid - kD;
     const size_t chA = (tid < kD ? 0 : 2 * HD) + (size_t)h * kD + i;
     const size_t chB = HD + (size_t)h * kD + i;
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
         lds_barrier();  // the next token rewrites the shared arrays
     }
 
-    float *Sout = a.state_out + (size_t)bh * kD * kD;
+    float *Sout = a.state_out + sofs * kD * kD;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         __builtin_nontemporal_store(s[j], reinterpret_cast<f32x4 *>(Sout + (rg + 8 * j) * kD + 4 * cg));
@@ -225,7 +234,9 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
 hipError_t launch_decode_multi(const DecodeMultiArgs &a, hipStream_t stream) {
     dim3 grid((unsigned)((size_t)a.B * a.c.H)), block(kThreads);
     void *args[] = {const_cast<DecodeMultiArgs *>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&decode_multi_kernel), grid, block, args, 0, stream);
+    const void *fn = a.slots ? reinterpret_cast<const void *>(&decode_multi_kernel<true>)
+                             : reinterpret_cast<const void *>(&decode_multi_kernel<false>);
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 }  // namespace kda

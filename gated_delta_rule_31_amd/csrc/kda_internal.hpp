@@ -42,6 +42,10 @@ struct DecodeMultiArgs {
     const float *conv_w, *A_log, *dt_bias, *norm_w;
     const float *state_in, *conv_in;
     float *state_out, *conv_out, *out;
+    // NULL: row b owns entry b of the state and window buffers.  Otherwise row b owns
+    // pool entry slots[b] of the `pool` entries (rows outside are skipped).
+    const int32_t *slots;
+    int pool;
 };
 
 // Prefill launch plans (kda_config.prefill_path):

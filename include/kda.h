@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
     KDA_OK = 0,
@@ -201,6 +201,35 @@ kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens
                             const float *state_in, float *state_out,
                             const float *conv_state_in, float *conv_state_out,
                             float *out, void *stream);
+
+/*
+ * kda_decode_multi_slots -- kda_decode_multi for states held in pools, as
+ * kda_decode_step_slots is for kda_decode_step: batch row r (its tokens, its n_tokens
+ * entry and its output rows) reads entry slots[r] of state_in / conv_state_in and writes
+ * entry slots[r] of state_out / conv_state_out.  The per-row work is exactly
+ * kda_decode_multi's (the same kernel), so verify and roll back work the same way over a
+ * pool: candidates into a second pool (state_out != state_in), then the accepted
+ * prefixes committed in place.
+ *
+ *   slots                  device int32 [B]; a row whose slot lies outside
+ *                          [0, pool_size) is skipped (its pool entries and output rows are
+ *                          not touched); two rows must not name the same slot
+ *   pool_size              P >= 0 entries in each of the four pools (0: nothing queued)
+ *   state_in, state_out    [P, H, D, D] fp32; the same buffer or disjoint
+ *   conv_state_in, conv_state_out   [P, 3*H*D, 3] fp32; the same buffer or disjoint
+ *   all other arguments    as for kda_decode_multi ([B, T, ...] token rows, out [B, T, H*D])
+ * Alignment: every fp32 pointer 16-byte aligned, n_tokens and slots 4-byte aligned.
+ * Limits: B*H <= 16,777,215; B*T <= 2^31-1.
+ */
+kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
+                                  const int32_t *slots, int32_t pool_size,
+                                  const float *q, const float *k, const float *v,
+                                  const float *z, const float *b, const float *g,
+                                  const float *conv_w, const float *A_log, const float *dt_bias,
+                                  const float *norm_w,
+                                  const float *state_in, float *state_out,
+                                  const float *conv_state_in, float *conv_state_out,
+                                  float *out, void *stream);
 
 /*
  * kda_prefill -- a packed batch of whole sequences (varlen), processed in chunks of

@@ -242,3 +242,26 @@ def test_state_copy_rejects_bad_arguments():
     assert _copy(_cfg(), 1, src, 4, [0], (A + st, B), 4, [0]) == BAD_SHAPE
     assert _copy(_cfg(), 1, src, 4, [0], (B, A + 8 * st + 16), 4, [0]) == BAD_SHAPE
     assert _copy(_cfg(), 1, src, 4, [0], (A + 8 * st, B), 4, [0]) == BAD_SHAPE  # dst state on src conv
+
+
+def _multi_slots(cfg, B, T, P, slots=ctypes.c_void_p(FAKE), n_tokens=None, ptrs=None):
+    p = [ctypes.c_void_p(FAKE)] * 15 if ptrs is None else ptrs
+    return kda.lib().kda_decode_multi_slots(ctypes.byref(cfg), B, T, n_tokens, slots, P, *p, None)
+
+
+def test_decode_multi_slots_rejects_bad_arguments():
+    assert _multi_slots(_cfg(head_dim=64), 1, 2, 4) == BAD_CONFIG
+    assert _multi_slots(_cfg(), -1, 2, 4) == BAD_SHAPE
+    assert _multi_slots(_cfg(), 1, 2, -4) == BAD_SHAPE
+    assert _multi_slots(_cfg(), 2, 0, 4) == BAD_SHAPE
+    assert _multi_slots(_cfg(), 0, 2, 4) == OK   # empty batch: nothing queued
+    assert _multi_slots(_cfg(), 2, 2, 0) == OK   # empty pool: every row would be skipped
+    assert _multi_slots(_cfg(), 2, 2, 4, slots=None) == NULL_ARG
+    assert _multi_slots(_cfg(), 2, 2, 4, slots=ctypes.c_void_p(FAKE + 2)) == MISALIGNED
+    assert _multi_slots(_cfg(), 2, 2, 4, n_tokens=ctypes.c_void_p(FAKE + 1)) == MISALIGNED
+    for i in range(15):
+        p = [ctypes.c_void_p(FAKE)] * 15
+        p[i] = None
+        assert _multi_slots(_cfg(), 2, 3, 4, ptrs=p) == NULL_ARG, i
+        p[i] = ctypes.c_void_p(FAKE + 4)
+        assert _multi_slots(_cfg(), 2, 3, 4, ptrs=p) == MISALIGNED, i

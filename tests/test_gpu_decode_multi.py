@@ -132,3 +132,43 @@ def test_k3_shape_four_tokens(device):
             worst = max(worst, slice_rel(o[b, i, h], ref[(b, h)].out[i]))
         worst = max(worst, slice_rel(s[b, h], ref[(b, h)].state))
     assert worst <= DECODE_REL_TOL, worst
+
+
+def test_pool_verify_and_commit_matches_dense(device):
+    """kda_decode_multi_slots over a pool: candidates into a second pool, then the accepted
+    prefixes committed in place; every applied row and entry equals the dense call's bits,
+    and a row aimed past the pool leaves everything untouched."""
+    case = ki.decode_case(314, 3, 4, 5, "multi-slots")
+    B, H, T, P = case.B, case.H, 5, 6
+    home = [4, 0, 2]
+    print(f"[decode-multi] {case.name} B={B} H={H} T={T} P={P} home={home}", flush=True)
+    mr = MultiRun(case, T, device)
+    pool_s = torch.full((P, H, D, D), 3.0, dtype=torch.float32, device=device)
+    pool_c = torch.full((P, 3 * H * D, 3), 3.0, dtype=torch.float32, device=device)
+    for bi, e in enumerate(home):
+        pool_s[e] = mr.state0[bi]
+        pool_c[e] = mr.conv0[bi]
+    before_s, before_c = pool_s.clone(), pool_c.clone()
+    # rows: the three sequences plus one aimed past the pool (it carries sequence 0's tokens)
+    rows = [0, 1, 2, 0]
+    slots = torch.tensor(home + [P + 3], dtype=torch.int32, device=device)
+    xs = [x[rows].contiguous() for x in mr.xs]
+    out = torch.full((4, T, H * D), float("nan"), dtype=torch.float32, device=device)
+    cand_s, cand_c = torch.zeros_like(pool_s), torch.zeros_like(pool_c)
+    kda.kda_decode_multi_slots(mr.cfg, slots, *xs, *mr.prm, pool_s, pool_c, state_out=cand_s,
+                               conv_state_out=cand_c, out=out)
+    accepted = torch.tensor([5, 2, 0, 5], dtype=torch.int32, device=device)
+    out2 = torch.full_like(out, float("nan"))
+    kda.kda_decode_multi_slots(mr.cfg, slots, *xs, *mr.prm, pool_s, pool_c, n_tokens=accepted, out=out2)
+    torch.cuda.synchronize()
+    dense_out = mr.call(mr.state0.clone(), mr.conv0.clone(), torch.empty_like(mr.state0), torch.empty_like(mr.conv0))
+    for bi, e in enumerate(home):
+        assert torch.equal(out[bi], dense_out[bi]), bi
+        a = int(accepted[bi])
+        assert torch.equal(out2[bi, :a], dense_out[bi, :a]) and torch.isnan(out2[bi, a:]).all(), bi
+        outs, st, cst = _single_steps(case, a, device) if a else ([], mr.state0, mr.conv0)
+        assert torch.equal(pool_s[e], st[bi]) and torch.equal(pool_c[e], cst[bi]), bi
+    assert torch.isnan(out[3]).all() and torch.isnan(out2[3]).all()
+    for e in set(range(P)) - set(home):
+        assert torch.equal(pool_s[e], before_s[e]) and torch.equal(pool_c[e], before_c[e]), e
+        assert (cand_s[e] == 0).all() and (cand_c[e] == 0).all(), e

@@ -95,11 +95,9 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeMultiArgs &a, hipStream_t stream);
+// the whole prefill in the chosen layout (kda_prefill.hip); the chunked layout's last
+// launch, the carry, is in kda_carry.hip
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
-// the chunked plan's kernels (kda_prefill.hip: chunk table, chunk records; kda_carry.hip:
-// the carry)
-hipError_t launch_chunk_table(const PrefillArgs &a, hipStream_t stream);
-hipError_t launch_chunk_records(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_carry(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace kda

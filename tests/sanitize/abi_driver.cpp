@@ -1,0 +1,94 @@
+// Host-only driver for the address / undefined-behaviour sanitizer build of the C ABI's
+// argument checks: kda_api.hip is linked with launchers that fail the test if reached,
+// and every call below must be rejected (or accepted as empty) before any HIP call.
+#include <stdint.h>
+#include <stdio.h>
+
+#include "kda.h"
+#include "kda_internal.hpp"
+
+namespace kda {
+static int reached = 0;
+hipError_t launch_decode(const DecodeArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
+hipError_t launch_decode_multi(const DecodeMultiArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
+hipError_t launch_prefill(const PrefillArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
+hipError_t launch_carry(const PrefillArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
+}  // namespace kda
+
+static int failures = 0;
+#define EXPECT(call, want)                                                               \
+    do {                                                                                 \
+        const int got_ = (int)(call);                                                    \
+        if (got_ != (int)(want)) {                                                       \
+            printf("line %d: %s returned %d, expected %d\n", __LINE__, #call, got_, (int)(want)); \
+            ++failures;                                                                  \
+        }                                                                                \
+    } while (0)
+
+int main() {
+    float *F = reinterpret_cast<float *>(0x10000);  // aligned, never dereferenced
+    float *Fm = reinterpret_cast<float *>(0x10004);
+    const uint16_t *Hh = reinterpret_cast<const uint16_t *>(0x10000);
+    const int32_t *I = reinterpret_cast<const int32_t *>(0x10000);
+    kda_config c = kda_config_default();
+    kda_config bad = c;
+    bad.head_dim = 64;
+
+    // decode, one token
+    EXPECT(kda_decode_step(nullptr, 1, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
+    EXPECT(kda_decode_step(&bad, 1, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_CONFIG);
+    EXPECT(kda_decode_step(&c, -1, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_decode_step(&c, 0, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_OK);
+    EXPECT(kda_decode_step(&c, 2, F, F, F, nullptr, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
+    EXPECT(kda_decode_step(&c, 2, F, F, F, F, F, F, F, F, F, F, F, Fm, F, nullptr), KDA_ERR_MISALIGNED);
+    EXPECT(kda_decode_step_slots(&c, 2, nullptr, 4, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
+    EXPECT(kda_decode_step_slots(&c, 2, I, 0, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_OK);
+    EXPECT(kda_decode_step_slots(&c, 2, I, -1, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
+
+    // decode, several tokens
+    EXPECT(kda_decode_multi(&c, 2, 0, nullptr, F, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_decode_multi(&c, 65536, 65536, nullptr, F, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
+           KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_decode_multi(&c, 2, 3, nullptr, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr, nullptr),
+           KDA_ERR_NULL_ARG);
+    EXPECT(kda_decode_multi_slots(&c, 2, 3, nullptr, nullptr, 4, F, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
+           KDA_ERR_NULL_ARG);
+    EXPECT(kda_decode_multi_slots(&c, 2, 3, nullptr, I, 0, F, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
+           KDA_OK);
+
+    // prefill
+    c.prefill_path = 7;
+    EXPECT(kda_prefill(&c, 1, 64, I, Hh, Hh, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
+           KDA_ERR_BAD_CONFIG);
+    c.prefill_path = KDA_PREFILL_CHUNKED;
+    EXPECT(kda_prefill(&c, 1, 64, I, Hh, Hh, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
+           KDA_ERR_WORKSPACE);
+    EXPECT(kda_prefill(&c, -1, 64, I, Hh, Hh, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
+           KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_prefill(&c, 0, 0, I, Hh, Hh, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
+           KDA_OK);
+    if (kda_prefill_workspace_bytes(&c, 1, 8192) != (size_t)256 + (size_t)(128 + 1) * 96 * 115200) {
+        printf("unexpected workspace size %zu\n", kda_prefill_workspace_bytes(&c, 1, 8192));
+        ++failures;
+    }
+    c.prefill_path = KDA_PREFILL_AUTO;
+
+    // state copies: slots outside the buffers, overlapping buffers
+    const int32_t s0[1] = {0}, s9[1] = {9};
+    float *A = reinterpret_cast<float *>(0x100000000ULL), *B = reinterpret_cast<float *>(0x200000000ULL);
+    float *Ac = A + 8 * 96 * 128 * 128;
+    EXPECT(kda_state_copy(&c, 1, A, Ac, 4, s9, B, B + 8 * 96 * 128 * 128, 4, s0, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_state_copy(&c, 1, A, Ac, 4, s0, A + 96 * 128 * 128, B, 4, s0, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_state_copy(&c, 1, A, Ac, 4, nullptr, B, B, 4, s0, nullptr), KDA_ERR_NULL_ARG);
+    EXPECT(kda_state_copy(&c, 0, A, Ac, 4, s0, B, B, 4, s0, nullptr), KDA_OK);
+
+    for (int s = 0; s <= 6; ++s)
+        if (!kda_status_str((kda_status)s)[0]) ++failures;
+    if (kda::reached) {
+        printf("%d calls reached a launcher\n", kda::reached);
+        ++failures;
+    }
+    if (failures) return 1;
+    printf("ok\n");
+    return 0;
+}

@@ -59,7 +59,8 @@ constexpr int OFF_TAB = 143360;  // small fp32 tables
 constexpr int kTabFloats = 512 + 640 + 768 + 512 + 512 + 128 + 256;
 constexpr int OFF_CW = OFF_TAB + kTabFloats * 4;  // conv taps of this head, fp32 [3][128][4]
 constexpr int OFF_DTB = OFF_CW + 3 * 128 * 4 * 4;  // dt_bias of this head, fp32 [128]
-constexpr int kLdsBytes = OFF_DTB + 128 * 4;
+constexpr int OFF_NW = OFF_DTB + 128 * 4;  // RMSNorm weight, fp32 [128] (fused layout's epilogue)
+constexpr int kLdsBytes = OFF_NW + 128 * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 // raw q, k, v rows of a chunk, staged once per chunk in regions 4-7 (free until phase 2):
@@ -186,6 +187,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     float *sNorm = sExpEnd + 128;                              // [2 halves][q,k][64] sums of squares
     float *sConvW = reinterpret_cast<float *>(smem + OFF_CW);  // [3][128][4] taps, oldest first
     float *sDtb = reinterpret_cast<float *>(smem + OFF_DTB);   // [128] dt_bias
+    float *sNw = reinterpret_cast<float *>(smem + OFF_NW);     // [128] RMSNorm weight
 
     const int H = a.c.H;
     const int N = a.N;
@@ -249,7 +251,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         const int blk = i >> 7, c = i & 127;
         const size_t ch = (size_t)blk * HD + (size_t)h * kD + c;
         *reinterpret_cast<float4 *>(sConvW + i * 4) = *reinterpret_cast<const float4 *>(a.conv_w + ch * 4);
-        if (i < kD) sDtb[i] = a.dt_bias[(size_t)h * kD + i];
+        if (i < kD) {
+            sDtb[i] = a.dt_bias[(size_t)h * kD + i];
+            if (!kChunked) sNw[i] = a.norm_w[i];
+        }
         if (cbeg == 0) {
 #pragma unroll
             for (int j = 0; j < 3; ++j)
@@ -840,10 +845,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 float *orow = a.out + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
 #pragma unroll
                 for (int j = 0; j < 16; j += 8) {
-                    float g8[8], y[8];
+                    float g8[8], nw[8], y[8];
                     unpack8(graw[j / 8], g8);
+                    lds_read8(sNw + v0 + j, nw);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[j + e] * rinv * a.norm_w[v0 + j + e]);
+                    for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[j + e] * rinv * nw[e]);
                     *reinterpret_cast<float4 *>(orow + j) = make_float4(y[0], y[1], y[2], y[3]);
                     *reinterpret_cast<float4 *>(orow + j + 4) = make_float4(y[4], y[5], y[6], y[7]);
                 }

@@ -339,12 +339,29 @@ def bench_prefill(args, dev):
     tf = flops / (kern_ms * 1e-3) / 1e12
     gbs = byts / (kern_ms * 1e-3) / 1e9
     mf, hf = tf / BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS
+    # the same call with bf16 outputs (kda_config.out_dtype), timed the same way
+    cfg16 = kda.KdaConfig(num_heads=H, prefill_path=path, out_dtype=torch.bfloat16)
+    out16 = torch.empty((N, H * D), dtype=torch.bfloat16, device=dev)
+    launch16 = lambda: kda.kda_prefill(cfg16, cu, *xs, *prm, None, None, out=out16, final_state=fs,
+                                       final_conv_state=fcs, workspace=ws)
+    launch16()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        launch16()
+    e1.record()
+    torch.cuda.synchronize()
+    ms16 = e0.elapsed_time(e1) / n
+    byts16 = byts - N * H * D * 2  # outputs at 2 bytes instead of 4
     return {"workload": "kda-prefill-1x8192tok-96head", "layout": args.prefill_path if path else
             ("chunked" if ws_bytes else "fused"), "workspace_bytes": ws_bytes,
             "tokens_per_s": round(N / (ms * 1e-3), 1),
             "ms_per_call": round(ms, 4), "kernel_avg_us": round(kern_ms * 1e3, 2),
             "mfma_frac": round(mf, 4), "hbm_frac": round(hf, 4), "roofline_frac": round(max(mf, hf), 4),
-            "alg_flops": flops, "alg_bytes": byts, "achieved_tflops": round(tf, 2), "achieved_gbs": round(gbs, 1)}
+            "alg_flops": flops, "alg_bytes": byts, "achieved_tflops": round(tf, 2), "achieved_gbs": round(gbs, 1),
+            "bf16_out": {"ms_per_call": round(ms16, 4), "tokens_per_s": round(N / (ms16 * 1e-3), 1),
+                         "alg_bytes": byts16, "hbm_frac": round(byts16 / (ms16 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
 def cpu_baseline(n_steps: int = 16, min_seconds: float = 10.0):

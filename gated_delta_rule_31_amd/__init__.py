@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi",
                     "kda_decode_multi_slots", "kda_prefill", "kda_prefill_workspace_bytes",
                     "kda_state_copy", "kda_status_str", "kda_abi_version")
-ABI_VERSION = 6
+ABI_VERSION = 7
 HEAD_DIM = 128
 CONV = 4
 
@@ -36,6 +36,7 @@ class _CConfig(ctypes.Structure):
         ("rms_eps", ctypes.c_float),
         ("q_scale", ctypes.c_float),
         ("prefill_path", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
     ]
 
 # kda_config.prefill_path values
@@ -54,10 +55,13 @@ class KdaConfig:
     rms_eps: float = 1e-5
     q_scale: float = 0.0  # <= 0 selects head_dim ** -0.5
     prefill_path: int = PREFILL_AUTO
+    out_dtype: torch.dtype = torch.float32  # or torch.bfloat16: element type of the outputs
 
     def _c(self) -> _CConfig:
+        if self.out_dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError(f"out_dtype must be torch.float32 or torch.bfloat16, not {self.out_dtype}")
         return _CConfig(self.num_heads, self.head_dim, self.conv_size, self.gate_lower_bound, self.l2_eps,
-                        self.rms_eps, self.q_scale, self.prefill_path)
+                        self.rms_eps, self.q_scale, self.prefill_path, 1 if self.out_dtype == torch.bfloat16 else 0)
 
 
 class KdaError(RuntimeError):
@@ -131,20 +135,20 @@ def _stream(stream) -> ctypes.c_void_p:
 def kda_decode_step(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state, conv_state,
                     out=None, stream=None) -> torch.Tensor:
     """One token per sequence.  q,k,v,z,g: [B, H*D] fp32; b: [B, H]; state [B,H,D,D] and
-    conv_state [B,3*H*D,3] are updated in place.  Returns out [B, H*D] fp32."""
+    conv_state [B,3*H*D,3] are updated in place.  Returns out [B, H*D] (cfg.out_dtype)."""
     H, D = cfg.num_heads, cfg.head_dim
     B = q.shape[0]
     HD = H * D
     f32 = torch.float32
     if out is None:
-        out = torch.empty((B, HD), dtype=f32, device=q.device)
+        out = torch.empty((B, HD), dtype=cfg.out_dtype, device=q.device)
     args = [
         _ptr(q, f32, (B, HD), "q"), _ptr(k, f32, (B, HD), "k"), _ptr(v, f32, (B, HD), "v"),
         _ptr(z, f32, (B, HD), "z"), _ptr(b, f32, (B, H), "b"), _ptr(g, f32, (B, HD), "g"),
         _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
         _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
         _ptr(state, f32, (B, H, D, D), "state"), _ptr(conv_state, f32, (B, 3 * HD, CONV - 1), "conv_state"),
-        _ptr(out, f32, (B, HD), "out"),
+        _ptr(out, cfg.out_dtype, (B, HD), "out"),
     ]
     c = cfg._c()
     st = _lib.kda_decode_step(ctypes.byref(c), B, *args, _stream(stream))
@@ -159,14 +163,14 @@ def kda_decode_step_slots(cfg: KdaConfig, slots, q, k, v, z, b, g, conv_w, A_log
     ``slots[r]`` (int32 [B] on the GPU) of state_pool [P,H,D,D] and conv_pool
     [P,3*H*D,3], in place; rows whose slot lies outside [0, P) are skipped and their
     output rows left as they were.  q,k,v,z,g: [B, H*D] fp32; b: [B, H].  Returns out
-    [B, H*D] fp32."""
+    [B, H*D] (cfg.out_dtype)."""
     H, D = cfg.num_heads, cfg.head_dim
     B = q.shape[0]
     P = state_pool.shape[0]
     HD = H * D
     f32 = torch.float32
     if out is None:
-        out = torch.empty((B, HD), dtype=f32, device=q.device)
+        out = torch.empty((B, HD), dtype=cfg.out_dtype, device=q.device)
     args = [
         _ptr(q, f32, (B, HD), "q"), _ptr(k, f32, (B, HD), "k"), _ptr(v, f32, (B, HD), "v"),
         _ptr(z, f32, (B, HD), "z"), _ptr(b, f32, (B, H), "b"), _ptr(g, f32, (B, HD), "g"),
@@ -174,7 +178,7 @@ def kda_decode_step_slots(cfg: KdaConfig, slots, q, k, v, z, b, g, conv_w, A_log
         _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
         _ptr(state_pool, f32, (P, H, D, D), "state_pool"),
         _ptr(conv_pool, f32, (P, 3 * HD, CONV - 1), "conv_pool"),
-        _ptr(out, f32, (B, HD), "out"),
+        _ptr(out, cfg.out_dtype, (B, HD), "out"),
     ]
     c = cfg._c()
     st = _lib.kda_decode_step_slots(ctypes.byref(c), B, _ptr(slots, torch.int32, (B,), "slots"), P, *args,
@@ -196,7 +200,7 @@ def _decode_multi(cfg, slots, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, 
     if conv_state_out is None:
         conv_state_out = conv_state_in
     if out is None:
-        out = torch.empty((B, T, HD), dtype=f32, device=q.device)
+        out = torch.empty((B, T, HD), dtype=cfg.out_dtype, device=q.device)
     args = [
         _ptr(q, f32, (B, T, HD), "q"), _ptr(k, f32, (B, T, HD), "k"), _ptr(v, f32, (B, T, HD), "v"),
         _ptr(z, f32, (B, T, HD), "z"), _ptr(b, f32, (B, T, H), "b"), _ptr(g, f32, (B, T, HD), "g"),
@@ -205,7 +209,7 @@ def _decode_multi(cfg, slots, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, 
         _ptr(state_in, f32, (P, H, D, D), "state_in"), _ptr(state_out, f32, (P, H, D, D), "state_out"),
         _ptr(conv_state_in, f32, (P, 3 * HD, CONV - 1), "conv_state_in"),
         _ptr(conv_state_out, f32, (P, 3 * HD, CONV - 1), "conv_state_out"),
-        _ptr(out, f32, (B, T, HD), "out"),
+        _ptr(out, cfg.out_dtype, (B, T, HD), "out"),
     ]
     c = cfg._c()
     nt = _ptr(n_tokens, torch.int32, (B,), "n_tokens")
@@ -223,7 +227,7 @@ def kda_decode_multi(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, n
                      state_out=None, conv_state_out=None, n_tokens=None, out=None, stream=None) -> torch.Tensor:
     """Up to T tokens per sequence in one call.  q,k,v,z,g: [B, T, H*D] fp32; b: [B, T, H];
     n_tokens: int32 [B] on the GPU or None (T each).  The states are written to
-    ``state_out`` / ``conv_state_out`` (default: in place).  Returns out [B, T, H*D] fp32
+    ``state_out`` / ``conv_state_out`` (default: in place).  Returns out [B, T, H*D] (cfg.out_dtype)
     (rows of tokens past n_tokens[b] are left as they were)."""
     return _decode_multi(cfg, None, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in, conv_state_in,
                          state_out, conv_state_out, n_tokens, out, stream, "kda_decode_multi")
@@ -249,7 +253,7 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
                 initial_state=None, initial_conv_state=None, out=None, final_state=None,
                 final_conv_state=None, workspace=None, stream=None):
     """Varlen prefill.  cu_seqlens: int32 [B+1] on the GPU; q,k,v,z,g: [N, H*D] bf16;
-    b: [N, H] bf16.  Returns (out [N, H*D] fp32, final_state, final_conv_state).
+    b: [N, H] bf16.  Returns (out [N, H*D] (cfg.out_dtype), final_state, final_conv_state).
     ``final_state`` may be ``initial_state`` (in-place carry)."""
     H, D = cfg.num_heads, cfg.head_dim
     B = cu_seqlens.shape[0] - 1
@@ -258,7 +262,7 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
     f32, bf = torch.float32, torch.bfloat16
     dev = q.device
     if out is None:
-        out = torch.empty((N, HD), dtype=f32, device=dev)
+        out = torch.empty((N, HD), dtype=cfg.out_dtype, device=dev)
     if final_state is None:
         final_state = torch.empty((B, H, D, D), dtype=f32, device=dev)
     if final_conv_state is None:
@@ -277,7 +281,7 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
         _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
         _ptr(initial_state, f32, (B, H, D, D), "initial_state"),
         _ptr(initial_conv_state, f32, (B, 3 * HD, CONV - 1), "initial_conv_state"),
-        _ptr(out, f32, (N, HD), "out"), _ptr(final_state, f32, (B, H, D, D), "final_state"),
+        _ptr(out, cfg.out_dtype, (N, HD), "out"), _ptr(final_state, f32, (B, H, D, D), "final_state"),
         _ptr(final_conv_state, f32, (B, 3 * HD, CONV - 1), "final_conv_state"),
     ]
     ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None

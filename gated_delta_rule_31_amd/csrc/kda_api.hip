@@ -24,11 +24,13 @@ kda_status check_config(const kda_config *cfg, kda::MixerConsts *out) {
     if (!isfinite(cfg->gate_lower_bound) || !finite_nonneg(cfg->l2_eps) || !finite_nonneg(cfg->rms_eps) ||
         !isfinite(cfg->q_scale))
         return KDA_ERR_BAD_CONFIG;
+    if (cfg->out_dtype != KDA_OUT_F32 && cfg->out_dtype != KDA_OUT_BF16) return KDA_ERR_BAD_CONFIG;
     out->H = cfg->num_heads;
     out->gate_lower_bound = cfg->gate_lower_bound;
     out->l2_eps = cfg->l2_eps;
     out->rms_eps = cfg->rms_eps;
     out->q_scale = cfg->q_scale > 0.0f ? cfg->q_scale : 1.0f / sqrtf((float)kda::kD);
+    out->out_bf16 = cfg->out_dtype == KDA_OUT_BF16;
     return KDA_OK;
 }
 
@@ -76,13 +78,14 @@ kda_config kda_config_default(void) {
     c.rms_eps = 1e-5f;
     c.q_scale = 0.0f;
     c.prefill_path = KDA_PREFILL_AUTO;
+    c.out_dtype = KDA_OUT_F32;
     return c;
 }
 
 kda_status kda_decode_step(const kda_config *cfg, int32_t batch, const float *q, const float *k,
                            const float *v, const float *z, const float *b, const float *g,
                            const float *conv_w, const float *A_log, const float *dt_bias,
-                           const float *norm_w, float *state, float *conv_state, float *out,
+                           const float *norm_w, float *state, float *conv_state, void *out,
                            void *stream) {
     kda::DecodeArgs a;
     kda_status st = check_config(cfg, &a.c);
@@ -106,7 +109,7 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch, const float *q,
 kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int32_t *slots, int32_t pool_size,
                                  const float *q, const float *k, const float *v, const float *z, const float *b,
                                  const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
-                                 const float *norm_w, float *state_pool, float *conv_pool, float *out,
+                                 const float *norm_w, float *state_pool, float *conv_pool, void *out,
                                  void *stream) {
     kda::DecodeArgs a;
     kda_status st = check_config(cfg, &a.c);
@@ -138,7 +141,7 @@ kda_status decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, co
                         bool pooled, const int32_t *slots, int32_t pool_size, const float *q, const float *k, const float *v,
                         const float *z, const float *b, const float *g, const float *conv_w, const float *A_log,
                         const float *dt_bias, const float *norm_w, const float *state_in, float *state_out,
-                        const float *conv_state_in, float *conv_state_out, float *out, void *stream) {
+                        const float *conv_state_in, float *conv_state_out, void *out, void *stream) {
     kda::DecodeMultiArgs a;
     kda_status st = check_config(cfg, &a.c);
     if (st != KDA_OK) return st;
@@ -178,7 +181,7 @@ kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens
                             const float *q, const float *k, const float *v, const float *z, const float *b,
                             const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
                             const float *norm_w, const float *state_in, float *state_out,
-                            const float *conv_state_in, float *conv_state_out, float *out, void *stream) {
+                            const float *conv_state_in, float *conv_state_out, void *out, void *stream) {
     return decode_multi(cfg, batch, tokens, n_tokens, false, nullptr, 0, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
                         state_in, state_out, conv_state_in, conv_state_out, out, stream);
 }
@@ -188,7 +191,7 @@ kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t 
                                   const float *v, const float *z, const float *b, const float *g,
                                   const float *conv_w, const float *A_log, const float *dt_bias,
                                   const float *norm_w, const float *state_in, float *state_out,
-                                  const float *conv_state_in, float *conv_state_out, float *out, void *stream) {
+                                  const float *conv_state_in, float *conv_state_out, void *out, void *stream) {
     return decode_multi(cfg, batch, tokens, n_tokens, true, slots, pool_size, q, k, v, z, b, g, conv_w, A_log, dt_bias,
                         norm_w, state_in, state_out, conv_state_in, conv_state_out, out, stream);
 }
@@ -204,7 +207,7 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
                        const int32_t *cu_seqlens, const uint16_t *q, const uint16_t *k,
                        const uint16_t *v, const uint16_t *z, const uint16_t *b, const uint16_t *g,
                        const float *conv_w, const float *A_log, const float *dt_bias, const float *norm_w,
-                       const float *initial_state, const float *initial_conv_state, float *out,
+                       const float *initial_state, const float *initial_conv_state, void *out,
                        float *final_state, float *final_conv_state, void *workspace,
                        size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
@@ -301,7 +304,7 @@ const char *kda_status_str(kda_status s) {
     switch (s) {
         case KDA_OK: return "ok";
         case KDA_ERR_NULL_ARG: return "a required pointer is NULL";
-        case KDA_ERR_BAD_CONFIG: return "unsupported config (head_dim must be 128, conv_size 4, num_heads >= 1, finite eps >= 0, prefill_path 0..2)";
+        case KDA_ERR_BAD_CONFIG: return "unsupported config (head_dim must be 128, conv_size 4, num_heads >= 1, finite eps >= 0, prefill_path 0..2, out_dtype 0..1)";
         case KDA_ERR_BAD_SHAPE: return "negative, inconsistent or too large sizes";
         case KDA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
         case KDA_ERR_WORKSPACE: return "workspace too small";

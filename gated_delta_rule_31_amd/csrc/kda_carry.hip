@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         ss += __shfl_xor(ss, 4, 64);
         if (tok < L) {
             const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
-            float *orow = a.out + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
+            const size_t orow = (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 float g8[8], nw[8], y[8];
@@ -145,8 +145,8 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                 lds_read8(sNw + v0 + 8 * j, nw);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[8 * j + e] * rinv * nw[e]);
-                *reinterpret_cast<float4 *>(orow + 8 * j) = make_float4(y[0], y[1], y[2], y[3]);
-                *reinterpret_cast<float4 *>(orow + 8 * j + 4) = make_float4(y[4], y[5], y[6], y[7]);
+                store_out4(a.out, orow + 8 * j, y[0], y[1], y[2], y[3], a.c.out_bf16);
+                store_out4(a.out, orow + 8 * j + 4, y[4], y[5], y[6], y[7], a.c.out_bf16);
             }
         }
     };

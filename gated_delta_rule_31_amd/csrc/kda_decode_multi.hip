@@ -208,12 +208,9 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
             const float ss = group_sum<32>(o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3]);
             const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
             const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + 4 * cg);
-            float4 y;
-            y.x = sh_gate[4 * cg + 0] * (o[0] * rinv * w.x);
-            y.y = sh_gate[4 * cg + 1] * (o[1] * rinv * w.y);
-            y.z = sh_gate[4 * cg + 2] * (o[2] * rinv * w.z);
-            y.w = sh_gate[4 * cg + 3] * (o[3] * rinv * w.w);
-            *reinterpret_cast<float4 *>(a.out + tok + 4 * cg) = y;
+            store_out4(a.out, tok + 4 * cg, sh_gate[4 * cg + 0] * (o[0] * rinv * w.x),
+                       sh_gate[4 * cg + 1] * (o[1] * rinv * w.y), sh_gate[4 * cg + 2] * (o[2] * rinv * w.z),
+                       sh_gate[4 * cg + 3] * (o[3] * rinv * w.w), a.c.out_bf16);
         }
         lds_barrier();  // the next token rewrites the shared arrays
     }

@@ -18,14 +18,28 @@ struct MixerConsts {
     float l2_eps;
     float rms_eps;
     float q_scale;
+    int out_bf16;  // the output buffers hold bf16 (round to nearest even), else fp32
 };
+
+// Four consecutive output values at element i (a multiple of 4) of an fp32 or bf16
+// output buffer: one 16- or 8-byte store.
+__device__ __forceinline__ void store_out4(void *out, size_t i, float a, float b, float c, float d, bool bf16) {
+    if (bf16) {
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        const bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+        *reinterpret_cast<bf16x4_t *>(static_cast<__bf16 *>(out) + i) = v;
+    } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(out) + i) = make_float4(a, b, c, d);
+    }
+}
 
 struct DecodeArgs {
     MixerConsts c;
     int B;
     const float *q, *k, *v, *z, *b, *g;
     const float *conv_w, *A_log, *dt_bias, *norm_w;
-    float *state, *conv_state, *out;
+    float *state, *conv_state;
+    void *out;  // fp32 or bf16 (c.out_bf16)
     // NULL: row b owns state[b] and conv_state[b].  Otherwise row b owns pool entry
     // slots[b] of the `pool` entries of state / conv_state (rows outside are skipped).
     const int32_t *slots;
@@ -41,7 +55,8 @@ struct DecodeMultiArgs {
     const float *q, *k, *v, *z, *b, *g;
     const float *conv_w, *A_log, *dt_bias, *norm_w;
     const float *state_in, *conv_in;
-    float *state_out, *conv_out, *out;
+    float *state_out, *conv_out;
+    void *out;  // fp32 or bf16 (c.out_bf16)
     // NULL: row b owns entry b of the state and window buffers.  Otherwise row b owns
     // pool entry slots[b] of the `pool` entries (rows outside are skipped).
     const int32_t *slots;
@@ -90,7 +105,8 @@ struct PrefillArgs {
     const uint16_t *q, *k, *v, *z, *b, *g;
     const float *conv_w, *A_log, *dt_bias, *norm_w;
     const float *initial_state, *initial_conv_state;
-    float *out, *final_state, *final_conv_state;
+    void *out;  // fp32 or bf16 (c.out_bf16)
+    float *final_state, *final_conv_state;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

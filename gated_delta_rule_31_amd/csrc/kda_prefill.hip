@@ -842,7 +842,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             ss += __shfl_xor(ss, 4, 64);
             if (tok < L) {
                 const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
-                float *orow = a.out + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
+                const size_t orow = (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
 #pragma unroll
                 for (int j = 0; j < 16; j += 8) {
                     float g8[8], nw[8], y[8];
@@ -850,8 +850,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     lds_read8(sNw + v0 + j, nw);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[j + e] * rinv * nw[e]);
-                    *reinterpret_cast<float4 *>(orow + j) = make_float4(y[0], y[1], y[2], y[3]);
-                    *reinterpret_cast<float4 *>(orow + j + 4) = make_float4(y[4], y[5], y[6], y[7]);
+                    store_out4(a.out, orow + j, y[0], y[1], y[2], y[3], a.c.out_bf16);
+                    store_out4(a.out, orow + j + 4, y[4], y[5], y[6], y[7], a.c.out_bf16);
                 }
             }
         }

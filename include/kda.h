@@ -28,7 +28,9 @@
  *   state                                 [B, H, D, D]    S[key][value], fp32
  *   conv_state                            [B, 3*H*D, 3]   the 3 previous pre-conv inputs
  *                                                         of each channel, oldest first
- *   out                                   [tokens, H*D]   fp32
+ *   out                                   [tokens, H*D]   fp32, or bf16 (raw bit
+ *                                                         patterns, round to nearest
+ *                                                         even) with KDA_OUT_BF16
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers (HIP) unless stated; the caller owns every buffer.
@@ -54,13 +56,14 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
     KDA_ERR_BAD_CONFIG = 2, /* head_dim != 128, conv_size != 4, num_heads < 1, bad eps,
-                               prefill_path outside 0..2 (kda_prefill) */
+                               prefill_path outside 0..2 (kda_prefill), out_dtype outside
+                               0..1 */
     KDA_ERR_BAD_SHAPE = 3,  /* negative or inconsistent sizes, or sizes past the limits */
     KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned (workspace: 256-byte) */
     KDA_ERR_WORKSPACE = 5,  /* workspace smaller than kda_prefill_workspace_bytes() */
@@ -77,7 +80,14 @@ typedef struct {
     float rms_eps;          /* eps of the per-head RMSNorm of o; the loader's rms default 1e-5 */
     float q_scale;          /* scale of the normalised q; <= 0 selects D^-0.5 */
     int32_t prefill_path;   /* KDA_PREFILL_AUTO, _FUSED or _CHUNKED (kda_prefill only) */
+    int32_t out_dtype;      /* KDA_OUT_F32 or KDA_OUT_BF16: element type of every `out` */
 } kda_config;
+
+/* Element type of the output buffers.  With KDA_OUT_BF16 each output is the fp32 result
+ * rounded to the nearest bf16 (ties to even), at half the bytes; states and conv windows
+ * stay fp32 either way. */
+#define KDA_OUT_F32 0
+#define KDA_OUT_BF16 1
 
 /* How kda_prefill lays out its work (the result is the same up to rounding order):
  *   KDA_PREFILL_FUSED    one workgroup per (sequence, head) walks the sequence chunk by
@@ -93,7 +103,8 @@ typedef struct {
 
 /* Defaults: H = 96, D = 128, conv 4, gmin -5, l2_eps 1e-6, rms_eps 1e-5, q_scale D^-0.5
  * (page "colibri/c/kimi_k3.c": header comment "KDA per-head recurrence" and the
- * config loader's rms_norm_eps default), prefill_path KDA_PREFILL_AUTO. */
+ * config loader's rms_norm_eps default), prefill_path KDA_PREFILL_AUTO, out_dtype
+ * KDA_OUT_F32. */
 kda_config kda_config_default(void);
 
 /*
@@ -113,7 +124,8 @@ kda_config kda_config_default(void);
  *   conv_w, A_log, dt_bias, norm_w   fp32 parameters (layouts above)
  *   state                  [B, H, D, D] fp32, read and overwritten in place
  *   conv_state             [B, 3*H*D, 3] fp32, read and overwritten in place
- *   out                    [B, H*D] fp32, written; must not overlap any input
+ *   out                    [B, H*D] fp32 or bf16 (cfg->out_dtype), written; must not
+ *                          overlap any input
  *   stream                 hipStream_t or NULL
  * Alignment: every pointer 16-byte aligned.  Limits: B*H <= 16,777,215 (one
  * workgroup of 256 lanes per (sequence, head) in one dispatch).
@@ -123,7 +135,7 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
                            const float *z, const float *b, const float *g,
                            const float *conv_w, const float *A_log, const float *dt_bias,
                            const float *norm_w,
-                           float *state, float *conv_state, float *out,
+                           float *state, float *conv_state, void *out,
                            void *stream);
 
 /*
@@ -149,7 +161,8 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
  *   state_pool             [P, H, D, D] fp32, entries of valid slots read and
  *                          overwritten in place
  *   conv_pool              [P, 3*H*D, 3] fp32, likewise
- *   out                    [B, H*D] fp32; must not overlap any input
+ *   out                    [B, H*D] fp32 or bf16 (cfg->out_dtype); must not overlap any
+ *                          input
  *   stream                 hipStream_t or NULL
  * Alignment: every fp32 pointer 16-byte aligned, slots 4-byte aligned.
  * Limits: B*H <= 16,777,215.
@@ -159,7 +172,7 @@ kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int
                                  const float *z, const float *b, const float *g,
                                  const float *conv_w, const float *A_log, const float *dt_bias,
                                  const float *norm_w,
-                                 float *state_pool, float *conv_pool, float *out,
+                                 float *state_pool, float *conv_pool, void *out,
                                  void *stream);
 
 /*
@@ -186,8 +199,9 @@ kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int
  *   state_in, state_out    [B, H, D, D] fp32; either the same buffer (update in place)
  *                          or disjoint
  *   conv_state_in, conv_state_out   [B, 3*H*D, 3] fp32; the same buffer or disjoint
- *   out                    [B, T, H*D] fp32: rows of applied tokens are written, the
- *                          others are left untouched; must not overlap any input
+ *   out                    [B, T, H*D] fp32 or bf16 (cfg->out_dtype): rows of applied
+ *                          tokens are written, the others are left untouched; must not
+ *                          overlap any input
  *   stream                 hipStream_t or NULL
  * A sequence with n_tokens 0 copies its state and windows to the outputs.
  * Alignment: every fp32 pointer 16-byte aligned, n_tokens 4-byte aligned.
@@ -200,7 +214,7 @@ kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens
                             const float *norm_w,
                             const float *state_in, float *state_out,
                             const float *conv_state_in, float *conv_state_out,
-                            float *out, void *stream);
+                            void *out, void *stream);
 
 /*
  * kda_decode_multi_slots -- kda_decode_multi for states held in pools, as
@@ -229,7 +243,7 @@ kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t 
                                   const float *norm_w,
                                   const float *state_in, float *state_out,
                                   const float *conv_state_in, float *conv_state_out,
-                                  float *out, void *stream);
+                                  void *out, void *stream);
 
 /*
  * kda_prefill -- a packed batch of whole sequences (varlen), processed in chunks of
@@ -251,7 +265,7 @@ kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t 
  *   conv_w, A_log, dt_bias, norm_w   fp32 parameters
  *   initial_state          [B, H, D, D] fp32, or NULL for zeros
  *   initial_conv_state     [B, 3*H*D, 3] fp32, or NULL for zeros
- *   out                    [N, H*D] fp32, written
+ *   out                    [N, H*D] fp32 or bf16 (cfg->out_dtype), written
  *   final_state            [B, H, D, D] fp32, written; may be the same pointer as
  *                          initial_state (in-place carry), must not partially overlap it
  *   final_conv_state       [B, 3*H*D, 3] fp32, written; may equal initial_conv_state
@@ -276,7 +290,7 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
                        const float *conv_w, const float *A_log, const float *dt_bias,
                        const float *norm_w,
                        const float *initial_state, const float *initial_conv_state,
-                       float *out, float *final_state, float *final_conv_state,
+                       void *out, float *final_state, float *final_conv_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device scratch kda_prefill needs for these sizes with cfg->prefill_path: 0 for the

@@ -60,6 +60,9 @@ def test_decode_rejects_bad_config():
     assert _decode(_cfg(num_heads=0), 1) == BAD_CONFIG
     assert _decode(_cfg(l2_eps=-1.0), 1) == BAD_CONFIG
     assert _decode(_cfg(rms_eps=float("nan")), 1) == BAD_CONFIG
+    assert _decode(_cfg(out_dtype=2), 1) == BAD_CONFIG
+    assert _decode(_cfg(out_dtype=-1), 1) == BAD_CONFIG
+    assert kda.lib().kda_config_default().out_dtype == 0
 
 
 def test_decode_rejects_bad_shapes_and_pointers():

@@ -4,7 +4,10 @@
 // chunks of 64 tokens and carries the 128x128 fp32 state in MFMA accumulator registers.
 // Every step of the header comment "KDA per-head recurrence" (page "colibri/c/kimi_k3.c")
 // is fused: conv with the carried window, SiLU, L2 norms, gates, the chunked state update
-// and readout, the gated RMSNorm and the final state / conv window write.
+// and readout, the gated RMSNorm (written fp32 or bf16) and the final state / conv window
+// write.  Instantiated with kChunked, the same kernel instead stops each chunk after its
+// state-independent products and stores them as a record for the carry kernel
+// (kda_carry.hip), one workgroup per 4-chunk segment and head.
 //
 // Chunk algebra (exact rewrite of the token recurrence; G_t = sum_{s<=t} gk_s per key
 // channel, chunk-local):

@@ -446,7 +446,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--prefill-path", choices=["auto", "fused", "chunked"], default="auto",
-                    help="prefill work layout (auto: chunked below 512 (sequence, head) units)")
+                    help="prefill work layout (auto: the library's estimate of the faster one)")
     ap.add_argument("--only", choices=["all", "decode", "decode-multi", "decode-slots", "decode-cfg4", "prefill",
                                        "copy"],
                     default="all",

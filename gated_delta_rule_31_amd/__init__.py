@@ -40,7 +40,7 @@ class _CConfig(ctypes.Structure):
     ]
 
 # kda_config.prefill_path values
-PREFILL_AUTO = 0     # chunked below 512 (sequence, head) units, fused otherwise
+PREFILL_AUTO = 0     # the layout an estimate of both times predicts faster
 PREFILL_FUSED = 1    # one workgroup per (sequence, head) over all chunks; no workspace
 PREFILL_CHUNKED = 2  # chunk records in parallel, then the carry; needs a workspace
 

@@ -51,8 +51,17 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     const int64_t segs = kda::seg_cap(B, cap);
     const bool chunked_fits = cap * H <= kda::kMaxPrefillUnits && segs * H <= kda::kMaxPrefillUnits;
     int path = cfg->prefill_path;
-    if (path == kda::kPathAuto)
-        path = (B * H < kda::kChunkedBelowUnits && chunked_fits) ? kda::kPathChunked : kda::kPathFused;
+    if (path == kda::kPathAuto) {
+        path = kda::kPathFused;
+        if (chunked_fits && B > 0) {
+            const double rounds = (double)((B * H + kda::kComputeUnits - 1) / kda::kComputeUnits);
+            const double chunks = (double)((N + 64 * B - 1) / (64 * B));  // mean length, rounded up
+            const double fused = rounds * chunks * kda::kFusedChunkUs;
+            const double chunked =
+                (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits + rounds * chunks * kda::kCarryChunkUs;
+            if (chunked < fused) path = kda::kPathChunked;
+        }
+    }
     if (path != kda::kPathFused && path != kda::kPathChunked) return false;
     if (path == kda::kPathChunked && !chunked_fits) return false;
     plan->path = path;

@@ -75,9 +75,20 @@ enum PrefillPath { kPathAuto = 0, kPathFused = 1, kPathChunked = 2 };
 constexpr int64_t kMaxPrefillUnits = (int64_t)0xFFFFFFFF / 512;  // workgroups of 512 lanes
 constexpr int64_t kMaxDecodeUnits = (int64_t)0xFFFFFFFF / 256;   // workgroups of 256 lanes
 
-// Below this many (sequence, head) units the fused plan leaves most compute units idle
-// and the chunked plan is chosen.
-constexpr int64_t kChunkedBelowUnits = 512;
+// The automatic choice between the two prefill plans compares estimates of their times,
+// with per-chunk costs measured on MI355X (256 compute units, one 8-wave prefill
+// workgroup per compute unit):
+//   fused:   rounds * chunks * 17.6 us                 (every workgroup walks its sequence)
+//   chunked: records * 17.0 us / 256 + rounds * chunks * 5.9 us
+//            (the records spread over all compute units, then the carry walks them)
+// where rounds = ceil(B*H / 256) waves of workgroups, chunks = the mean sequence length
+// in 64-token chunks and records = (floor(N/64) + B) * H.  (The host does not read
+// cu_seqlens, so the lengths are taken as equal.)  The model matches the measured times
+// of both plans within about 10% from 1 to 16 sequences of 1K-8K tokens.
+constexpr int kComputeUnits = 256;
+constexpr double kFusedChunkUs = 17.6;
+constexpr double kRecordUs = 17.0;
+constexpr double kCarryChunkUs = 5.9;
 
 // Bytes of one chunk record (the layout is in kda_device.hpp); a multiple of 256.
 constexpr int kRecBytes = 115200;

@@ -96,7 +96,10 @@ typedef struct {
  *                        state-independent products into the workspace, then one
  *                        workgroup per (sequence, head) carries the state through them.
  *                        Fills the GPU when B*H is small (a few long sequences).
- *   KDA_PREFILL_AUTO     CHUNKED when B*H < 512, else FUSED. */
+ *   KDA_PREFILL_AUTO     the one an estimate of both times on MI355X predicts faster,
+ *                        from B, H and N (the sequences taken as equal in length): CHUNKED
+ *                        for a few long sequences (e.g. B*H = 96 or 288 units), FUSED when
+ *                        B*H fills whole rounds of 256 workgroups (e.g. 192, 384, 1536). */
 #define KDA_PREFILL_AUTO 0
 #define KDA_PREFILL_FUSED 1
 #define KDA_PREFILL_CHUNKED 2

@@ -143,13 +143,30 @@ def bench_decode(args, dev):
         ev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_eager = (t1 - t0) * 1e3 / args.steps
     kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    # the same K steps launched as one HIP graph (as a serving loop would replay them):
+    # captured and replayed once untimed, then one timed replay
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(args.steps):
+                kda.kda_decode_step(cfg, *xs, conv_w, A_log, dt_bias, norm_w, states[i % n_sets],
+                                    convs[i % n_sets], out=out, stream=side)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
     alg = decode_bytes(B, H)
     state_b = 2 * B * H * D * D * 4
     achieved = alg / (kern_ms * 1e-3) / 1e9
     return dict(
-        B=B, H=H, ms_per_step=ms_step, kernel_ms=kern_ms,
+        B=B, H=H, ms_per_step=ms_step, kernel_ms=kern_ms, ms_per_step_eager=ms_eager,
         state_gbs=state_b / (ms_step * 1e-3) / 1e9,
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -482,7 +499,8 @@ def main():
         return
     log("decode: 64 seq x 96 heads")
     dec = bench_decode(args, dev)
-    log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")
+    log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step as a graph, {dec['ms_per_step_eager'] * 1e3:.1f} eager, "
+        f"kernel {dec['kernel_ms'] * 1e3:.1f} us")
     dec["roofline"]["traffic"] = measured_decode_traffic()
     multi = slots = None
     if args.only == "all":
@@ -516,13 +534,15 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 5),
+        "ms_per_step_eager": round(dec["ms_per_step_eager"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "kda-decode-64seq-96head", "batch": dec["B"], "heads": dec["H"], "head_dim": D,
-                   "state_dtype": "f32", "state_sets_rotated": 3},
+                   "state_dtype": "f32", "state_sets_rotated": 3,
+                   "timed_as": "one HIP graph replay of the K steps (eager launches: ms_per_step_eager)"},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
         "decode_multi": multi,

@@ -72,7 +72,8 @@ class KdaError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m gated_delta_rule_31_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python gated_delta_rule_31_amd/build.py` "
+                          "or `python __graft_entry__.py build`")
     L = ctypes.CDLL(LIB_PATH)
     vp, fp = ctypes.c_void_p, ctypes.c_void_p
     L.kda_config_default.restype = _CConfig

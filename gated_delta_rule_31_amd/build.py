@@ -1,6 +1,8 @@
 """Build libkda.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m gated_delta_rule_31_amd.build
+    python gated_delta_rule_31_amd/build.py
+
+(run as a file: the package itself refuses to import until the library exists)
 """
 from __future__ import annotations
 

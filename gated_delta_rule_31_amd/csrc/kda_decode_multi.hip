@@ -88,10 +88,13 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
     }
     const float dtb = a.dt_bias[h * kD + i];
     const float rate = expf(a.A_log[h]);
+    // the RMSNorm weight of this lane's 4 output columns (lanes 0..31 write the outputs)
+    const float4 wn = *reinterpret_cast<const float4 *>(a.norm_w + 4 * cg);
 
     // This lane's inputs of a token (A: q or v, B: k or z, G: g, beta logit), loaded one
-    // token ahead.  The loop's barriers wait for LDS traffic only, so these loads stay in
-    // flight across them.
+    // token ahead: requested once the current token's inputs are consumed (so that no wait
+    // for them also waits for these), and the loop's barriers wait for LDS traffic only,
+    // so they stay in flight across them.
     struct TokenLoads {
         float A, B, G, b;
     };
@@ -107,12 +110,21 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
     };
     TokenLoads cur = {0.f, 0.f, 0.f, 0.f};
     if (n > 0) cur = load_token(0);
+    // Wait once, here, for everything loaded so far.  The compiler cannot count memory
+    // operations across the loop's back edge; with loads from before the loop still
+    // possibly in flight it makes the loop wait for all of them, and so for the next
+    // token's loads and this token's output store too, on every token.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(s[j]));
+    asm volatile("" ::"v"(wA.x), "v"(wA.y), "v"(wA.z), "v"(wA.w), "v"(wB.x), "v"(wB.y), "v"(wB.z), "v"(wB.w));
+    asm volatile("" ::"v"(winA[0]), "v"(winA[1]), "v"(winA[2]), "v"(winB[0]), "v"(winB[1]), "v"(winB[2]));
+    asm volatile("" ::"v"(dtb), "v"(rate), "v"(wn.x), "v"(wn.y), "v"(wn.z), "v"(wn.w));
+    asm volatile("" ::"v"(cur.A), "v"(cur.B), "v"(cur.G), "v"(cur.b));
 
     for (int t = 0; t < n; ++t) {
         const size_t row = (size_t)bs * T + t;
         const size_t tok = row * HD + (size_t)h * kD;
         const TokenLoads x = cur;
-        if (t + 1 < n) cur = load_token(t + 1);
         // ---- prologue of token t ----
         float uq = 0.f, uk = 0.f;
         if (tid < kD) {
@@ -141,6 +153,7 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
             sh_gate[i] = sigmoid_f(x.G);
             if (i == 0) sh_beta = sigmoid_f(x.b);
         }
+        if (t + 1 < n) cur = load_token(t + 1);
         lds_barrier();
 
         const float ssq = sh_red[0][0] + sh_red[1][0];
@@ -207,10 +220,9 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
         if (tid < 32) {
             const float ss = group_sum<32>(o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3]);
             const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
-            const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + 4 * cg);
-            store_out4(a.out, tok + 4 * cg, sh_gate[4 * cg + 0] * (o[0] * rinv * w.x),
-                       sh_gate[4 * cg + 1] * (o[1] * rinv * w.y), sh_gate[4 * cg + 2] * (o[2] * rinv * w.z),
-                       sh_gate[4 * cg + 3] * (o[3] * rinv * w.w), a.c.out_bf16);
+            store_out4(a.out, tok + 4 * cg, sh_gate[4 * cg + 0] * (o[0] * rinv * wn.x),
+                       sh_gate[4 * cg + 1] * (o[1] * rinv * wn.y), sh_gate[4 * cg + 2] * (o[2] * rinv * wn.z),
+                       sh_gate[4 * cg + 3] * (o[3] * rinv * wn.w), a.c.out_bf16);
         }
         lds_barrier();  // the next token rewrites the shared arrays
     }

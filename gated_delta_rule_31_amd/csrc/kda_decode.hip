@@ -23,34 +23,12 @@
 // are in flight.  The kernel is bound by HBM: 128 KiB of state traffic per (sequence,
 // head) against ~98 KFLOP.
 
-#include "kda_internal.hpp"
+#include "kda_decode_common.hpp"
 
 namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
-
-// Workgroups are dealt to the 8 XCDs round-robin in id order.  This maps hardware id i
-// (XCD i % 8, its (i / 8)-th workgroup) to a logical id so that each XCD walks one
-// contiguous eighth of the (sequence, head) range in order: its L2, address translation
-// and DRAM pages then see one streaming region instead of every eighth 64 KiB state.
-// A bijection for any n, so the result does not depend on the dispatch order.
-__device__ __forceinline__ int xcd_contiguous(int i, int n) {
-    const int q = n >> 3, r = n & 7, x = i & 7;
-    return x * q + min(x, r) + (i >> 3);
-}
-
-// sum over groups of W consecutive lanes (W a power of two <= 64)
-template <int W>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
 
 // kSlots: batch row bs updates pool entry a.slots[bs] of the state and conv-window
 // pools instead of entry bs; a row whose slot lies outside [0, a.pool) is skipped.
@@ -81,9 +59,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int j = 0; j < 16; ++j)
         s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (rg + 8 * j) * kD + 4 * cg));
 
-    __shared__ float sh_kh[kD];     // normalised k
-    __shared__ float sh_ak[kD];     // alpha * k
-    __shared__ float sh_aq[kD];     // alpha * q (scaled)
+    __shared__ float2 sh_akq[kD];   // (alpha k^, alpha q^) of a key row (q^ scaled)
+    __shared__ float2 sh_alk[kD];   // (alpha, k^) of a key row
     __shared__ float sh_alpha[kD];  // decay
     __shared__ float sh_v[kD];      // SiLU(conv(v))
     __shared__ float sh_gate[kD];   // sigmoid(g)
@@ -105,12 +82,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         float *wnk = cstate + chk * 3;
         const float q0 = wnq[0], q1 = wnq[1], q2 = wnq[2], xq = a.q[tok + i];
         const float k0 = wnk[0], k1 = wnk[1], k2 = wnk[2], xk = a.k[tok + i];
-        const float yq = wq.x * q0 + wq.y * q1 + wq.z * q2 + wq.w * xq;
-        const float yk = wk.x * k0 + wk.y * k1 + wk.z * k2 + wk.w * xk;
         wnq[0] = q1; wnq[1] = q2; wnq[2] = xq;
         wnk[0] = k1; wnk[1] = k2; wnk[2] = xk;
-        uq = yq * sigmoid_f(yq);
-        uk = yk * sigmoid_f(yk);
+        uq = silu(conv4(wq, q0, q1, q2, xq));
+        uk = silu(conv4(wk, k0, k1, k2, xk));
         const float sqq = group_sum<64>(uq * uq);
         const float skk = group_sum<64>(uk * uk);
         const float sqk = group_sum<64>(uq * uk);
@@ -125,41 +100,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const float4 wv = *reinterpret_cast<const float4 *>(a.conv_w + chv * 4);
         float *wnv = cstate + chv * 3;
         const float v0 = wnv[0], v1 = wnv[1], v2 = wnv[2], xv = a.v[tok + i];
-        const float yv = wv.x * v0 + wv.y * v1 + wv.z * v2 + wv.w * xv;
         wnv[0] = v1; wnv[1] = v2; wnv[2] = xv;
-        sh_v[i] = yv * sigmoid_f(yv);
+        sh_v[i] = silu(conv4(wv, v0, v1, v2, xv));
         const float rate = expf(a.A_log[h]);
-        const float gk = a.c.gate_lower_bound * sigmoid_f(rate * (a.z[tok + i] + a.dt_bias[h * kD + i]));
-        sh_alpha[i] = expf(gk);
-        sh_gate[i] = sigmoid_f(a.g[tok + i]);
-        if (i == 0) sh_beta = sigmoid_f(a.b[(size_t)bs * H + h]);
+        sh_alpha[i] = decay(a.c.gate_lower_bound, rate, a.z[tok + i], a.dt_bias[h * kD + i]);
+        sh_gate[i] = sigm(a.g[tok + i]);
+        if (i == 0) sh_beta = sigm(a.b[(size_t)bs * H + h]);
     }
     __syncthreads();
 
     const float ssq = sh_red[0][0] + sh_red[1][0];
     const float ssk = sh_red[0][1] + sh_red[1][1];
     const float sqk = sh_red[0][2] + sh_red[1][2];
-    const float inv_q = a.c.q_scale / sqrtf(ssq + a.c.l2_eps);
-    const float inv_k = 1.0f / sqrtf(ssk + a.c.l2_eps);
+    const float inv_q = a.c.q_scale * inv_sqrt(ssq + a.c.l2_eps);
+    const float inv_k = inv_sqrt(ssk + a.c.l2_eps);
     const float kappa = sqk * inv_q * inv_k;  // k^ . q^
     const float beta = sh_beta;
     if (tid < kD) {
         const float qh = uq * inv_q, kh = uk * inv_k, al = sh_alpha[tid];
-        sh_kh[tid] = kh;
-        sh_ak[tid] = al * kh;
-        sh_aq[tid] = al * qh;
+        sh_alk[tid] = make_float2(al, kh);
+        sh_akq[tid] = make_float2(al * kh, al * qh);
     }
     __syncthreads();
 
     // ---- 3. a = S^T(alpha k), c = S^T(alpha q) over this lane's 16 rows ----
     float pa[4] = {0.f, 0.f, 0.f, 0.f}, pc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int r = rg + 8 * j;
-        const float fk = sh_ak[r], fq = sh_aq[r];
-        pa[0] += s[j].x * fk; pa[1] += s[j].y * fk; pa[2] += s[j].z * fk; pa[3] += s[j].w * fk;
-        pc[0] += s[j].x * fq; pc[1] += s[j].y * fq; pc[2] += s[j].z * fq; pc[3] += s[j].w * fq;
-    }
+    key_dots(s, sh_akq, rg, pa, pc);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         pa[c] += __shfl_xor(pa[c], 32, 64);
@@ -176,30 +142,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     // ---- 4. u = beta (v - a), o = c + kappa u, S' = D_a S + k u^T ----
     float u[4], o[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int col = 4 * cg + c;
-        const float av = sh_part[0][0][col] + sh_part[1][0][col] + sh_part[2][0][col] + sh_part[3][0][col];
-        const float cv = sh_part[0][1][col] + sh_part[1][1][col] + sh_part[2][1][col] + sh_part[3][1][col];
-        u[c] = beta * (sh_v[col] - av);
-        o[c] = cv + kappa * u[c];
-    }
+    delta_and_readout(sh_part, sh_v, beta, kappa, cg, u, o);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int r = rg + 8 * j;
-        const float al = sh_alpha[r], kr = sh_kh[r];
-        f32x4 n;
-        n.x = al * s[j].x + kr * u[0];
-        n.y = al * s[j].y + kr * u[1];
-        n.z = al * s[j].z + kr * u[2];
-        n.w = al * s[j].w + kr * u[3];
-        __builtin_nontemporal_store(n, reinterpret_cast<f32x4 *>(S + r * kD + 4 * cg));
+        __builtin_nontemporal_store(update_row(s[j], sh_alk[r], u), reinterpret_cast<f32x4 *>(S + r * kD + 4 * cg));
     }
 
     // ---- 5. out = sigmoid(g) * RMSNorm(o) (lanes 0..31 of wave 0 hold all 128 columns) ----
     if (tid < 32) {
-        const float ss = group_sum<32>(o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3]);
-        const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
+        const float rinv = rms_inv(o, a.c.rms_eps);
         const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + 4 * cg);
         store_out4(a.out, tok + 4 * cg, sh_gate[4 * cg + 0] * (o[0] * rinv * w.x),
                    sh_gate[4 * cg + 1] * (o[1] * rinv * w.y), sh_gate[4 * cg + 2] * (o[2] * rinv * w.z),

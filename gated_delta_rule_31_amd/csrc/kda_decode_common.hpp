@@ -1,0 +1,98 @@
+// kda_decode_common.hpp -- the per-token arithmetic of the two decode kernels
+// (kda_decode.hip: one token; kda_decode_multi.hip: several tokens per launch).  Both
+// evaluate each step of a token with these functions, so that n tokens of the
+// multi-token kernel give the bits of n one-token calls.  Not part of the public ABI.
+//
+// Floating-point contraction is off from here to the end of the including file, and every
+// fused multiply-add is written out (fmaf): left to the compiler, the choice of which
+// product of a*b + c*d to fuse depends on the surrounding code and on register pressure,
+// and so could differ between the two kernels.
+#pragma once
+
+#include "kda_device.hpp"
+
+#pragma clang fp contract(off)
+
+namespace kda {
+
+// Workgroups are dealt to the 8 XCDs round-robin in id order.  This maps hardware id i
+// (XCD i % 8, its (i / 8)-th workgroup) to a logical id so that each XCD walks one
+// contiguous eighth of the (sequence, head) range in order: its L2, address translation
+// and DRAM pages then see one streaming region instead of every eighth 64 KiB state.
+// A bijection for any n, so the result does not depend on the dispatch order.
+__device__ __forceinline__ int xcd_contiguous(int i, int n) {
+    const int q = n >> 3, r = n & 7, x = i & 7;
+    return x * q + min(x, r) + (i >> 3);
+}
+
+// sum over groups of W consecutive lanes (W a power of two <= 64)
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// ShortConv4 of one channel: taps w against the carried window (w0 oldest) and the new
+// input x
+__device__ __forceinline__ float conv4(const float4 &w, float w0, float w1, float w2, float x) {
+    return fmaf(w.w, x, fmaf(w.z, w2, fmaf(w.y, w1, w.x * w0)));
+}
+
+__device__ __forceinline__ float silu(float y) { return y * sigm(y); }
+
+// the decay of one key channel, alpha = exp(lower * sigmoid(rate (z + dt_bias)))
+__device__ __forceinline__ float decay(float lower, float rate, float z, float dtb) {
+    return __expf(lower * sigm(rate * (z + dtb)));
+}
+
+// 1 / sqrt(x) from the hardware reciprocal square root (about 1 ulp), for the L2 and RMS
+// norms
+__device__ __forceinline__ float inv_sqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// One lane's share of the state: rows rg + 8j (j < 16) of value columns 4cg .. 4cg+3.
+
+// pa += S^T (alpha k^), pc += S^T (alpha q^) over the lane's 16 rows; akq[r] holds
+// (alpha k^, alpha q^) of key row r
+__device__ __forceinline__ void key_dots(const f32x4 (&s)[16], const float2 *akq, int rg, float (&pa)[4],
+                                         float (&pc)[4]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float2 f = akq[rg + 8 * j];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pa[c] = fmaf(s[j][c], f.x, pa[c]);
+            pc[c] = fmaf(s[j][c], f.y, pc[c]);
+        }
+    }
+}
+
+// u = beta (v - a) and o = c + (k^ . q^) u on the lane's 4 columns, from the four waves'
+// partial dot products part[wave][0: a, 1: c][column]
+__device__ __forceinline__ void delta_and_readout(const float (*part)[2][kD], const float *v, float beta, float kappa,
+                                                  int cg, float (&u)[4], float (&o)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int col = 4 * cg + c;
+        const float av = part[0][0][col] + part[1][0][col] + part[2][0][col] + part[3][0][col];
+        const float cv = part[0][1][col] + part[1][1][col] + part[2][1][col] + part[3][1][col];
+        u[c] = beta * (v[col] - av);
+        o[c] = fmaf(kappa, u[c], cv);
+    }
+}
+
+// one row of S' = Diag(alpha) S + k^ u^T; alk = (alpha, k^) of the row
+__device__ __forceinline__ f32x4 update_row(const f32x4 &s, float2 alk, const float (&u)[4]) {
+    f32x4 n;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) n[c] = fmaf(alk.y, u[c], alk.x * s[c]);
+    return n;
+}
+
+// 1 / RMS over the 128 columns held by lanes 0..31 (4 each) of one wave
+__device__ __forceinline__ float rms_inv(const float (&o)[4], float eps) {
+    const float ss = group_sum<32>(fmaf(o[3], o[3], fmaf(o[2], o[2], fmaf(o[1], o[1], o[0] * o[0]))));
+    return inv_sqrt(fmaf(ss, 1.0f / kD, eps));
+}
+
+}  // namespace kda

@@ -4,35 +4,19 @@
 // the 64 KiB head state is read once, carried in registers through the tokens, and
 // written once (to state_out, which may be state_in); the conv windows likewise stay in
 // registers.  Each token follows the header comment "KDA per-head recurrence" (page
-// "colibri/c/kimi_k3.c") with decode_kernel's arithmetic, expression for expression, so
-// n tokens here give the bits of n calls of decode_kernel.  Lanes < 128 own the q and k
+// "colibri/c/kimi_k3.c") with decode_kernel's arithmetic (the helpers of
+// kda_decode_common.hpp, in the same order), so n tokens here give the bits of n calls
+// of decode_kernel.  Lanes < 128 own the q and k
 // channel of their index, lanes >= 128 the v channel; the state layout (lane (rg, cg):
 // rows rg + 8j of columns 4cg..4cg+3) and the two key reductions are decode_kernel's.
 // Outputs of tokens t >= n_tokens[b] are not written.
 
-#include "kda_device.hpp"
+#include "kda_decode_common.hpp"
 
 namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-
-// the same helpers as decode_kernel's, so that the roundings agree bit for bit
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
-
-// decode_kernel's XCD-contiguous workgroup order (each XCD walks one contiguous eighth of
-// the (sequence, head) range)
-__device__ __forceinline__ int xcd_contiguous(int i, int n) {
-    const int q = n >> 3, r = n & 7, x = i & 7;
-    return x * q + min(x, r) + (i >> 3);
-}
-
-template <int W>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
 
 // kSlots: batch row bs reads and writes pool entry a.slots[bs] of the state and window
 // pools instead of entry bs; a row whose slot lies outside [0, a.pool) is skipped.
@@ -63,12 +47,15 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
     for (int j = 0; j < 16; ++j)
         s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sin + (rg + 8 * j) * kD + 4 * cg));
 
-    __shared__ float sh_kh[kD];
-    __shared__ float sh_ak[kD];
-    __shared__ float sh_aq[kD];
+    // Three barriers per token.  The arrays a token's prologue writes and that its
+    // predecessor's update and epilogue still read (v, output gate) alternate between two
+    // copies by token parity; every other array is rewritten only behind a barrier that
+    // all reads of its previous contents precede.
+    __shared__ float2 sh_akq[kD];  // (alpha k^, alpha q^) of a key row
+    __shared__ float2 sh_alk[kD];  // (alpha, k^) of a key row
     __shared__ float sh_alpha[kD];
-    __shared__ float sh_v[kD];
-    __shared__ float sh_gate[kD];
+    __shared__ float sh_v[2][kD];
+    __shared__ float sh_gate[2][kD];
     __shared__ float sh_red[2][3];
     __shared__ float sh_beta;
     __shared__ float sh_part[4][2][kD];
@@ -125,16 +112,15 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
         const size_t row = (size_t)bs * T + t;
         const size_t tok = row * HD + (size_t)h * kD;
         const TokenLoads x = cur;
+        const int p = t & 1;
         // ---- prologue of token t ----
         float uq = 0.f, uk = 0.f;
         if (tid < kD) {
             const float xq = x.A, xk = x.B;
-            const float yq = wA.x * winA[0] + wA.y * winA[1] + wA.z * winA[2] + wA.w * xq;
-            const float yk = wB.x * winB[0] + wB.y * winB[1] + wB.z * winB[2] + wB.w * xk;
+            uq = silu(conv4(wA, winA[0], winA[1], winA[2], xq));
+            uk = silu(conv4(wB, winB[0], winB[1], winB[2], xk));
             winA[0] = winA[1]; winA[1] = winA[2]; winA[2] = xq;
             winB[0] = winB[1]; winB[1] = winB[2]; winB[2] = xk;
-            uq = yq * sigmoid_f(yq);
-            uk = yk * sigmoid_f(yk);
             const float sqq = group_sum<64>(uq * uq);
             const float skk = group_sum<64>(uk * uk);
             const float sqk = group_sum<64>(uq * uk);
@@ -145,13 +131,11 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
             }
         } else {
             const float xv = x.A;
-            const float yv = wA.x * winA[0] + wA.y * winA[1] + wA.z * winA[2] + wA.w * xv;
+            sh_v[p][i] = silu(conv4(wA, winA[0], winA[1], winA[2], xv));
             winA[0] = winA[1]; winA[1] = winA[2]; winA[2] = xv;
-            sh_v[i] = yv * sigmoid_f(yv);
-            const float gk = a.c.gate_lower_bound * sigmoid_f(rate * (x.B + dtb));
-            sh_alpha[i] = expf(gk);
-            sh_gate[i] = sigmoid_f(x.G);
-            if (i == 0) sh_beta = sigmoid_f(x.b);
+            sh_alpha[i] = decay(a.c.gate_lower_bound, rate, x.B, dtb);
+            sh_gate[p][i] = sigm(x.G);
+            if (i == 0) sh_beta = sigm(x.b);
         }
         if (t + 1 < n) cur = load_token(t + 1);
         lds_barrier();
@@ -159,27 +143,20 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
         const float ssq = sh_red[0][0] + sh_red[1][0];
         const float ssk = sh_red[0][1] + sh_red[1][1];
         const float sqk = sh_red[0][2] + sh_red[1][2];
-        const float inv_q = a.c.q_scale / sqrtf(ssq + a.c.l2_eps);
-        const float inv_k = 1.0f / sqrtf(ssk + a.c.l2_eps);
+        const float inv_q = a.c.q_scale * inv_sqrt(ssq + a.c.l2_eps);
+        const float inv_k = inv_sqrt(ssk + a.c.l2_eps);
         const float kappa = sqk * inv_q * inv_k;
         const float beta = sh_beta;
         if (tid < kD) {
             const float qh = uq * inv_q, kh = uk * inv_k, al = sh_alpha[tid];
-            sh_kh[tid] = kh;
-            sh_ak[tid] = al * kh;
-            sh_aq[tid] = al * qh;
+            sh_alk[tid] = make_float2(al, kh);
+            sh_akq[tid] = make_float2(al * kh, al * qh);
         }
         lds_barrier();
 
         // ---- a = S^T(alpha k), c = S^T(alpha q) ----
         float pa[4] = {0.f, 0.f, 0.f, 0.f}, pc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = rg + 8 * j;
-            const float fk = sh_ak[r], fq = sh_aq[r];
-            pa[0] += s[j].x * fk; pa[1] += s[j].y * fk; pa[2] += s[j].z * fk; pa[3] += s[j].w * fk;
-            pc[0] += s[j].x * fq; pc[1] += s[j].y * fq; pc[2] += s[j].z * fq; pc[3] += s[j].w * fq;
-        }
+        key_dots(s, sh_akq, rg, pa, pc);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             pa[c] += __shfl_xor(pa[c], 32, 64);
@@ -196,35 +173,17 @@ __global__ __launch_bounds__(kThreads) void decode_multi_kernel(DecodeMultiArgs 
 
         // ---- u = beta (v - a), o = c + kappa u, S' = D_a S + k u^T ----
         float u[4], o[4];
+        delta_and_readout(sh_part, sh_v[p], beta, kappa, cg, u, o);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int col = 4 * cg + c;
-            const float av = sh_part[0][0][col] + sh_part[1][0][col] + sh_part[2][0][col] + sh_part[3][0][col];
-            const float cv = sh_part[0][1][col] + sh_part[1][1][col] + sh_part[2][1][col] + sh_part[3][1][col];
-            u[c] = beta * (sh_v[col] - av);
-            o[c] = cv + kappa * u[c];
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = rg + 8 * j;
-            const float al = sh_alpha[r], kr = sh_kh[r];
-            f32x4 nw;
-            nw.x = al * s[j].x + kr * u[0];
-            nw.y = al * s[j].y + kr * u[1];
-            nw.z = al * s[j].z + kr * u[2];
-            nw.w = al * s[j].w + kr * u[3];
-            s[j] = nw;
-        }
+        for (int j = 0; j < 16; ++j) s[j] = update_row(s[j], sh_alk[rg + 8 * j], u);
 
         // ---- out = sigmoid(g) * RMSNorm(o) ----
         if (tid < 32) {
-            const float ss = group_sum<32>(o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3]);
-            const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
-            store_out4(a.out, tok + 4 * cg, sh_gate[4 * cg + 0] * (o[0] * rinv * wn.x),
-                       sh_gate[4 * cg + 1] * (o[1] * rinv * wn.y), sh_gate[4 * cg + 2] * (o[2] * rinv * wn.z),
-                       sh_gate[4 * cg + 3] * (o[3] * rinv * wn.w), a.c.out_bf16);
+            const float rinv = rms_inv(o, a.c.rms_eps);
+            const float *gt = sh_gate[p] + 4 * cg;
+            store_out4(a.out, tok + 4 * cg, gt[0] * (o[0] * rinv * wn.x), gt[1] * (o[1] * rinv * wn.y),
+                       gt[2] * (o[2] * rinv * wn.z), gt[3] * (o[3] * rinv * wn.w), a.c.out_bf16);
         }
-        lds_barrier();  // the next token rewrites the shared arrays
     }
 
     float *Sout = a.state_out + sofs * kD * kD;

@@ -1,6 +1,8 @@
 // kda_device.hpp -- device-side helpers shared by the prefill kernels (kda_prefill.hip,
 // kda_carry.hip): vector types, MFMA wrappers, swizzled LDS tile indexing, bf16
-// conversions, and the layout of one chunk record of the chunk-parallel prefill.
+// conversions, and the layout of one chunk record of the chunk-parallel prefill.  The
+// decode kernels use its vector types, barrier and sigmoid (through
+// kda_decode_common.hpp).
 // Not part of the public ABI.
 #pragma once
 

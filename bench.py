@@ -77,13 +77,16 @@ def prefill_bytes(N: int, B: int, H: int, initial: bool) -> int:
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_31_amd", "csrc", "kda_decode.hip")
+# the decode kernel's sources: the kernel and the per-token arithmetic it includes
+DECODE_SRCS = [os.path.join(ROOT, "gated_delta_rule_31_amd", "csrc", n)
+               for n in ("kda_decode.hip", "kda_decode_common.hpp")]
 DECODE_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_64seq_96head.md")
 
 
 def measured_decode_traffic():
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None
-    if the summary is missing or was taken on a different decode kernel source."""
+    if the summary is missing or was taken on a different decode kernel source (the
+    sha256 of the kernel's source files, concatenated in DECODE_SRCS order)."""
     import hashlib
 
     if not os.path.exists(DECODE_PROFILE):
@@ -94,8 +97,11 @@ def measured_decode_traffic():
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].split(": ", 1)
                 vals[k.strip()] = v.strip().strip("`")
-    with open(DECODE_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for src in DECODE_SRCS:
+        with open(src, "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()
     if vals.get("kernel_source_sha256") != sha:
         return None
     try:

@@ -5,9 +5,9 @@
 // accumulator registers.  Per chunk, in the notation of the chunk algebra there,
 //   U = U' - W S0,   O = Q~ S0 + P U,   S_end = Diag(e^{G_end}) S0 + K_end^T U,
 // followed by out = sigmoid(g) * RMSNorm(O) (header comment "KDA per-head recurrence",
-// page "colibri/c/kimi_k3.c").  These are the state-side products of the fused kernel,
-// with the same operand precisions: S0 enters W S0 and Q~ S0 as bf16, U enters P U and
-// K_end^T U split into bf16 hi + lo, P and K_end are stored split.
+// page "colibri/c/kimi_k3.c").  These are the state-side products of the fused kernel
+// with the same operand precisions, in the same order: S0 enters W S0 and Q~ S0 as bf16,
+// U enters P U and K_end^T U split into bf16 hi + lo, P and K_end are stored split.
 //
 // Eight waves, two per SIMD so that each hides the other's LDS and MFMA latencies: wave w
 // owns value columns 16w .. 16w+15 for all 128 keys.  Inside each 32-key block the rows
@@ -15,11 +15,18 @@
 // + m%4), so a lane's 8 accumulator values of one column are 8 consecutive keys, the
 // B-operand layout of a K = 32 MFMA; U interleaves its tokens the same way.
 //
-// Overlap: the next chunk's record is loaded into registers in three parts, issued
-// between the phases of the current chunk (a record is 115 KB per workgroup, about 2K
-// cycles of the compute unit's load path, so issuing it at once would stall every wave
-// behind it), and a chunk's epilogue runs after the next chunk's first barrier, beside
-// that chunk's MFMAs, from a second O tile.
+// Streaming.  A record's operand pieces (77 KB, in the order the MFMAs read them) go
+// straight from global memory into LDS with direct-to-LDS loads, double-buffered: the
+// next chunk's pieces are requested right after the barrier that opens the current chunk
+// and have the whole chunk to arrive, without occupying registers or issue slots for LDS
+// writes.  Each chunk-parity buffer is its own LDS array and the loop body is
+// instantiated once per parity, so the compiler can tell the buffer being read from the
+// one being filled and does not wait for the loads in flight.  U' (this wave's 4 KB) is
+// prefetched into registers one chunk ahead.  O is computed transposed and normalised
+// from registers; a chunk's epilogue runs after the next chunk's opening barrier, which
+// publishes every wave's partial sums of squares.
+
+#include <type_traits>
 
 #include "kda_device.hpp"
 
@@ -27,67 +34,30 @@ namespace kda {
 namespace {
 
 constexpr int kCarryThreads = 512;
+constexpr int kBufBytes = kRecPieces * REC_PIECE;  // 78,848
+constexpr int kPiecesPerWave = (kRecPieces + 7) / 8;  // 10 (the last ones repeat piece 76)
 
-// ---- LDS map (bytes) ----
-constexpr int C_E = REC_IMG;                         // e^{G_end} fp32 [128]
-constexpr int C_NW = C_E + 512;                      // norm_w fp32 [128]
-constexpr int C_O = C_NW + 512;                      // O fp32 [2 tiles][64][CO_LD]
-constexpr int CO_LD = 132;                           // padded row pitch of O
-constexpr int kOTile = kChunk * CO_LD;               // floats of one O tile
-constexpr int kCarryLds = C_O + 2 * kOTile * 4;      // the operand images sit at 0
-static_assert(kCarryLds <= 160 * 1024, "LDS budget");
-static_assert(REC_IMG % (16 * kCarryThreads) == 0, "image pieces split evenly over the lanes");
-constexpr int kImgPieces = REC_IMG / 16 / kCarryThreads;  // 10
+// The two chunk-parity buffers of operand pieces, and the RMS partial sums [parity][64
+// tokens][8 waves].
+__shared__ __align__(16) unsigned char carry_buf0[kBufBytes];
+__shared__ __align__(16) unsigned char carry_buf1[kBufBytes];
+__shared__ __align__(16) float carry_part[2][kChunk * 8];
 
-// One record as this lane loads it: its pieces of the operand images (copied to LDS
-// as they are), a piece of e^{G_end} (lanes < 32) and its U' values.
-struct RecordLoads {
-    u32x4 img[kImgPieces];
-    u32x4 e;
-    f32x4 u[2][2];  // [tp][x]
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-// image pieces J0 .. J1-1 of a record
-template <int J0, int J1>
-__device__ __forceinline__ void load_images(RecordLoads &r, const unsigned char *rec, int tid) {
-#pragma unroll
-    for (int j = J0; j < J1; ++j) r.img[j] = *reinterpret_cast<const u32x4 *>(rec + (tid + kCarryThreads * j) * 16);
-}
-// e^{G_end} and U' of a record
-__device__ __forceinline__ void load_tail(RecordLoads &r, const unsigned char *rec, int tid) {
-    const int w = tid >> 6, lane = tid & 63;
-    r.e = *reinterpret_cast<const u32x4 *>(rec + REC_E + min(tid, 31) * 16);
-#pragma unroll
-    for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-            r.u[tp][x] = *reinterpret_cast<const f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
+// Workgroup barrier after every global load (direct-to-LDS ones included), store and LDS
+// access of each wave has completed: s_waitcnt vmcnt(0) lgkmcnt(0), as a builtin so that
+// the compiler's own wait insertion knows the loads are done, then s_barrier.  The empty
+// statements with a memory clobber keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_all_mem() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
 }
 
-// Lane coordinates.  (Unlike the chunk kernel, this one has the registers to keep its
-// lane-dependent LDS addresses across the chunk loop, so the compiler may hoist them: that
-// halves the loop's VALU work.)
-#define CARRY_LANE_IDS()                                       \
-    int tid_ = (int)threadIdx.x;                               \
-    const int w = __builtin_amdgcn_readfirstlane(tid_ >> 6);   \
-    const int lr = tid_ & 15;                                  \
-    const int lg = (tid_ >> 4) & 3;                            \
-    (void)w;                                                   \
-    (void)lr;                                                  \
-    (void)lg
-
+// kBf16: the output buffer holds bf16 (round to nearest even), else fp32
+template <bool kBf16>
 __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const __bf16 *sW = reinterpret_cast<const __bf16 *>(smem + REC_W);
-    const __bf16 *sQ = reinterpret_cast<const __bf16 *>(smem + REC_Q);
-    const __bf16 *sPh = reinterpret_cast<const __bf16 *>(smem + REC_PH);
-    const __bf16 *sPl = reinterpret_cast<const __bf16 *>(smem + REC_PL);
-    const __bf16 *sKh = reinterpret_cast<const __bf16 *>(smem + REC_KH);
-    const __bf16 *sKl = reinterpret_cast<const __bf16 *>(smem + REC_KL);
-    const float *sE = reinterpret_cast<const float *>(smem + C_E);
-    float *sNw = reinterpret_cast<float *>(smem + C_NW);
-    float *sO = reinterpret_cast<float *>(smem + C_O);
-
     const int H = a.c.H;
     const int N = a.N;
     const int seq = blockIdx.x / H;
@@ -103,10 +73,15 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
     const size_t rec_stride = (size_t)H * kRecBytes;
     const unsigned char *rec0 = a.records + ((size_t)r0 * H + h) * kRecBytes;
 
+    const int tid = (int)threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lr = tid & 15;
+    const int lg = (tid >> 4) & 3;
+
     // ---- the state: S[P][x][i] = S[key 32P + 8lg + 4x + i][value 16w + lr] ----
     f32x4 S[4][2];
     {
-        CARRY_LANE_IDS();
         const float *S0 = a.initial_state ? a.initial_state + ((size_t)seq * H + h) * kD * kD : nullptr;
 #pragma unroll
         for (int P = 0; P < 4; ++P)
@@ -117,179 +92,148 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                     const int key = 32 * P + 8 * lg + 4 * x + i;
                     S[P][x][i] = S0 ? S0[key * kD + 16 * w + lr] : 0.0f;
                 }
-        if (tid_ < kD) sNw[tid_] = a.norm_w[tid_];
     }
+    float nw[4];  // the RMSNorm weight of this lane's output columns 16w + 4lg + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nw[i] = a.norm_w[16 * w + 4 * lg + i];
 
-    // out = sigmoid(g) * RMSNorm(O) for the L tokens from c0 of an O tile: eight adjacent
-    // lanes own one token row (16 values each), 16-byte loads and stores
-    auto epilogue = [&](const float *tile, const u32x4 *graw, int c0, int L) {
-        const int tid_ = (int)threadIdx.x;
-        const int tok = tid_ >> 3;
-        const int v0 = 16 * (tid_ & 7);
-        float o[16];
-        lds_read8(tile + tok * CO_LD + v0, o);
-        lds_read8(tile + tok * CO_LD + v0 + 8, o + 8);
-        float ss = 0.f;
+    // record c's operand pieces into an LDS buffer (wave w: pieces 8j + w) and its U' into
+    // registers; c is clamped to the last record, so the request past it is a harmless
+    // reload, and every wave issues the same number of loads on every path
+    auto request = [&](lds_void *dst_base, int c, f32x4 (&Un)[2][2]) {
+        const unsigned char *rec = rec0 + (size_t)min(c, nrec - 1) * rec_stride;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ss += o[j] * o[j];
-        ss += __shfl_xor(ss, 1, 64);
-        ss += __shfl_xor(ss, 2, 64);
-        ss += __shfl_xor(ss, 4, 64);
-        if (tok < L) {
-            const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
-            const size_t orow = (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
+        for (int j = 0; j < kPiecesPerWave; ++j) {
+            const int piece = min(8 * j + w, kRecPieces - 1);
+            __builtin_amdgcn_global_load_lds(rec + piece * REC_PIECE + lane * 16,
+                                             (lds_void *)((__attribute__((address_space(3))) unsigned char *)dst_base +
+                                                          piece * REC_PIECE),
+                                             16, 0, 0);
+        }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float g8[8], nw[8], y[8];
-                unpack8(graw[j], g8);
-                lds_read8(sNw + v0 + 8 * j, nw);
+        for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[8 * j + e] * rinv * nw[e]);
-                store_out4(a.out, orow + 8 * j, y[0], y[1], y[2], y[3], a.c.out_bf16);
-                store_out4(a.out, orow + 8 * j + 4, y[4], y[5], y[6], y[7], a.c.out_bf16);
+            for (int x = 0; x < 2; ++x)
+                Un[tp][x] = *reinterpret_cast<const f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
+    };
+
+    f32x4 Unext[2][2] = {};
+    f32x4 oprev[4] = {};  // the previous chunk's O^T tiles, normalised one chunk later
+    uint2 gprev[4] = {};  // and its output-gate logits
+
+    // one chunk; the buffer parity B is a compile-time constant
+    auto chunk = [&](auto parity, int c) {
+        constexpr int B = decltype(parity)::value;
+        const unsigned char *cur = B ? carry_buf1 : carry_buf0;
+        lds_void *nxt_lds = B ? (lds_void *)carry_buf0 : (lds_void *)carry_buf1;
+        float *part = carry_part[B];
+        const float *part_prev = carry_part[B ^ 1];
+        const int c0 = c * kChunk;
+        const int L = min(kChunk, T - c0);
+
+        // this chunk's pieces (every wave's) are in `cur`; nobody reads `nxt` any more;
+        // the previous chunk's partial sums are published
+        barrier_all_mem();
+
+        f32x4 U[2][2];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) U[tp][x] = Unext[tp][x];
+        request(nxt_lds, c + 1, Unext);
+
+        // the previous chunk's epilogue (a full chunk: only the last can be partial)
+        if (c > 0)
+            gated_rms_store<kBf16>(oprev, gprev, part_prev, nw, a.c.rms_eps, a.out, HD, h, t0 + c0 - kChunk, kChunk, w,
+                                   lr, lg);
+        uint2 g4[4];
+        load_gate4(g4, a.g, HD, h, t0 + c0, L, w, lr, lg);
+
+        auto opnd = [&](int piece) { return *reinterpret_cast<const bf16x8 *>(cur + piece * REC_PIECE + lane * 16); };
+
+        bf16x8 Sh[4];  // S0 as the B operand of key contractions
+#pragma unroll
+        for (int P = 0; P < 4; ++P) {
+            const float v8[8] = {S[P][0][0], S[P][0][1], S[P][0][2], S[P][0][3],
+                                 S[P][1][0], S[P][1][1], S[P][1][2], S[P][1][3]};
+            Sh[P] = to_bf8(v8);
+        }
+        // U = U' - W S0
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int P = 0; P < 4; ++P) ws = mma(opnd(rec_w_piece(tp, x, P)), Sh[P], ws);
+                U[tp][x] -= ws;
             }
+        bf16x8 Uh[2], Ul[2];  // U as the B operand of token contractions, hi/lo [tp]
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            const float v8[8] = {U[tp][0][0], U[tp][0][1], U[tp][0][2], U[tp][0][3],
+                                 U[tp][1][0], U[tp][1][1], U[tp][1][2], U[tp][1][3]};
+            split8(v8, Uh[tp], Ul[tp]);
+        }
+        // O^T = S0^T Q~^T + U^T P^T
+        f32x4 o[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int P = 0; P < 4; ++P) acc = mma(Sh[P], opnd(rec_q_piece(tt, P)), acc);
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                if (tp > (tt >> 1)) continue;  // P is lower triangular
+                const bf16x8 Ph = opnd(rec_p_piece(tt, tp, 0));
+                const bf16x8 Pl = opnd(rec_p_piece(tt, tp, 1));
+                acc = mma(Uh[tp], Ph, acc);
+                acc = mma(Uh[tp], Pl, acc);
+                acc = mma(Ul[tp], Ph, acc);
+            }
+            o[tt] = acc;
+        }
+        rms_partials(o, part, w, lr, lg);
+        // S = Diag(e^{G_end}) S0 + K_end^T U
+        const float *sE = reinterpret_cast<const float *>(cur + REC_E * REC_PIECE);
+#pragma unroll
+        for (int P = 0; P < 4; ++P)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                f32x4 acc = S[P][x] * *reinterpret_cast<const f32x4 *>(sE + 32 * P + 8 * lg + 4 * x);
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    const bf16x8 Kh = opnd(rec_k_piece(P, x, tp, 0));
+                    const bf16x8 Kl = opnd(rec_k_piece(P, x, tp, 1));
+                    acc = mma(Kh, Uh[tp], acc);
+                    acc = mma(Kl, Uh[tp], acc);
+                    acc = mma(Kh, Ul[tp], acc);
+                }
+                S[P][x] = acc;
+            }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            oprev[tt] = o[tt];
+            gprev[tt] = g4[tt];
         }
     };
 
-    RecordLoads ld = {};
     if (nrec > 0) {
-        const int tid_ = (int)threadIdx.x;
-        load_images<0, kImgPieces>(ld, rec0, tid_);
-        load_tail(ld, rec0, tid_);
+        request((lds_void *)carry_buf0, 0, Unext);
+        for (int c = 0; c < nrec; c += 2) {
+            chunk(std::integral_constant<int, 0>{}, c);
+            if (c + 1 < nrec) chunk(std::integral_constant<int, 1>{}, c + 1);
+        }
+        // the last chunk's epilogue; the wait also drains the reload requested past the
+        // last record before the workgroup's LDS is released
+        barrier_all_mem();
+        const int cl = nrec - 1;
+        gated_rms_store<kBf16>(oprev, gprev, carry_part[cl & 1], nw, a.c.rms_eps, a.out, HD, h, t0 + cl * kChunk,
+                               min(kChunk, T - cl * kChunk), w, lr, lg);
     }
-    u32x4 gprev[2] = {};  // output-gate logits of the previous chunk
-
-    for (int c = 0; c < nrec; ++c) {
-        const int c0 = c * kChunk;
-        const int L = min(kChunk, T - c0);
-        const bool more = c + 1 < nrec;
-        const unsigned char *next = rec0 + (size_t)(c + 1) * rec_stride;
-        float *tile = sO + (c & 1) * kOTile;
-
-        // ---- this chunk's operand images and e^{G_end} into LDS; U' into registers ----
-        f32x4 U[2][2];
-        {
-            const int tid_ = (int)threadIdx.x;
-#pragma unroll
-            for (int j = 0; j < kImgPieces; ++j)
-                *reinterpret_cast<u32x4 *>(smem + (tid_ + kCarryThreads * j) * 16) = ld.img[j];
-            if (tid_ < 32) *reinterpret_cast<u32x4 *>(smem + C_E + tid_ * 16) = ld.e;
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-                for (int x = 0; x < 2; ++x) U[tp][x] = ld.u[tp][x];
-        }
-        lds_barrier();
-
-        // the previous chunk's epilogue (a full chunk: only the last can be partial)
-        if (c > 0) epilogue(sO + ((c - 1) & 1) * kOTile, gprev, c0 - kChunk, kChunk);
-        // this chunk's output-gate logits, used by its epilogue one chunk later
-        u32x4 gcur[2];
-        {
-            const int tid_ = (int)threadIdx.x;
-            const int tok = min(tid_ >> 3, L - 1);
-            const uint16_t *gp = a.g + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + 16 * (tid_ & 7);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) gcur[j] = *reinterpret_cast<const u32x4 *>(gp + 8 * j);
-            if (more) load_images<0, 4>(ld, next, tid_);
-        }
-
-        bf16x8 Sh[4];  // S0 as the B operand of key contractions
-        bf16x8 Uh[2], Ul[2];  // U as the B operand of token contractions, hi/lo [tp]
-        {
-            CARRY_LANE_IDS();
-#pragma unroll
-            for (int P = 0; P < 4; ++P) {
-                const float v8[8] = {S[P][0][0], S[P][0][1], S[P][0][2], S[P][0][3],
-                                     S[P][1][0], S[P][1][1], S[P][1][2], S[P][1][3]};
-                Sh[P] = to_bf8(v8);
-            }
-            // U = U' - W S0
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int trow = 32 * tp + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                    f32x4 ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int P = 0; P < 4; ++P) {
-                        const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + swi128(trow, 32 * P + 8 * lg));
-                        ws = mma(A8, Sh[P], ws);
-                    }
-                    U[tp][x] -= ws;
-                }
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                const float v8[8] = {U[tp][0][0], U[tp][0][1], U[tp][0][2], U[tp][0][3],
-                                     U[tp][1][0], U[tp][1][1], U[tp][1][2], U[tp][1][3]};
-                split8(v8, Uh[tp], Ul[tp]);
-            }
-        }
-        {
-            const int tid_ = (int)threadIdx.x;
-            if (more) load_images<4, 7>(ld, next, tid_);
-        }
-        {
-            CARRY_LANE_IDS();
-            // O = Q~ S0 + P U   (rows: token 16tt + 4lg + i)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int P = 0; P < 4; ++P) {
-                    const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sQ + sw128(16 * tt + lr, 32 * P + 8 * lg));
-                    acc = mma(A8, Sh[P], acc);
-                }
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    if (tp > (tt >> 1)) continue;  // P is lower triangular
-                    const bf16x8 Ph = *reinterpret_cast<const bf16x8 *>(sPh + sw64(16 * tt + lr, 32 * tp + 8 * lg));
-                    const bf16x8 Pl = *reinterpret_cast<const bf16x8 *>(sPl + sw64(16 * tt + lr, 32 * tp + 8 * lg));
-                    acc = mma(Ph, Uh[tp], acc);
-                    acc = mma(Pl, Uh[tp], acc);
-                    acc = mma(Ph, Ul[tp], acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tile[(16 * tt + 4 * lg + i) * CO_LD + 16 * w + lr] = acc[i];
-            }
-        }
-        {
-            const int tid_ = (int)threadIdx.x;
-            if (more) {
-                load_images<7, kImgPieces>(ld, next, tid_);
-                load_tail(ld, next, tid_);
-            }
-        }
-        {
-            CARRY_LANE_IDS();
-            // S = Diag(e^{G_end}) S0 + K_end^T U
-#pragma unroll
-            for (int P = 0; P < 4; ++P)
-#pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int krow = 32 * P + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                    f32x4 acc = S[P][x] * *reinterpret_cast<const f32x4 *>(sE + 32 * P + 8 * lg + 4 * x);
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp) {
-                        const bf16x8 Kh = *reinterpret_cast<const bf16x8 *>(sKh + swi64(krow, 32 * tp + 8 * lg));
-                        const bf16x8 Kl = *reinterpret_cast<const bf16x8 *>(sKl + swi64(krow, 32 * tp + 8 * lg));
-                        acc = mma(Kh, Uh[tp], acc);
-                        acc = mma(Kl, Uh[tp], acc);
-                        acc = mma(Kh, Ul[tp], acc);
-                    }
-                    S[P][x] = acc;
-                }
-        }
-        gprev[0] = gcur[0];
-        gprev[1] = gcur[1];
-        lds_barrier();  // the operand images are rewritten by the next chunk
-    }
-    if (nrec > 0)
-        epilogue(sO + ((nrec - 1) & 1) * kOTile, gprev, (nrec - 1) * kChunk, min(kChunk, T - (nrec - 1) * kChunk));
 
     // ---- final state ----
     {
-        CARRY_LANE_IDS();
         float *Sf = a.final_state + ((size_t)seq * H + h) * kD * kD;
         // (the initial state may alias the final one: each element is read and written by
         //  the same lane)
@@ -305,7 +249,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
     }
     // ---- final conv windows: the last 3 pre-conv inputs (from the initial window if T < 3) ----
     const size_t conv_seq = (size_t)seq * 3 * HD * 3;
-    for (int q = threadIdx.x; q < 3 * kD; q += kCarryThreads) {
+    for (int q = tid; q < 3 * kD; q += kCarryThreads) {
         const int blk = q >> 7, cc = q & 127;
         const size_t ch = (size_t)blk * HD + (size_t)h * kD + cc;
         float win[3];
@@ -323,17 +267,14 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
     }
 }
 
-#undef CARRY_LANE_IDS
-
 }  // namespace
 
 hipError_t launch_carry(const PrefillArgs &a, hipStream_t stream) {
-    const void *fn = reinterpret_cast<const void *>(&carry_kernel);
-    static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kCarryLds);
-    if (attr != hipSuccess) return attr;
+    const void *fn = a.c.out_bf16 ? reinterpret_cast<const void *>(&carry_kernel<true>)
+                                   : reinterpret_cast<const void *>(&carry_kernel<false>);
     dim3 grid((unsigned)((size_t)a.B * a.c.H)), block(kCarryThreads);
     void *args[] = {const_cast<PrefillArgs *>(&a)};
-    return hipLaunchKernel(fn, grid, block, args, kCarryLds, stream);
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 }  // namespace kda

@@ -92,21 +92,97 @@ __device__ __forceinline__ void lds_write8(float *p, const float *x) {
     *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 
-// ---- one chunk record of the chunk-parallel prefill (bytes) ----
-// Everything a chunk contributes that does not depend on the state entering it: the
-// first five entries are the LDS images (swizzled as above) of the MFMA A operands of
-// the state-side products, U' is stored in the register order of the consumer (value
-// column group cg of 16, token pair tp, interleave x, lane: 16 bytes each, the
-// accumulator rows of token 32tp + 8(l/16) + 4x + i, column 16cg + l%16).
-constexpr int REC_W = 0;           // W = T (beta k e^G)        bf16 swi128 [64 tok][128 key]
-constexpr int REC_Q = 16384;       // Q~ = q e^G                 bf16 sw128 [64 tok][128 key]
-constexpr int REC_PH = 32768;      // P, hi part                 bf16 sw64  [64 tok][64 tok]
-constexpr int REC_PL = 40960;      // P, lo part
-constexpr int REC_KH = 49152;      // K_end^T = (k e^{G_end-G})^T, hi   bf16 swi64 [128 key][64 tok]
-constexpr int REC_KL = 65536;      // K_end^T, lo part
-constexpr int REC_IMG = 81920;     // bytes of the five operand images
-constexpr int REC_U = 81920;       // U' = T (beta v)            fp32 [8 cg][2 tp][2 x][64 lanes][4]
-constexpr int REC_E = 114688;      // e^{G_end}                  fp32 [128 key]
-static_assert(REC_U + 8 * 2 * 2 * 64 * 16 == REC_E && REC_E + 512 == kRecBytes, "record layout");
+// ---- one chunk record of the chunk-parallel prefill ----
+// Everything a chunk contributes that does not depend on the state entering it.  The
+// first kRecPieces pieces of 1 KB are the MFMA operands of the carry's products in the
+// order the carry reads them: piece p holds at byte 16l the 16 bytes (8 bf16) that lane
+// l = 16lg + lr of every carry wave reads for that MFMA.  The carry copies the pieces into
+// LDS as they are (one direct-to-LDS load of 1 KB each) and reads each operand with one
+// linear, conflict-free 16-byte LDS read.
+//   W   16 pieces (tp, x, P):       W[32tp + 8(lr/4) + 4x + lr%4][32P + 8lg .. +7]
+//   Q~  16 pieces (tt, P):          Q~[16tt + lr][32P + 8lg .. +7]
+//   P   12 pieces (slab s, hi/lo):  P[16tt + lr][32tp + 8lg .. +7] for the slabs
+//                                   s = (tt, tp) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+//                                   (the others are zero: P is lower triangular)
+//   K   32 pieces (P, x, tp, hi/lo): K_end^T[32P + 8(lr/4) + 4x + lr%4][32tp + 8lg .. +7]
+//   E    1 piece:                   e^{G_end} fp32 [128 keys], then 512 zero bytes
+// with W = T (beta k e^G), Q~ = q e^G, K_end = k e^{G_end - G}, P and K_end split into
+// bf16 hi + lo.  After the pieces, U' = T (beta v) in fp32, in the register order of the
+// consumer: [8 waves][2 tp][2 x][64 lanes][4] (the accumulator rows of token
+// 32tp + 8lg + 4x + i, value column 16w + lr).
+constexpr int REC_PIECE = 1024;
+constexpr int REC_W = 0;    // piece indices
+constexpr int REC_Q = 16;
+constexpr int REC_P = 32;
+constexpr int REC_K = 44;
+constexpr int REC_E = 76;
+constexpr int kRecPieces = 77;
+constexpr int REC_U = kRecPieces * REC_PIECE;  // byte offset of U'
+static_assert(REC_U + 8 * 2 * 2 * 64 * 16 == kRecBytes, "record layout");
+__device__ __forceinline__ int rec_w_piece(int tp, int x, int P) { return REC_W + (tp * 2 + x) * 4 + P; }
+__device__ __forceinline__ int rec_q_piece(int tt, int P) { return REC_Q + tt * 4 + P; }
+__device__ __forceinline__ int rec_p_piece(int tt, int tp, int hl) { return REC_P + 2 * (tt < 2 ? tt : 2 * tt - 2 + tp) + hl; }
+__device__ __forceinline__ int rec_k_piece(int P, int x, int tp, int hl) { return REC_K + ((P * 2 + x) * 2 + tp) * 2 + hl; }
+
+// ---- the state-side readout and its epilogue, shared by the fused and chunked plans ----
+// O is computed transposed, O^T = S0^T Q~^T + U^T P^T, so that lane (lr, lg) of wave w
+// holds o[tt][i] = O[token 16tt + lr][value 16w + 4lg + i]: four consecutive values of one
+// output row, stored with one 16-byte (fp32) or 8-byte (bf16) store.  Both plans run the
+// same MFMAs in the same order and the same reductions below, so they give the same bits.
+
+// The wave's partial sums of squares of each token's 16 values, into part[token][wave]
+// ([64][8] fp32).
+__device__ __forceinline__ void rms_partials(const f32x4 (&o)[4], float *part, int w, int lr, int lg) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        float s = o[tt][0] * o[tt][0];
+        s = __builtin_fmaf(o[tt][1], o[tt][1], s);
+        s = __builtin_fmaf(o[tt][2], o[tt][2], s);
+        s = __builtin_fmaf(o[tt][3], o[tt][3], s);
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        if (lg == 0) part[(16 * tt + lr) * 8 + w] = s;
+    }
+}
+
+// The output-gate logits of this lane's values (4 bf16 of each of its 4 tokens; rows
+// past the sequence's end are clamped to its last row and never stored).
+__device__ __forceinline__ void load_gate4(uint2 (&g4)[4], const uint16_t *g, size_t HD, int h, int tok0, int L,
+                                           int w, int lr, int lg) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int tok = min(16 * tt + lr, L - 1);
+        g4[tt] = *reinterpret_cast<const uint2 *>(g + (size_t)(tok0 + tok) * HD + (size_t)h * kD + 16 * w + 4 * lg);
+    }
+}
+
+// out = sigmoid(g) * RMSNorm(O) for tokens 16tt + lr < L of a chunk whose first token is
+// packed row tok0, once every wave's partial sums are in part.  nw: the RMSNorm weight of
+// this lane's 4 value columns.  kBf16: the output buffer holds bf16 (round to nearest
+// even), else fp32.  The norm's reciprocal square root is the hardware one (about 1 ulp).
+// Branch-free when L is the full chunk, so that the compiler can interleave it with
+// independent MFMAs.
+template <bool kBf16>
+__device__ __forceinline__ void gated_rms_store(const f32x4 (&o)[4], const uint2 (&g4)[4], const float *part,
+                                                const float (&nw)[4], float rms_eps, void *out, size_t HD, int h,
+                                                int tok0, int L, int w, int lr, int lg) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int tok = 16 * tt + lr;
+        const float2 pp = *reinterpret_cast<const float2 *>(part + tok * 8 + 2 * lg);
+        float s = pp.x + pp.y;
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        const float rinv = __builtin_amdgcn_rsqf(s * (1.0f / kD) + rms_eps);
+        const float gg[4] = {__uint_as_float(g4[tt].x << 16), __uint_as_float(g4[tt].x & 0xffff0000u),
+                             __uint_as_float(g4[tt].y << 16), __uint_as_float(g4[tt].y & 0xffff0000u)};
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = sigm(gg[i]) * (o[tt][i] * rinv * nw[i]);
+        if (tok < L)
+            store_out4(out, (size_t)(tok0 + tok) * HD + (size_t)h * kD + 16 * w + 4 * lg, y[0], y[1], y[2], y[3],
+                       kBf16);
+    }
+}
 
 }  // namespace kda

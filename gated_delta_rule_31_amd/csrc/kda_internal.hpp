@@ -91,7 +91,7 @@ constexpr double kRecordUs = 17.0;
 constexpr double kCarryChunkUs = 5.9;
 
 // Bytes of one chunk record (the layout is in kda_device.hpp); a multiple of 256.
-constexpr int kRecBytes = 115200;
+constexpr int kRecBytes = 111616;
 
 // Chunk records that a batch of B sequences and N tokens can need at most:
 // sum_s ceil(len_s / 64) <= floor(N / 64) + B.

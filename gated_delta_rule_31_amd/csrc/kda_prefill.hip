@@ -52,7 +52,7 @@ constexpr int kThreads = 512;
 
 // ---- LDS map (bytes).  Regions are reused once their first tenant is dead. ----
 constexpr int OFF_R1 = 0;        // sCB fp32 [64][132]          -> sKe hi/lo bf16 [128][64] x2
-constexpr int OFF_R2 = 33792;    // sVt hi/lo bf16 [128][64] x2 -> sO fp32 [64][128]
+constexpr int OFF_R2 = 33792;    // sVt hi/lo bf16 [128][64] x2 -> RMS partial sums fp32 [64][8]
 constexpr int OFF_R3 = 66560;    // sWr bf16 [128][64]          (beta k e^G, transposed)
 constexpr int OFF_R4 = 82944;    // sA fp32 [64][68]            -> sW bf16 [64][128]
 constexpr int OFF_R5 = 100352;   // sPh, sPl bf16 [64][64] (P split hi/lo)
@@ -172,7 +172,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     __bf16 *sKeLo = sKeHi + 128 * 64;
     __bf16 *sVtHi = reinterpret_cast<__bf16 *>(smem + OFF_R2);          // [128][64] (beta v)^T
     __bf16 *sVtLo = sVtHi + 128 * 64;
-    float *sO = reinterpret_cast<float *>(smem + OFF_R2);               // [64][128] readout
     __bf16 *sWr = reinterpret_cast<__bf16 *>(smem + OFF_R3);            // [128][64] (beta k e^G)^T
     float *sA = reinterpret_cast<float *>(smem + OFF_R4);               // [64][68]
     __bf16 *sW = reinterpret_cast<__bf16 *>(smem + OFF_R4);             // [64][128]
@@ -726,34 +725,50 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int x = 0; x < 2; ++x)
                     *reinterpret_cast<f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16) = U[tp][x];
-            // the operand images, copied as they sit in LDS: W (region 4), Q~ (region 6),
-            // P hi/lo (region 5), K_end^T hi/lo (region 1); 10 pieces of 16 bytes per lane
+            // the operand pieces, in the order the carry reads them: piece 8j + w is copied
+            // by wave w, lane l taking the 16 bytes lane l of a carry wave reads
+            const int lr2 = lane & 15, lg2 = lane >> 4;
 #pragma unroll
-            for (int j = 0; j < REC_IMG / 16 / kThreads; ++j) {
-                const int off = (tid_ + kThreads * j) * 16;
-                const int src = j < 2 ? OFF_R4 + off
-                              : j < 4 ? OFF_R6 + (off - REC_Q)
-                              : j < 6 ? OFF_R5 + (off - REC_PH)
-                                      : OFF_R1 + (off - REC_KH);
-                *reinterpret_cast<u32x4 *>(rec + off) = *reinterpret_cast<const u32x4 *>(smem + src);
+            for (int j = 0; j < (kRecPieces + 7) / 8; ++j) {
+                const int piece = 8 * j + w;
+                if (piece >= kRecPieces) break;  // (uniform)
+                const unsigned char *src;
+                if (piece < REC_Q) {
+                    const int tp = piece >> 3, x = (piece >> 2) & 1, P = piece & 3;
+                    const int trow = 32 * tp + 8 * (lr2 >> 2) + 4 * x + (lr2 & 3);
+                    src = reinterpret_cast<const unsigned char *>(sW + swi128(trow, 32 * P + 8 * lg2));
+                } else if (piece < REC_P) {
+                    const int tt = (piece - REC_Q) >> 2, P = (piece - REC_Q) & 3;
+                    src = reinterpret_cast<const unsigned char *>(sQe + sw128(16 * tt + lr2, 32 * P + 8 * lg2));
+                } else if (piece < REC_K) {
+                    const int sl = (piece - REC_P) >> 1, hl = (piece - REC_P) & 1;
+                    const int tt = sl < 2 ? sl : (sl + 2) >> 1, tp = sl < 2 ? 0 : (sl & 1);
+                    src = reinterpret_cast<const unsigned char *>((hl ? sPl : sPh) + sw64(16 * tt + lr2, 32 * tp + 8 * lg2));
+                } else if (piece < REC_E) {
+                    const int q = piece - REC_K;
+                    const int hl = q & 1, tp = (q >> 1) & 1, x = (q >> 2) & 1, P = q >> 3;
+                    const int krow = 32 * P + 8 * (lr2 >> 2) + 4 * x + (lr2 & 3);
+                    src = reinterpret_cast<const unsigned char *>((hl ? sKeLo : sKeHi) + swi64(krow, 32 * tp + 8 * lg2));
+                } else {
+                    src = reinterpret_cast<const unsigned char *>(sExpEnd + 4 * min(lane, 31));
+                }
+                u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+                if (piece == REC_E && lane >= 32) v = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(rec + piece * REC_PIECE + lane * 16) = v;
             }
-            if (tid_ < 32)
-                *reinterpret_cast<u32x4 *>(rec + REC_E + tid_ * 16) = *reinterpret_cast<const u32x4 *>(sExpEnd + 4 * tid_);
             lds_barrier();  // LDS is rewritten by the next chunk
             continue;
         }
 
-        // ================= phase 5: state side =================
+        // ================= phase 5: state side and epilogue =================
         // (the epilogue's output-gate logits are loaded now, to arrive during the MFMAs)
-        u32x4 graw[2];
+        uint2 g4[4];
         {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
-            const int tok = min(tid_ >> 3, L - 1);
-            const uint16_t *gp = a.g + (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + 16 * (tid_ & 7);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) graw[j] = *reinterpret_cast<const u32x4 *>(gp + 8 * j);
+            KDA_LANE_IDS();
+            load_gate4(g4, a.g, HD, h, t0 + c0, L, w, lr, lg);
         }
+        float *sRms = reinterpret_cast<float *>(smem + OFF_R2);  // [64][8] (beta v is dead)
+        f32x4 o[4];  // o[tt][i] = O[token 16tt + lr][value 16w + 4lg + i]
         {
             KDA_LANE_IDS();
             bf16x8 Sh[4];  // S0 as the B operand of key contractions (hi part)
@@ -784,27 +799,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                                U[tp][1][0], U[tp][1][1], U[tp][1][2], U[tp][1][3]};
                 split8(v8, Uh[tp], Ul[tp]);
             }
-            // O = Q~ S0 + P U   (rows: token 16tt + 4lg + i), parked in region 2 (beta v is dead)
+            // O^T = S0^T Q~^T + U^T P^T
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int P = 0; P < 4; ++P) {
-                    const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sQe + sw128(16 * tt + lr, 32 * P + 8 * lg));
-                    acc = mma(A8, Sh[P], acc);
+                    const bf16x8 B8 = *reinterpret_cast<const bf16x8 *>(sQe + sw128(16 * tt + lr, 32 * P + 8 * lg));
+                    acc = mma(Sh[P], B8, acc);
                 }
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
                     if (tp > (tt >> 1)) continue;  // P is lower triangular
                     const bf16x8 Ph = *reinterpret_cast<const bf16x8 *>(sPh + sw64(16 * tt + lr, 32 * tp + 8 * lg));
                     const bf16x8 Pl = *reinterpret_cast<const bf16x8 *>(sPl + sw64(16 * tt + lr, 32 * tp + 8 * lg));
-                    acc = mma(Ph, Uh[tp], acc);
-                    acc = mma(Pl, Uh[tp], acc);
-                    acc = mma(Ph, Ul[tp], acc);
+                    acc = mma(Uh[tp], Ph, acc);
+                    acc = mma(Uh[tp], Pl, acc);
+                    acc = mma(Ul[tp], Ph, acc);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sO[(16 * tt + 4 * lg + i) * kD + 16 * w + lr] = acc[i];
+                o[tt] = acc;
             }
+            rms_partials(o, sRms, w, lr, lg);
             // S = Diag(e^{G_end}) S0 + K_end^T U
 #pragma unroll
             for (int P = 0; P < 4; ++P)
@@ -828,35 +843,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         lds_barrier();
 
         // ================= epilogue: out = sigmoid(g) * RMSNorm(o) =================
-        // eight adjacent lanes own one token row: 16 values each, 16-byte loads and stores
         {
-            int tid_ = (int)threadIdx.x;
-            asm volatile("" : "+v"(tid_));
-            const int tok = tid_ >> 3;
-            const int v0 = 16 * (tid_ & 7);
-            float o[16];
-            lds_read8(sO + tok * kD + v0, o);
-            lds_read8(sO + tok * kD + v0 + 8, o + 8);
-            float ss = 0.f;
+            KDA_LANE_IDS();
+            float nw[4];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) ss += o[j] * o[j];
-            ss += __shfl_xor(ss, 1, 64);
-            ss += __shfl_xor(ss, 2, 64);
-            ss += __shfl_xor(ss, 4, 64);
-            if (tok < L) {
-                const float rinv = 1.0f / sqrtf(ss * (1.0f / kD) + a.c.rms_eps);
-                const size_t orow = (size_t)(t0 + c0 + tok) * HD + (size_t)h * kD + v0;
-#pragma unroll
-                for (int j = 0; j < 16; j += 8) {
-                    float g8[8], nw[8], y[8];
-                    unpack8(graw[j / 8], g8);
-                    lds_read8(sNw + v0 + j, nw);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] = sigm(g8[e]) * (o[j + e] * rinv * nw[e]);
-                    store_out4(a.out, orow + j, y[0], y[1], y[2], y[3], a.c.out_bf16);
-                    store_out4(a.out, orow + j + 4, y[4], y[5], y[6], y[7], a.c.out_bf16);
-                }
-            }
+            for (int i = 0; i < 4; ++i) nw[i] = sNw[16 * w + 4 * lg + i];
+            if (a.c.out_bf16)
+                gated_rms_store<true>(o, g4, sRms, nw, a.c.rms_eps, a.out, HD, h, t0 + c0, L, w, lr, lg);
+            else
+                gated_rms_store<false>(o, g4, sRms, nw, a.c.rms_eps, a.out, HD, h, t0 + c0, L, w, lr, lg);
         }
         lds_barrier();  // LDS is rewritten by the next chunk
     }

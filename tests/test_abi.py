@@ -111,7 +111,7 @@ def test_workspace_query_is_host_only():
     assert kda.kda_prefill_workspace_bytes(kda.KdaConfig(), 16, 40000) >= 0
 
 
-REC_BYTES = 115200  # one chunk record
+REC_BYTES = 111616  # one chunk record
 
 
 def _ws(cfg, B, N):

@@ -49,6 +49,7 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kPiecesPerWave = (kRecPieces + 7) / 8;  // record pieces each wave copies
 
 // ---- LDS map (bytes).  Regions are reused once their first tenant is dead. ----
 constexpr int OFF_R1 = 0;        // sCB fp32 [64][132]          -> sKe hi/lo bf16 [128][64] x2
@@ -280,6 +281,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     //  stores issued after them across the loop's back edge and makes phase 1 wait for
     //  every memory operation in flight, stores included)
     asm volatile("" ::"v"(ld.z[0]), "v"(ld.z[1]), "v"(ld.b));
+
+    // chunked plan: the LDS byte offset (/16, two per register) of the 16 bytes this lane
+    // copies into each record piece it writes (pieces 8j + w); see the record layout in
+    // kda_device.hpp
+    uint32_t rec_src[(kPiecesPerWave + 1) / 2] = {};
+    if constexpr (kChunked) {
+        const int tid = (int)threadIdx.x;
+        const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < kPiecesPerWave; ++j) {
+            const int piece = 8 * j + w;
+            int off = 0;  // bytes from smem
+            if (piece < REC_Q) {
+                const int tp = piece >> 3, x = (piece >> 2) & 1, P = piece & 3;
+                const int trow = 32 * tp + 8 * (lr >> 2) + 4 * x + (lr & 3);
+                off = OFF_R4 + 2 * swi128(trow, 32 * P + 8 * lg);  // W
+            } else if (piece < REC_P) {
+                const int tt = (piece - REC_Q) >> 2, P = (piece - REC_Q) & 3;
+                off = OFF_R6 + 2 * sw128(16 * tt + lr, 32 * P + 8 * lg);  // Q~
+            } else if (piece < REC_K) {
+                const int sl = (piece - REC_P) >> 1, hl = (piece - REC_P) & 1;
+                const int tt = sl < 2 ? sl : (sl + 2) >> 1, tp = sl < 2 ? 0 : (sl & 1);
+                off = OFF_R5 + hl * 64 * 64 * 2 + 2 * sw64(16 * tt + lr, 32 * tp + 8 * lg);  // P hi / lo
+            } else if (piece < REC_E) {
+                const int q = piece - REC_K;
+                const int hl = q & 1, tp = (q >> 1) & 1, x = (q >> 2) & 1, P = q >> 3;
+                const int krow = 32 * P + 8 * (lr >> 2) + 4 * x + (lr & 3);
+                off = OFF_R1 + hl * 128 * 64 * 2 + 2 * swi64(krow, 32 * tp + 8 * lg);  // K_end^T hi / lo
+            } else if (piece == REC_E) {
+                off = OFF_TAB + (512 + 640 + 768 + 512 + 512) * 4 + 16 * min(lane, 31);  // e^{G_end}
+            }
+            rec_src[j >> 1] |= (uint32_t)(off >> 4) << (16 * (j & 1));
+        }
+#pragma unroll
+        for (int i = 0; i < (kPiecesPerWave + 1) / 2; ++i) asm volatile("" : "+v"(rec_src[i]));
+    }
 
     const int cend = kChunked ? min(min(cbeg + kSegChunks * kChunk, nrec * kChunk), T) : T;
     // (inside the chunk loop every cross-wave dependency goes through LDS, so its
@@ -726,33 +763,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 for (int x = 0; x < 2; ++x)
                     *reinterpret_cast<f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16) = U[tp][x];
             // the operand pieces, in the order the carry reads them: piece 8j + w is copied
-            // by wave w, lane l taking the 16 bytes lane l of a carry wave reads
-            const int lr2 = lane & 15, lg2 = lane >> 4;
+            // by wave w, lane l taking the 16 bytes lane l of a carry wave reads (source
+            // offsets computed once, before the chunk loop)
 #pragma unroll
-            for (int j = 0; j < (kRecPieces + 7) / 8; ++j) {
+            for (int j = 0; j < kPiecesPerWave; ++j) {
                 const int piece = 8 * j + w;
                 if (piece >= kRecPieces) break;  // (uniform)
-                const unsigned char *src;
-                if (piece < REC_Q) {
-                    const int tp = piece >> 3, x = (piece >> 2) & 1, P = piece & 3;
-                    const int trow = 32 * tp + 8 * (lr2 >> 2) + 4 * x + (lr2 & 3);
-                    src = reinterpret_cast<const unsigned char *>(sW + swi128(trow, 32 * P + 8 * lg2));
-                } else if (piece < REC_P) {
-                    const int tt = (piece - REC_Q) >> 2, P = (piece - REC_Q) & 3;
-                    src = reinterpret_cast<const unsigned char *>(sQe + sw128(16 * tt + lr2, 32 * P + 8 * lg2));
-                } else if (piece < REC_K) {
-                    const int sl = (piece - REC_P) >> 1, hl = (piece - REC_P) & 1;
-                    const int tt = sl < 2 ? sl : (sl + 2) >> 1, tp = sl < 2 ? 0 : (sl & 1);
-                    src = reinterpret_cast<const unsigned char *>((hl ? sPl : sPh) + sw64(16 * tt + lr2, 32 * tp + 8 * lg2));
-                } else if (piece < REC_E) {
-                    const int q = piece - REC_K;
-                    const int hl = q & 1, tp = (q >> 1) & 1, x = (q >> 2) & 1, P = q >> 3;
-                    const int krow = 32 * P + 8 * (lr2 >> 2) + 4 * x + (lr2 & 3);
-                    src = reinterpret_cast<const unsigned char *>((hl ? sKeLo : sKeHi) + swi64(krow, 32 * tp + 8 * lg2));
-                } else {
-                    src = reinterpret_cast<const unsigned char *>(sExpEnd + 4 * min(lane, 31));
-                }
-                u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+                const uint32_t off = ((rec_src[j >> 1] >> (16 * (j & 1))) & 0xffffu) << 4;
+                u32x4 v = *reinterpret_cast<const u32x4 *>(smem + off);
                 if (piece == REC_E && lane >= 32) v = u32x4{0u, 0u, 0u, 0u};
                 *reinterpret_cast<u32x4 *>(rec + piece * REC_PIECE + lane * 16) = v;
             }

@@ -126,9 +126,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Rows are clamped into the sequence [t0, t1): rows before its start are replaced by the
 // carried window later, rows past its end belong to padding tokens and are never used.
-// The base row is uniform, so lane offsets stay 32-bit.
-__device__ __forceinline__ ChunkLoads load_chunk(const PrefillArgs &a, int tid, int h, int t0, int t1, int c0) {
-    ChunkLoads r;
+// The base row is uniform, so lane offsets stay 32-bit.  The loads come in two parts,
+// issued in different phases so that no wave stalls behind a full memory pipe at a
+// barrier: part 0 the q rows, the lane's z row and beta logit; part 1 the k and v rows
+// and the 3 rows before the chunk.
+template <int kPart>
+__device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, int tid, int h, int t0, int t1,
+                                           int c0) {
     const size_t HD = (size_t)a.c.H * kD;
     // every row below lies in [rbase, t1 - 1] (t1 > t0), also when c0 is past the end
     const int rbase = min(max(t0 + c0 - 3, t0), t1 - 1);
@@ -136,29 +140,29 @@ __device__ __forceinline__ ChunkLoads load_chunk(const PrefillArgs &a, int tid, 
     const uint16_t *X[3] = {a.q, a.k, a.v};
     const uint32_t piece = 8u * (uint32_t)(tid & 15);
 #pragma unroll
-    for (int blk = 0; blk < 3; ++blk)
+    for (int blk = (kPart == 0 ? 0 : 1); blk < (kPart == 0 ? 1 : 3); ++blk)
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int row = (tid >> 4) + 32 * k;  // chunk row 0..63
             const uint32_t tok = (uint32_t)(min(max(t0 + c0 + row, t0), t1 - 1) - rbase);
             r.row[blk][k] = *reinterpret_cast<const u32x4 *>(X[blk] + ebase + (tok * (uint32_t)HD + piece));
         }
-    {
+    if constexpr (kPart == 1) {
         const int i = min(tid, 143);  // 3 blocks x 3 rows x 16 pieces
         const int blk = i / 48, row = (i % 48) >> 4;  // history row 0..2 = token c0 - 3 + row
         const uint16_t *src = blk == 0 ? a.q : (blk == 1 ? a.k : a.v);
         const uint32_t tok = (uint32_t)(min(max(t0 + c0 - 3 + row, t0), t1 - 1) - rbase);
         r.hist = *reinterpret_cast<const u32x4 *>(src + ebase + (tok * (uint32_t)HD + piece));
-    }
-    const int lane_t = 16 * wave_sub(tid >> 6) + (tid & 15);    // the prologue token of this lane
-    const int cbase = 64 * (tid >> 8) + 16 * ((tid >> 4) & 3);  // and its 16 channels
-    const int tauc = min(max(t0 + c0 + lane_t, t0), t1 - 1);
-    const uint32_t ztok = (uint32_t)(tauc - rbase);
+    } else {
+        const int lane_t = 16 * wave_sub(tid >> 6) + (tid & 15);    // the prologue token of this lane
+        const int cbase = 64 * (tid >> 8) + 16 * ((tid >> 4) & 3);  // and its 16 channels
+        const int tauc = min(max(t0 + c0 + lane_t, t0), t1 - 1);
+        const uint32_t ztok = (uint32_t)(tauc - rbase);
 #pragma unroll
-    for (int pc = 0; pc < 2; ++pc)
-        r.z[pc] = *reinterpret_cast<const u32x4 *>(a.z + ebase + (ztok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
-    r.b = bf2f(a.b[(size_t)tauc * a.c.H + h]);
-    return r;
+        for (int pc = 0; pc < 2; ++pc)
+            r.z[pc] = *reinterpret_cast<const u32x4 *>(a.z + ebase + (ztok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
+        r.b = bf2f(a.b[(size_t)tauc * a.c.H + h]);
+    }
 }
 
 // kChunked = false: the fused plan, one workgroup per (sequence, head) over all chunks.
@@ -274,7 +278,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     if (T > 0) {
         int tid_ = (int)threadIdx.x;
         asm volatile("" : "+v"(tid_));
-        ld = load_chunk(a, tid_, h, t0, t1, cbeg);
+        load_chunk<0>(ld, a, tid_, h, t0, t1, cbeg);
+        load_chunk<1>(ld, a, tid_, h, t0, t1, cbeg);
     }
     // (the prefetched z and b are marked consumed where no store is in flight: once here,
     //  and in every chunk before its stores; without that the compiler cannot count the
@@ -646,11 +651,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     sTb[sw64(16 * I + (lane >> 4), 16 * J + (lane & 15))] = (__bf16)0.0f;
                 }
             }
-            // The next chunk's raw inputs are requested now, to arrive during phases 3-5
-            // (past the last chunk this reloads clamped rows that are never used).  Issuing
-            // all eight waves' loads occupies the CU's memory pipe for about 2K cycles: the
-            // other waves do it while wave 3 inverts, and wave 3 after its inverse.
-            ld = load_chunk(a, tid_, h, t0, t1, c0 + kChunk);
+            // The next chunk's raw inputs are requested now and in the next phase, to arrive
+            // during phases 3-5 (past the last chunk this reloads clamped rows that are never
+            // used).  Issuing all eight waves' loads at once held the memory pipe for about
+            // 2K cycles and wave 3, issuing after its inverse, waited behind them: part 0
+            // here (the other waves while wave 3 inverts), part 1 after the off-diagonal
+            // blocks.
+            load_chunk<0>(ld, a, tid_, h, t0, t1, c0 + kChunk);
         }
         lds_barrier();
         // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ: wave J (< 3) walks
@@ -691,6 +698,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             if (w == 0) column(std::integral_constant<int, 0>{});
             else if (w == 1) column(std::integral_constant<int, 1>{});
             else if (w == 2) column(std::integral_constant<int, 2>{});
+            load_chunk<1>(ld, a, tid_, h, t0, t1, c0 + kChunk);
         }
         lds_barrier();
         // sT is dead: Q~ = q e^G into region 6

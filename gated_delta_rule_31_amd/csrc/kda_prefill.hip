@@ -438,12 +438,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 lds_read8(sDtb + cbase + 8 * pc, dtb);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int c = cbase + 8 * pc + j;
-                    float g = valid ? gmin * sigm(rate * (zz[j] + dtb[j])) : 0.f;
-                    g = row_scan16(g);
-                    if (lr == 15) sTot[sub * 128 + c] = g;
-                    gs[8 * pc + j] = g;
+                    const float g = valid ? gmin * sigm(rate * (zz[j] + dtb[j])) : 0.f;
+                    gs[8 * pc + j] = row_scan16(g);
                 }
+            }
+            // the sub-chunk's totals (the scan's last lane), one masked block of stores
+            if (lr == 15) {
+                lds_write8(sTot + sub * 128 + cbase, gs);
+                lds_write8(sTot + sub * 128 + cbase + 8, gs + 8);
             }
         }
         lds_barrier();

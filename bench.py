@@ -163,22 +163,29 @@ def bench_decode(args, dev):
                                     convs[i % n_sets], out=out, stream=side)
     g.replay()
     torch.cuda.synchronize()
+    # the timed replay: wall clock for ms_per_step, and HIP events on the stream the graph
+    # is replayed on for the kernels' average duration (the K launches run back to back)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    g0.record()
     g.replay()
+    g1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_graph_ms = g0.elapsed_time(g1) / args.steps
     alg = decode_bytes(B, H)
     state_b = 2 * B * H * D * D * 4
-    achieved = alg / (kern_ms * 1e-3) / 1e9
+    achieved = alg / (kern_graph_ms * 1e-3) / 1e9
     return dict(
-        B=B, H=H, ms_per_step=ms_step, kernel_ms=kern_ms, ms_per_step_eager=ms_eager,
+        B=B, H=H, ms_per_step=ms_step, kernel_ms=kern_graph_ms, ms_per_step_eager=ms_eager,
         state_gbs=state_b / (ms_step * 1e-3) / 1e9,
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                   "kernel": "decode_kernel", "alg_bytes_per_launch": alg,
-                  "kernel_avg_us": round(kern_ms * 1e3, 2),
-                  "state_only_frac": round(state_b / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                  "kernel_avg_us": round(kern_graph_ms * 1e3, 2),
+                  "kernel_avg_us_eager": round(kern_ms * 1e3, 2),
+                  "state_only_frac": round(state_b / (kern_graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     )
 
 

@@ -298,7 +298,7 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
 
 /* Device scratch kda_prefill needs for these sizes with cfg->prefill_path: 0 for the
  * fused layout; for the chunked one a table of 2(B+1) int32 (padded to 256 bytes) and one
- * 115,200-byte record per (chunk, head) for floor(N/64) + B chunks (the most that B
+ * 111,616-byte record per (chunk, head) for floor(N/64) + B chunks (the most that B
  * sequences of N tokens in total can need).  Returns 0 for arguments kda_prefill would
  * reject. */
 size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens);

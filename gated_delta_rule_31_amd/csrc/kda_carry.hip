@@ -42,6 +42,7 @@ constexpr int kPiecesPerWave = (kRecPieces + 7) / 8;  // 10 (the last ones repea
 __shared__ __align__(16) unsigned char carry_buf0[kBufBytes];
 __shared__ __align__(16) unsigned char carry_buf1[kBufBytes];
 __shared__ __align__(16) float carry_part[2][kChunk * 8];
+__shared__ int carry_order[kOrderMaxSeqs];  // longest-first workgroup order
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -60,8 +61,8 @@ template <bool kBf16>
 __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) {
     const int H = a.c.H;
     const int N = a.N;
-    const int seq = blockIdx.x / H;
-    const int h = blockIdx.x - seq * H;
+    const int h = blockIdx.x % H;
+    const int seq = seq_longest_first(a.cu_seqlens, a.B, N, blockIdx.x / H, carry_order);
     const size_t HD = (size_t)H * kD;
     int t0 = a.cu_seqlens[seq];
     int t1 = a.cu_seqlens[seq + 1];

@@ -92,6 +92,36 @@ __device__ __forceinline__ void lds_write8(float *p, const float *x) {
     *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 
+// ---- workgroup order of the per-(sequence, head) prefill kernels ----
+// Workgroups start in id order as compute units free up, so in a batch of unequal
+// sequences the last long ones would run alone at the end.  For batches of up to
+// kOrderMaxSeqs sequences the fused kernel and the carry give workgroup r*H + h the
+// r-th longest sequence (ties by index), longest first; larger batches keep index order.
+// Every workgroup ranks the lengths itself (at most kOrderMaxSeqs comparisons per lane),
+// so no table is needed.  order: kOrderMaxSeqs ints of LDS, free until the barrier.
+constexpr int kOrderMaxSeqs = 64;
+__device__ __forceinline__ int seq_longest_first(const int32_t *cu_seqlens, int B, int N, int r, int *order) {
+    if (B > kOrderMaxSeqs) return r;  // (uniform)
+    const int tid = (int)threadIdx.x;
+    auto len = [&](int s) {
+        const int t0 = min(max(cu_seqlens[s], 0), N);
+        return min(max(cu_seqlens[s + 1], t0), N) - t0;
+    };
+    if (tid < B) {
+        const int ls = len(tid);
+        int rank = 0;
+        for (int s = 0; s < B; ++s) {
+            const int l = len(s);
+            rank += (l > ls || (l == ls && s < tid)) ? 1 : 0;
+        }
+        order[rank] = tid;  // the ranks are a permutation of 0 .. B-1
+    }
+    __syncthreads();
+    const int seq = order[r];
+    __syncthreads();  // the caller reuses the space
+    return seq;
+}
+
 // ---- one chunk record of the chunk-parallel prefill ----
 // Everything a chunk contributes that does not depend on the state entering it.  The
 // first kRecPieces pieces of 1 KB are the MFMA operands of the carry's products in the

@@ -216,8 +216,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         nrec = a.chunk_start[seq + 1] - rec0;  // ceil(T / 64) for a valid batch
         cbeg = (sg - a.seg_start[seq]) * kSegChunks * kChunk;
     } else {
-        seq = blockIdx.x / H;
-        h = blockIdx.x - seq * H;
+        const int r = blockIdx.x / H;
+        h = blockIdx.x - r * H;
+        // (region 1 is free until the first chunk's operand rows)
+        seq = seq_longest_first(a.cu_seqlens, a.B, N, r, reinterpret_cast<int *>(smem + OFF_R1));
         cbeg = 0;
     }
     const size_t HD = (size_t)H * kD;

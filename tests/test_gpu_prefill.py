@@ -61,6 +61,18 @@ def test_varlen_small_with_empty_and_short_sequences(device, path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("B", [64, 80])
+def test_many_sequences(device, path, B):
+    # up to 64 sequences the fused kernel and the carry hand out sequences longest first
+    # (ties by index), above that in index order: both sides of the limit, with repeated
+    # lengths, empty and 1-token sequences, every (sequence, head) pair checked
+    rng = np.random.default_rng(150 + B)
+    lengths = rng.choice([0, 1, 7, 64, 65, 100, 130], size=B).tolist()
+    case = ki.prefill_case(150 + B, 2, lengths, True, f"many-{B}")
+    _run_and_check(case, device, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_zero_initial_state_multi_chunk(device, path):
     case = ki.prefill_case(121, 4, [333, 190], False, "zero-init")
     _run_and_check(case, device, path)

@@ -42,13 +42,15 @@ bool units_fit(int64_t rows, int64_t H, int64_t max_units) { return rows >= 0 &&
 struct PrefillPlan {
     int path;
     int64_t nchunk_cap, nseg_cap;
+    int seg_chunks;
     size_t table_bytes, workspace_bytes;
 };
 bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan) {
     const int64_t H = cfg->num_heads;
     if (B < 0 || N < 0 || N > INT32_MAX || !units_fit(B, H, kda::kMaxPrefillUnits)) return false;
     const int64_t cap = kda::chunk_cap(B, N);
-    const int64_t segs = kda::seg_cap(B, cap);
+    const int seg_chunks = kda::seg_chunks_for(B, N, H);
+    const int64_t segs = kda::seg_cap(B, cap, seg_chunks);
     const bool chunked_fits = cap * H <= kda::kMaxPrefillUnits && segs * H <= kda::kMaxPrefillUnits;
     int path = cfg->prefill_path;
     if (path == kda::kPathAuto) {
@@ -67,6 +69,7 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     plan->path = path;
     plan->nchunk_cap = cap;
     plan->nseg_cap = segs;
+    plan->seg_chunks = seg_chunks;
     plan->table_bytes = (size_t)((8 * (B + 1) + 255) / 256 * 256);  // chunk_start, seg_start
     plan->workspace_bytes =
         path == kda::kPathFused ? 0 : plan->table_bytes + (size_t)cap * (size_t)H * (size_t)kda::kRecBytes;
@@ -248,6 +251,7 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
     a.path = plan.path;
     a.nchunk_cap = (int)plan.nchunk_cap;
     a.nseg_cap = (int)plan.nseg_cap;
+    a.seg_chunks = plan.seg_chunks;
     const bool chunked = plan.path == kda::kPathChunked;
     a.chunk_start = chunked ? static_cast<int32_t *>(workspace) : nullptr;
     a.seg_start = chunked ? static_cast<int32_t *>(workspace) + (num_seqs + 1) : nullptr;

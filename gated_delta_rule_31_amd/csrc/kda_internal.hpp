@@ -97,11 +97,34 @@ constexpr int kRecBytes = 111616;
 // sum_s ceil(len_s / 64) <= floor(N / 64) + B.
 inline int64_t chunk_cap(int64_t B, int64_t N) { return N / kChunk + B; }
 
-// The chunk kernel gives each workgroup a segment of up to kSegChunks consecutive chunks
+// The chunk kernel gives each workgroup a segment of up to seg_chunks consecutive chunks
 // of one sequence (it loads a chunk's inputs while it finishes the one before).  A batch
-// whose sequences hold n_s records in total has at most floor(sum n_s / 4) + B segments.
-constexpr int kSegChunks = 4;
-inline int64_t seg_cap(int64_t B, int64_t nchunk_cap) { return nchunk_cap / kSegChunks + B; }
+// whose sequences hold n_s records in total has at most floor(sum n_s / seg_chunks) + B
+// segments.
+inline int64_t seg_cap(int64_t B, int64_t nchunk_cap, int seg_chunks) { return nchunk_cap / seg_chunks + B; }
+
+// Segment length: longer segments start fewer workgroups, and a workgroup's first chunk
+// costs about a quarter chunk more than the others (nothing overlaps its input loads),
+// but a last round of workgroups that fills only part of the compute units wastes the
+// rest.  Of 4, 8 and 16 chunks this takes the length whose rounds * (length + 1/4) is
+// least, the sequences taken at the batch's mean length (the shorter length on a tie).
+// Measured on MI355X with 96 heads: 16 for one 8K sequence, 8 for five of 130-3000
+// tokens, 4 for one 2K sequence, each the fastest of the three.
+inline int seg_chunks_for(int64_t B, int64_t N, int64_t H) {
+    if (B <= 0) return 4;
+    const int64_t chunks = (N + kChunk * B - 1) / (kChunk * B);  // mean length, rounded up
+    int best = 4;
+    double best_t = 0.0;
+    for (int s = 4; s <= 16; s *= 2) {
+        const int64_t wgs = B * ((chunks + s - 1) / s) * H;
+        const double t = (double)((wgs + kComputeUnits - 1) / kComputeUnits) * (s + 0.25);
+        if (s == 4 || t < best_t) {
+            best = s;
+            best_t = t;
+        }
+    }
+    return best;
+}
 
 struct PrefillArgs {
     MixerConsts c;
@@ -109,6 +132,7 @@ struct PrefillArgs {
     int path;            // kPathFused or kPathChunked (resolved)
     int nchunk_cap;      // chunked plan: records available in the workspace
     int nseg_cap;        // chunked plan: chunk-kernel workgroups per head
+    int seg_chunks;      // chunked plan: chunks per chunk-kernel segment (4, 8 or 16)
     int32_t *chunk_start;     // chunked plan: [B+1] first record row of each sequence
     int32_t *seg_start;       // chunked plan: [B+1] first segment of each sequence
     unsigned char *records;   // chunked plan: [nchunk_cap][H] records

@@ -166,7 +166,7 @@ __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, 
 }
 
 // kChunked = false: the fused plan, one workgroup per (sequence, head) over all chunks.
-// kChunked = true: one workgroup per (segment, head) computes up to kSegChunks
+// kChunked = true: one workgroup per (segment, head) computes up to a.seg_chunks
 // consecutive chunks of one sequence up to U' and stores each chunk's record instead of
 // carrying the state.
 template <bool kChunked>
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         seq = lo;
         rec0 = a.chunk_start[seq];
         nrec = a.chunk_start[seq + 1] - rec0;  // ceil(T / 64) for a valid batch
-        cbeg = (sg - a.seg_start[seq]) * kSegChunks * kChunk;
+        cbeg = (sg - a.seg_start[seq]) * a.seg_chunks * kChunk;
     } else {
         const int r = blockIdx.x / H;
         h = blockIdx.x - r * H;
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < (kPiecesPerWave + 1) / 2; ++i) asm volatile("" : "+v"(rec_src[i]));
     }
 
-    const int cend = kChunked ? min(min(cbeg + kSegChunks * kChunk, nrec * kChunk), T) : T;
+    const int cend = kChunked ? min(min(cbeg + a.seg_chunks * kChunk, nrec * kChunk), T) : T;
     // (inside the chunk loop every cross-wave dependency goes through LDS, so its
     //  barriers wait for LDS traffic only: the next chunk's loads and this chunk's output
     //  stores stay in flight across them)
@@ -926,7 +926,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 // ---- the chunked plan's tables ----
 // Sequence s owns record rows chunk_start[s] .. chunk_start[s+1]-1, one per chunk of 64
 // tokens (a partial last chunk included), in order, and chunk-kernel segments
-// seg_start[s] .. seg_start[s+1]-1 of up to kSegChunks of those rows each.  The running
+// seg_start[s] .. seg_start[s+1]-1 of up to seg_chunks of those rows each.  The running
 // record count is capped at nchunk_cap, so no record lies past the workspace even for a
 // cu_seqlens that breaks its contract (such a batch then loses its trailing chunks,
 // never memory safety); the segment count then stays within nseg_cap.
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs 
         const long long incl = block_scan(part, n);
         const long long tile = part[kTableThreads - 1];
         const long long lo = min(carry_c + incl - n, cap), hi = min(carry_c + incl, cap);
-        const long long nseg = (hi - lo + kSegChunks - 1) / kSegChunks;
+        const long long nseg = (hi - lo + a.seg_chunks - 1) / a.seg_chunks;
         __syncthreads();
         const long long incl_s = block_scan(part, nseg);
         const long long tile_s = part[kTableThreads - 1];

@@ -138,6 +138,18 @@ def test_layouts_agree_bitwise(device):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("lengths", [[8192], [1024, 2048, 3000, 500, 130]], ids=["1x8192", "mix5"])
+def test_layouts_agree_bitwise_long_segments(device, lengths):
+    """With 32 heads the chunked plan gives each chunk-kernel workgroup 16 chunks of the
+    8192-token sequence and 8 chunks of the five-sequence batch (the plan's segment length
+    follows B, N and H); the records, and so every output bit, stay the fused kernel's."""
+    case = ki.prefill_case(127, 32, lengths, True, "long-segments")
+    a = prefill_gpu(case, device, path=PATH_FUSED)
+    b = prefill_gpu(case, device, path=PATH_CHUNKED)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_packing_invariance(device, path):
     """Each sequence of a packed batch gives what it gives alone."""

@@ -25,11 +25,27 @@ __device__ __forceinline__ int xcd_contiguous(int i, int n) {
     return x * q + min(x, r) + (i >> 3);
 }
 
-// sum over groups of W consecutive lanes (W a power of two <= 64)
+// x + x of the lane that the DPP control ctrl names (the source lane always active)
+template <int kCtrl>
+__device__ __forceinline__ float add_dpp(float x) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum over groups of W consecutive lanes (W a power of two <= 64), the same bits on every
+// lane of a group: a butterfly over lane distances 1, 2, 4, ..., W/2, smallest first.
+// Distances 1 and 2 pair lanes l and l ^ d (DPP quad permutes); after them each quad
+// holds one value, so distances 4 and 8 may pair whole quads and octets by reversing
+// half-rows and rows (DPP mirrors) instead of by l ^ d; 16 and 32 take the permlane
+// swaps.  Each stage adds two equal-length partial sums, and both lanes of a pair add
+// the same two numbers.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    if constexpr (W >= 2) x = add_dpp<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+    if constexpr (W >= 4) x = add_dpp<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+    if constexpr (W >= 8) x = add_dpp<0x141>(x);  // row_half_mirror
+    if constexpr (W >= 16) x = add_dpp<0x140>(x); // row_mirror
+    if constexpr (W >= 32) x = add_xor16(x);
+    if constexpr (W >= 64) x = add_xor32(x);
     return x;
 }
 

@@ -169,8 +169,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         key_dots(s, sh_akq, rg, pa, pc);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            pa[c] += __shfl_xor(pa[c], 32, 64);
-            pc[c] += __shfl_xor(pc[c], 32, 64);
+            pa[c] = add_xor32(pa[c]);
+            pc[c] = add_xor32(pc[c]);
         }
         if (lane < 32) {
 #pragma unroll

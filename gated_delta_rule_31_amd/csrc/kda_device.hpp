@@ -45,6 +45,22 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// x[l] + x[l ^ 32] on every lane l of the wave.  v_permlane32_swap with both operands x
+// returns x of lane l & 31 in its first result and of lane l | 32 in its second, so one
+// instruction replaces the LDS permute (and its lane-index arithmetic) of a shuffle.  The
+// sum has the same two terms as x + shuffle_xor(x, 32), in the same order on lanes
+// 0..31 and swapped on lanes 32..63, which fp32 addition does not see: same bits.
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x[l] + x[l ^ 16], likewise with v_permlane16_swap (first result: lane l & ~16, second:
+// lane l | 16)
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroup barrier for LDS traffic.  __syncthreads() also waits for all of the wave's
 // outstanding global loads and stores (this GPU counts both on one counter), which would
 // expose the latency of prefetches and output stores meant to run across it; this one
@@ -169,8 +185,8 @@ __device__ __forceinline__ void rms_partials(const f32x4 (&o)[4], float *part, i
         s = __builtin_fmaf(o[tt][1], o[tt][1], s);
         s = __builtin_fmaf(o[tt][2], o[tt][2], s);
         s = __builtin_fmaf(o[tt][3], o[tt][3], s);
-        s += __shfl_xor(s, 16, 64);
-        s += __shfl_xor(s, 32, 64);
+        s = add_xor16(s);
+        s = add_xor32(s);
         if (lg == 0) part[(16 * tt + lr) * 8 + w] = s;
     }
 }
@@ -201,8 +217,8 @@ __device__ __forceinline__ void gated_rms_store(const f32x4 (&o)[4], const uint2
         const int tok = 16 * tt + lr;
         const float2 pp = *reinterpret_cast<const float2 *>(part + tok * 8 + 2 * lg);
         float s = pp.x + pp.y;
-        s += __shfl_xor(s, 16, 64);
-        s += __shfl_xor(s, 32, 64);
+        s = add_xor16(s);
+        s = add_xor32(s);
         const float rinv = __builtin_amdgcn_rsqf(s * (1.0f / kD) + rms_eps);
         const float gg[4] = {__uint_as_float(g4[tt].x << 16), __uint_as_float(g4[tt].x & 0xffff0000u),
                              __uint_as_float(g4[tt].y << 16), __uint_as_float(g4[tt].y & 0xffff0000u)};

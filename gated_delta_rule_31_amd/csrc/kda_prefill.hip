@@ -423,10 +423,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     ssk += uk[8 * pc + j] * uk[8 * pc + j];
                 }
             }
-            ssq += __shfl_xor(ssq, 16, 64);
-            ssq += __shfl_xor(ssq, 32, 64);
-            ssk += __shfl_xor(ssk, 16, 64);
-            ssk += __shfl_xor(ssk, 32, 64);
+            ssq = add_xor32(add_xor16(ssq));
+            ssk = add_xor32(add_xor16(ssk));
             if (lg == 0) {
                 sNorm[half * 128 + t] = ssq;
                 sNorm[half * 128 + 64 + t] = ssk;

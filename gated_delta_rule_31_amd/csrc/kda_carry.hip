@@ -145,8 +145,8 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
 
         // the previous chunk's epilogue (a full chunk: only the last can be partial)
         if (c > 0)
-            gated_rms_store<kBf16>(oprev, gprev, part_prev, nw, a.c.rms_eps, a.out, HD, h, t0 + c0 - kChunk, kChunk, w,
-                                   lr, lg);
+            gated_rms_store<kBf16, false>(oprev, gprev, part_prev, nw, a.c.rms_eps, a.out, HD, h, t0 + c0 - kChunk,
+                                          kChunk, 0, w, lr, lg);
         uint2 g4[4];
         load_gate4(g4, a.g, HD, h, t0 + c0, L, w, lr, lg);
 
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         // last record before the workgroup's LDS is released
         barrier_all_mem();
         const int cl = nrec - 1;
-        gated_rms_store<kBf16>(oprev, gprev, carry_part[cl & 1], nw, a.c.rms_eps, a.out, HD, h, t0 + cl * kChunk,
-                               min(kChunk, T - cl * kChunk), w, lr, lg);
+        gated_rms_store<kBf16, false>(oprev, gprev, carry_part[cl & 1], nw, a.c.rms_eps, a.out, HD, h,
+                                      t0 + cl * kChunk, min(kChunk, T - cl * kChunk), 0, w, lr, lg);
     }
 
     // ---- final state ----

@@ -791,9 +791,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         // ================= phase 5: state side and epilogue =================
         // (the epilogue's output-gate logits are loaded now, to arrive during the MFMAs)
         uint2 g4[4];
+        size_t lane_off;  // this lane's epilogue offset, for the gate loads and the output stores
         {
             KDA_LANE_IDS();
-            load_gate4(g4, a.g, HD, h, t0 + c0, L, w, lr, lg);
+            lane_off = epi_lane_offset(HD, w, lr, lg);
+            load_gate4_off(g4, a.g, HD, h, t0 + c0, L, lane_off, w, lr, lg);
         }
         float *sRms = reinterpret_cast<float *>(smem + OFF_R2);  // [64][8] (beta v is dead)
         f32x4 o[4];  // o[tt][i] = O[token 16tt + lr][value 16w + 4lg + i]
@@ -877,9 +879,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) nw[i] = sNw[16 * w + 4 * lg + i];
             if (a.c.out_bf16)
-                gated_rms_store<true>(o, g4, sRms, nw, a.c.rms_eps, a.out, HD, h, t0 + c0, L, w, lr, lg);
+                gated_rms_store<true, true>(o, g4, sRms, nw, a.c.rms_eps, a.out, HD, h, t0 + c0, L, lane_off, w, lr,
+                                            lg);
             else
-                gated_rms_store<false>(o, g4, sRms, nw, a.c.rms_eps, a.out, HD, h, t0 + c0, L, w, lr, lg);
+                gated_rms_store<false, true>(o, g4, sRms, nw, a.c.rms_eps, a.out, HD, h, t0 + c0, L, lane_off, w, lr,
+                                             lg);
         }
         lds_barrier();  // LDS is rewritten by the next chunk
     }

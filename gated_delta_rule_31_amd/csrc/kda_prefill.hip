@@ -7,7 +7,8 @@
 // and readout, the gated RMSNorm (written fp32 or bf16) and the final state / conv window
 // write.  Instantiated with kChunked, the same kernel instead stops each chunk after its
 // state-independent products and stores them as a record for the carry kernel
-// (kda_carry.hip), one workgroup per 4-chunk segment and head.
+// (kda_carry.hip), one workgroup per segment of 4, 8 or 16 chunks (the host's choice for
+// the batch's size) and head.
 //
 // Chunk algebra (exact rewrite of the token recurrence; G_t = sum_{s<=t} gk_s per key
 // channel, chunk-local):

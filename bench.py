@@ -110,6 +110,16 @@ def measured_decode_traffic():
         return None
 
 
+def recorded_digest(name: str):
+    """The digest of case `name`'s generated inputs recorded in tests/golden/input_digests.json
+    (None if absent)."""
+    try:
+        with open(os.path.join(ROOT, "tests", "golden", "input_digests.json")) as f:
+            return json.load(f).get(name)
+    except OSError:
+        return None
+
+
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -179,6 +189,7 @@ def bench_decode(args, dev):
     achieved = alg / (kern_graph_ms * 1e-3) / 1e9
     return dict(
         B=B, H=H, ms_per_step=ms_step, kernel_ms=kern_graph_ms, ms_per_step_eager=ms_eager,
+        inputs_sha256=ki.digest(case),
         state_gbs=state_b / (ms_step * 1e-3) / 1e9,
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -384,7 +395,8 @@ def bench_prefill(args, dev):
     torch.cuda.synchronize()
     ms16 = e0.elapsed_time(e1) / n
     byts16 = byts - N * H * D * 2  # outputs at 2 bytes instead of 4
-    return {"workload": "kda-prefill-1x8192tok-96head", "layout": args.prefill_path if path else
+    return {"workload": "kda-prefill-1x8192tok-96head", "inputs_sha256": ki.digest(case),
+            "layout": args.prefill_path if path else
             ("chunked" if ws_bytes else "fused"), "workspace_bytes": ws_bytes,
             "tokens_per_s": round(N / (ms * 1e-3), 1),
             "ms_per_call": round(ms, 4), "kernel_avg_us": round(kern_ms * 1e3, 2),
@@ -528,6 +540,7 @@ def main():
         log("prefill: 1 x 8192 tokens x 96 heads")
         try:
             pre = bench_prefill(args, dev)
+            pre["inputs_match_recorded"] = pre["inputs_sha256"] == recorded_digest("cfg2-prefill")
         except Exception as e:  # a prefill failure must not hide the decode line
             pre = {"error": str(e)}
         log(f"prefill: {pre}")
@@ -554,7 +567,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "kda-decode-64seq-96head", "batch": dec["B"], "heads": dec["H"], "head_dim": D,
-                   "state_dtype": "f32", "state_sets_rotated": 3,
+                   "state_dtype": "f32", "state_sets_rotated": 3, "inputs_sha256": dec["inputs_sha256"],
+                   "inputs_match_recorded": dec["inputs_sha256"] == recorded_digest("cfg1-decode"),
                    "timed_as": "one HIP graph replay of the K steps (eager launches: ms_per_step_eager)"},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,

@@ -24,6 +24,7 @@ states ``[B, H, D, D]``, conv states ``[B, 3*H*D, 3]``.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
@@ -251,3 +252,41 @@ def case3_lengths(n: int = 16) -> np.ndarray:
 def case3_prefill(H: int = 96) -> PrefillCase:
     """16 sequences of lengths U[512, 4096], nonzero initial states and conv states."""
     return prefill_case(3, H, case3_lengths(), True, "cfg3-prefill")
+
+
+# ---------------------------------------------------------------------------------
+# Digests
+# ---------------------------------------------------------------------------------
+
+def digest(case) -> str:
+    """SHA-256 of a case's generated bytes: for each array, in a fixed order, its name,
+    dtype and shape, then its bytes (C order).  A decode case covers its parameters,
+    states and every step's token inputs; a prefill case its cu_seqlens, parameters,
+    token inputs and initial states (absent ones named with no bytes)."""
+    h = hashlib.sha256()
+
+    def put(name, a):
+        if a is None:
+            h.update(f"{name}:none;".encode())
+            return
+        a = np.ascontiguousarray(a)
+        h.update(f"{name}:{a.dtype.str}:{a.shape};".encode())
+        h.update(a.tobytes())
+
+    p = case.params
+    for n in ("conv_w", "dt_bias", "A_log", "norm_w"):
+        put(n, getattr(p, n))
+    if isinstance(case, DecodeCase):
+        put("state", case.state)
+        put("conv_state", case.conv_state)
+        for i in range(case.n_steps):
+            x = case.step(i)
+            for n in "qkvzbg":
+                put(f"step{i}.{n}", getattr(x, n))
+    else:
+        put("cu_seqlens", case.cu_seqlens)
+        for n in "qkvzbg":
+            put(n, getattr(case.x, n))
+        put("initial_state", case.initial_state)
+        put("initial_conv_state", case.initial_conv_state)
+    return h.hexdigest()

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi",
                     "kda_decode_multi_slots", "kda_prefill", "kda_prefill_workspace_bytes",
                     "kda_state_copy", "kda_status_str", "kda_abi_version")
-ABI_VERSION = 7
+ABI_VERSION = 8
 HEAD_DIM = 128
 CONV = 4
 
@@ -79,18 +79,20 @@ def _load() -> ctypes.CDLL:
     L.kda_config_default.restype = _CConfig
     L.kda_config_default.argtypes = []
     L.kda_decode_step.restype = ctypes.c_int
-    L.kda_decode_step.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32] + [fp] * 13 + [vp]
+    i64 = ctypes.c_int64
+    L.kda_decode_step.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32] + [fp] * 3 + [i64] + [fp] * 10 + [vp]
     L.kda_decode_step_slots.restype = ctypes.c_int
-    L.kda_decode_step_slots.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32, vp, ctypes.c_int32] + [fp] * 13 + [vp]
+    L.kda_decode_step_slots.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, vp, ctypes.c_int32] + [fp] * 3 +
+                                        [i64] + [fp] * 10 + [vp])
     L.kda_decode_multi.restype = ctypes.c_int
-    L.kda_decode_multi.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [fp] * 15 +
-                                   [vp])
+    L.kda_decode_multi.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [fp] * 3 +
+                                   [i64] + [fp] * 12 + [vp])
     L.kda_decode_multi_slots.restype = ctypes.c_int
     L.kda_decode_multi_slots.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp, vp,
-                                          ctypes.c_int32] + [fp] * 15 + [vp])
+                                          ctypes.c_int32] + [fp] * 3 + [i64] + [fp] * 12 + [vp])
     L.kda_prefill.restype = ctypes.c_int
-    L.kda_prefill.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 6 +
-                              [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp, ctypes.c_size_t, vp])
+    L.kda_prefill.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 3 + [i64] +
+                              [vp] * 3 + [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp, ctypes.c_size_t, vp])
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32]
     L.kda_state_copy.restype = ctypes.c_int
@@ -127,6 +129,41 @@ def _ptr(t: torch.Tensor | None, dtype: torch.dtype, shape: tuple, name: str):
     return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
 
 
+def _rows_ptr(t: torch.Tensor, dtype: torch.dtype, shape: tuple, name: str):
+    """Pointer and row stride (elements) of a q/k/v tensor: the given shape, channels
+    contiguous, and its token rows (every index but the last, flattened) equally spaced,
+    e.g. a slice of the last dimension of a fused [..., 3*H*D] projection output."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if t.numel() == 0:
+        return None, 0
+    if t.stride()[-1] != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name}: channels must be contiguous")
+    # the row dimensions (all but the last) that hold more than one index, innermost first
+    dims = [(t.shape[d], t.stride(d)) for d in range(t.dim() - 2, -1, -1) if t.shape[d] > 1]
+    ld = dims[0][1] if dims else shape[-1]
+    span = ld
+    for n, st in dims:
+        if st != span:
+            raise ValueError(f"{name}: token rows must be equally spaced")
+        span = st * n
+    return ctypes.c_void_p(t.data_ptr()), int(ld)
+
+
+def _qkv(q, k, v, dtype, shape):
+    """Pointers of q, k, v and their common row stride (0 when all are dense)."""
+    (pq, lq), (pk, lk), (pv, lv) = (_rows_ptr(x, dtype, shape, n) for x, n in ((q, "q"), (k, "k"), (v, "v")))
+    lds = {l for l, p in ((lq, pq), (lk, pk), (lv, pv)) if p is not None}
+    if len(lds) > 1:
+        raise ValueError(f"q, k, v must share one row stride, got {sorted(lds)}")
+    ld = lds.pop() if lds else 0
+    return pq, pk, pv, (0 if ld == shape[-1] else ld)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -135,7 +172,8 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def kda_decode_step(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state, conv_state,
                     out=None, stream=None) -> torch.Tensor:
-    """One token per sequence.  q,k,v,z,g: [B, H*D] fp32; b: [B, H]; state [B,H,D,D] and
+    """One token per sequence.  q,k,v,z,g: [B, H*D] fp32 (q, k, v may be row-strided views,
+    e.g. of one [B, 3*H*D] projection output); b: [B, H]; state [B,H,D,D] and
     conv_state [B,3*H*D,3] are updated in place.  Returns out [B, H*D] (cfg.out_dtype)."""
     H, D = cfg.num_heads, cfg.head_dim
     B = q.shape[0]
@@ -144,7 +182,7 @@ def kda_decode_step(cfg: KdaConfig, q, k, v, z, b, g, conv_w, A_log, dt_bias, no
     if out is None:
         out = torch.empty((B, HD), dtype=cfg.out_dtype, device=q.device)
     args = [
-        _ptr(q, f32, (B, HD), "q"), _ptr(k, f32, (B, HD), "k"), _ptr(v, f32, (B, HD), "v"),
+        *_qkv(q, k, v, f32, (B, HD)),
         _ptr(z, f32, (B, HD), "z"), _ptr(b, f32, (B, H), "b"), _ptr(g, f32, (B, HD), "g"),
         _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
         _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
@@ -173,7 +211,7 @@ def kda_decode_step_slots(cfg: KdaConfig, slots, q, k, v, z, b, g, conv_w, A_log
     if out is None:
         out = torch.empty((B, HD), dtype=cfg.out_dtype, device=q.device)
     args = [
-        _ptr(q, f32, (B, HD), "q"), _ptr(k, f32, (B, HD), "k"), _ptr(v, f32, (B, HD), "v"),
+        *_qkv(q, k, v, f32, (B, HD)),
         _ptr(z, f32, (B, HD), "z"), _ptr(b, f32, (B, H), "b"), _ptr(g, f32, (B, HD), "g"),
         _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
         _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
@@ -203,7 +241,7 @@ def _decode_multi(cfg, slots, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, 
     if out is None:
         out = torch.empty((B, T, HD), dtype=cfg.out_dtype, device=q.device)
     args = [
-        _ptr(q, f32, (B, T, HD), "q"), _ptr(k, f32, (B, T, HD), "k"), _ptr(v, f32, (B, T, HD), "v"),
+        *_qkv(q, k, v, f32, (B, T, HD)),
         _ptr(z, f32, (B, T, HD), "z"), _ptr(b, f32, (B, T, H), "b"), _ptr(g, f32, (B, T, HD), "g"),
         _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
         _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),
@@ -253,8 +291,8 @@ def kda_prefill_workspace_bytes(cfg: KdaConfig, num_seqs: int, total_tokens: int
 def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
                 initial_state=None, initial_conv_state=None, out=None, final_state=None,
                 final_conv_state=None, workspace=None, stream=None):
-    """Varlen prefill.  cu_seqlens: int32 [B+1] on the GPU; q,k,v,z,g: [N, H*D] bf16;
-    b: [N, H] bf16.  Returns (out [N, H*D] (cfg.out_dtype), final_state, final_conv_state).
+    """Varlen prefill.  cu_seqlens: int32 [B+1] on the GPU; q,k,v,z,g: [N, H*D] bf16 (q, k,
+    v may be row-strided views, e.g. of one [N, 3*H*D] projection output); b: [N, H] bf16.  Returns (out [N, H*D] (cfg.out_dtype), final_state, final_conv_state).
     ``final_state`` may be ``initial_state`` (in-place carry)."""
     H, D = cfg.num_heads, cfg.head_dim
     B = cu_seqlens.shape[0] - 1
@@ -276,7 +314,7 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
         ws_bytes = workspace.numel() * workspace.element_size()
     args = [
         _ptr(cu_seqlens, torch.int32, (B + 1,), "cu_seqlens"),
-        _ptr(q, bf, (N, HD), "q"), _ptr(k, bf, (N, HD), "k"), _ptr(v, bf, (N, HD), "v"),
+        *_qkv(q, k, v, bf, (N, HD)),
         _ptr(z, bf, (N, HD), "z"), _ptr(b, bf, (N, H), "b"), _ptr(g, bf, (N, HD), "g"),
         _ptr(conv_w, f32, (3 * HD, CONV), "conv_w"), _ptr(A_log, f32, (H,), "A_log"),
         _ptr(dt_bias, f32, (HD,), "dt_bias"), _ptr(norm_w, f32, (D,), "norm_w"),

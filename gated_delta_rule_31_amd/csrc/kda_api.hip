@@ -15,11 +15,51 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A byte range of a buffer the call reads or writes (null or empty: no range).
+struct Span {
+    const void *p;
+    size_t n;
+};
+bool overlaps(Span a, Span b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+    return x < y + b.n && y < x + a.n;
+}
+// The byte span of `rows` rows of `width` elements, `ld` elements apart.
+Span rows_span(const void *p, int64_t rows, int64_t width, int64_t ld, size_t esize) {
+    if (rows <= 0) return {p, 0};
+    return {p, ((size_t)(rows - 1) * (size_t)ld + (size_t)width) * esize};
+}
+// Every output is disjoint from every input and from the other outputs, except that
+// output i may coincide exactly with its allowed alias alias[i] (same pointer, same size).
+kda_status check_disjoint(const Span *outs, const Span *alias, int n_out, const Span *ins, int n_in) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j) {
+            const bool exact = alias && alias[i].p && ins[j].p == alias[i].p && outs[i].p == alias[i].p &&
+                               outs[i].n == ins[j].n;
+            if (!exact && overlaps(outs[i], ins[j])) return KDA_ERR_OVERLAP;
+        }
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], outs[j])) return KDA_ERR_OVERLAP;
+    }
+    return KDA_OK;
+}
+// qkv_row_stride: 0 selects dense rows (H*D); otherwise >= H*D, a multiple of 8 (16-byte
+// rows for bf16 and fp32) and at most kMaxRowStride.
+bool resolve_stride(int64_t stride, int H, size_t *ld) {
+    const int64_t HD = (int64_t)H * kda::kD;
+    if (stride == 0) stride = HD;
+    if (stride < HD || stride % 8 != 0 || stride > kda::kMaxRowStride) return false;
+    *ld = (size_t)stride;
+    return true;
+}
+
 bool finite_nonneg(float x) { return isfinite(x) && x >= 0.0f; }
 
 kda_status check_config(const kda_config *cfg, kda::MixerConsts *out) {
     if (!cfg) return KDA_ERR_NULL_ARG;
-    if (cfg->num_heads < 1 || cfg->head_dim != kda::kD || cfg->conv_size != kda::kConv)
+    if (cfg->num_heads < 1 || cfg->num_heads > kda::kMaxHeads || cfg->head_dim != kda::kD ||
+        cfg->conv_size != kda::kConv)
         return KDA_ERR_BAD_CONFIG;
     if (!isfinite(cfg->gate_lower_bound) || !finite_nonneg(cfg->l2_eps) || !finite_nonneg(cfg->rms_eps) ||
         !isfinite(cfg->q_scale))
@@ -76,9 +116,65 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     return true;
 }
 
+// The byte spans of the fp32 per-token inputs and parameters of a decode call over `rows`
+// token rows (q, k, v strided), in the order q, k, v, z, b, g, conv_w, A_log, dt_bias,
+// norm_w.
+void decode_input_spans(Span *sp, int64_t rows, int H, size_t ld, const float *q, const float *k, const float *v,
+                        const float *z, const float *b, const float *g, const float *conv_w, const float *A_log,
+                        const float *dt_bias, const float *norm_w) {
+    const int64_t HD = (int64_t)H * kda::kD;
+    sp[0] = rows_span(q, rows, HD, ld, 4);
+    sp[1] = rows_span(k, rows, HD, ld, 4);
+    sp[2] = rows_span(v, rows, HD, ld, 4);
+    sp[3] = rows_span(z, rows, HD, HD, 4);
+    sp[4] = rows_span(b, rows, H, H, 4);
+    sp[5] = rows_span(g, rows, HD, HD, 4);
+    sp[6] = {conv_w, (size_t)3 * HD * kda::kConv * 4};
+    sp[7] = {A_log, (size_t)H * 4};
+    sp[8] = {dt_bias, (size_t)HD * 4};
+    sp[9] = {norm_w, (size_t)kda::kD * 4};
+}
+
+// kda_decode_step and (pooled) kda_decode_step_slots
+kda_status decode_one(const kda_config *cfg, int32_t batch, const int32_t *slots, int32_t pool_size, bool pooled,
+                      const float *q, const float *k, const float *v, int64_t qkv_row_stride, const float *z,
+                      const float *b, const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
+                      const float *norm_w, float *state, float *conv_state, void *out, void *stream) {
+    kda::DecodeArgs a;
+    kda_status st = check_config(cfg, &a.c);
+    if (st != KDA_OK) return st;
+    if (batch < 0 || pool_size < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits)) return KDA_ERR_BAD_SHAPE;
+    if (!resolve_stride(qkv_row_stride, a.c.H, &a.qkv_ld)) return KDA_ERR_BAD_SHAPE;
+    if (batch == 0 || (pooled && pool_size == 0)) return KDA_OK;  // nothing to do / every row skipped
+    const void *ptrs[] = {q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state, conv_state, out};
+    if (pooled && !slots) return KDA_ERR_NULL_ARG;
+    for (const void *p : ptrs)
+        if (!p) return KDA_ERR_NULL_ARG;
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    if (pooled && (reinterpret_cast<uintptr_t>(slots) & 3u) != 0) return KDA_ERR_MISALIGNED;
+    const int64_t HD = (int64_t)a.c.H * kda::kD;
+    const int64_t entries = pooled ? pool_size : batch;
+    Span ins[11];
+    decode_input_spans(ins, batch, a.c.H, a.qkv_ld, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w);
+    ins[10] = {slots, pooled ? (size_t)batch * 4 : 0};
+    const Span outs[3] = {{state, (size_t)entries * HD * kda::kD * 4},
+                          {conv_state, (size_t)entries * 3 * HD * (kda::kConv - 1) * 4},
+                          {out, (size_t)batch * HD * (a.c.out_bf16 ? 2 : 4)}};
+    if ((st = check_disjoint(outs, nullptr, 3, ins, 11)) != KDA_OK) return st;
+    a.B = batch;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
+    a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
+    a.state = state; a.conv_state = conv_state; a.out = out;
+    a.slots = pooled ? slots : nullptr;
+    a.pool = pooled ? pool_size : 0;
+    return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
 
 kda_config kda_config_default(void) {
     kda_config c;
@@ -95,53 +191,21 @@ kda_config kda_config_default(void) {
 }
 
 kda_status kda_decode_step(const kda_config *cfg, int32_t batch, const float *q, const float *k,
-                           const float *v, const float *z, const float *b, const float *g,
+                           const float *v, int64_t qkv_row_stride, const float *z, const float *b, const float *g,
                            const float *conv_w, const float *A_log, const float *dt_bias,
                            const float *norm_w, float *state, float *conv_state, void *out,
                            void *stream) {
-    kda::DecodeArgs a;
-    kda_status st = check_config(cfg, &a.c);
-    if (st != KDA_OK) return st;
-    if (batch < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits)) return KDA_ERR_BAD_SHAPE;
-    if (batch == 0) return KDA_OK;
-    const void *ptrs[] = {q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state, conv_state, out};
-    for (const void *p : ptrs)
-        if (!p) return KDA_ERR_NULL_ARG;
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return KDA_ERR_MISALIGNED;
-    a.B = batch;
-    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
-    a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
-    a.state = state; a.conv_state = conv_state; a.out = out;
-    a.slots = nullptr;
-    a.pool = 0;
-    return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return decode_one(cfg, batch, nullptr, 0, false, q, k, v, qkv_row_stride, z, b, g, conv_w, A_log, dt_bias, norm_w,
+                      state, conv_state, out, stream);
 }
 
 kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int32_t *slots, int32_t pool_size,
-                                 const float *q, const float *k, const float *v, const float *z, const float *b,
-                                 const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
-                                 const float *norm_w, float *state_pool, float *conv_pool, void *out,
-                                 void *stream) {
-    kda::DecodeArgs a;
-    kda_status st = check_config(cfg, &a.c);
-    if (st != KDA_OK) return st;
-    if (batch < 0 || pool_size < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits)) return KDA_ERR_BAD_SHAPE;
-    if (batch == 0 || pool_size == 0) return KDA_OK;  // every row would be skipped
-    const void *ptrs[] = {q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_pool, conv_pool, out};
-    if (!slots) return KDA_ERR_NULL_ARG;
-    for (const void *p : ptrs)
-        if (!p) return KDA_ERR_NULL_ARG;
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return KDA_ERR_MISALIGNED;
-    if ((reinterpret_cast<uintptr_t>(slots) & 3u) != 0) return KDA_ERR_MISALIGNED;
-    a.B = batch;
-    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
-    a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
-    a.state = state_pool; a.conv_state = conv_pool; a.out = out;
-    a.slots = slots;
-    a.pool = pool_size;
-    return kda::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+                                 const float *q, const float *k, const float *v, int64_t qkv_row_stride,
+                                 const float *z, const float *b, const float *g, const float *conv_w,
+                                 const float *A_log, const float *dt_bias, const float *norm_w, float *state_pool,
+                                 float *conv_pool, void *out, void *stream) {
+    return decode_one(cfg, batch, slots, pool_size, true, q, k, v, qkv_row_stride, z, b, g, conv_w, A_log, dt_bias,
+                      norm_w, state_pool, conv_pool, out, stream);
 }
 
 }  // extern "C"
@@ -151,7 +215,7 @@ namespace {
 // pooled: the slot-indexed form (slots required)
 kda_status decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
                         bool pooled, const int32_t *slots, int32_t pool_size, const float *q, const float *k, const float *v,
-                        const float *z, const float *b, const float *g, const float *conv_w, const float *A_log,
+                        int64_t qkv_row_stride, const float *z, const float *b, const float *g, const float *conv_w, const float *A_log,
                         const float *dt_bias, const float *norm_w, const float *state_in, float *state_out,
                         const float *conv_state_in, float *conv_state_out, void *out, void *stream) {
     kda::DecodeMultiArgs a;
@@ -160,6 +224,7 @@ kda_status decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, co
     if (batch < 0 || tokens < 0 || pool_size < 0 || !units_fit(batch, a.c.H, kda::kMaxDecodeUnits) ||
         !units_fit(batch, tokens, INT32_MAX))
         return KDA_ERR_BAD_SHAPE;
+    if (!resolve_stride(qkv_row_stride, a.c.H, &a.qkv_ld)) return KDA_ERR_BAD_SHAPE;
     if (batch == 0) return KDA_OK;
     if (tokens == 0) return KDA_ERR_BAD_SHAPE;
     if (pooled && !slots) return KDA_ERR_NULL_ARG;
@@ -172,6 +237,23 @@ kda_status decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, co
         if (!aligned16(p)) return KDA_ERR_MISALIGNED;
     if ((reinterpret_cast<uintptr_t>(n_tokens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(slots) & 3u) != 0)
         return KDA_ERR_MISALIGNED;
+    {
+        const int64_t HD = (int64_t)a.c.H * kda::kD;
+        const int64_t entries = pooled ? pool_size : batch;
+        const size_t sbytes = (size_t)entries * HD * kda::kD * 4;
+        const size_t cbytes = (size_t)entries * 3 * HD * (kda::kConv - 1) * 4;
+        Span ins[14];
+        decode_input_spans(ins, (int64_t)batch * tokens, a.c.H, a.qkv_ld, q, k, v, z, b, g, conv_w, A_log, dt_bias,
+                           norm_w);
+        ins[10] = {state_in, sbytes};
+        ins[11] = {conv_state_in, cbytes};
+        ins[12] = {n_tokens, n_tokens ? (size_t)batch * 4 : 0};
+        ins[13] = {pooled ? slots : nullptr, pooled ? (size_t)batch * 4 : 0};
+        const Span outs[3] = {{state_out, sbytes}, {conv_state_out, cbytes},
+                              {out, (size_t)batch * tokens * HD * (a.c.out_bf16 ? 2 : 4)}};
+        const Span alias[3] = {{state_in, sbytes}, {conv_state_in, cbytes}, {nullptr, 0}};
+        if ((st = check_disjoint(outs, alias, 3, ins, 14)) != KDA_OK) return st;
+    }
     a.B = batch;
     a.T = tokens;
     a.n_tokens = n_tokens;
@@ -190,21 +272,25 @@ kda_status decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, co
 extern "C" {
 
 kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
-                            const float *q, const float *k, const float *v, const float *z, const float *b,
+                            const float *q, const float *k, const float *v, int64_t qkv_row_stride,
+                            const float *z, const float *b,
                             const float *g, const float *conv_w, const float *A_log, const float *dt_bias,
                             const float *norm_w, const float *state_in, float *state_out,
                             const float *conv_state_in, float *conv_state_out, void *out, void *stream) {
-    return decode_multi(cfg, batch, tokens, n_tokens, false, nullptr, 0, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
+    return decode_multi(cfg, batch, tokens, n_tokens, false, nullptr, 0, q, k, v, qkv_row_stride, z, b, g, conv_w, A_log,
+                        dt_bias, norm_w,
                         state_in, state_out, conv_state_in, conv_state_out, out, stream);
 }
 
 kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
                                   const int32_t *slots, int32_t pool_size, const float *q, const float *k,
-                                  const float *v, const float *z, const float *b, const float *g,
+                                  const float *v, int64_t qkv_row_stride, const float *z, const float *b,
+                                  const float *g,
                                   const float *conv_w, const float *A_log, const float *dt_bias,
                                   const float *norm_w, const float *state_in, float *state_out,
                                   const float *conv_state_in, float *conv_state_out, void *out, void *stream) {
-    return decode_multi(cfg, batch, tokens, n_tokens, true, slots, pool_size, q, k, v, z, b, g, conv_w, A_log, dt_bias,
+    return decode_multi(cfg, batch, tokens, n_tokens, true, slots, pool_size, q, k, v, qkv_row_stride, z, b, g, conv_w,
+                        A_log, dt_bias,
                         norm_w, state_in, state_out, conv_state_in, conv_state_out, out, stream);
 }
 
@@ -217,7 +303,8 @@ size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int3
 
 kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
                        const int32_t *cu_seqlens, const uint16_t *q, const uint16_t *k,
-                       const uint16_t *v, const uint16_t *z, const uint16_t *b, const uint16_t *g,
+                       const uint16_t *v, int64_t qkv_row_stride, const uint16_t *z, const uint16_t *b,
+                       const uint16_t *g,
                        const float *conv_w, const float *A_log, const float *dt_bias, const float *norm_w,
                        const float *initial_state, const float *initial_conv_state, void *out,
                        float *final_state, float *final_conv_state, void *workspace,
@@ -228,6 +315,7 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
     if (cfg->prefill_path < kda::kPathAuto || cfg->prefill_path > kda::kPathChunked) return KDA_ERR_BAD_CONFIG;
     PrefillPlan plan;
     if (!plan_prefill(cfg, num_seqs, total_tokens, &plan)) return KDA_ERR_BAD_SHAPE;
+    if (!resolve_stride(qkv_row_stride, a.c.H, &a.qkv_ld)) return KDA_ERR_BAD_SHAPE;
     if (num_seqs == 0) return total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
     const void *req[] = {cu_seqlens, conv_w, A_log, dt_bias, norm_w, final_state, final_conv_state};
     for (const void *p : req)
@@ -246,6 +334,23 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_MISALIGNED;
     if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace)) return KDA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
+    {
+        const int64_t H = a.c.H, HD = H * kda::kD, N = total_tokens, B = num_seqs;
+        const size_t sbytes = (size_t)B * HD * kda::kD * 4;
+        const size_t cbytes = (size_t)B * 3 * HD * (kda::kConv - 1) * 4;
+        const Span ins[13] = {{cu_seqlens, (size_t)(B + 1) * 4},
+                              rows_span(q, N, HD, a.qkv_ld, 2), rows_span(k, N, HD, a.qkv_ld, 2),
+                              rows_span(v, N, HD, a.qkv_ld, 2), rows_span(z, N, HD, HD, 2),
+                              rows_span(b, N, H, H, 2), rows_span(g, N, HD, HD, 2),
+                              {conv_w, (size_t)3 * HD * kda::kConv * 4}, {A_log, (size_t)H * 4},
+                              {dt_bias, (size_t)HD * 4}, {norm_w, (size_t)kda::kD * 4},
+                              {initial_state, initial_state ? sbytes : 0},
+                              {initial_conv_state, initial_conv_state ? cbytes : 0}};
+        const Span outs[4] = {{out, (size_t)N * HD * (a.c.out_bf16 ? 2 : 4)}, {final_state, sbytes},
+                              {final_conv_state, cbytes}, {workspace, plan.workspace_bytes}};
+        const Span alias[4] = {{nullptr, 0}, {initial_state, sbytes}, {initial_conv_state, cbytes}, {nullptr, 0}};
+        if ((st = check_disjoint(outs, alias, 4, ins, 13)) != KDA_OK) return st;
+    }
     a.B = num_seqs;
     a.N = total_tokens;
     a.path = plan.path;
@@ -297,7 +402,7 @@ kda_status kda_state_copy(const kda_config *cfg, int32_t n, const float *src_sta
     if ((src_state != dst_state && !disjoint(src_state, ss_n, dst_state, ds_n)) ||
         (src_conv != dst_conv && !disjoint(src_conv, sc_n, dst_conv, dc_n)) ||
         !disjoint(src_state, ss_n, dst_conv, dc_n) || !disjoint(src_conv, sc_n, dst_state, ds_n))
-        return KDA_ERR_BAD_SHAPE;
+        return KDA_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int32_t i = 0; i < n; ++i) {
         const size_t si = (size_t)src_slots[i], di = (size_t)dst_slots[i];
@@ -305,10 +410,10 @@ kda_status kda_state_copy(const kda_config *cfg, int32_t n, const float *src_sta
         char *ds = reinterpret_cast<char *>(dst_state) + di * state_bytes;
         const char *sc = reinterpret_cast<const char *>(src_conv) + si * conv_bytes;
         char *dc = reinterpret_cast<char *>(dst_conv) + di * conv_bytes;
-        if (ss == ds) continue;  // an entry onto itself
-        if (hipMemcpyAsync(ds, ss, state_bytes, hipMemcpyDefault, s) != hipSuccess ||
-            hipMemcpyAsync(dc, sc, conv_bytes, hipMemcpyDefault, s) != hipSuccess)
-            return KDA_ERR_LAUNCH;
+        // an entry onto itself is left as it is; the state and the conv windows are
+        // decided separately (one may map onto itself while the other does not)
+        if (ss != ds && hipMemcpyAsync(ds, ss, state_bytes, hipMemcpyDefault, s) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (sc != dc && hipMemcpyAsync(dc, sc, conv_bytes, hipMemcpyDefault, s) != hipSuccess) return KDA_ERR_LAUNCH;
     }
     return KDA_OK;
 }
@@ -317,11 +422,12 @@ const char *kda_status_str(kda_status s) {
     switch (s) {
         case KDA_OK: return "ok";
         case KDA_ERR_NULL_ARG: return "a required pointer is NULL";
-        case KDA_ERR_BAD_CONFIG: return "unsupported config (head_dim must be 128, conv_size 4, num_heads >= 1, finite eps >= 0, prefill_path 0..2, out_dtype 0..1)";
+        case KDA_ERR_BAD_CONFIG: return "unsupported config (head_dim must be 128, conv_size 4, num_heads 1..65536, finite eps >= 0, prefill_path 0..2, out_dtype 0..1)";
         case KDA_ERR_BAD_SHAPE: return "negative, inconsistent or too large sizes";
         case KDA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
         case KDA_ERR_WORKSPACE: return "workspace too small";
         case KDA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch or a copy";
+        case KDA_ERR_OVERLAP: return "an output buffer overlaps an input or another output";
     }
     return "unknown status";
 }

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
             const int tok = t1 - 3 + j;
             const uint16_t *src = blk == 0 ? a.q : (blk == 1 ? a.k : a.v);
             if (tok >= t0)
-                win[j] = bf2f(src[(size_t)tok * HD + (size_t)h * kD + cc]);
+                win[j] = bf2f(src[(size_t)tok * a.qkv_ld + (size_t)h * kD + cc]);
             else
                 win[j] = a.initial_conv_state ? a.initial_conv_state[conv_seq + ch * 3 + (tok - t0 + 3)] : 0.f;
         }

@@ -69,7 +69,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     __shared__ float sh_part[4][2][kD];  // per-wave partial S^T(alpha k), S^T(alpha q)
 
     // ---- 2. prologue: conv + SiLU (+ sums for the L2 norms), gates ----
-    const size_t tok = (size_t)bs * HD + (size_t)h * kD;  // this head's channels of the token row
+    const size_t tok = (size_t)bs * HD + (size_t)h * kD;        // this head's channels of the token row
+    const size_t tokx = (size_t)bs * a.qkv_ld + (size_t)h * kD;  // the same in the q, k, v rows
     float *cstate = a.conv_state + (size_t)slot * 3 * HD * 3;
     float uq = 0.f, uk = 0.f;
     if (tid < kD) {
@@ -80,8 +81,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const float4 wk = *reinterpret_cast<const float4 *>(a.conv_w + chk * 4);
         float *wnq = cstate + chq * 3;
         float *wnk = cstate + chk * 3;
-        const float q0 = wnq[0], q1 = wnq[1], q2 = wnq[2], xq = a.q[tok + i];
-        const float k0 = wnk[0], k1 = wnk[1], k2 = wnk[2], xk = a.k[tok + i];
+        const float q0 = wnq[0], q1 = wnq[1], q2 = wnq[2], xq = a.q[tokx + i];
+        const float k0 = wnk[0], k1 = wnk[1], k2 = wnk[2], xk = a.k[tokx + i];
         wnq[0] = q1; wnq[1] = q2; wnq[2] = xq;
         wnk[0] = k1; wnk[1] = k2; wnk[2] = xk;
         uq = silu(conv4(wq, q0, q1, q2, xq));
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const size_t chv = 2 * HD + (size_t)h * kD + i;
         const float4 wv = *reinterpret_cast<const float4 *>(a.conv_w + chv * 4);
         float *wnv = cstate + chv * 3;
-        const float v0 = wnv[0], v1 = wnv[1], v2 = wnv[2], xv = a.v[tok + i];
+        const float v0 = wnv[0], v1 = wnv[1], v2 = wnv[2], xv = a.v[tokx + i];
         wnv[0] = v1; wnv[1] = v2; wnv[2] = xv;
         sh_v[i] = silu(conv4(wv, v0, v1, v2, xv));
         const float rate = expf(a.A_log[h]);

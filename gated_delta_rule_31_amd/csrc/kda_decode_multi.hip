@@ -92,6 +92,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const bool qk_wave = __builtin_amdgcn_readfirstlane(tid) < kD;  // waves 0-1: q and k; 2-3: v and z
     const float *srcA = qk_wave ? a.q : a.v;
     const float *srcB = qk_wave ? a.k : a.z;
+    const size_t ldB = qk_wave ? a.qkv_ld : HD;  // k rows or z rows (uniform)
     struct TokenLoads {
         float A, B, G, b;
     };
@@ -99,8 +100,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const size_t row = (size_t)bs * T + t;
         const size_t head0 = row * HD + (size_t)h * kD;
         TokenLoads r;
-        r.A = srcA[head0 + (unsigned)i];
-        r.B = srcB[head0 + (unsigned)i];
+        r.A = srcA[row * a.qkv_ld + (size_t)h * kD + (unsigned)i];
+        r.B = srcB[row * ldB + (size_t)h * kD + (unsigned)i];
         r.G = a.g[head0 + (unsigned)i];
         r.b = a.b[row * H + h];
         return r;

@@ -37,6 +37,7 @@ struct DecodeArgs {
     MixerConsts c;
     int B;
     const float *q, *k, *v, *z, *b, *g;
+    size_t qkv_ld;  // elements between consecutive token rows of q, k, v (>= H*D)
     const float *conv_w, *A_log, *dt_bias, *norm_w;
     float *state, *conv_state;
     void *out;  // fp32 or bf16 (c.out_bf16)
@@ -53,6 +54,7 @@ struct DecodeMultiArgs {
     int B, T;
     const int32_t *n_tokens;  // device [B] tokens to apply per sequence, or null (= T)
     const float *q, *k, *v, *z, *b, *g;
+    size_t qkv_ld;  // elements between consecutive token rows of q, k, v (>= H*D)
     const float *conv_w, *A_log, *dt_bias, *norm_w;
     const float *state_in, *conv_in;
     float *state_out, *conv_out;
@@ -70,6 +72,11 @@ struct DecodeMultiArgs {
 //                products into the workspace (chunk records), then one workgroup per
 //                (sequence, head) carries the state across the records
 enum PrefillPath { kPathAuto = 0, kPathFused = 1, kPathChunked = 2 };
+
+// Head count and q/k/v row-stride limits: the kernels form in-chunk row offsets
+// (up to 67 rows) of H*D and of the row stride in 32 bits.
+constexpr int kMaxHeads = 65536;
+constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
 
 // Launch-size limits: a dispatch holds fewer than 2^32 work-items per grid dimension.
 constexpr int64_t kMaxPrefillUnits = (int64_t)0xFFFFFFFF / 512;  // workgroups of 512 lanes
@@ -138,6 +145,7 @@ struct PrefillArgs {
     unsigned char *records;   // chunked plan: [nchunk_cap][H] records
     const int32_t *cu_seqlens;
     const uint16_t *q, *k, *v, *z, *b, *g;
+    size_t qkv_ld;  // elements between consecutive token rows of q, k, v (>= H*D)
     const float *conv_w, *A_log, *dt_bias, *norm_w;
     const float *initial_state, *initial_conv_state;
     void *out;  // fp32 or bf16 (c.out_bf16)

@@ -135,9 +135,11 @@ template <int kPart>
 __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, int tid, int h, int t0, int t1,
                                            int c0) {
     const size_t HD = (size_t)a.c.H * kD;
+    const uint32_t LDX = (uint32_t)a.qkv_ld;  // q, k, v row stride (<= 2^24, so 67 rows fit 32 bits)
     // every row below lies in [rbase, t1 - 1] (t1 > t0), also when c0 is past the end
     const int rbase = min(max(t0 + c0 - 3, t0), t1 - 1);
-    const size_t ebase = (size_t)rbase * HD + (size_t)h * kD;
+    const size_t ebase = (size_t)rbase * HD + (size_t)h * kD;        // z rows
+    const size_t xbase = (size_t)rbase * a.qkv_ld + (size_t)h * kD;  // q, k, v rows
     const uint16_t *X[3] = {a.q, a.k, a.v};
     const uint32_t piece = 8u * (uint32_t)(tid & 15);
 #pragma unroll
@@ -146,14 +148,14 @@ __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, 
         for (int k = 0; k < 2; ++k) {
             const int row = (tid >> 4) + 32 * k;  // chunk row 0..63
             const uint32_t tok = (uint32_t)(min(max(t0 + c0 + row, t0), t1 - 1) - rbase);
-            r.row[blk][k] = *reinterpret_cast<const u32x4 *>(X[blk] + ebase + (tok * (uint32_t)HD + piece));
+            r.row[blk][k] = *reinterpret_cast<const u32x4 *>(X[blk] + xbase + (tok * LDX + piece));
         }
     if constexpr (kPart == 1) {
         const int i = min(tid, 143);  // 3 blocks x 3 rows x 16 pieces
         const int blk = i / 48, row = (i % 48) >> 4;  // history row 0..2 = token c0 - 3 + row
         const uint16_t *src = blk == 0 ? a.q : (blk == 1 ? a.k : a.v);
         const uint32_t tok = (uint32_t)(min(max(t0 + c0 - 3 + row, t0), t1 - 1) - rbase);
-        r.hist = *reinterpret_cast<const u32x4 *>(src + ebase + (tok * (uint32_t)HD + piece));
+        r.hist = *reinterpret_cast<const u32x4 *>(src + xbase + (tok * LDX + piece));
     } else {
         const int lane_t = 16 * wave_sub(tid >> 6) + (tid & 15);    // the prologue token of this lane
         const int cbase = 64 * (tid >> 8) + 16 * ((tid >> 4) & 3);  // and its 16 channels
@@ -915,7 +917,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             const int tok = t1 - 3 + j;
             const uint16_t *src = blk == 0 ? a.q : (blk == 1 ? a.k : a.v);
             if (tok >= t0)
-                win[j] = bf2f(src[(size_t)tok * HD + (size_t)h * kD + cc]);
+                win[j] = bf2f(src[(size_t)tok * a.qkv_ld + (size_t)h * kD + cc]);
             else
                 win[j] = a.initial_conv_state ? a.initial_conv_state[conv_seq + ch * 3 + (tok - t0 + 3)] : 0.f;
         }

@@ -19,7 +19,8 @@
  * The projections that produce the pre-conv q/k/v and the z/b/g logits, and the output
  * projection, are not part of this library.
  *
- * Layouts (row-major, every array dense):
+ * Layouts (row-major; every array dense except q, k, v, whose rows are qkv_row_stride
+ * elements apart):
  *   per-token activations q, k, v, z, g   [tokens, H*D]   channel h*D+i of head h
  *   beta logits b                         [tokens, H]
  *   conv_w                                [3*H*D, 4]      rows: the q block (H*D), then
@@ -45,6 +46,16 @@
  *     synchronisation.
  *   - Calls on different streams that touch different buffers may run concurrently;
  *     calls that write the same state buffer must be ordered by the caller.
+ *   - qkv_row_stride: element distance between consecutive token rows of q, k and v (0
+ *     means dense, H*D).  Otherwise it must be >= H*D, a multiple of 8 and at most 2^24,
+ *     so that q, k and v can be row-strided views of one fused [tokens, 3*H*D]
+ *     projection output (the header comment "KDA per-head recurrence" derives q, k and v
+ *     from the three projections W{q,k,v} x, which one GEMM produces side by side).  The
+ *     three views may overlap each other: they are only read.
+ *   - Outputs never overlap inputs or each other (KDA_ERR_OVERLAP), except the exact
+ *     in-place aliases an entry point names (e.g. final_state == initial_state).  Extents
+ *     are the byte ranges the sizes describe; q, k, v span (rows-1)*stride + H*D
+ *     elements.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -56,23 +67,26 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
-    KDA_ERR_BAD_CONFIG = 2, /* head_dim != 128, conv_size != 4, num_heads < 1, bad eps,
+    KDA_ERR_BAD_CONFIG = 2, /* head_dim != 128, conv_size != 4, num_heads outside
+                               1..65536, bad eps,
                                prefill_path outside 0..2 (kda_prefill), out_dtype outside
                                0..1 */
     KDA_ERR_BAD_SHAPE = 3,  /* negative or inconsistent sizes, or sizes past the limits */
     KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned (workspace: 256-byte) */
     KDA_ERR_WORKSPACE = 5,  /* workspace smaller than kda_prefill_workspace_bytes() */
-    KDA_ERR_LAUNCH = 6      /* the HIP runtime refused a kernel launch or a copy */
+    KDA_ERR_LAUNCH = 6,     /* the HIP runtime refused a kernel launch or a copy */
+    KDA_ERR_OVERLAP = 7     /* an output buffer overlaps an input or another output (other
+                               than an exact in-place alias the entry point allows) */
 } kda_status;
 
 /* Mixer constants.  Fill with kda_config_default() and set num_heads. */
 typedef struct {
-    int32_t num_heads;      /* H >= 1 */
+    int32_t num_heads;      /* H, 1 .. 65536 */
     int32_t head_dim;       /* D; must be 128 (the pages' KDA head dim) */
     int32_t conv_size;      /* ShortConv taps; must be 4 */
     float gate_lower_bound; /* gmin of the decay gate; the pages' value is -5 */
@@ -120,21 +134,22 @@ kda_config kda_config_default(void);
  * exactly once per call.
  *
  *   batch                  B >= 0 (0: nothing queued, KDA_OK)
- *   q, k, v                [B, H*D] fp32 pre-conv inputs of the new token
+ *   q, k, v                [B, H*D] fp32 pre-conv inputs of the new token, rows
+ *                          qkv_row_stride elements apart (0: dense)
  *   z                      [B, H*D] fp32 decay logits, before dt_bias
  *   b                      [B, H]   fp32 beta logits
  *   g                      [B, H*D] fp32 output-gate logits
  *   conv_w, A_log, dt_bias, norm_w   fp32 parameters (layouts above)
  *   state                  [B, H, D, D] fp32, read and overwritten in place
  *   conv_state             [B, 3*H*D, 3] fp32, read and overwritten in place
- *   out                    [B, H*D] fp32 or bf16 (cfg->out_dtype), written; must not
- *                          overlap any input
+ *   out                    [B, H*D] fp32 or bf16 (cfg->out_dtype), written
  *   stream                 hipStream_t or NULL
+ * state, conv_state and out must not overlap each other or any input (KDA_ERR_OVERLAP).
  * Alignment: every pointer 16-byte aligned.  Limits: B*H <= 16,777,215 (one
  * workgroup of 256 lanes per (sequence, head) in one dispatch).
  */
 kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
-                           const float *q, const float *k, const float *v,
+                           const float *q, const float *k, const float *v, int64_t qkv_row_stride,
                            const float *z, const float *b, const float *g,
                            const float *conv_w, const float *A_log, const float *dt_bias,
                            const float *norm_w,
@@ -159,19 +174,20 @@ kda_status kda_decode_step(const kda_config *cfg, int32_t batch,
  *                          result for that slot is unspecified, every access still
  *                          stays inside the pool)
  *   pool_size              P >= 0 entries in state_pool and conv_pool
- *   q, k, v, z, g          [B, H*D] fp32;  b [B, H] fp32 (row r is slot slots[r]'s token)
+ *   q, k, v, z, g          [B, H*D] fp32 (q, k, v rows qkv_row_stride apart);  b [B, H]
+ *                          fp32 (row r is slot slots[r]'s token)
  *   conv_w, A_log, dt_bias, norm_w   fp32 parameters (layouts above)
  *   state_pool             [P, H, D, D] fp32, entries of valid slots read and
  *                          overwritten in place
  *   conv_pool              [P, 3*H*D, 3] fp32, likewise
- *   out                    [B, H*D] fp32 or bf16 (cfg->out_dtype); must not overlap any
- *                          input
+ *   out                    [B, H*D] fp32 or bf16 (cfg->out_dtype)
  *   stream                 hipStream_t or NULL
+ * state_pool, conv_pool and out must not overlap each other or any input.
  * Alignment: every fp32 pointer 16-byte aligned, slots 4-byte aligned.
  * Limits: B*H <= 16,777,215.
  */
 kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int32_t *slots, int32_t pool_size,
-                                 const float *q, const float *k, const float *v,
+                                 const float *q, const float *k, const float *v, int64_t qkv_row_stride,
                                  const float *z, const float *b, const float *g,
                                  const float *conv_w, const float *A_log, const float *dt_bias,
                                  const float *norm_w,
@@ -196,22 +212,24 @@ kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int
  *   tokens                 T >= 1 when B > 0: the token slots per sequence
  *   n_tokens               device int32 [B]: tokens to apply to sequence s (clamped to
  *                          [0, T]; the rest of its slots are ignored), or NULL for T each
- *   q, k, v, z, g          [B, T, H*D] fp32 (row s*T + t is token t of sequence s)
+ *   q, k, v, z, g          [B, T, H*D] fp32 (row s*T + t is token t of sequence s; the
+ *                          rows of q, k, v are qkv_row_stride elements apart)
  *   b                      [B, T, H] fp32
  *   conv_w, A_log, dt_bias, norm_w   fp32 parameters (layouts above)
  *   state_in, state_out    [B, H, D, D] fp32; either the same buffer (update in place)
  *                          or disjoint
  *   conv_state_in, conv_state_out   [B, 3*H*D, 3] fp32; the same buffer or disjoint
  *   out                    [B, T, H*D] fp32 or bf16 (cfg->out_dtype): rows of applied
- *                          tokens are written, the others are left untouched; must not
- *                          overlap any input
+ *                          tokens are written, the others are left untouched
  *   stream                 hipStream_t or NULL
  * A sequence with n_tokens 0 copies its state and windows to the outputs.
+ * state_out, conv_state_out and out must not overlap each other or any input other than
+ * their own exact alias (state_out == state_in, conv_state_out == conv_state_in).
  * Alignment: every fp32 pointer 16-byte aligned, n_tokens 4-byte aligned.
  * Limits: B*H <= 16,777,215; B*T <= 2^31-1.
  */
 kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
-                            const float *q, const float *k, const float *v,
+                            const float *q, const float *k, const float *v, int64_t qkv_row_stride,
                             const float *z, const float *b, const float *g,
                             const float *conv_w, const float *A_log, const float *dt_bias,
                             const float *norm_w,
@@ -240,7 +258,7 @@ kda_status kda_decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens
  */
 kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t tokens, const int32_t *n_tokens,
                                   const int32_t *slots, int32_t pool_size,
-                                  const float *q, const float *k, const float *v,
+                                  const float *q, const float *k, const float *v, int64_t qkv_row_stride,
                                   const float *z, const float *b, const float *g,
                                   const float *conv_w, const float *A_log, const float *dt_bias,
                                   const float *norm_w,
@@ -263,7 +281,8 @@ kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t 
  *   cu_seqlens             device int32 [B+1]: sequence s holds tokens
  *                          cu_seqlens[s] .. cu_seqlens[s+1]-1; must start at 0, be
  *                          non-decreasing and end at N (values are clamped to [0, N])
- *   q, k, v, z, g          [N, H*D] bf16 (raw bit patterns)
+ *   q, k, v, z, g          [N, H*D] bf16 (raw bit patterns); the rows of q, k, v are
+ *                          qkv_row_stride elements apart (0: dense)
  *   b                      [N, H]   bf16
  *   conv_w, A_log, dt_bias, norm_w   fp32 parameters
  *   initial_state          [B, H, D, D] fp32, or NULL for zeros
@@ -271,7 +290,9 @@ kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t 
  *   out                    [N, H*D] fp32 or bf16 (cfg->out_dtype), written
  *   final_state            [B, H, D, D] fp32, written; may be the same pointer as
  *                          initial_state (in-place carry), must not partially overlap it
- *   final_conv_state       [B, 3*H*D, 3] fp32, written; may equal initial_conv_state
+ *                          (KDA_ERR_OVERLAP)
+ *   final_conv_state       [B, 3*H*D, 3] fp32, written; may equal initial_conv_state,
+ *                          must not partially overlap it
  *   workspace              device scratch of workspace_bytes >=
  *                          kda_prefill_workspace_bytes(cfg, B, N), 256-byte aligned;
  *                          may be NULL when that is 0.  Contents on entry are ignored
@@ -279,6 +300,8 @@ kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t 
  *                          time must not share it.
  *   stream                 hipStream_t or NULL
  * A sequence of length 0 copies its initial state and conv state to the final ones.
+ * out, final_state, final_conv_state and the workspace must not overlap each other or
+ * any input other than the two exact aliases above.
  * Alignment: every fp32/bf16 array pointer 16-byte aligned, cu_seqlens 4-byte aligned.
  * Limits: N <= 2^31-1; B*H <= 8,388,607 (one workgroup of 512 lanes per (sequence,
  * head) in one dispatch); for the chunked layout also (floor(N/64) + B)*H <= 8,388,607
@@ -288,7 +311,7 @@ kda_status kda_decode_multi_slots(const kda_config *cfg, int32_t batch, int32_t 
  */
 kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
                        const int32_t *cu_seqlens,
-                       const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t qkv_row_stride,
                        const uint16_t *z, const uint16_t *b, const uint16_t *g,
                        const float *conv_w, const float *A_log, const float *dt_bias,
                        const float *norm_w,
@@ -325,8 +348,9 @@ size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int3
  * Each buffer is device memory or host memory; with pinned host memory (hipHostMalloc)
  * the copies are asynchronous on the stream, with pageable host memory the runtime may
  * complete them before returning.  A source and a destination buffer are either the same
- * buffer or do not overlap (KDA_ERR_BAD_SHAPE otherwise); within one buffer the copies
- * run in slot-list order.  Every slot is checked before anything is queued; a
+ * buffer or do not overlap (KDA_ERR_OVERLAP otherwise); within one buffer the copies run
+ * in slot-list order, and an entry copied onto itself is left as it is (the state and the
+ * conv entry are each decided on their own).  Every slot is checked before anything is queued; a
  * KDA_ERR_LAUNCH (the runtime refused a copy) can leave the entries before the failing
  * one copied.
  * Alignment: the four buffer pointers 16-byte aligned.

@@ -35,37 +35,37 @@ int main() {
     bad.head_dim = 64;
 
     // decode, one token
-    EXPECT(kda_decode_step(nullptr, 1, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
-    EXPECT(kda_decode_step(&bad, 1, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_CONFIG);
-    EXPECT(kda_decode_step(&c, -1, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
-    EXPECT(kda_decode_step(&c, 0, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_OK);
-    EXPECT(kda_decode_step(&c, 2, F, F, F, nullptr, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
-    EXPECT(kda_decode_step(&c, 2, F, F, F, F, F, F, F, F, F, F, F, Fm, F, nullptr), KDA_ERR_MISALIGNED);
-    EXPECT(kda_decode_step_slots(&c, 2, nullptr, 4, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
-    EXPECT(kda_decode_step_slots(&c, 2, I, 0, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_OK);
-    EXPECT(kda_decode_step_slots(&c, 2, I, -1, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_decode_step(nullptr, 1, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
+    EXPECT(kda_decode_step(&bad, 1, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_CONFIG);
+    EXPECT(kda_decode_step(&c, -1, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_decode_step(&c, 0, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_OK);
+    EXPECT(kda_decode_step(&c, 2, F, F, F, 0, nullptr, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
+    EXPECT(kda_decode_step(&c, 2, F, F, F, 0, F, F, F, F, F, F, F, F, Fm, F, nullptr), KDA_ERR_MISALIGNED);
+    EXPECT(kda_decode_step_slots(&c, 2, nullptr, 4, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_NULL_ARG);
+    EXPECT(kda_decode_step_slots(&c, 2, I, 0, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_OK);
+    EXPECT(kda_decode_step_slots(&c, 2, I, -1, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
 
     // decode, several tokens
-    EXPECT(kda_decode_multi(&c, 2, 0, nullptr, F, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
-    EXPECT(kda_decode_multi(&c, 65536, 65536, nullptr, F, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
+    EXPECT(kda_decode_multi(&c, 2, 0, nullptr, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_decode_multi(&c, 65536, 65536, nullptr, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
            KDA_ERR_BAD_SHAPE);
-    EXPECT(kda_decode_multi(&c, 2, 3, nullptr, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr, nullptr),
+    EXPECT(kda_decode_multi(&c, 2, 3, nullptr, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, F, nullptr, nullptr),
            KDA_ERR_NULL_ARG);
-    EXPECT(kda_decode_multi_slots(&c, 2, 3, nullptr, nullptr, 4, F, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
+    EXPECT(kda_decode_multi_slots(&c, 2, 3, nullptr, nullptr, 4, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
            KDA_ERR_NULL_ARG);
-    EXPECT(kda_decode_multi_slots(&c, 2, 3, nullptr, I, 0, F, F, F, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
+    EXPECT(kda_decode_multi_slots(&c, 2, 3, nullptr, I, 0, F, F, F, 0, F, F, F, F, F, F, F, F, F, F, F, F, nullptr),
            KDA_OK);
 
     // prefill
     c.prefill_path = 7;
-    EXPECT(kda_prefill(&c, 1, 64, I, Hh, Hh, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
+    EXPECT(kda_prefill(&c, 1, 64, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
            KDA_ERR_BAD_CONFIG);
     c.prefill_path = KDA_PREFILL_CHUNKED;
-    EXPECT(kda_prefill(&c, 1, 64, I, Hh, Hh, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
+    EXPECT(kda_prefill(&c, 1, 64, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
            KDA_ERR_WORKSPACE);
-    EXPECT(kda_prefill(&c, -1, 64, I, Hh, Hh, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
+    EXPECT(kda_prefill(&c, -1, 64, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
            KDA_ERR_BAD_SHAPE);
-    EXPECT(kda_prefill(&c, 0, 0, I, Hh, Hh, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
+    EXPECT(kda_prefill(&c, 0, 0, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
            KDA_OK);
     if (kda_prefill_workspace_bytes(&c, 1, 8192) != (size_t)256 + (size_t)(128 + 1) * 96 * 111616) {
         printf("unexpected workspace size %zu\n", kda_prefill_workspace_bytes(&c, 1, 8192));
@@ -78,11 +78,38 @@ int main() {
     float *A = reinterpret_cast<float *>(0x100000000ULL), *B = reinterpret_cast<float *>(0x200000000ULL);
     float *Ac = A + 8 * 96 * 128 * 128;
     EXPECT(kda_state_copy(&c, 1, A, Ac, 4, s9, B, B + 8 * 96 * 128 * 128, 4, s0, nullptr), KDA_ERR_BAD_SHAPE);
-    EXPECT(kda_state_copy(&c, 1, A, Ac, 4, s0, A + 96 * 128 * 128, B, 4, s0, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_state_copy(&c, 1, A, Ac, 4, s0, A + 96 * 128 * 128, B, 4, s0, nullptr), KDA_ERR_OVERLAP);
     EXPECT(kda_state_copy(&c, 1, A, Ac, 4, nullptr, B, B, 4, s0, nullptr), KDA_ERR_NULL_ARG);
     EXPECT(kda_state_copy(&c, 0, A, Ac, 4, s0, B, B, 4, s0, nullptr), KDA_OK);
 
-    for (int s = 0; s <= 6; ++s)
+    // q/k/v row strides: below H*D, not a multiple of 8, past 2^24
+    EXPECT(kda_decode_step(&c, 2, F, F, F, 96 * 128 - 8, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_decode_step(&c, 2, F, F, F, 96 * 128 + 4, F, F, F, F, F, F, F, F, F, F, nullptr), KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_prefill(&c, 1, 64, I, Hh, Hh, Hh, (1 << 24) + 8, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F,
+                       nullptr, 0, nullptr),
+           KDA_ERR_BAD_SHAPE);
+    // outputs over inputs: far-apart buffers with one output moved onto an input
+    {
+        const uintptr_t G = (uintptr_t)1 << 32;
+        float *P[13];
+        for (int i = 0; i < 13; ++i) P[i] = reinterpret_cast<float *>((i + 1) * G);
+        EXPECT(kda_decode_step(&c, 4, P[0], P[1], P[2], 0, P[3], P[4], P[5], P[6], P[7], P[8], P[9], P[10], P[11],
+                               P[0] + 4, nullptr),
+               KDA_ERR_OVERLAP);
+        EXPECT(kda_decode_multi(&c, 2, 3, nullptr, P[0], P[1], P[2], 0, P[3], P[4], P[5], P[6], P[7], P[8], P[9],
+                                P[10], P[10] + 4, P[11], P[12], P[12] + 4096 * 1024, nullptr),
+               KDA_ERR_OVERLAP);
+        const uint16_t *Q[7];
+        for (int i = 0; i < 7; ++i) Q[i] = reinterpret_cast<const uint16_t *>((i + 1) * G);
+        const int32_t *cu = reinterpret_cast<const int32_t *>(8 * G);
+        EXPECT(kda_prefill(&c, 2, 100, cu, Q[0], Q[1], Q[2], 0, Q[3], Q[4], Q[5], P[8], P[9], P[10], P[11], P[12],
+                           P[12] + 8 * 96 * 128 * 128 * 4, reinterpret_cast<float *>(20 * G), P[12] + 4,
+                           reinterpret_cast<float *>(22 * G), nullptr, 0, nullptr),
+               KDA_ERR_OVERLAP);
+    }
+    EXPECT(kda_state_copy(&c, 1, A, Ac, 4, s0, A, Ac + 16, 4, s0, nullptr), KDA_ERR_OVERLAP);
+
+    for (int s = 0; s <= 7; ++s)
         if (!kda_status_str((kda_status)s)[0]) ++failures;
     if (kda::reached) {
         printf("%d calls reached a launcher\n", kda::reached);

@@ -11,7 +11,7 @@ import gated_delta_rule_31_amd as kda
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kda.h")
 
-OK, NULL_ARG, BAD_CONFIG, BAD_SHAPE, MISALIGNED, WORKSPACE, LAUNCH = range(7)
+OK, NULL_ARG, BAD_CONFIG, BAD_SHAPE, MISALIGNED, WORKSPACE, LAUNCH, OVERLAP = range(8)
 
 
 def declared_functions():
@@ -34,16 +34,17 @@ def test_abi_version_and_defaults():
     c = L.kda_config_default()
     assert (c.num_heads, c.head_dim, c.conv_size) == (96, 128, 4)
     assert c.gate_lower_bound == -5.0 and c.l2_eps == pytest.approx(1e-6) and c.rms_eps == pytest.approx(1e-5)
-    for s in range(7):
+    for s in range(8):
         assert isinstance(L.kda_status_str(s), bytes) and L.kda_status_str(s)
+    assert L.kda_status_str(OVERLAP) != L.kda_status_str(99)
 
 
 FAKE = 0x10000  # a 16-byte aligned non-NULL address; never dereferenced by rejected calls
 
 
-def _decode(cfg, batch, ptrs=None):
+def _decode(cfg, batch, ptrs=None, stride=0):
     p = [ctypes.c_void_p(FAKE)] * 13 if ptrs is None else ptrs
-    return kda.lib().kda_decode_step(ctypes.byref(cfg), batch, *p, None)
+    return kda.lib().kda_decode_step(ctypes.byref(cfg), batch, *p[:3], stride, *p[3:], None)
 
 
 def _cfg(**over):
@@ -54,7 +55,9 @@ def _cfg(**over):
 
 
 def test_decode_rejects_bad_config():
-    assert kda.lib().kda_decode_step(None, 1, *([ctypes.c_void_p(FAKE)] * 13), None) == NULL_ARG
+    assert kda.lib().kda_decode_step(None, 1, *([ctypes.c_void_p(FAKE)] * 3), 0, *([ctypes.c_void_p(FAKE)] * 10),
+                                     None) == NULL_ARG
+    assert _decode(_cfg(num_heads=65537), 1) == BAD_CONFIG
     assert _decode(_cfg(head_dim=64), 1) == BAD_CONFIG
     assert _decode(_cfg(conv_size=3), 1) == BAD_CONFIG
     assert _decode(_cfg(num_heads=0), 1) == BAD_CONFIG
@@ -77,9 +80,9 @@ def test_decode_rejects_bad_shapes_and_pointers():
         assert _decode(_cfg(), 4, p) == MISALIGNED
 
 
-def _prefill(cfg, B, N, ptrs=None, ws_bytes=0):
+def _prefill(cfg, B, N, ptrs=None, ws_bytes=0, stride=0, ws=None):
     p = [ctypes.c_void_p(FAKE)] * 16 if ptrs is None else ptrs
-    return kda.lib().kda_prefill(ctypes.byref(cfg), B, N, *p, None, ws_bytes, None)
+    return kda.lib().kda_prefill(ctypes.byref(cfg), B, N, *p[:4], stride, *p[4:], ws, ws_bytes, None)
 
 
 def test_prefill_rejects_bad_arguments():
@@ -145,7 +148,7 @@ def test_prefill_rejects_bad_path_and_small_or_misaligned_workspace():
 
     def call(ws, nbytes, path=2):
         c = _cfg(prefill_path=path)
-        return lib.kda_prefill(ctypes.byref(c), 2, 100, *p, ws, nbytes, None)
+        return lib.kda_prefill(ctypes.byref(c), 2, 100, *p[:4], 0, *p[4:], ws, nbytes, None)
 
     assert call(None, 0) == WORKSPACE
     assert call(ctypes.c_void_p(FAKE), need - 1) == WORKSPACE
@@ -166,9 +169,9 @@ def test_launch_size_limits():
     assert _ws(_cfg(num_heads=1), 1, big_n) == 0
 
 
-def _multi(cfg, B, T, n_tokens=None, ptrs=None):
+def _multi(cfg, B, T, n_tokens=None, ptrs=None, stride=0):
     p = [ctypes.c_void_p(FAKE)] * 15 if ptrs is None else ptrs
-    return kda.lib().kda_decode_multi(ctypes.byref(cfg), B, T, n_tokens, *p, None)
+    return kda.lib().kda_decode_multi(ctypes.byref(cfg), B, T, n_tokens, *p[:3], stride, *p[3:], None)
 
 
 def test_decode_multi_rejects_bad_arguments():
@@ -190,9 +193,9 @@ def test_decode_multi_rejects_bad_arguments():
     assert _multi(_cfg(), 2, 3, n_tokens=ctypes.c_void_p(FAKE + 2)) == MISALIGNED
 
 
-def _slots(cfg, B, P, slots=ctypes.c_void_p(FAKE), ptrs=None):
+def _slots(cfg, B, P, slots=ctypes.c_void_p(FAKE), ptrs=None, stride=0):
     p = [ctypes.c_void_p(FAKE)] * 13 if ptrs is None else ptrs
-    return kda.lib().kda_decode_step_slots(ctypes.byref(cfg), B, slots, P, *p, None)
+    return kda.lib().kda_decode_step_slots(ctypes.byref(cfg), B, slots, P, *p[:3], stride, *p[3:], None)
 
 
 def test_decode_slots_rejects_bad_arguments():
@@ -246,14 +249,15 @@ def test_state_copy_rejects_bad_arguments():
     for ss, ds in (([4], [0]), ([-1], [0]), ([0], [4]), ([0], [-2]), ([0, 1, 9], [0, 1, 2])):
         assert _copy(_cfg(), len(ss), src, 4, ss, dst, 4, ds) == BAD_SHAPE, (ss, ds)
     # distinct source and destination buffers that overlap
-    assert _copy(_cfg(), 1, src, 4, [0], (A + st, B), 4, [0]) == BAD_SHAPE
-    assert _copy(_cfg(), 1, src, 4, [0], (B, A + 8 * st + 16), 4, [0]) == BAD_SHAPE
-    assert _copy(_cfg(), 1, src, 4, [0], (A + 8 * st, B), 4, [0]) == BAD_SHAPE  # dst state on src conv
+    assert _copy(_cfg(), 1, src, 4, [0], (A + st, B), 4, [0]) == OVERLAP
+    assert _copy(_cfg(), 1, src, 4, [0], (B, A + 8 * st + 16), 4, [0]) == OVERLAP
+    assert _copy(_cfg(), 1, src, 4, [0], (A + 8 * st, B), 4, [0]) == OVERLAP  # dst state on src conv
 
 
-def _multi_slots(cfg, B, T, P, slots=ctypes.c_void_p(FAKE), n_tokens=None, ptrs=None):
+def _multi_slots(cfg, B, T, P, slots=ctypes.c_void_p(FAKE), n_tokens=None, ptrs=None, stride=0):
     p = [ctypes.c_void_p(FAKE)] * 15 if ptrs is None else ptrs
-    return kda.lib().kda_decode_multi_slots(ctypes.byref(cfg), B, T, n_tokens, slots, P, *p, None)
+    return kda.lib().kda_decode_multi_slots(ctypes.byref(cfg), B, T, n_tokens, slots, P, *p[:3], stride, *p[3:],
+                                            None)
 
 
 def test_decode_multi_slots_rejects_bad_arguments():
@@ -272,3 +276,104 @@ def test_decode_multi_slots_rejects_bad_arguments():
         assert _multi_slots(_cfg(), 2, 3, 4, ptrs=p) == NULL_ARG, i
         p[i] = ctypes.c_void_p(FAKE + 4)
         assert _multi_slots(_cfg(), 2, 3, 4, ptrs=p) == MISALIGNED, i
+
+
+def test_qkv_row_stride_rejections():
+    H = 96
+    HD = H * 128
+    # 0 = dense; otherwise >= H*D, a multiple of 8, at most 2^24
+    for bad in (HD - 8, HD + 4, -8, (1 << 24) + 8):
+        assert _decode(_cfg(), 2, stride=bad) == BAD_SHAPE, bad
+        assert _slots(_cfg(), 2, 4, stride=bad) == BAD_SHAPE, bad
+        assert _multi(_cfg(), 2, 3, stride=bad) == BAD_SHAPE, bad
+        assert _multi_slots(_cfg(), 2, 3, 4, stride=bad) == BAD_SHAPE, bad
+        assert _prefill(_cfg(), 2, 100, stride=bad) == BAD_SHAPE, bad
+
+
+def _spaced(n, gap=1 << 32):
+    """n 16-byte aligned addresses, `gap` bytes apart (far enough that no extent overlaps)."""
+    return [ctypes.c_void_p((i + 1) * gap) for i in range(n)]
+
+
+def test_decode_rejects_overlapping_outputs():
+    # q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state, conv_state, out
+    B, H = 4, 96
+    HD = H * 128
+    p = _spaced(13)  # (the call with these disjoint buffers would launch: it is not made here)
+    out, state, conv = 12, 10, 11
+    cases = [
+        (out, 0, 0),                      # out on q
+        (out, 3, 4 * (B * HD - 4)),       # out's first row on z's last values
+        (state, 6, 16),                   # state inside conv_w
+        (conv, state, 16),                # conv_state inside state
+        (out, conv, 0),                   # out on conv_state
+    ]
+    for dst, src, off in cases:
+        q = list(p)
+        q[dst] = ctypes.c_void_p(p[src].value + off)
+        assert _decode(_cfg(), B, q) == OVERLAP, (dst, src, off)
+        assert _slots(_cfg(), B, 8, ptrs=q) == OVERLAP, (dst, src, off)
+    # q, k, v may overlap each other (views of one fused projection): only the outputs count
+    q = list(p)
+    q[1] = ctypes.c_void_p(p[0].value + 4 * HD)
+    q[2] = ctypes.c_void_p(p[0].value + 8 * HD)
+    q[out] = ctypes.c_void_p(p[0].value + 4 * ((B - 1) * 3 * HD + HD - 4))  # on q's last row
+    assert _decode(_cfg(), B, q, stride=3 * HD) == OVERLAP
+
+
+def test_decode_multi_overlap_rules():
+    # q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, state_in, state_out, conv_in, conv_out, out
+    B, T, H = 2, 3, 96
+    p = _spaced(15)
+    st = B * H * 128 * 128 * 4
+    q = list(p)
+    q[11] = ctypes.c_void_p(p[10].value + 16)  # state_out partly over state_in
+    assert _multi(_cfg(), B, T, ptrs=q) == OVERLAP
+    assert _multi_slots(_cfg(), B, T, 4, ptrs=q) == OVERLAP
+    q = list(p)
+    q[13] = ctypes.c_void_p(p[12].value + 16)  # conv_out partly over conv_in
+    assert _multi(_cfg(), B, T, ptrs=q) == OVERLAP
+    q = list(p)
+    q[14] = ctypes.c_void_p(p[10].value + st - 16)  # out on the end of state_in
+    assert _multi(_cfg(), B, T, ptrs=q) == OVERLAP
+    q = list(p)
+    q[11] = ctypes.c_void_p(p[0].value)  # state_out on q
+    assert _multi(_cfg(), B, T, ptrs=q) == OVERLAP
+
+
+def test_prefill_overlap_rules():
+    # cu, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, init_state, init_conv, out,
+    # final_state, final_conv
+    B, N, H = 2, 100, 96
+    HD = H * 128
+    p = _spaced(16)
+    cases = [
+        (14, 11, 16),    # final_state partly over initial_state
+        (15, 12, 48),    # final_conv partly over initial_conv
+        (13, 1, 0),      # out on q
+        (14, 7, 0),      # final_state on conv_w
+        (15, 13, 16),    # final_conv inside out
+        (13, 0, 0),      # out on cu_seqlens
+    ]
+    for dst, src, off in cases:
+        q = list(p)
+        q[dst] = ctypes.c_void_p(p[src].value + off)
+        assert _prefill(_cfg(prefill_path=1), B, N, q) == OVERLAP, (dst, src, off)
+    # the workspace of the chunked layout counts as an output
+    need = _ws(_cfg(prefill_path=2), B, N)
+    assert _prefill(_cfg(prefill_path=2), B, N, p, ws_bytes=need, ws=ctypes.c_void_p(p[13].value)) == OVERLAP
+    assert _prefill(_cfg(prefill_path=2), B, N, p, ws_bytes=need, ws=ctypes.c_void_p(p[4].value + 256)) == OVERLAP
+    # strided q whose last row reaches into out
+    q = list(p)
+    q[13] = ctypes.c_void_p(p[1].value + 2 * (N - 1) * 3 * HD)
+    assert _prefill(_cfg(prefill_path=1), B, N, q, stride=3 * HD) == OVERLAP
+
+
+def test_state_copy_conv_entry_onto_itself_is_still_checked():
+    # the state entry maps onto itself (same buffer, same slot) while the conv windows go
+    # to another buffer: accepted (the conv copy is queued on its own); an overlapping
+    # conv destination is still rejected
+    H = 96
+    st, cv = H * 128 * 128 * 4, 3 * H * 128 * 3 * 4
+    A, Bc, Cc = 0x100000000, 0x200000000, 0x300000000
+    assert _copy(_cfg(), 1, (A, Bc), 4, [0], (A, Bc + cv), 4, [0]) == OVERLAP  # conv buffers overlap

@@ -55,16 +55,6 @@ def test_cfg1_k3_shape_one_step_all_heads(device):
     _run_steps(case, device, [(b, h) for b in range(case.B) for h in range(case.H)])
 
 
-def test_cfg4_large_batch_32_chained_steps_sampled(device):
-    case = ki.case4_decode()
-    print(f"[decode] {case.name} B={case.B} H={case.H} steps={case.n_steps}", flush=True)
-    rng = np.random.default_rng(404)
-    bs = [0, case.B - 1] + list(rng.choice(np.arange(1, case.B - 1), 10, replace=False))
-    hs = [0, case.H - 1] + list(rng.choice(np.arange(1, case.H - 1), 4, replace=False))
-    pairs = [(int(b), int(h)) for b in bs for h in hs]
-    _run_steps(case, device, pairs)
-
-
 @pytest.mark.parametrize("B,H", [(1, 1), (3, 5), (7, 16)])
 def test_odd_shapes_multi_step(device, B, H):
     case = ki.decode_case(50 + B * 10 + H, B, H, 5, f"odd-{B}x{H}")

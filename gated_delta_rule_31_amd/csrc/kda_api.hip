@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda.h"
 #include "kda_internal.hpp"
 
@@ -85,7 +87,10 @@ struct PrefillPlan {
     int seg_chunks;
     size_t table_bytes, workspace_bytes;
 };
-bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan) {
+// max_workspace >= 0: the workspace is a fixed array of that many bytes; the automatic
+// choice then takes the chunked layout only if its workspace fits (else fused, which
+// needs none).
+bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan, int64_t max_workspace = -1) {
     const int64_t H = cfg->num_heads;
     if (B < 0 || N < 0 || N > INT32_MAX || !units_fit(B, H, kda::kMaxPrefillUnits)) return false;
     const int64_t cap = kda::chunk_cap(B, N);
@@ -101,7 +106,8 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
             const double fused = rounds * chunks * kda::kFusedChunkUs;
             const double chunked =
                 (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits + rounds * chunks * kda::kCarryChunkUs;
-            if (chunked < fused) path = kda::kPathChunked;
+            const size_t need = (size_t)((8 * (B + 1) + 255) / 256 * 256) + (size_t)cap * (size_t)H * kda::kRecBytes;
+            if (chunked < fused && (max_workspace < 0 || need <= (size_t)max_workspace)) path = kda::kPathChunked;
         }
     }
     if (path != kda::kPathFused && path != kda::kPathChunked) return false;
@@ -267,6 +273,112 @@ kda_status decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, co
     return kda::launch_decode_multi(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+// ---- the scratch array of kda_prefill_noalloc ----
+// The chunked layout's workspace (chunk table and records) for callers that cannot
+// allocate: a fixed array in device memory, one per device the library runs on, held
+// until the process ends.  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, looked up once per device (with that device
+// current) and kept.  Every call on a device uses that device's array, and nothing in
+// it has to start at any value (each call writes its table and records before reading
+// them), so it is never cleared.
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices] = {};
+
+kda_status device_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_LAUNCH;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return KDA_OK;
+}
+
+// kda_prefill, and (static_scratch) kda_prefill_noalloc: the workspace is then this
+// device's scratch array, looked up after every argument check has passed
+kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens, const int32_t *cu_seqlens,
+                        const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t qkv_row_stride,
+                        const uint16_t *z, const uint16_t *b, const uint16_t *g, const float *conv_w,
+                        const float *A_log, const float *dt_bias, const float *norm_w, const float *initial_state,
+                        const float *initial_conv_state, void *out, float *final_state, float *final_conv_state,
+                        void *workspace, size_t workspace_bytes, bool static_scratch, void *stream) {
+    kda::PrefillArgs a;
+    kda_status st = check_config(cfg, &a.c);
+    if (st != KDA_OK) return st;
+    if (cfg->prefill_path < kda::kPathAuto || cfg->prefill_path > kda::kPathChunked) return KDA_ERR_BAD_CONFIG;
+    PrefillPlan plan;
+    if (!plan_prefill(cfg, num_seqs, total_tokens, &plan, static_scratch ? (int64_t)kScratchBytes : -1))
+        return KDA_ERR_BAD_SHAPE;
+    if (!resolve_stride(qkv_row_stride, a.c.H, &a.qkv_ld)) return KDA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
+    const void *req[] = {cu_seqlens, conv_w, A_log, dt_bias, norm_w, final_state, final_conv_state};
+    for (const void *p : req)
+        if (!p) return KDA_ERR_NULL_ARG;
+    if (total_tokens > 0) {
+        const void *tok[] = {q, k, v, z, b, g, out};
+        for (const void *p : tok)
+            if (!p) return KDA_ERR_NULL_ARG;
+        for (const void *p : tok)
+            if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    }
+    const void *al[] = {conv_w, A_log, dt_bias, norm_w, final_state, final_conv_state, initial_state,
+                        initial_conv_state};
+    for (const void *p : al)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_MISALIGNED;
+    if (static_scratch) {
+        if (plan.workspace_bytes > kScratchBytes) return KDA_ERR_WORKSPACE;  // explicit chunked layout
+    } else {
+        if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
+            return KDA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
+    }
+    {
+        const int64_t H = a.c.H, HD = H * kda::kD, N = total_tokens, B = num_seqs;
+        const size_t sbytes = (size_t)B * HD * kda::kD * 4;
+        const size_t cbytes = (size_t)B * 3 * HD * (kda::kConv - 1) * 4;
+        const Span ins[13] = {{cu_seqlens, (size_t)(B + 1) * 4},
+                              rows_span(q, N, HD, a.qkv_ld, 2), rows_span(k, N, HD, a.qkv_ld, 2),
+                              rows_span(v, N, HD, a.qkv_ld, 2), rows_span(z, N, HD, HD, 2),
+                              rows_span(b, N, H, H, 2), rows_span(g, N, HD, HD, 2),
+                              {conv_w, (size_t)3 * HD * kda::kConv * 4}, {A_log, (size_t)H * 4},
+                              {dt_bias, (size_t)HD * 4}, {norm_w, (size_t)kda::kD * 4},
+                              {initial_state, initial_state ? sbytes : 0},
+                              {initial_conv_state, initial_conv_state ? cbytes : 0}};
+        const Span outs[4] = {{out, (size_t)N * HD * (a.c.out_bf16 ? 2 : 4)}, {final_state, sbytes},
+                              {final_conv_state, cbytes}, {workspace, plan.workspace_bytes}};
+        const Span alias[4] = {{nullptr, 0}, {initial_state, sbytes}, {initial_conv_state, cbytes}, {nullptr, 0}};
+        if ((st = check_disjoint(outs, alias, 4, ins, 13)) != KDA_OK) return st;
+    }
+    if (static_scratch && plan.workspace_bytes > 0 && (st = device_scratch(&workspace)) != KDA_OK) return st;
+    a.B = num_seqs;
+    a.N = total_tokens;
+    a.path = plan.path;
+    a.nchunk_cap = (int)plan.nchunk_cap;
+    a.nseg_cap = (int)plan.nseg_cap;
+    a.seg_chunks = plan.seg_chunks;
+    const bool chunked = plan.path == kda::kPathChunked;
+    a.chunk_start = chunked ? static_cast<int32_t *>(workspace) : nullptr;
+    a.seg_start = chunked ? static_cast<int32_t *>(workspace) + (num_seqs + 1) : nullptr;
+    a.records = chunked ? static_cast<unsigned char *>(workspace) + plan.table_bytes : nullptr;
+    a.cu_seqlens = cu_seqlens;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
+    a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
+    a.initial_state = initial_state;
+    a.initial_conv_state = initial_conv_state;
+    a.out = out;
+    a.final_state = final_state;
+    a.final_conv_state = final_conv_state;
+    return kda::launch_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,67 +421,20 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
                        const float *initial_state, const float *initial_conv_state, void *out,
                        float *final_state, float *final_conv_state, void *workspace,
                        size_t workspace_bytes, void *stream) {
-    kda::PrefillArgs a;
-    kda_status st = check_config(cfg, &a.c);
-    if (st != KDA_OK) return st;
-    if (cfg->prefill_path < kda::kPathAuto || cfg->prefill_path > kda::kPathChunked) return KDA_ERR_BAD_CONFIG;
-    PrefillPlan plan;
-    if (!plan_prefill(cfg, num_seqs, total_tokens, &plan)) return KDA_ERR_BAD_SHAPE;
-    if (!resolve_stride(qkv_row_stride, a.c.H, &a.qkv_ld)) return KDA_ERR_BAD_SHAPE;
-    if (num_seqs == 0) return total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
-    const void *req[] = {cu_seqlens, conv_w, A_log, dt_bias, norm_w, final_state, final_conv_state};
-    for (const void *p : req)
-        if (!p) return KDA_ERR_NULL_ARG;
-    if (total_tokens > 0) {
-        const void *tok[] = {q, k, v, z, b, g, out};
-        for (const void *p : tok)
-            if (!p) return KDA_ERR_NULL_ARG;
-        for (const void *p : tok)
-            if (!aligned16(p)) return KDA_ERR_MISALIGNED;
-    }
-    const void *al[] = {conv_w, A_log, dt_bias, norm_w, final_state, final_conv_state, initial_state,
-                        initial_conv_state};
-    for (const void *p : al)
-        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
-    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_MISALIGNED;
-    if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace)) return KDA_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
-    {
-        const int64_t H = a.c.H, HD = H * kda::kD, N = total_tokens, B = num_seqs;
-        const size_t sbytes = (size_t)B * HD * kda::kD * 4;
-        const size_t cbytes = (size_t)B * 3 * HD * (kda::kConv - 1) * 4;
-        const Span ins[13] = {{cu_seqlens, (size_t)(B + 1) * 4},
-                              rows_span(q, N, HD, a.qkv_ld, 2), rows_span(k, N, HD, a.qkv_ld, 2),
-                              rows_span(v, N, HD, a.qkv_ld, 2), rows_span(z, N, HD, HD, 2),
-                              rows_span(b, N, H, H, 2), rows_span(g, N, HD, HD, 2),
-                              {conv_w, (size_t)3 * HD * kda::kConv * 4}, {A_log, (size_t)H * 4},
-                              {dt_bias, (size_t)HD * 4}, {norm_w, (size_t)kda::kD * 4},
-                              {initial_state, initial_state ? sbytes : 0},
-                              {initial_conv_state, initial_conv_state ? cbytes : 0}};
-        const Span outs[4] = {{out, (size_t)N * HD * (a.c.out_bf16 ? 2 : 4)}, {final_state, sbytes},
-                              {final_conv_state, cbytes}, {workspace, plan.workspace_bytes}};
-        const Span alias[4] = {{nullptr, 0}, {initial_state, sbytes}, {initial_conv_state, cbytes}, {nullptr, 0}};
-        if ((st = check_disjoint(outs, alias, 4, ins, 13)) != KDA_OK) return st;
-    }
-    a.B = num_seqs;
-    a.N = total_tokens;
-    a.path = plan.path;
-    a.nchunk_cap = (int)plan.nchunk_cap;
-    a.nseg_cap = (int)plan.nseg_cap;
-    a.seg_chunks = plan.seg_chunks;
-    const bool chunked = plan.path == kda::kPathChunked;
-    a.chunk_start = chunked ? static_cast<int32_t *>(workspace) : nullptr;
-    a.seg_start = chunked ? static_cast<int32_t *>(workspace) + (num_seqs + 1) : nullptr;
-    a.records = chunked ? static_cast<unsigned char *>(workspace) + plan.table_bytes : nullptr;
-    a.cu_seqlens = cu_seqlens;
-    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
-    a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
-    a.initial_state = initial_state;
-    a.initial_conv_state = initial_conv_state;
-    a.out = out;
-    a.final_state = final_state;
-    a.final_conv_state = final_conv_state;
-    return kda::launch_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return prefill_impl(cfg, num_seqs, total_tokens, cu_seqlens, q, k, v, qkv_row_stride, z, b, g, conv_w, A_log,
+                        dt_bias, norm_w, initial_state, initial_conv_state, out, final_state, final_conv_state,
+                        workspace, workspace_bytes, false, stream);
+}
+
+kda_status kda_prefill_noalloc(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
+                               const int32_t *cu_seqlens, const uint16_t *q, const uint16_t *k,
+                               const uint16_t *v, int64_t qkv_row_stride, const uint16_t *z, const uint16_t *b,
+                               const uint16_t *g, const float *conv_w, const float *A_log, const float *dt_bias,
+                               const float *norm_w, const float *initial_state, const float *initial_conv_state,
+                               void *out, float *final_state, float *final_conv_state, void *stream) {
+    return prefill_impl(cfg, num_seqs, total_tokens, cu_seqlens, q, k, v, qkv_row_stride, z, b, g, conv_w, A_log,
+                        dt_bias, norm_w, initial_state, initial_conv_state, out, final_state, final_conv_state,
+                        nullptr, 0, true, stream);
 }
 
 kda_status kda_state_copy(const kda_config *cfg, int32_t n, const float *src_state, const float *src_conv,

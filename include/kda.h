@@ -319,6 +319,35 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
                        void *out, float *final_state, float *final_conv_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kda_prefill_noalloc -- kda_prefill for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation (the same kernels, so the same bits) with no workspace
+ * arguments: the chunked layout's workspace is a scratch array the library holds in
+ * each device's memory (KDA_NOALLOC_SCRATCH_BYTES = 256 MiB, kept until the process
+ * ends), never a caller buffer; the call allocates nothing.
+ *
+ *   all arguments          as for kda_prefill
+ * Layout: cfg->prefill_path as for kda_prefill, except that KDA_PREFILL_AUTO takes the
+ * chunked layout only when its workspace (kda_prefill_workspace_bytes with
+ * KDA_PREFILL_CHUNKED) fits in the scratch array, and the fused layout (no workspace)
+ * otherwise.  An explicit KDA_PREFILL_CHUNKED that needs more than
+ * KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_WORKSPACE.
+ * The first call on a device looks up that device's array (hipGetSymbolAddress, with
+ * the device current); KDA_ERR_LAUNCH if the runtime refuses.  Every call on one device
+ * uses the same array and leaves its contents behind: two calls that overlap in time on
+ * one device (e.g. on two streams) race, so the caller must order them.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+kda_status kda_prefill_noalloc(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
+                               const int32_t *cu_seqlens,
+                               const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t qkv_row_stride,
+                               const uint16_t *z, const uint16_t *b, const uint16_t *g,
+                               const float *conv_w, const float *A_log, const float *dt_bias,
+                               const float *norm_w,
+                               const float *initial_state, const float *initial_conv_state,
+                               void *out, float *final_state, float *final_conv_state, void *stream);
+
 /* Device scratch kda_prefill needs for these sizes with cfg->prefill_path: 0 for the
  * fused layout; for the chunked one a table of 2(B+1) int32 (padded to 256 bytes) and one
  * 111,616-byte record per (chunk, head) for floor(N/64) + B chunks (the most that B

@@ -109,6 +109,27 @@ int main() {
     }
     EXPECT(kda_state_copy(&c, 1, A, Ac, 4, s0, A, Ac + 16, 4, s0, nullptr), KDA_ERR_OVERLAP);
 
+    // the allocation-free prefill: the same checks; an explicit chunked layout past the
+    // scratch array is rejected before the array is looked up
+    EXPECT(kda_prefill_noalloc(&c, -1, 64, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F,
+                               nullptr),
+           KDA_ERR_BAD_SHAPE);
+    EXPECT(kda_prefill_noalloc(&c, 0, 0, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F,
+                               nullptr),
+           KDA_OK);
+    {
+        const uintptr_t G = (uintptr_t)1 << 32;
+        const uint16_t *Q[7];
+        float *P[8];
+        for (int i = 0; i < 7; ++i) Q[i] = reinterpret_cast<const uint16_t *>((i + 1) * G);
+        for (int i = 0; i < 8; ++i) P[i] = reinterpret_cast<float *>((i + 10) * G);
+        kda_config cc = c;
+        cc.prefill_path = KDA_PREFILL_CHUNKED;
+        EXPECT(kda_prefill_noalloc(&cc, 1, 4096, reinterpret_cast<const int32_t *>(Q[6]), Q[0], Q[1], Q[2], 0, Q[3],
+                                   Q[4], Q[5], P[0], P[1], P[2], P[3], nullptr, nullptr, P[4], P[5], P[6], nullptr),
+               KDA_ERR_WORKSPACE);
+    }
+
     for (int s = 0; s <= 7; ++s)
         if (!kda_status_str((kda_status)s)[0]) ++failures;
     if (kda::reached) {

@@ -377,3 +377,25 @@ def test_state_copy_conv_entry_onto_itself_is_still_checked():
     st, cv = H * 128 * 128 * 4, 3 * H * 128 * 3 * 4
     A, Bc, Cc = 0x100000000, 0x200000000, 0x300000000
     assert _copy(_cfg(), 1, (A, Bc), 4, [0], (A, Bc + cv), 4, [0]) == OVERLAP  # conv buffers overlap
+
+
+def _noalloc(cfg, B, N, ptrs=None, stride=0):
+    p = [ctypes.c_void_p(FAKE)] * 16 if ptrs is None else ptrs
+    return kda.lib().kda_prefill_noalloc(ctypes.byref(cfg), B, N, *p[:4], stride, *p[4:], None)
+
+
+def test_prefill_noalloc_host_rejections():
+    # the same argument checks as kda_prefill, before the scratch array is looked up
+    assert _noalloc(_cfg(head_dim=64), 1, 8) == BAD_CONFIG
+    assert _noalloc(_cfg(), -1, 8) == BAD_SHAPE
+    assert _noalloc(_cfg(), 0, 0) == OK
+    p = [ctypes.c_void_p(FAKE)] * 16
+    p[1] = None
+    assert _noalloc(_cfg(), 2, 100, p) == NULL_ARG
+    p = _spaced(16)
+    q = list(p)
+    q[14] = ctypes.c_void_p(p[11].value + 16)
+    assert _noalloc(_cfg(prefill_path=1), 2, 100, q) == OVERLAP
+    # an explicit chunked layout whose records would not fit the 256 MiB scratch array
+    assert _ws(_cfg(prefill_path=2, num_heads=96), 1, 4096) > 256 << 20
+    assert _noalloc(_cfg(prefill_path=2, num_heads=96), 1, 4096, p) == WORKSPACE

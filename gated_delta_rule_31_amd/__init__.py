@@ -16,7 +16,8 @@ import torch
 
 __all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_decode_multi_slots",
            "kda_prefill", "kda_prefill_noalloc", "kda_prefill_workspace_bytes", "kda_state_copy", "KdaError",
-           "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED"]
+           "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED",
+           "PRECISION_STANDARD", "PRECISION_HIGH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi",
@@ -38,12 +39,16 @@ class _CConfig(ctypes.Structure):
         ("q_scale", ctypes.c_float),
         ("prefill_path", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
+        ("precision", ctypes.c_int32),
     ]
 
 # kda_config.prefill_path values
 PREFILL_AUTO = 0     # the layout an estimate of both times predicts faster
 PREFILL_FUSED = 1    # one workgroup per (sequence, head) over all chunks; no workspace
 PREFILL_CHUNKED = 2  # chunk records in parallel, then the carry; needs a workspace
+# kda_config.precision values (kda_prefill)
+PRECISION_STANDARD = 0  # bf16 MFMA operands, the decisive ones split hi + lo
+PRECISION_HIGH = 1      # every MFMA operand of the chunk algebra split hi + lo
 
 
 @dataclass
@@ -57,12 +62,14 @@ class KdaConfig:
     q_scale: float = 0.0  # <= 0 selects head_dim ** -0.5
     prefill_path: int = PREFILL_AUTO
     out_dtype: torch.dtype = torch.float32  # or torch.bfloat16: element type of the outputs
+    precision: int = PRECISION_STANDARD     # kda_prefill operand precision
 
     def _c(self) -> _CConfig:
         if self.out_dtype not in (torch.float32, torch.bfloat16):
             raise ValueError(f"out_dtype must be torch.float32 or torch.bfloat16, not {self.out_dtype}")
         return _CConfig(self.num_heads, self.head_dim, self.conv_size, self.gate_lower_bound, self.l2_eps,
-                        self.rms_eps, self.q_scale, self.prefill_path, 1 if self.out_dtype == torch.bfloat16 else 0)
+                        self.rms_eps, self.q_scale, self.prefill_path, 1 if self.out_dtype == torch.bfloat16 else 0,
+                        self.precision)
 
 
 class KdaError(RuntimeError):

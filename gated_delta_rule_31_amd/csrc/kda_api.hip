@@ -67,12 +67,14 @@ kda_status check_config(const kda_config *cfg, kda::MixerConsts *out) {
         !isfinite(cfg->q_scale))
         return KDA_ERR_BAD_CONFIG;
     if (cfg->out_dtype != KDA_OUT_F32 && cfg->out_dtype != KDA_OUT_BF16) return KDA_ERR_BAD_CONFIG;
+    if (cfg->precision != KDA_PRECISION_STANDARD && cfg->precision != KDA_PRECISION_HIGH) return KDA_ERR_BAD_CONFIG;
     out->H = cfg->num_heads;
     out->gate_lower_bound = cfg->gate_lower_bound;
     out->l2_eps = cfg->l2_eps;
     out->rms_eps = cfg->rms_eps;
     out->q_scale = cfg->q_scale > 0.0f ? cfg->q_scale : 1.0f / sqrtf((float)kda::kD);
     out->out_bf16 = cfg->out_dtype == KDA_OUT_BF16;
+    out->precise = cfg->precision == KDA_PRECISION_HIGH;
     return KDA_OK;
 }
 
@@ -106,7 +108,8 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
             const double fused = rounds * chunks * kda::kFusedChunkUs;
             const double chunked =
                 (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits + rounds * chunks * kda::kCarryChunkUs;
-            const size_t need = (size_t)((8 * (B + 1) + 255) / 256 * 256) + (size_t)cap * (size_t)H * kda::kRecBytes;
+            const size_t need = (size_t)((8 * (B + 1) + 255) / 256 * 256) +
+                                (size_t)cap * (size_t)H * (size_t)kda::rec_bytes(cfg->precision == KDA_PRECISION_HIGH);
             if (chunked < fused && (max_workspace < 0 || need <= (size_t)max_workspace)) path = kda::kPathChunked;
         }
     }
@@ -118,7 +121,9 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     plan->seg_chunks = seg_chunks;
     plan->table_bytes = (size_t)((8 * (B + 1) + 255) / 256 * 256);  // chunk_start, seg_start
     plan->workspace_bytes =
-        path == kda::kPathFused ? 0 : plan->table_bytes + (size_t)cap * (size_t)H * (size_t)kda::kRecBytes;
+        path == kda::kPathFused ? 0
+                                : plan->table_bytes + (size_t)cap * (size_t)H *
+                                                          (size_t)kda::rec_bytes(cfg->precision == KDA_PRECISION_HIGH);
     return true;
 }
 
@@ -193,6 +198,7 @@ kda_config kda_config_default(void) {
     c.q_scale = 0.0f;
     c.prefill_path = KDA_PREFILL_AUTO;
     c.out_dtype = KDA_OUT_F32;
+    c.precision = KDA_PRECISION_STANDARD;
     return c;
 }
 
@@ -487,7 +493,7 @@ const char *kda_status_str(kda_status s) {
     switch (s) {
         case KDA_OK: return "ok";
         case KDA_ERR_NULL_ARG: return "a required pointer is NULL";
-        case KDA_ERR_BAD_CONFIG: return "unsupported config (head_dim must be 128, conv_size 4, num_heads 1..65536, finite eps >= 0, prefill_path 0..2, out_dtype 0..1)";
+        case KDA_ERR_BAD_CONFIG: return "unsupported config (head_dim must be 128, conv_size 4, num_heads 1..65536, finite eps >= 0, prefill_path 0..2, out_dtype 0..1, precision 0..1)";
         case KDA_ERR_BAD_SHAPE: return "negative, inconsistent or too large sizes";
         case KDA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
         case KDA_ERR_WORKSPACE: return "workspace too small";

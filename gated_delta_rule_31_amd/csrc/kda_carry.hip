@@ -34,8 +34,11 @@ namespace kda {
 namespace {
 
 constexpr int kCarryThreads = 512;
-constexpr int kBufBytes = kRecPieces * REC_PIECE;  // 78,848
-constexpr int kPiecesPerWave = (kRecPieces + 7) / 8;  // 10 (the last ones repeat piece 76)
+using RecS = Rec<false>;
+using RecP = Rec<true>;
+constexpr int kBufBytes = RecS::kPieces * REC_PIECE;  // 78,848
+constexpr int kPiecesPerWave = (RecS::kPieces + 7) / 8;  // 10 (the last ones repeat piece 76)
+constexpr int kPiecesPerWaveP = (RecP::kPieces + 7) / 8;  // 14 (the last ones repeat piece 108)
 
 // The two chunk-parity buffers of operand pieces, and the RMS partial sums [parity][64
 // tokens][8 waves].
@@ -43,6 +46,10 @@ __shared__ __align__(16) unsigned char carry_buf0[kBufBytes];
 __shared__ __align__(16) unsigned char carry_buf1[kBufBytes];
 __shared__ __align__(16) float carry_part[2][kChunk * 8];
 __shared__ int carry_order[kOrderMaxSeqs];  // longest-first workgroup order
+// the high-precision carry's single buffer of record pieces (109 KB: two would not fit)
+// and its RMS partial sums [64 tokens][8 waves]
+__shared__ __align__(16) unsigned char carry_pbuf[RecP::kPieces * REC_PIECE];
+__shared__ __align__(16) float carry_ppart[kChunk * 8];
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -54,6 +61,51 @@ __device__ __forceinline__ void barrier_all_mem() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0070);
     asm volatile("s_barrier" ::: "memory");
+}
+
+// The final state (from the carry's registers) and the final conv windows (the last 3
+// pre-conv inputs of the sequence, from the initial window if it has fewer than 3 tokens).
+__device__ __forceinline__ void carry_finish(const PrefillArgs &a, const f32x4 (&S)[4][2], int seq, int h, int t0,
+                                             int t1) {
+    const int H = a.c.H;
+    const size_t HD = (size_t)H * kD;
+    const int tid = (int)threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = tid & 15;
+    const int lg = (tid >> 4) & 3;
+    // ---- final state ----
+    {
+        float *Sf = a.final_state + ((size_t)seq * H + h) * kD * kD;
+        // (the initial state may alias the final one: each element is read and written by
+        //  the same lane)
+#pragma unroll
+        for (int P = 0; P < 4; ++P)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 32 * P + 8 * lg + 4 * x + i;
+                    Sf[key * kD + 16 * w + lr] = S[P][x][i];
+                }
+    }
+    // ---- final conv windows: the last 3 pre-conv inputs (from the initial window if T < 3) ----
+    const size_t conv_seq = (size_t)seq * 3 * HD * 3;
+    for (int q = tid; q < 3 * kD; q += kCarryThreads) {
+        const int blk = q >> 7, cc = q & 127;
+        const size_t ch = (size_t)blk * HD + (size_t)h * kD + cc;
+        float win[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int tok = t1 - 3 + j;
+            const uint16_t *src = blk == 0 ? a.q : (blk == 1 ? a.k : a.v);
+            if (tok >= t0)
+                win[j] = bf2f(src[(size_t)tok * a.qkv_ld + (size_t)h * kD + cc]);
+            else
+                win[j] = a.initial_conv_state ? a.initial_conv_state[conv_seq + ch * 3 + (tok - t0 + 3)] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) a.final_conv_state[conv_seq + ch * 3 + j] = win[j];
+    }
 }
 
 // kBf16: the output buffer holds bf16 (round to nearest even), else fp32
@@ -71,8 +123,8 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
     const int T = t1 - t0;
     const int r0 = a.chunk_start[seq];
     const int nrec = a.chunk_start[seq + 1] - r0;  // ceil(T / 64) for a valid batch
-    const size_t rec_stride = (size_t)H * kRecBytes;
-    const unsigned char *rec0 = a.records + ((size_t)r0 * H + h) * kRecBytes;
+    const size_t rec_stride = (size_t)H * RecS::kBytes;
+    const unsigned char *rec0 = a.records + ((size_t)r0 * H + h) * RecS::kBytes;
 
     const int tid = (int)threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,7 +157,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         const unsigned char *rec = rec0 + (size_t)min(c, nrec - 1) * rec_stride;
 #pragma unroll
         for (int j = 0; j < kPiecesPerWave; ++j) {
-            const int piece = min(8 * j + w, kRecPieces - 1);
+            const int piece = min(8 * j + w, RecS::kPieces - 1);
             __builtin_amdgcn_global_load_lds(rec + piece * REC_PIECE + lane * 16,
                                              (lds_void *)((__attribute__((address_space(3))) unsigned char *)dst_base +
                                                           piece * REC_PIECE),
@@ -115,7 +167,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
             for (int x = 0; x < 2; ++x)
-                Un[tp][x] = *reinterpret_cast<const f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
+                Un[tp][x] = *reinterpret_cast<const f32x4 *>(rec + RecS::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
     };
 
     f32x4 Unext[2][2] = {};
@@ -166,7 +218,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
             for (int x = 0; x < 2; ++x) {
                 f32x4 ws = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int P = 0; P < 4; ++P) ws = mma(opnd(rec_w_piece(tp, x, P)), Sh[P], ws);
+                for (int P = 0; P < 4; ++P) ws = mma(opnd(RecS::w(tp, x, P)), Sh[P], ws);
                 U[tp][x] -= ws;
             }
         bf16x8 Uh[2], Ul[2];  // U as the B operand of token contractions, hi/lo [tp]
@@ -182,12 +234,12 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         for (int tt = 0; tt < 4; ++tt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int P = 0; P < 4; ++P) acc = mma(Sh[P], opnd(rec_q_piece(tt, P)), acc);
+            for (int P = 0; P < 4; ++P) acc = mma(Sh[P], opnd(RecS::q(tt, P)), acc);
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp) {
                 if (tp > (tt >> 1)) continue;  // P is lower triangular
-                const bf16x8 Ph = opnd(rec_p_piece(tt, tp, 0));
-                const bf16x8 Pl = opnd(rec_p_piece(tt, tp, 1));
+                const bf16x8 Ph = opnd(RecS::p(tt, tp, 0));
+                const bf16x8 Pl = opnd(RecS::p(tt, tp, 1));
                 acc = mma(Uh[tp], Ph, acc);
                 acc = mma(Uh[tp], Pl, acc);
                 acc = mma(Ul[tp], Ph, acc);
@@ -196,7 +248,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         }
         rms_partials(o, part, w, lr, lg);
         // S = Diag(e^{G_end}) S0 + K_end^T U
-        const float *sE = reinterpret_cast<const float *>(cur + REC_E * REC_PIECE);
+        const float *sE = reinterpret_cast<const float *>(cur + RecS::kE * REC_PIECE);
 #pragma unroll
         for (int P = 0; P < 4; ++P)
 #pragma unroll
@@ -204,8 +256,8 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                 f32x4 acc = S[P][x] * *reinterpret_cast<const f32x4 *>(sE + 32 * P + 8 * lg + 4 * x);
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
-                    const bf16x8 Kh = opnd(rec_k_piece(P, x, tp, 0));
-                    const bf16x8 Kl = opnd(rec_k_piece(P, x, tp, 1));
+                    const bf16x8 Kh = opnd(RecS::k(P, x, tp, 0));
+                    const bf16x8 Kl = opnd(RecS::k(P, x, tp, 1));
                     acc = mma(Kh, Uh[tp], acc);
                     acc = mma(Kl, Uh[tp], acc);
                     acc = mma(Kh, Ul[tp], acc);
@@ -233,11 +285,40 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                                       t0 + cl * kChunk, min(kChunk, T - cl * kChunk), 0, w, lr, lg);
     }
 
-    // ---- final state ----
+    carry_finish(a, S, seq, h, t0, t1);
+}
+
+// The high-precision carry (records of the precise chunk kernel): the same products with
+// every operand split into bf16 hi + lo, W S0 and Q~ S0 included.  Its 109-piece record does
+// not fit twice in the LDS, so one buffer holds the current chunk's pieces and the next
+// chunk's are requested once every wave is done with them; their latency overlaps the
+// chunk's epilogue only.
+template <bool kBf16>
+__global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel_precise(PrefillArgs a) {
+    const int H = a.c.H;
+    const int N = a.N;
+    const int h = blockIdx.x % H;
+    const int seq = seq_longest_first(a.cu_seqlens, a.B, N, blockIdx.x / H, carry_order);
+    const size_t HD = (size_t)H * kD;
+    int t0 = a.cu_seqlens[seq];
+    int t1 = a.cu_seqlens[seq + 1];
+    t0 = min(max(t0, 0), N);
+    t1 = min(max(t1, t0), N);
+    const int T = t1 - t0;
+    const int r0 = a.chunk_start[seq];
+    const int nrec = a.chunk_start[seq + 1] - r0;  // ceil(T / 64) for a valid batch
+    const size_t rec_stride = (size_t)H * RecP::kBytes;
+    const unsigned char *rec0 = a.records + ((size_t)r0 * H + h) * RecP::kBytes;
+
+    const int tid = (int)threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lr = tid & 15;
+    const int lg = (tid >> 4) & 3;
+
+    f32x4 S[4][2];  // S[P][x][i] = S[key 32P + 8lg + 4x + i][value 16w + lr]
     {
-        float *Sf = a.final_state + ((size_t)seq * H + h) * kD * kD;
-        // (the initial state may alias the final one: each element is read and written by
-        //  the same lane)
+        const float *S0 = a.initial_state ? a.initial_state + ((size_t)seq * H + h) * kD * kD : nullptr;
 #pragma unroll
         for (int P = 0; P < 4; ++P)
 #pragma unroll
@@ -245,34 +326,134 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = 32 * P + 8 * lg + 4 * x + i;
-                    Sf[key * kD + 16 * w + lr] = S[P][x][i];
+                    S[P][x][i] = S0 ? S0[key * kD + 16 * w + lr] : 0.0f;
                 }
     }
-    // ---- final conv windows: the last 3 pre-conv inputs (from the initial window if T < 3) ----
-    const size_t conv_seq = (size_t)seq * 3 * HD * 3;
-    for (int q = tid; q < 3 * kD; q += kCarryThreads) {
-        const int blk = q >> 7, cc = q & 127;
-        const size_t ch = (size_t)blk * HD + (size_t)h * kD + cc;
-        float win[3];
+    float nw[4];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int tok = t1 - 3 + j;
-            const uint16_t *src = blk == 0 ? a.q : (blk == 1 ? a.k : a.v);
-            if (tok >= t0)
-                win[j] = bf2f(src[(size_t)tok * a.qkv_ld + (size_t)h * kD + cc]);
-            else
-                win[j] = a.initial_conv_state ? a.initial_conv_state[conv_seq + ch * 3 + (tok - t0 + 3)] : 0.f;
+    for (int i = 0; i < 4; ++i) nw[i] = a.norm_w[16 * w + 4 * lg + i];
+
+    auto request = [&](int c, f32x4 (&Un)[2][2]) {
+        const unsigned char *rec = rec0 + (size_t)c * rec_stride;
+#pragma unroll
+        for (int j = 0; j < kPiecesPerWaveP; ++j) {
+            const int piece = min(8 * j + w, RecP::kPieces - 1);
+            __builtin_amdgcn_global_load_lds(rec + piece * REC_PIECE + lane * 16,
+                                             (lds_void *)((__attribute__((address_space(3))) unsigned char *)carry_pbuf +
+                                                          piece * REC_PIECE),
+                                             16, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) a.final_conv_state[conv_seq + ch * 3 + j] = win[j];
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                Un[tp][x] = *reinterpret_cast<const f32x4 *>(rec + RecP::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
+    };
+    auto opnd = [&](int piece) {
+        return *reinterpret_cast<const bf16x8 *>(carry_pbuf + piece * REC_PIECE + lane * 16);
+    };
+
+    f32x4 Unext[2][2] = {};
+    if (nrec > 0) request(0, Unext);
+    for (int c = 0; c < nrec; ++c) {
+        const int c0 = c * kChunk;
+        const int L = min(kChunk, T - c0);
+        barrier_all_mem();  // chunk c's pieces are in the buffer; the last epilogue is done
+        f32x4 U[2][2];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) U[tp][x] = Unext[tp][x];
+        uint2 g4[4];
+        load_gate4(g4, a.g, HD, h, t0 + c0, L, w, lr, lg);
+
+        bf16x8 Sh[4], Sl[4];
+#pragma unroll
+        for (int P = 0; P < 4; ++P) {
+            const float v8[8] = {S[P][0][0], S[P][0][1], S[P][0][2], S[P][0][3],
+                                 S[P][1][0], S[P][1][1], S[P][1][2], S[P][1][3]};
+            split8(v8, Sh[P], Sl[P]);
+        }
+        // U = U' - W S0
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int P = 0; P < 4; ++P) {
+                    const bf16x8 Wh = opnd(RecP::w(tp, x, P, 0));
+                    const bf16x8 Wl = opnd(RecP::w(tp, x, P, 1));
+                    ws = mma(Wh, Sh[P], ws);
+                    ws = mma(Wh, Sl[P], ws);
+                    ws = mma(Wl, Sh[P], ws);
+                }
+                U[tp][x] -= ws;
+            }
+        bf16x8 Uh[2], Ul[2];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            const float v8[8] = {U[tp][0][0], U[tp][0][1], U[tp][0][2], U[tp][0][3],
+                                 U[tp][1][0], U[tp][1][1], U[tp][1][2], U[tp][1][3]};
+            split8(v8, Uh[tp], Ul[tp]);
+        }
+        // O^T = S0^T Q~^T + U^T P^T
+        f32x4 o[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int P = 0; P < 4; ++P) {
+                const bf16x8 Qh = opnd(RecP::q(tt, P, 0));
+                const bf16x8 Ql = opnd(RecP::q(tt, P, 1));
+                acc = mma(Sh[P], Qh, acc);
+                acc = mma(Sh[P], Ql, acc);
+                acc = mma(Sl[P], Qh, acc);
+            }
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                if (tp > (tt >> 1)) continue;  // P is lower triangular
+                const bf16x8 Ph = opnd(RecP::p(tt, tp, 0));
+                const bf16x8 Pl = opnd(RecP::p(tt, tp, 1));
+                acc = mma(Uh[tp], Ph, acc);
+                acc = mma(Uh[tp], Pl, acc);
+                acc = mma(Ul[tp], Ph, acc);
+            }
+            o[tt] = acc;
+        }
+        rms_partials(o, carry_ppart, w, lr, lg);
+        // S = Diag(e^{G_end}) S0 + K_end^T U
+        const float *sE = reinterpret_cast<const float *>(carry_pbuf + RecP::kE * REC_PIECE);
+#pragma unroll
+        for (int P = 0; P < 4; ++P)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                f32x4 acc = S[P][x] * *reinterpret_cast<const f32x4 *>(sE + 32 * P + 8 * lg + 4 * x);
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    const bf16x8 Kh = opnd(RecP::k(P, x, tp, 0));
+                    const bf16x8 Kl = opnd(RecP::k(P, x, tp, 1));
+                    acc = mma(Kh, Uh[tp], acc);
+                    acc = mma(Kl, Uh[tp], acc);
+                    acc = mma(Kh, Ul[tp], acc);
+                }
+                S[P][x] = acc;
+            }
+        lds_barrier();  // every wave is done with the buffer and has published its sums
+        if (c + 1 < nrec) request(c + 1, Unext);
+        gated_rms_store<kBf16, false>(o, g4, carry_ppart, nw, a.c.rms_eps, a.out, HD, h, t0 + c0, L, 0, w, lr, lg);
     }
+    barrier_all_mem();  // the last epilogue's reads of the sums are done before the LDS is released
+    carry_finish(a, S, seq, h, t0, t1);
 }
 
 }  // namespace
 
 hipError_t launch_carry(const PrefillArgs &a, hipStream_t stream) {
-    const void *fn = a.c.out_bf16 ? reinterpret_cast<const void *>(&carry_kernel<true>)
-                                   : reinterpret_cast<const void *>(&carry_kernel<false>);
+    const void *fn = a.c.precise ? (a.c.out_bf16 ? reinterpret_cast<const void *>(&carry_kernel_precise<true>)
+                                                  : reinterpret_cast<const void *>(&carry_kernel_precise<false>))
+                                 : (a.c.out_bf16 ? reinterpret_cast<const void *>(&carry_kernel<true>)
+                                                 : reinterpret_cast<const void *>(&carry_kernel<false>));
     dim3 grid((unsigned)((size_t)a.B * a.c.H)), block(kCarryThreads);
     void *args[] = {const_cast<PrefillArgs *>(&a)};
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

@@ -140,7 +140,7 @@ __device__ __forceinline__ int seq_longest_first(const int32_t *cu_seqlens, int 
 
 // ---- one chunk record of the chunk-parallel prefill ----
 // Everything a chunk contributes that does not depend on the state entering it.  The
-// first kRecPieces pieces of 1 KB are the MFMA operands of the carry's products in the
+// first Rec::kPieces pieces of 1 KB are the MFMA operands of the carry's products in the
 // order the carry reads them: piece p holds at byte 16l the 16 bytes (8 bf16) that lane
 // l = 16lg + lr of every carry wave reads for that MFMA.  The carry copies the pieces into
 // LDS as they are (one direct-to-LDS load of 1 KB each) and reads each operand with one
@@ -153,22 +153,34 @@ __device__ __forceinline__ int seq_longest_first(const int32_t *cu_seqlens, int 
 //   K   32 pieces (P, x, tp, hi/lo): K_end^T[32P + 8(lr/4) + 4x + lr%4][32tp + 8lg .. +7]
 //   E    1 piece:                   e^{G_end} fp32 [128 keys], then 512 zero bytes
 // with W = T (beta k e^G), Q~ = q e^G, K_end = k e^{G_end - G}, P and K_end split into
-// bf16 hi + lo.  After the pieces, U' = T (beta v) in fp32, in the register order of the
-// consumer: [8 waves][2 tp][2 x][64 lanes][4] (the accumulator rows of token
+// bf16 hi + lo.  The high-precision record (kPrecise) also carries the lo parts of W and
+// Q~ (16 pieces each, right after their hi parts), so that the carry's W S0 and Q~ S0 take
+// both operands split.  After the pieces, U' = T (beta v) in fp32, in the register order of
+// the consumer: [8 waves][2 tp][2 x][64 lanes][4] (the accumulator rows of token
 // 32tp + 8lg + 4x + i, value column 16w + lr).
 constexpr int REC_PIECE = 1024;
-constexpr int REC_W = 0;    // piece indices
-constexpr int REC_Q = 16;
-constexpr int REC_P = 32;
-constexpr int REC_K = 44;
-constexpr int REC_E = 76;
-constexpr int kRecPieces = 77;
-constexpr int REC_U = kRecPieces * REC_PIECE;  // byte offset of U'
-static_assert(REC_U + 8 * 2 * 2 * 64 * 16 == kRecBytes, "record layout");
-__device__ __forceinline__ int rec_w_piece(int tp, int x, int P) { return REC_W + (tp * 2 + x) * 4 + P; }
-__device__ __forceinline__ int rec_q_piece(int tt, int P) { return REC_Q + tt * 4 + P; }
-__device__ __forceinline__ int rec_p_piece(int tt, int tp, int hl) { return REC_P + 2 * (tt < 2 ? tt : 2 * tt - 2 + tp) + hl; }
-__device__ __forceinline__ int rec_k_piece(int P, int x, int tp, int hl) { return REC_K + ((P * 2 + x) * 2 + tp) * 2 + hl; }
+template <bool kPrecise>
+struct Rec {
+    static constexpr int kW = 0;                       // piece indices
+    static constexpr int kWL = 16;                     // (kPrecise only)
+    static constexpr int kQ = kPrecise ? 32 : 16;
+    static constexpr int kQL = 48;                     // (kPrecise only)
+    static constexpr int kP = kPrecise ? 64 : 32;
+    static constexpr int kK = kPrecise ? 76 : 44;
+    static constexpr int kE = kPrecise ? 108 : 76;
+    static constexpr int kPieces = kE + 1;
+    static constexpr int kU = kPieces * REC_PIECE;     // byte offset of U'
+    static constexpr int kBytes = kU + 8 * 2 * 2 * 64 * 16;
+    // hl: 0 = hi, 1 = lo (the lo parts of W and Q~ exist in the precise record only)
+    __device__ static __forceinline__ int w(int tp, int x, int P, int hl = 0) {
+        return (hl ? kWL : kW) + (tp * 2 + x) * 4 + P;
+    }
+    __device__ static __forceinline__ int q(int tt, int P, int hl = 0) { return (hl ? kQL : kQ) + tt * 4 + P; }
+    __device__ static __forceinline__ int p(int tt, int tp, int hl) { return kP + 2 * (tt < 2 ? tt : 2 * tt - 2 + tp) + hl; }
+    __device__ static __forceinline__ int k(int P, int x, int tp, int hl) { return kK + ((P * 2 + x) * 2 + tp) * 2 + hl; }
+};
+static_assert(Rec<false>::kBytes == kRecBytes, "record layout");
+static_assert(Rec<true>::kBytes == kRecBytesPrecise, "record layout");
 
 // ---- the state-side readout and its epilogue, shared by the fused and chunked plans ----
 // O is computed transposed, O^T = S0^T Q~^T + U^T P^T, so that lane (lr, lg) of wave w

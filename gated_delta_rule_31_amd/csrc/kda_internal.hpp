@@ -19,6 +19,7 @@ struct MixerConsts {
     float rms_eps;
     float q_scale;
     int out_bf16;  // the output buffers hold bf16 (round to nearest even), else fp32
+    int precise;   // prefill: every MFMA operand of the chunk algebra split into bf16 hi + lo
 };
 
 // Four consecutive output values at element i (a multiple of 4) of an fp32 or bf16
@@ -97,8 +98,11 @@ constexpr double kFusedChunkUs = 17.6;
 constexpr double kRecordUs = 17.0;
 constexpr double kCarryChunkUs = 5.9;
 
-// Bytes of one chunk record (the layout is in kda_device.hpp); a multiple of 256.
+// Bytes of one chunk record (the layout is in kda_device.hpp); multiples of 256.  The
+// high-precision record also holds the lo parts of W and Q~.
 constexpr int kRecBytes = 111616;
+constexpr int kRecBytesPrecise = 144384;
+inline int64_t rec_bytes(bool precise) { return precise ? kRecBytesPrecise : kRecBytes; }
 
 // Chunk records that a batch of B sequences and N tokens can need at most:
 // sum_s ceil(len_s / 64) <= floor(N / 64) + B.

@@ -50,7 +50,6 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kPiecesPerWave = (kRecPieces + 7) / 8;  // record pieces each wave copies
 
 // ---- LDS map (bytes).  Regions are reused once their first tenant is dead. ----
 constexpr int OFF_R1 = 0;        // sCB fp32 [64][132]          -> sKe hi/lo bf16 [128][64] x2
@@ -74,6 +73,26 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 constexpr int STG_ROWS = kChunk + 3;
 constexpr int STG_LD = 136;
 static_assert(OFF_R4 + 3 * STG_ROWS * STG_LD * 2 <= OFF_TAB, "staging fits regions 4-7");
+
+// Where each tile lives, per precision mode (byte offsets into the LDS).  The
+// high-precision mode keeps the lo halves of beta k e^G, T, W and Q~ as well; K_end^T and
+// Q~ stay in registers until W and U' are done, so that their tiles can take the space
+// of beta v and beta k e^G:
+//   [0, 32768)        sVt hi/lo (phase 1 .. 4)                 -> sKe hi/lo (after 4)
+//   [32768, 65536)    staging (.. phase 1), sWr hi/lo (rows .. 4) -> sQe hi/lo (after 4)
+//   [65536, 99328)    sCB (tables .. phase 2) -> sA [65536, 82944) (combine .. 3) and
+//                     sPh/sPl [82944, 99328) (combine .. 5); sW hi [65536, 81920) (4 .. 5)
+//   [99328, 119808)   sPart (phase 2 .. combine) -> sT [99328, 116736) (3)
+//                     -> sW lo [99328, 115712) (4 .. 5)
+//   [116736, 133120)  sTb hi/lo (3 .. 4) -> RMS partial sums (5 .. epilogue)
+struct LdsMap {
+    int vt, wr, stg, cb, part, a, ph, t, tb, w, wl, ke, qe, rms;
+};
+constexpr LdsMap kMapStd = {OFF_R2, OFF_R3, OFF_R4, OFF_R1, OFF_R6, OFF_R4, OFF_R5,
+                            OFF_R6, OFF_R7, OFF_R4, -1,     OFF_R1, OFF_R6, OFF_R2};
+constexpr LdsMap kMapPrecise = {0, 32768, 32768, 65536, 99328, 65536, 82944, 99328, 116736, 65536, 99328, 0, 32768, 116736};
+static_assert(kMapPrecise.stg + 3 * STG_ROWS * STG_LD * 2 <= OFF_TAB, "staging fits");
+static_assert(kMapPrecise.tb + 2 * 64 * 64 * 2 <= OFF_TAB, "precise map fits");
 
 // One chunk's raw inputs as this lane loads them: the chunk's 64 rows of q, k, v as 16-byte
 // pieces (lane l loads piece l%16 of rows l/16 and l/16 + 32 of each block), one piece of
@@ -172,22 +191,31 @@ __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, 
 // kChunked = true: one workgroup per (segment, head) computes up to a.seg_chunks
 // consecutive chunks of one sequence up to U' and stores each chunk's record instead of
 // carrying the state.
-template <bool kChunked>
+// kPrecise: every MFMA operand of the chunk algebra is split into bf16 hi + lo (A's two
+// operands, T and beta k e^G in W, T in U', W and S0 in W S0, Q~ and S0 in Q~ S0, besides
+// the splits of the standard mode), so that no product rounds an operand to 8 bits.
+template <bool kChunked, bool kPrecise>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    float *sCB = reinterpret_cast<float *>(smem + OFF_R1);              // [64][132] k e^{r - G}
-    __bf16 *sKeHi = reinterpret_cast<__bf16 *>(smem + OFF_R1);          // [128][64] K_end^T
+    constexpr LdsMap M = kPrecise ? kMapPrecise : kMapStd;
+    using R = Rec<kPrecise>;
+    float *sCB = reinterpret_cast<float *>(smem + M.cb);                // [64][132] k e^{r - G}
+    __bf16 *sKeHi = reinterpret_cast<__bf16 *>(smem + M.ke);            // [128][64] K_end^T
     __bf16 *sKeLo = sKeHi + 128 * 64;
-    __bf16 *sVtHi = reinterpret_cast<__bf16 *>(smem + OFF_R2);          // [128][64] (beta v)^T
+    __bf16 *sVtHi = reinterpret_cast<__bf16 *>(smem + M.vt);            // [128][64] (beta v)^T
     __bf16 *sVtLo = sVtHi + 128 * 64;
-    __bf16 *sWr = reinterpret_cast<__bf16 *>(smem + OFF_R3);            // [128][64] (beta k e^G)^T
-    float *sA = reinterpret_cast<float *>(smem + OFF_R4);               // [64][68]
-    __bf16 *sW = reinterpret_cast<__bf16 *>(smem + OFF_R4);             // [64][128]
-    __bf16 *sPh = reinterpret_cast<__bf16 *>(smem + OFF_R5);           // [64][64] P, hi part
+    __bf16 *sWr = reinterpret_cast<__bf16 *>(smem + M.wr);              // [128][64] (beta k e^G)^T
+    __bf16 *sWrLo = sWr + 128 * 64;                                     // (kPrecise) its lo part
+    float *sA = reinterpret_cast<float *>(smem + M.a);                  // [64][68]
+    __bf16 *sW = reinterpret_cast<__bf16 *>(smem + M.w);                // [64][128]
+    __bf16 *sWLo = reinterpret_cast<__bf16 *>(smem + (kPrecise ? M.wl : 0));  // (kPrecise) [64][128]
+    __bf16 *sPh = reinterpret_cast<__bf16 *>(smem + M.ph);              // [64][64] P, hi part
     __bf16 *sPl = sPh + 64 * 64;                                        // [64][64] P, lo part
-    float *sT = reinterpret_cast<float *>(smem + OFF_R6);               // [64][68]
-    __bf16 *sQe = reinterpret_cast<__bf16 *>(smem + OFF_R6);            // [64][128] q e^G
-    __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + OFF_R7);            // [64][64]
+    float *sT = reinterpret_cast<float *>(smem + M.t);                  // [64][68]
+    __bf16 *sQe = reinterpret_cast<__bf16 *>(smem + M.qe);              // [64][128] q e^G
+    __bf16 *sQeLo = sQe + 64 * 128;                                     // (kPrecise) its lo part
+    __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + M.tb);              // [64][64]
+    __bf16 *sTbLo = sTb + 64 * 64;                                      // (kPrecise) its lo part
     float *sTot = reinterpret_cast<float *>(smem + OFF_TAB);  // [4][128] per-sub-chunk gk sums
     float *sRef = sTot + 512;                                  // [5][128] r_0..r_3, G_end
     float *sPair = sRef + 640;                                 // [6][128] e^{r_I - r_J}, J < I
@@ -278,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // Raw inputs of a chunk are loaded one chunk ahead (issued before the previous chunk's
     // state-side MFMAs, so that their latency is hidden) and the q, k, v rows are staged
     // in LDS at the chunk's start, each 16-byte piece once.
-    uint16_t *sStage = reinterpret_cast<uint16_t *>(smem + OFF_R4);
+    uint16_t *sStage = reinterpret_cast<uint16_t *>(smem + M.stg);
     ChunkLoads ld = {};
     if (T > 0) {
         int tid_ = (int)threadIdx.x;
@@ -295,37 +323,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // chunked plan: the LDS byte offset (/16, two per register) of the 16 bytes this lane
     // copies into each record piece it writes (pieces 8j + w); see the record layout in
     // kda_device.hpp
-    uint32_t rec_src[(kPiecesPerWave + 1) / 2] = {};
+    constexpr int kPPW = (R::kPieces + 7) / 8;  // record pieces each wave copies
+    uint32_t rec_src[(kPPW + 1) / 2] = {};
     if constexpr (kChunked) {
         const int tid = (int)threadIdx.x;
         const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-        for (int j = 0; j < kPiecesPerWave; ++j) {
+        for (int j = 0; j < kPPW; ++j) {
             const int piece = 8 * j + w;
             int off = 0;  // bytes from smem
-            if (piece < REC_Q) {
-                const int tp = piece >> 3, x = (piece >> 2) & 1, P = piece & 3;
+            if (piece < R::kQ) {
+                const int pw = piece - R::kW, hl = kPrecise ? pw >> 4 : 0, pp = pw & 15;
+                const int tp = pp >> 3, x = (pp >> 2) & 1, P = pp & 3;
                 const int trow = 32 * tp + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                off = OFF_R4 + 2 * swi128(trow, 32 * P + 8 * lg);  // W
-            } else if (piece < REC_P) {
-                const int tt = (piece - REC_Q) >> 2, P = (piece - REC_Q) & 3;
-                off = OFF_R6 + 2 * sw128(16 * tt + lr, 32 * P + 8 * lg);  // Q~
-            } else if (piece < REC_K) {
-                const int sl = (piece - REC_P) >> 1, hl = (piece - REC_P) & 1;
+                off = (hl ? M.wl : M.w) + 2 * swi128(trow, 32 * P + 8 * lg);  // W (hi / lo)
+            } else if (piece < R::kP) {
+                const int pq = piece - R::kQ, hl = kPrecise ? pq >> 4 : 0, pp = pq & 15;
+                const int tt = pp >> 2, P = pp & 3;
+                off = M.qe + hl * 64 * 128 * 2 + 2 * sw128(16 * tt + lr, 32 * P + 8 * lg);  // Q~ (hi / lo)
+            } else if (piece < R::kK) {
+                const int sl = (piece - R::kP) >> 1, hl = (piece - R::kP) & 1;
                 const int tt = sl < 2 ? sl : (sl + 2) >> 1, tp = sl < 2 ? 0 : (sl & 1);
-                off = OFF_R5 + hl * 64 * 64 * 2 + 2 * sw64(16 * tt + lr, 32 * tp + 8 * lg);  // P hi / lo
-            } else if (piece < REC_E) {
-                const int q = piece - REC_K;
+                off = M.ph + hl * 64 * 64 * 2 + 2 * sw64(16 * tt + lr, 32 * tp + 8 * lg);  // P hi / lo
+            } else if (piece < R::kE) {
+                const int q = piece - R::kK;
                 const int hl = q & 1, tp = (q >> 1) & 1, x = (q >> 2) & 1, P = q >> 3;
                 const int krow = 32 * P + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                off = OFF_R1 + hl * 128 * 64 * 2 + 2 * swi64(krow, 32 * tp + 8 * lg);  // K_end^T hi / lo
-            } else if (piece == REC_E) {
+                off = M.ke + hl * 128 * 64 * 2 + 2 * swi64(krow, 32 * tp + 8 * lg);  // K_end^T hi / lo
+            } else if (piece == R::kE) {
                 off = OFF_TAB + (512 + 640 + 768 + 512 + 512) * 4 + 16 * min(lane, 31);  // e^{G_end}
             }
             rec_src[j >> 1] |= (uint32_t)(off >> 4) << (16 * (j & 1));
         }
 #pragma unroll
-        for (int i = 0; i < (kPiecesPerWave + 1) / 2; ++i) asm volatile("" : "+v"(rec_src[i]));
+        for (int i = 0; i < (kPPW + 1) / 2; ++i) asm volatile("" : "+v"(rec_src[i]));
     }
 
     const int cend = kChunked ? min(min(cbeg + a.seg_chunks * kChunk, nrec * kChunk), T) : T;
@@ -506,6 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 
         // ---- rows that need the tables; MFMA operands of block row `sub` ----
         bf16x8 ak[2], aqh[2], aql[2], qe8[2];  // k e^{G-r}, q e^{G-r} (hi/lo), q e^G
+        bf16x8 akl[2], qel[2];                   // (kPrecise) lo parts of k e^{G-r} and q e^G
         float ke[16];                            // K_end = k e^{G_end - G}
         {
             KDA_LANE_IDS();
@@ -517,12 +549,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 for (int j = 0; j < 8; ++j) {
                     const int c = cbase + 8 * pc + j;
                     const float er = sExpRef[sub * 128 + c];
-                    sWr[sw64(c, t)] = (__bf16)(beta * kr[8 * pc + j] * er);
+                    const float bw = beta * kr[8 * pc + j] * er;
+                    const __bf16 bwh = (__bf16)bw;
+                    sWr[sw64(c, t)] = bwh;
+                    if constexpr (kPrecise) sWrLo[sw64(c, t)] = (__bf16)(bw - (float)bwh);
                     qe[j] = qr[8 * pc + j] * er;
                     ke[8 * pc + j] = cbk[8 * pc + j] * sEndRef[sub * 128 + c];
                 }
-                qe8[pc] = to_bf8(qe);
-                ak[pc] = to_bf8(kr + 8 * pc);
+                if constexpr (kPrecise) {
+                    split8(qe, qe8[pc], qel[pc]);
+                    split8(kr + 8 * pc, ak[pc], akl[pc]);
+                } else {
+                    qe8[pc] = to_bf8(qe);
+                    ak[pc] = to_bf8(kr + 8 * pc);
+                }
                 split8(qr + 8 * pc, aqh[pc], aql[pc]);
             }
         }
@@ -532,7 +572,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         // operands use the same channel order, so the contraction is over the half).  The
         // channel-half-1 waves park their partial tiles in regions 6-7 (free until phase 3);
         // the half-0 waves add them after the barrier (LDS float atomics are far slower).
-        float *sPart = reinterpret_cast<float *>(smem + OFF_R6);  // [10 blocks][A,P][64 lanes][4]
+        float *sPart = reinterpret_cast<float *>(smem + M.part);  // [10 blocks][A,P][64 lanes][4]
         f32x4 accA[4], accP[4];
         {
             KDA_LANE_IDS();
@@ -558,6 +598,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     // the transposed tiles: lane (lr, lg) receives the entries (t, s) of
                     // token t = 16 sub + lr and the 4 tokens s = 16J + 4lg + i
                     accA[J] = mma(ch, ak[ks], accA[J]);
+                    if constexpr (kPrecise) {
+                        accA[J] = mma(ch, akl[ks], accA[J]);
+                        accA[J] = mma(cl, ak[ks], accA[J]);
+                    }
                     accP[J] = mma(ch, aqh[ks], accP[J]);
                     accP[J] = mma(ch, aql[ks], accP[J]);
                     accP[J] = mma(cl, aqh[ks], accP[J]);
@@ -604,8 +648,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 }
             }
             // sCB is dead: K_end^T, hi/lo, into region 1 (channel half 1 now, half 0 in
-            // phase 4)
-            if (half == 1) {
+            // phase 4; the precise mode writes both halves after phase 4)
+            if (!kPrecise && half == 1) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int c = 64 * half + 16 * lg + j;
@@ -644,7 +688,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int tt = 0; tt < 16; ++tt) {
                     sT[(d + tt) * F_LD + d + lr] = x[tt];
-                    sTb[sw64(d + tt, d + lr)] = (__bf16)x[tt];
+                    const __bf16 xh = (__bf16)x[tt];
+                    sTb[sw64(d + tt, d + lr)] = xh;
+                    if constexpr (kPrecise) sTbLo[sw64(d + tt, d + lr)] = (__bf16)(x[tt] - (float)xh);
                 }
             } else if (w >= 4) {
                 // upper blocks (I < J) of sTb: 6 blocks x 256 values over 256 lanes
@@ -654,6 +700,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     const int I = b < 3 ? 0 : (b < 5 ? 1 : 2);
                     const int J = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3);
                     sTb[sw64(16 * I + (lane >> 4), 16 * J + (lane & 15))] = (__bf16)0.0f;
+                    if constexpr (kPrecise) sTbLo[sw64(16 * I + (lane >> 4), 16 * J + (lane & 15))] = (__bf16)0.0f;
                 }
             }
             // The next chunk's raw inputs are requested now and in the next phase, to arrive
@@ -697,7 +744,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     for (int kk = 0; kk < 4; ++kk) r = mma_f32(-tii[kk], M[kk], r);
                     R[I] = r;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sTb[sw64(16 * I + 4 * lg + i, 16 * J + lr)] = (__bf16)r[i];
+                    for (int i = 0; i < 4; ++i) {
+                        const __bf16 rh = (__bf16)r[i];
+                        sTb[sw64(16 * I + 4 * lg + i, 16 * J + lr)] = rh;
+                        if constexpr (kPrecise) sTbLo[sw64(16 * I + 4 * lg + i, 16 * J + lr)] = (__bf16)(r[i] - (float)rh);
+                    }
                 }
             };
             if (w == 0) column(std::integral_constant<int, 0>{});
@@ -706,8 +757,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             load_chunk<1>(ld, a, tid_, h, t0, t1, c0 + kChunk);
         }
         lds_barrier();
-        // sT is dead: Q~ = q e^G into region 6
-        {
+        // sT is dead: Q~ = q e^G into region 6 (the precise mode after phase 4)
+        if constexpr (!kPrecise) {
             KDA_LANE_IDS();
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc)
@@ -719,7 +770,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         {
             KDA_LANE_IDS();
             // K_end^T of channel half 0 (its LDS writes issue beside this phase's MFMAs)
-            if (half == 0) {
+            if (!kPrecise && half == 0) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int c = 16 * lg + j;
@@ -737,11 +788,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sTb + sw64(16 * tt + lr, 32 * ks + 8 * lg));
                     const bf16x8 B8 = *reinterpret_cast<const bf16x8 *>(sWr + sw64(16 * w + lr, 32 * ks + 8 * lg));
                     acc = mma(B8, A8, acc);  // W^T tile: keys 16w + 4lg + i of token 16tt + lr
+                    if constexpr (kPrecise) {
+                        const bf16x8 A8l = *reinterpret_cast<const bf16x8 *>(sTbLo + sw64(16 * tt + lr, 32 * ks + 8 * lg));
+                        const bf16x8 B8l = *reinterpret_cast<const bf16x8 *>(sWrLo + sw64(16 * w + lr, 32 * ks + 8 * lg));
+                        acc = mma(B8, A8l, acc);
+                        acc = mma(B8l, A8, acc);
+                    }
                 }
-                bf16x4 w4;
+                bf16x4 w4, w4l;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w4[i] = (__bf16)acc[i];
+                for (int i = 0; i < 4; ++i) {
+                    w4[i] = (__bf16)acc[i];
+                    if constexpr (kPrecise) w4l[i] = (__bf16)(acc[i] - (float)w4[i]);
+                }
                 *reinterpret_cast<bf16x4 *>(sW + swi128(16 * tt + lr, 16 * w + 4 * lg)) = w4;
+                if constexpr (kPrecise) *reinterpret_cast<bf16x4 *>(sWLo + swi128(16 * tt + lr, 16 * w + 4 * lg)) = w4l;
             }
             const int vrow = 16 * w + lr;
 #pragma unroll
@@ -758,33 +819,54 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                         const bf16x8 Bl = *reinterpret_cast<const bf16x8 *>(sVtLo + sw64(vrow, 32 * ks + 8 * lg));
                         acc = mma(A8, Bh, acc);
                         acc = mma(A8, Bl, acc);
+                        if constexpr (kPrecise) {
+                            const bf16x8 A8l = *reinterpret_cast<const bf16x8 *>(sTbLo + sw64(trow, 32 * ks + 8 * lg));
+                            acc = mma(A8l, Bh, acc);
+                        }
                     }
                     U[tp][x] = acc;
                 }
         }
         asm volatile("" ::"v"(ld.z[0]), "v"(ld.z[1]), "v"(ld.b));  // (see before the loop)
         lds_barrier();
+        if constexpr (kPrecise) {
+            // beta v and beta k e^G are dead: K_end^T hi/lo and Q~ hi/lo from registers
+            KDA_LANE_IDS();
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int c = 64 * half + 16 * lg + j;
+                const __bf16 hi = (__bf16)ke[j];
+                sKeHi[swi64(c, t)] = hi;
+                sKeLo[swi64(c, t)] = (__bf16)(ke[j] - (float)hi);
+            }
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc) {
+                *reinterpret_cast<bf16x8 *>(sQe + sw128(t, 64 * half + 16 * lg + 8 * pc)) = qe8[pc];
+                *reinterpret_cast<bf16x8 *>(sQeLo + sw128(t, 64 * half + 16 * lg + 8 * pc)) = qel[pc];
+            }
+            lds_barrier();
+        }
 
         if constexpr (kChunked) {
             // ================= the chunk record (layout in kda_device.hpp) =================
             KDA_LANE_IDS();
             const int lane = tid_ & 63;
-            unsigned char *rec = a.records + ((size_t)(rec0 + c0 / kChunk) * H + h) * kRecBytes;
+            unsigned char *rec = a.records + ((size_t)(rec0 + c0 / kChunk) * H + h) * R::kBytes;
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
                 for (int x = 0; x < 2; ++x)
-                    *reinterpret_cast<f32x4 *>(rec + REC_U + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16) = U[tp][x];
+                    *reinterpret_cast<f32x4 *>(rec + R::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16) = U[tp][x];
             // the operand pieces, in the order the carry reads them: piece 8j + w is copied
             // by wave w, lane l taking the 16 bytes lane l of a carry wave reads (source
             // offsets computed once, before the chunk loop)
 #pragma unroll
-            for (int j = 0; j < kPiecesPerWave; ++j) {
+            for (int j = 0; j < kPPW; ++j) {
                 const int piece = 8 * j + w;
-                if (piece >= kRecPieces) break;  // (uniform)
+                if (piece >= R::kPieces) break;  // (uniform)
                 const uint32_t off = ((rec_src[j >> 1] >> (16 * (j & 1))) & 0xffffu) << 4;
                 u32x4 v = *reinterpret_cast<const u32x4 *>(smem + off);
-                if (piece == REC_E && lane >= 32) v = u32x4{0u, 0u, 0u, 0u};
+                if (piece == R::kE && lane >= 32) v = u32x4{0u, 0u, 0u, 0u};
                 *reinterpret_cast<u32x4 *>(rec + piece * REC_PIECE + lane * 16) = v;
             }
             lds_barrier();  // LDS is rewritten by the next chunk
@@ -800,16 +882,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             lane_off = epi_lane_offset(HD, w, lr, lg);
             load_gate4_off(g4, a.g, HD, h, t0 + c0, L, lane_off, w, lr, lg);
         }
-        float *sRms = reinterpret_cast<float *>(smem + OFF_R2);  // [64][8] (beta v is dead)
+        float *sRms = reinterpret_cast<float *>(smem + M.rms);  // [64][8] (beta v is dead)
         f32x4 o[4];  // o[tt][i] = O[token 16tt + lr][value 16w + 4lg + i]
         {
             KDA_LANE_IDS();
-            bf16x8 Sh[4];  // S0 as the B operand of key contractions (hi part)
+            bf16x8 Sh[4], Sl[4];  // S0 as the B operand of key contractions (hi part; lo: kPrecise)
 #pragma unroll
             for (int P = 0; P < 4; ++P) {
                 float v8[8] = {S[P][0][0], S[P][0][1], S[P][0][2], S[P][0][3],
                                S[P][1][0], S[P][1][1], S[P][1][2], S[P][1][3]};
-                Sh[P] = to_bf8(v8);
+                if constexpr (kPrecise)
+                    split8(v8, Sh[P], Sl[P]);
+                else
+                    Sh[P] = to_bf8(v8);
             }
             // U = U' - W S0
 #pragma unroll
@@ -822,6 +907,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     for (int P = 0; P < 4; ++P) {
                         const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + swi128(trow, 32 * P + 8 * lg));
                         ws = mma(A8, Sh[P], ws);
+                        if constexpr (kPrecise) {
+                            const bf16x8 A8l = *reinterpret_cast<const bf16x8 *>(sWLo + swi128(trow, 32 * P + 8 * lg));
+                            ws = mma(A8, Sl[P], ws);
+                            ws = mma(A8l, Sh[P], ws);
+                        }
                     }
                     U[tp][x] -= ws;
                 }
@@ -840,6 +930,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 for (int P = 0; P < 4; ++P) {
                     const bf16x8 B8 = *reinterpret_cast<const bf16x8 *>(sQe + sw128(16 * tt + lr, 32 * P + 8 * lg));
                     acc = mma(Sh[P], B8, acc);
+                    if constexpr (kPrecise) {
+                        const bf16x8 B8l = *reinterpret_cast<const bf16x8 *>(sQeLo + sw128(16 * tt + lr, 32 * P + 8 * lg));
+                        acc = mma(Sh[P], B8l, acc);
+                        acc = mma(Sl[P], B8, acc);
+                    }
                 }
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
@@ -985,9 +1080,9 @@ __global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs 
     }
 }
 
-template <bool kChunked>
+template <bool kChunked, bool kPrecise>
 hipError_t launch_prefill_kernel(const PrefillArgs &a, size_t blocks, hipStream_t stream) {
-    const void *fn = reinterpret_cast<const void *>(&prefill_kernel<kChunked>);
+    const void *fn = reinterpret_cast<const void *>(&prefill_kernel<kChunked, kPrecise>);
     static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (attr != hipSuccess) return attr;
     dim3 grid((unsigned)blocks), block(kThreads);
@@ -998,12 +1093,15 @@ hipError_t launch_prefill_kernel(const PrefillArgs &a, size_t blocks, hipStream_
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
-    if (a.path == kPathFused) return launch_prefill_kernel<false>(a, (size_t)a.B * a.c.H, stream);
+    if (a.path == kPathFused)
+        return a.c.precise ? launch_prefill_kernel<false, true>(a, (size_t)a.B * a.c.H, stream)
+                           : launch_prefill_kernel<false, false>(a, (size_t)a.B * a.c.H, stream);
     void *args[] = {const_cast<PrefillArgs *>(&a)};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&chunk_table_kernel), dim3(1), dim3(kTableThreads),
                                    args, 0, stream);
     if (e != hipSuccess) return e;
-    e = launch_prefill_kernel<true>(a, (size_t)a.nseg_cap * a.c.H, stream);
+    e = a.c.precise ? launch_prefill_kernel<true, true>(a, (size_t)a.nseg_cap * a.c.H, stream)
+                    : launch_prefill_kernel<true, false>(a, (size_t)a.nseg_cap * a.c.H, stream);
     if (e != hipSuccess) return e;
     return launch_carry(a, stream);
 }

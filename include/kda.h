@@ -73,9 +73,8 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
     KDA_ERR_BAD_CONFIG = 2, /* head_dim != 128, conv_size != 4, num_heads outside
-                               1..65536, bad eps,
-                               prefill_path outside 0..2 (kda_prefill), out_dtype outside
-                               0..1 */
+                               1..65536, bad eps, prefill_path outside 0..2 (kda_prefill),
+                               out_dtype or precision outside 0..1 */
     KDA_ERR_BAD_SHAPE = 3,  /* negative or inconsistent sizes, or sizes past the limits */
     KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned (workspace: 256-byte) */
     KDA_ERR_WORKSPACE = 5,  /* workspace smaller than kda_prefill_workspace_bytes() */
@@ -95,7 +94,23 @@ typedef struct {
     float q_scale;          /* scale of the normalised q; <= 0 selects D^-0.5 */
     int32_t prefill_path;   /* KDA_PREFILL_AUTO, _FUSED or _CHUNKED (kda_prefill only) */
     int32_t out_dtype;      /* KDA_OUT_F32 or KDA_OUT_BF16: element type of every `out` */
+    int32_t precision;      /* KDA_PRECISION_STANDARD or _HIGH (kda_prefill only) */
 } kda_config;
+
+/* Operand precision of kda_prefill's chunked algebra (decode is fp32 throughout).
+ *   KDA_PRECISION_STANDARD  bf16 MFMA operands with fp32 accumulation, the operands that
+ *                           decide the state's and the output's error split into bf16
+ *                           hi + lo.  Within 2e-2 (outputs) and 5e-3 (states, relative) of
+ *                           the fp64 recurrence for gates with decay; with no decay and
+ *                           beta -> 1 on every token (the plain delta rule, where no
+ *                           rounding is ever forgotten) the output error grows to about
+ *                           2e-2 at 1K tokens and 2.6e-2 at 8K.
+ *   KDA_PRECISION_HIGH      every MFMA operand of the chunk algebra split into bf16 hi +
+ *                           lo (about 16 significant bits each): about 1e-4 in that regime
+ *                           too.  Costs more MFMA and VALU work per chunk, and the chunked
+ *                           layout's records grow from 111,616 to 144,384 bytes. */
+#define KDA_PRECISION_STANDARD 0
+#define KDA_PRECISION_HIGH 1
 
 /* Element type of the output buffers.  With KDA_OUT_BF16 each output is the fp32 result
  * rounded to the nearest bf16 (ties to even), at half the bytes; states and conv windows
@@ -121,7 +136,7 @@ typedef struct {
 /* Defaults: H = 96, D = 128, conv 4, gmin -5, l2_eps 1e-6, rms_eps 1e-5, q_scale D^-0.5
  * (page "colibri/c/kimi_k3.c": header comment "KDA per-head recurrence" and the
  * config loader's rms_norm_eps default), prefill_path KDA_PREFILL_AUTO, out_dtype
- * KDA_OUT_F32. */
+ * KDA_OUT_F32, precision KDA_PRECISION_STANDARD. */
 kda_config kda_config_default(void);
 
 /*
@@ -348,11 +363,11 @@ kda_status kda_prefill_noalloc(const kda_config *cfg, int32_t num_seqs, int32_t 
                                const float *initial_state, const float *initial_conv_state,
                                void *out, float *final_state, float *final_conv_state, void *stream);
 
-/* Device scratch kda_prefill needs for these sizes with cfg->prefill_path: 0 for the
- * fused layout; for the chunked one a table of 2(B+1) int32 (padded to 256 bytes) and one
- * 111,616-byte record per (chunk, head) for floor(N/64) + B chunks (the most that B
- * sequences of N tokens in total can need).  Returns 0 for arguments kda_prefill would
- * reject. */
+/* Device scratch kda_prefill needs for these sizes with cfg->prefill_path and
+ * cfg->precision: 0 for the fused layout; for the chunked one a table of 2(B+1) int32
+ * (padded to 256 bytes) and one record per (chunk, head) (111,616 bytes, or 144,384 with
+ * KDA_PRECISION_HIGH) for floor(N/64) + B chunks (the most that B sequences of N tokens in
+ * total can need).  Returns 0 for arguments kda_prefill would reject. */
 size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens);
 
 /*

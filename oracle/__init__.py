@@ -169,13 +169,21 @@ class PairResult:
 
 
 def forward(cfg: MixerConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bias, norm_w,
-            state=None, conv_state=None, pairs=None, threads: int | None = None, decode=None):
+            state=None, conv_state=None, pairs=None, threads: int | None = None, decode=None, gate_proj=None):
     """Run the oracle for every (sequence, head) in ``pairs`` (default: all).
 
     Activations may be any float dtype, or an encoding that ``decode`` turns into exact
     float values slice by slice (e.g. bf16 bit patterns); only the slices the pairs touch
     are converted to fp64.  ``state`` is ``[B, H, D, D]`` or None (zeros); ``conv_state``
     ``[B, 3*H*D, K-1]`` or None (zeros).  Returns ``{(s, h): PairResult}``.
+
+    ``gate_proj = (f, w_fb)`` replaces ``z`` (pass None): the decay logits are the second
+    factor of the low-rank decay projection applied to the first one's output, z = W_fb f
+    per token (page "colibri/c/kimi_k3.c", header comment "KDA per-head recurrence": the
+    gate's argument W_fb(W_fa x) + dt_bias; the ``Kda`` struct's ``fa, fb``), with
+    ``f = W_fa x`` of shape ``[N, R]`` (shared by the heads) and ``w_fb`` of shape
+    ``[H*D, R]``; channel i of head h takes row h*D + i.  Computed in fp64 from the
+    (decoded) values, as one matrix product per (sequence, head).
     """
     dec = decode if decode is not None else (lambda x: x)
     D, K = cfg.head_dim, cfg.conv_size
@@ -184,6 +192,10 @@ def forward(cfg: MixerConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bi
     HD = q.shape[1]
     H = HD // D
     assert HD == H * D and b.shape[1] == H and conv_w.shape == (3 * HD, K)
+    if gate_proj is not None:
+        assert z is None, "pass either z or gate_proj"
+        f_lr, w_fb = gate_proj
+        assert w_fb.shape[0] == HD and f_lr.shape[0] == q.shape[0] and f_lr.shape[1] == w_fb.shape[1]
     if pairs is None:
         pairs = [(s, h) for s in range(B) for h in range(H)]
     norm_w64 = _f64(norm_w)
@@ -196,7 +208,11 @@ def forward(cfg: MixerConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_bi
         t0, t1 = int(cu[s]), int(cu[s + 1])
         cs = slice(h * D, (h + 1) * D)
         xq, xk, xv = _f64(dec(q[t0:t1, cs])), _f64(dec(k[t0:t1, cs])), _f64(dec(v[t0:t1, cs]))
-        zz, gg = _f64(dec(z[t0:t1, cs])), _f64(dec(g[t0:t1, cs]))
+        if gate_proj is None:
+            zz = _f64(dec(z[t0:t1, cs]))
+        else:  # z_t = W_fb f_t for the head's D rows of W_fb
+            zz = np.ascontiguousarray(_f64(dec(f_lr[t0:t1])) @ _f64(dec(w_fb[h * D:(h + 1) * D])).T)
+        gg = _f64(dec(g[t0:t1, cs]))
         bb = _f64(dec(b[t0:t1, h]))
         wq = _f64(conv_w[0 * HD + h * D:0 * HD + (h + 1) * D])
         wk = _f64(conv_w[1 * HD + h * D:1 * HD + (h + 1) * D])

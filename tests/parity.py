@@ -138,9 +138,13 @@ def check_prefill(case: ki.PrefillCase, out, fs, fcs, pairs):
 PATH_AUTO, PATH_FUSED, PATH_CHUNKED = 0, 1, 2
 
 
-def prefill_gpu(case: ki.PrefillCase, dev, in_place: bool = False, path: int = PATH_AUTO):
+PRECISION_STANDARD, PRECISION_HIGH = 0, 1
+
+
+def prefill_gpu(case: ki.PrefillCase, dev, in_place: bool = False, path: int = PATH_AUTO,
+                precision: int = PRECISION_STANDARD):
     import gated_delta_rule_31_amd as kda
-    cfg = kda.KdaConfig(num_heads=case.H, prefill_path=path)
+    cfg = kda.KdaConfig(num_heads=case.H, prefill_path=path, precision=precision)
     p = case.params
     cu = t(case.cu_seqlens.astype(np.int32), dev)
     xs = [t(getattr(case.x, n), dev) for n in "qkvzbg"]

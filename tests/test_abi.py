@@ -399,3 +399,12 @@ def test_prefill_noalloc_host_rejections():
     # an explicit chunked layout whose records would not fit the 256 MiB scratch array
     assert _ws(_cfg(prefill_path=2, num_heads=96), 1, 4096) > 256 << 20
     assert _noalloc(_cfg(prefill_path=2, num_heads=96), 1, 4096, p) == WORKSPACE
+
+
+def test_precision_flag():
+    assert kda.lib().kda_config_default().precision == 0
+    assert _decode(_cfg(precision=2), 1) == BAD_CONFIG
+    assert _prefill(_cfg(precision=-1), 1, 8) == BAD_CONFIG
+    # the high-precision records carry the lo parts of W and Q~: 144,384 bytes each
+    assert _ws(_cfg(prefill_path=2, num_heads=96, precision=1), 1, 8192) == 256 + (128 + 1) * 96 * 144384
+    assert _ws(_cfg(prefill_path=1, precision=1), 1, 8192) == 0

@@ -1,8 +1,9 @@
 """Full-size GPU parity, every (sequence, head) pair against the fp64 oracle:
 
 - the 1 x 8192-token prefill (96 heads) and the 16-sequence varlen prefill (96 heads,
-  nonzero initial states), each on both work layouts: outputs within 2e-2 abs, final
-  states within 5e-3 relative, final conv windows exact, and the two layouts bit-identical;
+  nonzero initial states), each on both work layouts and in both operand precisions:
+  outputs within 2e-2 abs, final states within 5e-3 relative, final conv windows exact,
+  and the two layouts bit-identical in each precision;
 - the 512 x 96 decode batch over 32 chained steps: every output of every step and the
   final states within 1e-4 relative, final windows exact.
 
@@ -12,8 +13,9 @@ import pytest
 import torch
 
 import kda_inputs as ki
-from tests.parity import (DECODE_REL_TOL, PATH_CHUNKED, PATH_FUSED, PREFILL_OUT_ABS_TOL, PREFILL_STATE_REL_TOL,
-                          DecodeRun, _prefill_oracle, decode_oracle, prefill_gpu, slice_rel)
+from tests.parity import (DECODE_REL_TOL, PATH_CHUNKED, PATH_FUSED, PRECISION_HIGH, PRECISION_STANDARD,
+                          PREFILL_OUT_ABS_TOL, PREFILL_STATE_REL_TOL, DecodeRun, _prefill_oracle, decode_oracle,
+                          prefill_gpu, slice_rel)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,34 +25,38 @@ D = 128
 def _prefill_all_pairs(case, device, batch_pairs):
     H = case.H
     res = {}
-    for path in (PATH_FUSED, PATH_CHUNKED):
-        print(f"[full] {case.name} path={path} B={case.B} N={case.N} H={H}", flush=True)
-        out, fs, fcs = prefill_gpu(case, device, path=path)
-        res[path] = (out.cpu().numpy(), fs.cpu().numpy(), fcs.cpu().numpy())
-        del out, fs, fcs
-    a, b = res[PATH_FUSED], res[PATH_CHUNKED]
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)  # the layouts run the same arithmetic in the same order
-    out, fs, fcs = a
+    for prec in (PRECISION_STANDARD, PRECISION_HIGH):
+        got = {}
+        for path in (PATH_FUSED, PATH_CHUNKED):
+            print(f"[full] {case.name} path={path} precision={prec} B={case.B} N={case.N} H={H}", flush=True)
+            out, fs, fcs = prefill_gpu(case, device, path=path, precision=prec)
+            got[path] = (out.cpu().numpy(), fs.cpu().numpy(), fcs.cpu().numpy())
+            del out, fs, fcs
+        for x, y in zip(got[PATH_FUSED], got[PATH_CHUNKED]):
+            assert np.array_equal(x, y)  # the layouts run the same arithmetic in the same order
+        res[prec] = got[PATH_FUSED]
     cu = case.cu_seqlens
     pairs = [(s, h) for s in range(case.B) for h in range(H)]
-    worst_o, worst_s = 0.0, 0.0
+    worst = {p: [0.0, 0.0] for p in res}
     for i in range(0, len(pairs), batch_pairs):
         chunk = pairs[i:i + batch_pairs]
         ref = _prefill_oracle(case, chunk)
-        for (s, h) in chunk:
-            r = ref[(s, h)]
-            o = out[cu[s]:cu[s + 1], h * D:(h + 1) * D]
-            if o.size:
-                worst_o = max(worst_o, float(np.max(np.abs(o - r.out))))
-            worst_s = max(worst_s, slice_rel(fs[s, h], r.state))
-            got_c = np.stack([fcs[s, blk * H * D + h * D: blk * H * D + (h + 1) * D] for blk in range(3)])
-            np.testing.assert_array_equal(got_c, r.conv_state)
+        for prec, (out, fs, fcs) in res.items():
+            w = worst[prec]
+            for (s, h) in chunk:
+                r = ref[(s, h)]
+                o = out[cu[s]:cu[s + 1], h * D:(h + 1) * D]
+                if o.size:
+                    w[0] = max(w[0], float(np.max(np.abs(o - r.out))))
+                w[1] = max(w[1], slice_rel(fs[s, h], r.state))
+                got_c = np.stack([fcs[s, blk * H * D + h * D: blk * H * D + (h + 1) * D] for blk in range(3)])
+                np.testing.assert_array_equal(got_c, r.conv_state)
         del ref
-        print(f"[full] {case.name}: {i + len(chunk)}/{len(pairs)} pairs, out abs err {worst_o:.3e}, "
-              f"state rel err {worst_s:.3e}", flush=True)
-    assert worst_o <= PREFILL_OUT_ABS_TOL, worst_o
-    assert worst_s <= PREFILL_STATE_REL_TOL, worst_s
+        print(f"[full] {case.name}: {i + len(chunk)}/{len(pairs)} pairs, out abs err / state rel err: "
+              + ", ".join(f"precision {p}: {w[0]:.3e} / {w[1]:.3e}" for p, w in worst.items()), flush=True)
+    for prec, (wo, ws) in worst.items():
+        assert wo <= PREFILL_OUT_ABS_TOL, (prec, wo)
+        assert ws <= PREFILL_STATE_REL_TOL, (prec, ws)
 
 
 @pytest.mark.timeout(900)

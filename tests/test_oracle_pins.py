@@ -353,3 +353,57 @@ def test_page_constants_and_state_size():
     # "~434 MB per photo": one fp32 [heads, D, D] state per KDA layer
     photo = g["kda_layers"] * g["num_heads"] * g["head_dim"] ** 2 * 4
     assert round(photo / 1e6) == g["photo_mb_approx"]
+
+
+def test_gate_projection_one_hot_factor_selects_channels():
+    """A one-hot second factor (row h*D + i = unit vector e_{pi_h(i)}, pi_h a permutation
+    that differs per head) makes z[t, h*D + i] = f[t, pi_h(i)]: the oracle with the low-rank
+    projection equals the oracle given those logits directly, to the bit.  A transposed
+    factor, a wrong head slice or a wrong row order would pick other channels."""
+    rng = np.random.default_rng(31)
+    D, H, T = 16, 2, 7
+    HD = H * D
+    perms = [rng.permutation(D) for _ in range(H)]
+    w_fb = np.zeros((HD, D))
+    for h in range(H):
+        w_fb[h * D + np.arange(D), perms[h]] = 1.0
+    f = rng.standard_normal((T, D))
+    z_direct = np.concatenate([f[:, perms[h]] for h in range(H)], axis=1)
+    args = dict(q=rng.standard_normal((T, HD)), k=rng.standard_normal((T, HD)), v=rng.standard_normal((T, HD)),
+                b=rng.standard_normal((T, H)), g=rng.standard_normal((T, HD)),
+                conv_w=rng.standard_normal((3 * HD, 4)) * 0.5, A_log=rng.uniform(-2, 1, H),
+                dt_bias=rng.uniform(-1, 1, HD), norm_w=np.ones(D))
+    c = oracle.MixerConfig(head_dim=D)
+    a = oracle.forward(c, [0, T], args["q"], args["k"], args["v"], z_direct, args["b"], args["g"], args["conv_w"],
+                       args["A_log"], args["dt_bias"], args["norm_w"])
+    b = oracle.forward(c, [0, T], args["q"], args["k"], args["v"], None, args["b"], args["g"], args["conv_w"],
+                       args["A_log"], args["dt_bias"], args["norm_w"], gate_proj=(f, w_fb))
+    for h in range(H):
+        np.testing.assert_array_equal(a[(0, h)].out, b[(0, h)].out)
+        np.testing.assert_array_equal(a[(0, h)].state, b[(0, h)].state)
+
+
+def test_gate_projection_matches_explicit_sums():
+    """A dense factor of rank 8 against logits summed term by term in Python (no matrix
+    routine): z[t, h*D + i] = sum_r w_fb[h*D + i, r] f[t, r]."""
+    rng = np.random.default_rng(32)
+    D, H, T, R = 8, 2, 5, 8
+    HD = H * D
+    w_fb = rng.standard_normal((HD, R)) / np.sqrt(R)
+    f = rng.standard_normal((T, R))
+    z = np.zeros((T, HD))
+    for t in range(T):
+        for c in range(HD):
+            acc = 0.0
+            for r in range(R):
+                acc += w_fb[c, r] * f[t, r]
+            z[t, c] = acc
+    args = [rng.standard_normal((T, HD)) for _ in range(3)]
+    b, g = rng.standard_normal((T, H)), rng.standard_normal((T, HD))
+    prm = [rng.standard_normal((3 * HD, 4)) * 0.5, rng.uniform(-2, 1, H), rng.uniform(-1, 1, HD), np.ones(D)]
+    c = oracle.MixerConfig(head_dim=D)
+    a = oracle.forward(c, [0, T], *args, z, b, g, *prm)
+    bb = oracle.forward(c, [0, T], *args, None, b, g, *prm, gate_proj=(f, w_fb))
+    for h in range(H):
+        np.testing.assert_allclose(bb[(0, h)].out, a[(0, h)].out, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(bb[(0, h)].state, a[(0, h)].state, rtol=1e-12, atol=1e-14)

@@ -479,6 +479,54 @@ def bench_prefill(args, dev, which: str, with_bf16_out: bool = False):
     return res
 
 
+def bench_prefill_gate_proj(args, dev):
+    """The one-sequence prefill (8192 tokens, 96 heads) through kda_prefill_gate_proj: the
+    decay logits formed inside from f = W_fa x [8192, 128] and W_fb [12288, 128] (bf16)
+    instead of read as z [8192, 12288]."""
+    import torch
+
+    import kda_inputs as ki
+    import gated_delta_rule_31_amd as kda
+
+    case = ki.case2_prefill()
+    H, B, N = case.H, case.B, case.N
+    f, w_fb = ki.lowrank_gate(case.seed, N, H)
+    path = {"auto": kda.PREFILL_AUTO, "fused": kda.PREFILL_FUSED, "chunked": kda.PREFILL_CHUNKED}[args.prefill_path]
+    cfg = kda.KdaConfig(num_heads=H, prefill_path=path)
+    p = case.params
+    tt, bf = _tt(dev), _bf(dev)
+    cu = tt(case.cu_seqlens.astype(np.int32))
+    xs = {n: bf(getattr(case.x, n)) for n in "qkvbg"}
+    fd, wd = bf(f), bf(w_fb)
+    prm = [tt(p.conv_w), tt(p.A_log), tt(p.dt_bias), tt(p.norm_w)]
+    del case
+    out = torch.empty((N, H * D), dtype=torch.float32, device=dev)
+    fs = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    fcs = torch.empty((B, 3 * H * D, 3), dtype=torch.float32, device=dev)
+    ws_bytes = kda.kda_prefill_workspace_bytes(cfg, B, N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    call = lambda: kda.kda_prefill_gate_proj(cfg, cu, xs["q"], xs["k"], xs["v"], fd, wd, xs["b"], xs["g"], *prm,
+                                             None, None, out=out, final_state=fs, final_conv_state=fcs, workspace=ws)
+    for _ in range(max(1, args.warmup // 2)):
+        call()
+    torch.cuda.synchronize()
+    n = args.prefill_steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        call()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    # algorithmic bytes: z [N, H*D] replaced by f [N, 128] and W_fb [H*D, 128]
+    byts = prefill_bytes(N, B, H, initial=False) - N * H * D * 2 + N * 128 * 2 + H * D * 128 * 2
+    flops = prefill_flops([N], H) + 2 * N * H * D * 128  # plus z = W_fb f
+    return {"workload": "kda-prefill-gate-proj-1x8192tok-96head", "layout": "chunked" if ws_bytes else "fused",
+            "ms_per_call": round(kern_ms, 4), "tokens_per_s": round(N / (kern_ms * 1e-3), 1), "alg_bytes": byts,
+            "alg_flops": flops, "hbm_frac": round(byts / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def bench_copy(args, dev):
     """A plain device-to-device copy of 402,653,184 bytes: the calibration of the HBM
     traffic counters and a reference for achievable bandwidth."""
@@ -600,7 +648,7 @@ def main():
     ap.add_argument("--prefill-path", choices=["auto", "fused", "chunked"], default="auto",
                     help="prefill work layout (auto: the library's estimate of the faster one)")
     ap.add_argument("--only", choices=["all", "decode-cfg4", "decode-cfg1", "decode-multi", "decode-slots",
-                                       "prefill-cfg2", "prefill-cfg3", "copy"],
+                                       "prefill-cfg2", "prefill-cfg3", "prefill-gate-proj", "copy"],
                     default="all", help="run one part only (counter runs under rocprofv3 use this)")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
@@ -623,7 +671,8 @@ def main():
                   "decode-slots": lambda: bench_decode_slots(args, dev),
                   "decode-multi": lambda: [bench_decode_multi(args, dev, T) for T in (4, 8)],
                   "prefill-cfg2": lambda: bench_prefill(args, dev, "cfg2"),
-                  "prefill-cfg3": lambda: bench_prefill(args, dev, "cfg3")}
+                  "prefill-cfg3": lambda: bench_prefill(args, dev, "cfg3"),
+                  "prefill-gate-proj": lambda: bench_prefill_gate_proj(args, dev)}
         if args.only != "all":
             print(json.dumps({args.only: single[args.only]()}), flush=True)
             return
@@ -648,6 +697,9 @@ def main():
             log("prefill: 16 varlen sequences x 96 heads")
             pre3 = bench_prefill(args, dev, "cfg3")
             log(f"prefill cfg3: {pre3}")
+            log("prefill with the decay projection inside: 1 x 8192 tokens x 96 heads")
+            pre2["gate_proj"] = bench_prefill_gate_proj(args, dev)
+            log(f"prefill gate_proj: {pre2['gate_proj']}")
     except DigestMismatch as e:
         print(f"bench.py: {e}", file=sys.stderr, flush=True)
         sys.exit(3)

@@ -15,17 +15,20 @@ import numpy as np
 import torch
 
 __all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_decode_multi_slots",
-           "kda_prefill", "kda_prefill_noalloc", "kda_prefill_workspace_bytes", "kda_state_copy", "KdaError",
+           "kda_prefill", "kda_prefill_gate_proj", "kda_prefill_noalloc", "kda_prefill_workspace_bytes",
+           "kda_state_copy", "KdaError",
            "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED",
            "PRECISION_STANDARD", "PRECISION_HIGH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi",
-                    "kda_decode_multi_slots", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_workspace_bytes",
+                    "kda_decode_multi_slots", "kda_prefill", "kda_prefill_gate_proj", "kda_prefill_noalloc",
+                    "kda_prefill_workspace_bytes",
                     "kda_state_copy", "kda_status_str", "kda_abi_version")
 ABI_VERSION = 8
 HEAD_DIM = 128
 CONV = 4
+RANK = 128  # rank of the low-rank decay projection (kda_prefill_gate_proj)
 
 
 class _CConfig(ctypes.Structure):
@@ -101,6 +104,10 @@ def _load() -> ctypes.CDLL:
     L.kda_prefill.restype = ctypes.c_int
     L.kda_prefill.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 3 + [i64] +
                               [vp] * 3 + [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp, ctypes.c_size_t, vp])
+    L.kda_prefill_gate_proj.restype = ctypes.c_int
+    L.kda_prefill_gate_proj.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 3 +
+                                        [i64] + [vp] * 4 + [fp] * 4 + [fp] * 2 + [fp] * 3 +
+                                        [vp, ctypes.c_size_t, vp])
     L.kda_prefill_noalloc.restype = ctypes.c_int
     L.kda_prefill_noalloc.argtypes = ([ctypes.POINTER(_CConfig), ctypes.c_int32, ctypes.c_int32, vp] + [vp] * 3 +
                                       [i64] + [vp] * 3 + [fp] * 4 + [fp] * 2 + [fp] * 3 + [vp])
@@ -351,6 +358,36 @@ def kda_prefill(cfg: KdaConfig, cu_seqlens, q, k, v, z, b, g, conv_w, A_log, dt_
     if own_ws and stream is not None:
         # the workspace is released when this returns: keep the allocator from handing it
         # out again before the kernels queued on ``stream`` are done with it
+        workspace.record_stream(stream)
+    return out, final_state, final_conv_state
+
+
+def kda_prefill_gate_proj(cfg: KdaConfig, cu_seqlens, q, k, v, f, w_fb, b, g, conv_w, A_log, dt_bias, norm_w,
+                          initial_state=None, initial_conv_state=None, out=None, final_state=None,
+                          final_conv_state=None, workspace=None, stream=None):
+    """kda_prefill with the decay logits formed inside the library: f = W_fa x [N, 128]
+    bf16 (shared by the heads) and W_fb [H*D, 128] bf16 instead of z.  Returns (out,
+    final_state, final_conv_state)."""
+    H, D = cfg.num_heads, cfg.head_dim
+    bf = torch.bfloat16
+    B, N, args, out, final_state, final_conv_state = _prefill_args(
+        cfg, cu_seqlens, q, k, v, None, b, g, conv_w, A_log, dt_bias, norm_w, initial_state, initial_conv_state,
+        out, final_state, final_conv_state)
+    # args: cu, q, k, v, stride, z (NULL), b, ... -> cu, q, k, v, stride, f, w_fb, b, ...
+    fa = [_ptr(f, bf, (N, RANK), "f"), _ptr(w_fb, bf, (H * D, RANK), "w_fb")]
+    args = args[:5] + fa + args[6:]
+    ws_bytes = kda_prefill_workspace_bytes(cfg, B, N)
+    own_ws = bool(ws_bytes) and workspace is None
+    if own_ws:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    c = cfg._c()
+    st = _lib.kda_prefill_gate_proj(ctypes.byref(c), B, N, *args, ws, ctypes.c_size_t(ws_bytes), _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_prefill_gate_proj")
+    if own_ws and stream is not None:
         workspace.record_stream(stream)
     return out, final_state, final_conv_state
 

@@ -314,7 +314,8 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
                         const uint16_t *z, const uint16_t *b, const uint16_t *g, const float *conv_w,
                         const float *A_log, const float *dt_bias, const float *norm_w, const float *initial_state,
                         const float *initial_conv_state, void *out, float *final_state, float *final_conv_state,
-                        void *workspace, size_t workspace_bytes, bool static_scratch, void *stream) {
+                        void *workspace, size_t workspace_bytes, bool static_scratch, void *stream,
+                        bool gate_proj = false, const uint16_t *f = nullptr, const uint16_t *w_fb = nullptr) {
     kda::PrefillArgs a;
     kda_status st = check_config(cfg, &a.c);
     if (st != KDA_OK) return st;
@@ -327,13 +328,15 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
     const void *req[] = {cu_seqlens, conv_w, A_log, dt_bias, norm_w, final_state, final_conv_state};
     for (const void *p : req)
         if (!p) return KDA_ERR_NULL_ARG;
+    if (gate_proj && !w_fb) return KDA_ERR_NULL_ARG;
     if (total_tokens > 0) {
-        const void *tok[] = {q, k, v, z, b, g, out};
+        const void *tok[] = {q, k, v, gate_proj ? f : z, b, g, out};
         for (const void *p : tok)
             if (!p) return KDA_ERR_NULL_ARG;
         for (const void *p : tok)
             if (!aligned16(p)) return KDA_ERR_MISALIGNED;
     }
+    if (gate_proj && !aligned16(w_fb)) return KDA_ERR_MISALIGNED;
     const void *al[] = {conv_w, A_log, dt_bias, norm_w, final_state, final_conv_state, initial_state,
                         initial_conv_state};
     for (const void *p : al)
@@ -350,18 +353,20 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
         const int64_t H = a.c.H, HD = H * kda::kD, N = total_tokens, B = num_seqs;
         const size_t sbytes = (size_t)B * HD * kda::kD * 4;
         const size_t cbytes = (size_t)B * 3 * HD * (kda::kConv - 1) * 4;
-        const Span ins[13] = {{cu_seqlens, (size_t)(B + 1) * 4},
+        const Span ins[14] = {{cu_seqlens, (size_t)(B + 1) * 4},
                               rows_span(q, N, HD, a.qkv_ld, 2), rows_span(k, N, HD, a.qkv_ld, 2),
-                              rows_span(v, N, HD, a.qkv_ld, 2), rows_span(z, N, HD, HD, 2),
+                              rows_span(v, N, HD, a.qkv_ld, 2),
+                              gate_proj ? rows_span(f, N, kda::kRank, kda::kRank, 2) : rows_span(z, N, HD, HD, 2),
                               rows_span(b, N, H, H, 2), rows_span(g, N, HD, HD, 2),
                               {conv_w, (size_t)3 * HD * kda::kConv * 4}, {A_log, (size_t)H * 4},
                               {dt_bias, (size_t)HD * 4}, {norm_w, (size_t)kda::kD * 4},
                               {initial_state, initial_state ? sbytes : 0},
-                              {initial_conv_state, initial_conv_state ? cbytes : 0}};
+                              {initial_conv_state, initial_conv_state ? cbytes : 0},
+                              {w_fb, gate_proj ? (size_t)HD * kda::kRank * 2 : 0}};
         const Span outs[4] = {{out, (size_t)N * HD * (a.c.out_bf16 ? 2 : 4)}, {final_state, sbytes},
                               {final_conv_state, cbytes}, {workspace, plan.workspace_bytes}};
         const Span alias[4] = {{nullptr, 0}, {initial_state, sbytes}, {initial_conv_state, cbytes}, {nullptr, 0}};
-        if ((st = check_disjoint(outs, alias, 4, ins, 13)) != KDA_OK) return st;
+        if ((st = check_disjoint(outs, alias, 4, ins, 14)) != KDA_OK) return st;
     }
     if (static_scratch && plan.workspace_bytes > 0 && (st = device_scratch(&workspace)) != KDA_OK) return st;
     a.B = num_seqs;
@@ -375,7 +380,9 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
     a.seg_start = chunked ? static_cast<int32_t *>(workspace) + (num_seqs + 1) : nullptr;
     a.records = chunked ? static_cast<unsigned char *>(workspace) + plan.table_bytes : nullptr;
     a.cu_seqlens = cu_seqlens;
-    a.q = q; a.k = k; a.v = v; a.z = z; a.b = b; a.g = g;
+    a.q = q; a.k = k; a.v = v; a.z = gate_proj ? nullptr : z; a.b = b; a.g = g;
+    a.f = gate_proj ? f : nullptr;
+    a.w_fb = gate_proj ? w_fb : nullptr;
     a.conv_w = conv_w; a.A_log = A_log; a.dt_bias = dt_bias; a.norm_w = norm_w;
     a.initial_state = initial_state;
     a.initial_conv_state = initial_conv_state;
@@ -430,6 +437,18 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
     return prefill_impl(cfg, num_seqs, total_tokens, cu_seqlens, q, k, v, qkv_row_stride, z, b, g, conv_w, A_log,
                         dt_bias, norm_w, initial_state, initial_conv_state, out, final_state, final_conv_state,
                         workspace, workspace_bytes, false, stream);
+}
+
+kda_status kda_prefill_gate_proj(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
+                                 const int32_t *cu_seqlens, const uint16_t *q, const uint16_t *k,
+                                 const uint16_t *v, int64_t qkv_row_stride, const uint16_t *f, const uint16_t *w_fb,
+                                 const uint16_t *b, const uint16_t *g, const float *conv_w, const float *A_log,
+                                 const float *dt_bias, const float *norm_w, const float *initial_state,
+                                 const float *initial_conv_state, void *out, float *final_state,
+                                 float *final_conv_state, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(cfg, num_seqs, total_tokens, cu_seqlens, q, k, v, qkv_row_stride, nullptr, b, g, conv_w,
+                        A_log, dt_bias, norm_w, initial_state, initial_conv_state, out, final_state, final_conv_state,
+                        workspace, workspace_bytes, false, stream, true, f, w_fb);
 }
 
 kda_status kda_prefill_noalloc(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,

@@ -11,6 +11,7 @@ namespace kda {
 constexpr int kD = 128;     // head dim (key = value = 128)
 constexpr int kConv = 4;    // ShortConv taps
 constexpr int kChunk = 64;  // prefill chunk length
+constexpr int kRank = 128;  // rank of the low-rank decay projection (kda_prefill_gate_proj)
 
 struct MixerConsts {
     int H;
@@ -150,6 +151,9 @@ struct PrefillArgs {
     const int32_t *cu_seqlens;
     const uint16_t *q, *k, *v, *z, *b, *g;
     size_t qkv_ld;  // elements between consecutive token rows of q, k, v (>= H*D)
+    // the decay logits from the low-rank projection instead of z (z == nullptr):
+    // f [N, kRank] (W_fa x, shared by the heads) and w_fb [H*D, kRank], z = W_fb f
+    const uint16_t *f, *w_fb;
     const float *conv_w, *A_log, *dt_bias, *norm_w;
     const float *initial_state, *initial_conv_state;
     void *out;  // fp32 or bf16 (c.out_bf16)

@@ -85,24 +85,37 @@ static_assert(OFF_R4 + 3 * STG_ROWS * STG_LD * 2 <= OFF_TAB, "staging fits regio
 //   [99328, 119808)   sPart (phase 2 .. combine) -> sT [99328, 116736) (3)
 //                     -> sW lo [99328, 115712) (4 .. 5)
 //   [116736, 133120)  sTb hi/lo (3 .. 4) -> RMS partial sums (5 .. epilogue)
+// wfb: the head's rows of the decay projection's second factor [128][128] bf16 (gate
+// projection only), staged at the chunk start and read in phase 1, where the region is
+// free in either map (standard: sCB's, written after phase 1; precise: above the staging).
 struct LdsMap {
-    int vt, wr, stg, cb, part, a, ph, t, tb, w, wl, ke, qe, rms;
+    int vt, wr, stg, cb, part, a, ph, t, tb, w, wl, ke, qe, rms, wfb;
 };
 constexpr LdsMap kMapStd = {OFF_R2, OFF_R3, OFF_R4, OFF_R1, OFF_R6, OFF_R4, OFF_R5,
-                            OFF_R6, OFF_R7, OFF_R4, -1,     OFF_R1, OFF_R6, OFF_R2};
-constexpr LdsMap kMapPrecise = {0, 32768, 32768, 65536, 99328, 65536, 82944, 99328, 116736, 65536, 99328, 0, 32768, 116736};
+                            OFF_R6, OFF_R7, OFF_R4, -1,     OFF_R1, OFF_R6, OFF_R2, OFF_R1};
+constexpr LdsMap kMapPrecise = {0,     32768, 32768, 65536, 99328, 65536, 82944, 99328,
+                                116736, 65536, 99328, 0, 32768, 116736, 98304};
+static_assert(kMapStd.wfb + kD * kRank * 2 <= OFF_R2, "W_fb block fits region 1");
+static_assert(kMapPrecise.wfb >= kMapPrecise.stg + 3 * STG_ROWS * STG_LD * 2 &&
+                  kMapPrecise.wfb + kD * kRank * 2 <= OFF_TAB,
+              "W_fb block clear of the staging");
 static_assert(kMapPrecise.stg + 3 * STG_ROWS * STG_LD * 2 <= OFF_TAB, "staging fits");
 static_assert(kMapPrecise.tb + 2 * 64 * 64 * 2 <= OFF_TAB, "precise map fits");
 
 // One chunk's raw inputs as this lane loads them: the chunk's 64 rows of q, k, v as 16-byte
 // pieces (lane l loads piece l%16 of rows l/16 and l/16 + 32 of each block), one piece of
 // the 3 rows before the chunk (lanes < 144), and the lane's own z row and beta logit.
+// (With the gate projection the lane's f row is loaded in phase 1 instead of z.)
 struct ChunkLoads {
     u32x4 row[3][2];
     u32x4 hist;
     u32x4 z[2];
     float b;
 };
+
+// The 16-byte chunk swizzle of the staged W_fb block [128 rows][16 chunks]: distinct over
+// the 16 rows one MFMA's lanes read (rows 64h + 16(l/4) + 4m + l%4 of lanes l < 16).
+__device__ __forceinline__ int wfb_swz(int row) { return (row & 3) | (((row >> 4) & 3) << 2); }
 
 constexpr int CB_LD = 132;  // fp32 row pitch of sCB
 constexpr int F_LD = 68;    // fp32 row pitch of sA, sT
@@ -150,7 +163,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // issued in different phases so that no wave stalls behind a full memory pipe at a
 // barrier: part 0 the q rows, the lane's z row and beta logit; part 1 the k and v rows
 // and the 3 rows before the chunk.
-template <int kPart>
+template <int kPart, bool kGateProj>
 __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, int tid, int h, int t0, int t1,
                                            int c0) {
     const size_t HD = (size_t)a.c.H * kD;
@@ -180,9 +193,11 @@ __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, 
         const int cbase = 64 * (tid >> 8) + 16 * ((tid >> 4) & 3);  // and its 16 channels
         const int tauc = min(max(t0 + c0 + lane_t, t0), t1 - 1);
         const uint32_t ztok = (uint32_t)(tauc - rbase);
+        if constexpr (!kGateProj) {
 #pragma unroll
-        for (int pc = 0; pc < 2; ++pc)
-            r.z[pc] = *reinterpret_cast<const u32x4 *>(a.z + ebase + (ztok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
+            for (int pc = 0; pc < 2; ++pc)
+                r.z[pc] = *reinterpret_cast<const u32x4 *>(a.z + ebase + (ztok * (uint32_t)HD + (uint32_t)(cbase + 8 * pc)));
+        }
         r.b = bf2f(a.b[(size_t)tauc * a.c.H + h]);
     }
 }
@@ -194,7 +209,10 @@ __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, 
 // kPrecise: every MFMA operand of the chunk algebra is split into bf16 hi + lo (A's two
 // operands, T and beta k e^G in W, T in U', W and S0 in W S0, Q~ and S0 in Q~ S0, besides
 // the splits of the standard mode), so that no product rounds an operand to 8 bits.
-template <bool kChunked, bool kPrecise>
+// kGateProj: the decay logits are z = W_fb f (a.f, a.w_fb) instead of a.z: each chunk
+// stages the head's 128 rows of W_fb in LDS and phase 1 forms its 64 x 128 logits with
+// MFMAs, laid out as the gate computation wants them (see phase 1).
+template <bool kChunked, bool kPrecise, bool kGateProj>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr LdsMap M = kPrecise ? kMapPrecise : kMapStd;
@@ -311,14 +329,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     if (T > 0) {
         int tid_ = (int)threadIdx.x;
         asm volatile("" : "+v"(tid_));
-        load_chunk<0>(ld, a, tid_, h, t0, t1, cbeg);
-        load_chunk<1>(ld, a, tid_, h, t0, t1, cbeg);
+        load_chunk<0, kGateProj>(ld, a, tid_, h, t0, t1, cbeg);
+        load_chunk<1, kGateProj>(ld, a, tid_, h, t0, t1, cbeg);
     }
     // (the prefetched z and b are marked consumed where no store is in flight: once here,
     //  and in every chunk before its stores; without that the compiler cannot count the
     //  stores issued after them across the loop's back edge and makes phase 1 wait for
     //  every memory operation in flight, stores included)
-    asm volatile("" ::"v"(ld.z[0]), "v"(ld.z[1]), "v"(ld.b));
+    if constexpr (kGateProj)
+        asm volatile("" ::"v"(ld.b));
+    else
+        asm volatile("" ::"v"(ld.z[0]), "v"(ld.z[1]), "v"(ld.b));
 
     // chunked plan: the LDS byte offset (/16, two per register) of the 16 bytes this lane
     // copies into each record piece it writes (pieces 8j + w); see the record layout in
@@ -381,6 +402,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             if (tid_ < 144) {
                 const int blk = tid_ / 48, row = (tid_ % 48) >> 4;
                 *reinterpret_cast<u32x4 *>(sStage + (blk * STG_ROWS + row) * STG_LD + piece) = ld.hist;
+            }
+            if constexpr (kGateProj) {
+                // the head's W_fb block [128][128] bf16 into LDS (direct-to-LDS loads, 1 KB per
+                // wave instruction = 4 rows; lane l writes physical chunk l%16 of its row, which
+                // holds the row's logical chunk (l%16) ^ wfb_swz(row)); waited for in phase 1
+                const int w = tid_ >> 6, lane = tid_ & 63;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int n = w + 8 * i;  // rows 4n .. 4n+3
+                    const int row = 4 * n + (lane >> 4);
+                    const int j = (lane & 15) ^ wfb_swz(row);
+                    __builtin_amdgcn_global_load_lds(
+                        a.w_fb + ((size_t)h * kD + row) * kRank + 8 * j,
+                        (__attribute__((address_space(3))) void *)((__attribute__((address_space(3))) unsigned char *)
+                                                                       (smem + M.wfb) + n * 1024),
+                        16, 0, 0);
+                }
             }
         }
         lds_barrier();
@@ -463,12 +501,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 sNorm[half * 128 + t] = ssq;
                 sNorm[half * 128 + 64 + t] = ssk;
             }
+            // decay logits z = W_fb f of the lane's 16 channels (gate projection): four 16 x 16
+            // tiles per wave, A = W_fb rows from LDS, B = the f rows of the wave's 16 tokens.
+            // Tile m gives A-operand row r the channel 64 half + 16(r/4) + 4m + r%4, so output
+            // row 4lg + i is channel cbase + 4m + i and column lr the lane's token: each lane
+            // receives exactly its 16 logits.
+            float zf[16];
+            if constexpr (kGateProj) {
+                const int tauc = min(max(tau, t0), t1 - 1);
+                bf16x8 fop[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    fop[ks] = *reinterpret_cast<const bf16x8 *>(a.f + (size_t)tauc * kRank + 32 * ks + 8 * lg);
+                __builtin_amdgcn_s_waitcnt(0x0070);  // this wave's W_fb rows (and f rows) have landed
+                asm volatile("s_barrier" ::: "memory");  // and every other wave's
+                const __bf16 *sFb = reinterpret_cast<const __bf16 *>(smem + M.wfb);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int row = 64 * half + 16 * (lr >> 2) + 4 * m + (lr & 3);
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int j = (4 * ks + lg) ^ wfb_swz(row);
+                        acc = mma(*reinterpret_cast<const bf16x8 *>(sFb + row * kRank + 8 * j), fop[ks], acc);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) zf[4 * m + i] = acc[i];
+                }
+            }
             // decay gate gk = gmin * sigmoid(exp(A_log) * (z + dt_bias)) and its cumulative
             // sum over the sub-chunk's 16 tokens (= G_t - r_sub)
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 float zz[8], dtb[8];
-                unpack8(ld.z[pc], zz);
+                if constexpr (kGateProj) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) zz[j] = zf[8 * pc + j];
+                } else {
+                    unpack8(ld.z[pc], zz);
+                }
                 lds_read8(sDtb + cbase + 8 * pc, dtb);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -709,7 +780,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             // 2K cycles and wave 3, issuing after its inverse, waited behind them: part 0
             // here (the other waves while wave 3 inverts), part 1 after the off-diagonal
             // blocks.
-            load_chunk<0>(ld, a, tid_, h, t0, t1, c0 + kChunk);
+            load_chunk<0, kGateProj>(ld, a, tid_, h, t0, t1, c0 + kChunk);
         }
         lds_barrier();
         // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ: wave J (< 3) walks
@@ -754,7 +825,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             if (w == 0) column(std::integral_constant<int, 0>{});
             else if (w == 1) column(std::integral_constant<int, 1>{});
             else if (w == 2) column(std::integral_constant<int, 2>{});
-            load_chunk<1>(ld, a, tid_, h, t0, t1, c0 + kChunk);
+            load_chunk<1, kGateProj>(ld, a, tid_, h, t0, t1, c0 + kChunk);
         }
         lds_barrier();
         // sT is dead: Q~ = q e^G into region 6 (the precise mode after phase 4)
@@ -827,7 +898,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     U[tp][x] = acc;
                 }
         }
-        asm volatile("" ::"v"(ld.z[0]), "v"(ld.z[1]), "v"(ld.b));  // (see before the loop)
+        if constexpr (kGateProj)
+            asm volatile("" ::"v"(ld.b));  // (see before the loop)
+        else
+            asm volatile("" ::"v"(ld.z[0]), "v"(ld.z[1]), "v"(ld.b));
         lds_barrier();
         if constexpr (kPrecise) {
             // beta v and beta k e^G are dead: K_end^T hi/lo and Q~ hi/lo from registers
@@ -1080,9 +1154,9 @@ __global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs 
     }
 }
 
-template <bool kChunked, bool kPrecise>
-hipError_t launch_prefill_kernel(const PrefillArgs &a, size_t blocks, hipStream_t stream) {
-    const void *fn = reinterpret_cast<const void *>(&prefill_kernel<kChunked, kPrecise>);
+template <bool kChunked, bool kPrecise, bool kGateProj>
+hipError_t launch_prefill_kernel_t(const PrefillArgs &a, size_t blocks, hipStream_t stream) {
+    const void *fn = reinterpret_cast<const void *>(&prefill_kernel<kChunked, kPrecise, kGateProj>);
     static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (attr != hipSuccess) return attr;
     dim3 grid((unsigned)blocks), block(kThreads);
@@ -1090,18 +1164,25 @@ hipError_t launch_prefill_kernel(const PrefillArgs &a, size_t blocks, hipStream_
     return hipLaunchKernel(fn, grid, block, args, kLdsBytes, stream);
 }
 
+template <bool kChunked>
+hipError_t launch_prefill_kernel(const PrefillArgs &a, size_t blocks, hipStream_t stream) {
+    const bool gp = a.w_fb != nullptr;
+    if (a.c.precise)
+        return gp ? launch_prefill_kernel_t<kChunked, true, true>(a, blocks, stream)
+                  : launch_prefill_kernel_t<kChunked, true, false>(a, blocks, stream);
+    return gp ? launch_prefill_kernel_t<kChunked, false, true>(a, blocks, stream)
+              : launch_prefill_kernel_t<kChunked, false, false>(a, blocks, stream);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
-    if (a.path == kPathFused)
-        return a.c.precise ? launch_prefill_kernel<false, true>(a, (size_t)a.B * a.c.H, stream)
-                           : launch_prefill_kernel<false, false>(a, (size_t)a.B * a.c.H, stream);
+    if (a.path == kPathFused) return launch_prefill_kernel<false>(a, (size_t)a.B * a.c.H, stream);
     void *args[] = {const_cast<PrefillArgs *>(&a)};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&chunk_table_kernel), dim3(1), dim3(kTableThreads),
                                    args, 0, stream);
     if (e != hipSuccess) return e;
-    e = a.c.precise ? launch_prefill_kernel<true, true>(a, (size_t)a.nseg_cap * a.c.H, stream)
-                    : launch_prefill_kernel<true, false>(a, (size_t)a.nseg_cap * a.c.H, stream);
+    e = launch_prefill_kernel<true>(a, (size_t)a.nseg_cap * a.c.H, stream);
     if (e != hipSuccess) return e;
     return launch_carry(a, stream);
 }

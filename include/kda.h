@@ -335,6 +335,33 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs, int32_t total_to
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_prefill_gate_proj -- kda_prefill with the decay logits formed inside the library
+ * from the low-rank decay projection: instead of z = W_fb(W_fa x) the caller passes
+ * f = W_fa x, shared by all heads, and the second factor W_fb; each chunk forms its
+ * logits z = W_fb f with bf16 MFMAs (fp32 accumulation) before the gate.  The page
+ * "colibri/c/kimi_k3.c" gives the gate's argument as W_fb(W_fa x) + dt_bias (header
+ * comment "KDA per-head recurrence") and the two factors as the `Kda` struct's decay
+ * low-rank pair `fa, fb`.  This reads 256 bytes per token (f) instead of 256 bytes per
+ * token and head (z).
+ *
+ *   f                      [N, 128] bf16 (raw bit patterns): W_fa x of each token
+ *   w_fb                   [H*D, 128] bf16: row h*D + i is channel i of head h
+ *   all other arguments    as for kda_prefill (z is not taken; the rank is 128)
+ * The logits are not rounded to bf16 (kda_prefill takes them as bf16), so the results
+ * match kda_prefill's only up to that rounding.  Alignment: f and w_fb 16-byte aligned.
+ */
+kda_status kda_prefill_gate_proj(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens,
+                                 const int32_t *cu_seqlens,
+                                 const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t qkv_row_stride,
+                                 const uint16_t *f, const uint16_t *w_fb,
+                                 const uint16_t *b, const uint16_t *g,
+                                 const float *conv_w, const float *A_log, const float *dt_bias,
+                                 const float *norm_w,
+                                 const float *initial_state, const float *initial_conv_state,
+                                 void *out, float *final_state, float *final_conv_state,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kda_prefill_noalloc -- kda_prefill for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * The same computation (the same kernels, so the same bits) with no workspace

@@ -36,6 +36,7 @@ K = 4     # ShortConv taps
 
 # stream ids
 _S_STATE, _S_CONV_STATE, _S_CONV_W, _S_DT_BIAS, _S_A_LOG, _S_LENS = 1, 2, 3, 4, 5, 6
+_S_F, _S_W_FB = 7, 8
 _S_Q, _S_K, _S_V, _S_Z, _S_B, _S_G = 10, 11, 12, 13, 14, 15
 _STEP_STRIDE = 100  # decode step i uses stream id  base + STEP_STRIDE * (i + 1)
 
@@ -252,6 +253,14 @@ def case3_lengths(n: int = 16) -> np.ndarray:
 def case3_prefill(H: int = 96) -> PrefillCase:
     """16 sequences of lengths U[512, 4096], nonzero initial states and conv states."""
     return prefill_case(3, H, case3_lengths(), True, "cfg3-prefill")
+
+
+def lowrank_gate(seed: int, N: int, H: int, rank: int = 128):
+    """Inputs of the low-rank decay projection, as bf16 bit patterns: f = W_fa x [N, rank]
+    N(0, 1) (shared by the heads) and the second factor W_fb [H*D, rank] N(0, rank^-0.5),
+    so that z = W_fb f has the unit variance of the logits of the other workloads."""
+    return (normal(seed, _S_F, (N, rank), 1.0, bf16=True),
+            normal(seed, _S_W_FB, (H * D, rank), float(rank) ** -0.5, bf16=True))
 
 
 # ---------------------------------------------------------------------------------

@@ -109,6 +109,15 @@ int main() {
     }
     EXPECT(kda_state_copy(&c, 1, A, Ac, 4, s0, A, Ac + 16, 4, s0, nullptr), KDA_ERR_OVERLAP);
 
+    // the prefill with the decay projection inside: W_fb is required, and outputs may not
+    // overlap it
+    EXPECT(kda_prefill_gate_proj(&c, 1, 64, I, Hh, Hh, Hh, 0, Hh, nullptr, Hh, Hh, F, F, F, F, nullptr, nullptr, F,
+                                 F, F, nullptr, 0, nullptr),
+           KDA_ERR_NULL_ARG);
+    EXPECT(kda_prefill_gate_proj(&c, 0, 0, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F,
+                                 nullptr, 0, nullptr),
+           KDA_OK);
+
     // the allocation-free prefill: the same checks; an explicit chunked layout past the
     // scratch array is rejected before the array is looked up
     EXPECT(kda_prefill_noalloc(&c, -1, 64, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F,

@@ -408,3 +408,34 @@ def test_precision_flag():
     # the high-precision records carry the lo parts of W and Q~: 144,384 bytes each
     assert _ws(_cfg(prefill_path=2, num_heads=96, precision=1), 1, 8192) == 256 + (128 + 1) * 96 * 144384
     assert _ws(_cfg(prefill_path=1, precision=1), 1, 8192) == 0
+
+
+def _gate_proj(cfg, B, N, ptrs=None, stride=0, ws=None, ws_bytes=0):
+    # cu, q, k, v, f, w_fb, b, g, conv_w, A_log, dt_bias, norm_w, init_state, init_conv, out, final_state,
+    # final_conv
+    p = [ctypes.c_void_p(FAKE)] * 17 if ptrs is None else ptrs
+    return kda.lib().kda_prefill_gate_proj(ctypes.byref(cfg), B, N, *p[:4], stride, *p[4:], ws, ws_bytes, None)
+
+
+def test_prefill_gate_proj_rejections():
+    assert _gate_proj(_cfg(head_dim=64), 1, 8) == BAD_CONFIG
+    assert _gate_proj(_cfg(), -1, 8) == BAD_SHAPE
+    assert _gate_proj(_cfg(), 0, 0) == OK
+    for i in (4, 5):  # f and w_fb are required
+        p = [ctypes.c_void_p(FAKE)] * 17
+        p[i] = None
+        assert _gate_proj(_cfg(prefill_path=1), 2, 100, p) == NULL_ARG, i
+        p[i] = ctypes.c_void_p(FAKE + 8)
+        assert _gate_proj(_cfg(prefill_path=1), 2, 100, p) == MISALIGNED, i
+    # w_fb is still required with no tokens; f is not
+    p = [ctypes.c_void_p(FAKE)] * 17
+    p[5] = None
+    assert _gate_proj(_cfg(prefill_path=1), 2, 0, p) == NULL_ARG
+    # outputs over the factors
+    p = _spaced(17)
+    q = list(p)
+    q[14] = ctypes.c_void_p(p[5].value + 64)  # out on w_fb
+    assert _gate_proj(_cfg(prefill_path=1), 2, 100, q) == OVERLAP
+    q = list(p)
+    q[15] = ctypes.c_void_p(p[4].value)  # final_state on f
+    assert _gate_proj(_cfg(prefill_path=1), 2, 100, q) == OVERLAP

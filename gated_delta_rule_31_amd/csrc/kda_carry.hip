@@ -17,9 +17,9 @@
 //
 // Streaming.  A record's operand pieces (77 KB, in the order the MFMAs read them) go
 // straight from global memory into LDS with direct-to-LDS loads, double-buffered: the
-// next chunk's pieces are requested right after the barrier that opens the current chunk
-// and have the whole chunk to arrive, without occupying registers or issue slots for LDS
-// writes.  Each chunk-parity buffer is its own LDS array and the loop body is
+// next chunk's pieces are requested in four parts spread over the current chunk (after
+// its opening barrier, after the previous epilogue, after W S0 and after O) and arrive
+// while it computes, without occupying registers or issue slots for LDS writes.  Each chunk-parity buffer is its own LDS array and the loop body is
 // instantiated once per parity, so the compiler can tell the buffer being read from the
 // one being filled and does not wait for the loads in flight.  U' (this wave's 4 KB) is
 // prefetched into registers one chunk ahead.  O is computed transposed and normalised
@@ -150,25 +150,33 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) nw[i] = a.norm_w[16 * w + 4 * lg + i];
 
-    // record c's operand pieces into an LDS buffer (wave w: pieces 8j + w) and its U' into
-    // registers; c is clamped to the last record, so the request past it is a harmless
-    // reload, and every wave issues the same number of loads on every path
-    auto request = [&](lds_void *dst_base, int c, f32x4 (&Un)[2][2]) {
+    // Part `part` (0..3) of record c: operand pieces 8j + w for the part's j into an LDS
+    // buffer, and one of the wave's four U' tiles into registers.  c is clamped to the last
+    // record, so the request past it is a harmless reload, and every wave issues the same
+    // number of loads on every path.  (A CU streams about 21 B per cycle from memory, so a
+    // record takes most of a chunk to arrive; its four parts are issued between the
+    // chunk's products, so that no wave waits long to issue a load while the others
+    // compute.)
+    auto request = [&](auto part_c, lds_void *dst_base, int c, f32x4 (&Un)[2][2]) {
+        constexpr int part = decltype(part_c)::value;
+        constexpr int j0 = part == 0 ? 0 : (part == 1 ? 3 : (part == 2 ? 6 : 8));
+        constexpr int j1 = part == 0 ? 3 : (part == 1 ? 6 : (part == 2 ? 8 : kPiecesPerWave));
         const unsigned char *rec = rec0 + (size_t)min(c, nrec - 1) * rec_stride;
 #pragma unroll
-        for (int j = 0; j < kPiecesPerWave; ++j) {
+        for (int j = j0; j < j1; ++j) {
             const int piece = min(8 * j + w, RecS::kPieces - 1);
             __builtin_amdgcn_global_load_lds(rec + piece * REC_PIECE + lane * 16,
                                              (lds_void *)((__attribute__((address_space(3))) unsigned char *)dst_base +
                                                           piece * REC_PIECE),
                                              16, 0, 0);
         }
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-                Un[tp][x] = *reinterpret_cast<const f32x4 *>(rec + RecS::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
+        constexpr int tp = part >> 1, x = part & 1;
+        Un[tp][x] = *reinterpret_cast<const f32x4 *>(rec + RecS::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
     };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
 
     f32x4 Unext[2][2] = {};
     f32x4 oprev[4] = {};  // the previous chunk's O^T tiles, normalised one chunk later
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
             for (int x = 0; x < 2; ++x) U[tp][x] = Unext[tp][x];
-        request(nxt_lds, c + 1, Unext);
+        request(P0{}, nxt_lds, c + 1, Unext);
 
         // the previous chunk's epilogue (a full chunk: only the last can be partial)
         if (c > 0)
@@ -201,6 +209,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                                           kChunk, 0, w, lr, lg);
         uint2 g4[4];
         load_gate4(g4, a.g, HD, h, t0 + c0, L, w, lr, lg);
+        request(P1{}, nxt_lds, c + 1, Unext);
 
         auto opnd = [&](int piece) { return *reinterpret_cast<const bf16x8 *>(cur + piece * REC_PIECE + lane * 16); };
 
@@ -221,6 +230,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                 for (int P = 0; P < 4; ++P) ws = mma(opnd(RecS::w(tp, x, P)), Sh[P], ws);
                 U[tp][x] -= ws;
             }
+        request(P2{}, nxt_lds, c + 1, Unext);
         bf16x8 Uh[2], Ul[2];  // U as the B operand of token contractions, hi/lo [tp]
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
@@ -246,6 +256,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
             }
             o[tt] = acc;
         }
+        request(P3{}, nxt_lds, c + 1, Unext);
         rms_partials(o, part, w, lr, lg);
         // S = Diag(e^{G_end}) S0 + K_end^T U
         const float *sE = reinterpret_cast<const float *>(cur + RecS::kE * REC_PIECE);
@@ -272,7 +283,10 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
     };
 
     if (nrec > 0) {
-        request((lds_void *)carry_buf0, 0, Unext);
+        request(P0{}, (lds_void *)carry_buf0, 0, Unext);
+        request(P1{}, (lds_void *)carry_buf0, 0, Unext);
+        request(P2{}, (lds_void *)carry_buf0, 0, Unext);
+        request(P3{}, (lds_void *)carry_buf0, 0, Unext);
         for (int c = 0; c < nrec; c += 2) {
             chunk(std::integral_constant<int, 0>{}, c);
             if (c + 1 < nrec) chunk(std::integral_constant<int, 1>{}, c + 1);

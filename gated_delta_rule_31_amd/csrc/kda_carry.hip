@@ -22,9 +22,10 @@
 // while it computes, without occupying registers or issue slots for LDS writes.  Each chunk-parity buffer is its own LDS array and the loop body is
 // instantiated once per parity, so the compiler can tell the buffer being read from the
 // one being filled and does not wait for the loads in flight.  U' (this wave's 4 KB) is
-// prefetched into registers one chunk ahead.  O is computed transposed and normalised
-// from registers; a chunk's epilogue runs after the next chunk's opening barrier, which
-// publishes every wave's partial sums of squares.
+// prefetched into registers one chunk ahead.  O is computed transposed, staged in LDS as
+// token rows in the place of W and Q~ (dead by then), and normalised and stored a token per
+// 32 lanes early in the next chunk, so that every gate load and output store covers whole
+// rows.
 
 #include <type_traits>
 
@@ -36,15 +37,18 @@ namespace {
 constexpr int kCarryThreads = 512;
 using RecS = Rec<false>;
 using RecP = Rec<true>;
-constexpr int kBufBytes = RecS::kPieces * REC_PIECE;  // 78,848
+constexpr int kLoPieces = RecS::kP;                    // W and Q~: pieces 0 .. 31
+constexpr int kHiPieces = RecS::kPieces - RecS::kP;    // P, K_end, E: pieces 32 .. 76
 constexpr int kPiecesPerWave = (RecS::kPieces + 7) / 8;  // 10 (the last ones repeat piece 76)
 constexpr int kPiecesPerWaveP = (RecP::kPieces + 7) / 8;  // 14 (the last ones repeat piece 108)
 
-// The two chunk-parity buffers of operand pieces, and the RMS partial sums [parity][64
-// tokens][8 waves].
-__shared__ __align__(16) unsigned char carry_buf0[kBufBytes];
-__shared__ __align__(16) unsigned char carry_buf1[kBufBytes];
-__shared__ __align__(16) float carry_part[2][kChunk * 8];
+// The two chunk-parity buffers of operand pieces, each as two arrays (pieces 0 .. 31, which
+// later hold the staged O, and pieces 32 .. 76), so that the compiler can tell the part
+// being read from a part being filled and does not wait for the loads in flight.
+__shared__ __align__(16) unsigned char carry_lo0[kLoPieces * REC_PIECE];
+__shared__ __align__(16) unsigned char carry_hi0[kHiPieces * REC_PIECE];
+__shared__ __align__(16) unsigned char carry_lo1[kLoPieces * REC_PIECE];
+__shared__ __align__(16) unsigned char carry_hi1[kHiPieces * REC_PIECE];
 __shared__ int carry_order[kOrderMaxSeqs];  // longest-first workgroup order
 // the high-precision carry's single buffer of record pieces (109 KB: two would not fit)
 // and its RMS partial sums [64 tokens][8 waves]
@@ -108,6 +112,82 @@ __device__ __forceinline__ void carry_finish(const PrefillArgs &a, const f32x4 (
     }
 }
 
+// ---- the standard carry's epilogue, one token per 32 lanes ----
+// Wave w normalises and stores tokens 8w .. 8w+7 of a chunk, two per step s (0..3), from
+// the chunk's O staged in LDS as [64 tokens][128 values] fp32 (16-byte unit u of token r
+// at unit u ^ (r & 31), so that the O^T tiles' writes and the token reads are spread over
+// the banks).  Lane bits 0, 1, 4, 5 and 2 are bits 0..4 of the lane's unit j (values 4j ..
+// 4j+3) and lane bit 3 picks the step's token, so that each gate load and output store of
+// the wave covers two whole rows.  The RMS sum of a token is then a butterfly over j in bit
+// order: (j, j^1) and (j, j^2) by DPP, j^4 and j^8 by the permlane swaps, j^16 by a
+// swizzle.  That is the tree of the fused kernel's epilogue (the per-wave sums over
+// 4-value units j^1, j^2, then across waves j^4, j^8, j^16), so the layouts agree bit for
+// bit.
+__device__ __forceinline__ int epi_unit(int lane) {
+    return (lane & 3) | (((lane >> 4) & 3) << 2) | (((lane >> 2) & 1) << 4);
+}
+__device__ __forceinline__ int epi_token(int w, int s, int lane) { return 8 * w + 2 * s + ((lane >> 3) & 1); }
+
+// x[l] + x[l ^ m] for DPP control kCtrl: quad_perm 1,0,3,2 (m = 1) or 2,3,0,1 (m = 2)
+template <int kCtrl>
+__device__ __forceinline__ float add_dpp(float x) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float token_sum(float s) {
+    s = add_dpp<0xB1>(s);
+    s = add_dpp<0x4E>(s);
+    s = add_xor16(s);
+    s = add_xor32(s);
+    // x[l] + x[l ^ 4] inside each 32-lane half: swizzle with and-mask 31, xor-mask 4
+    return s + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(s), 0x101F));
+}
+
+// The output-gate logits of the lane's 4 values of its tokens (rows past the sequence's
+// end clamped to its last row, never stored)
+__device__ __forceinline__ void load_gate_rows(uint2 (&g4)[4], const uint16_t *g, size_t HD, int h, int tok0, int L,
+                                               int w, int lane) {
+    const int j = epi_unit(lane);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int r = min(epi_token(w, s, lane), L - 1);
+        g4[s] = *reinterpret_cast<const uint2 *>(g + (size_t)(tok0 + r) * HD + (size_t)h * kD + 4 * j);
+    }
+}
+
+// this wave's O^T tiles (values 16w + 4lg .. +3 of tokens 16tt + lr) into the staging area
+__device__ __forceinline__ void stage_o(const unsigned char *stage, const f32x4 (&o)[4], int w, int lr, int lg) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int r = 16 * tt + lr, u = 4 * w + lg;
+        *reinterpret_cast<f32x4 *>(const_cast<unsigned char *>(stage) + r * 512 + ((u ^ (r & 31)) << 4)) = o[tt];
+    }
+}
+
+// out = sigmoid(g) * RMSNorm(O) for the wave's tokens r < L of the staged chunk
+template <bool kBf16>
+__device__ __forceinline__ void epilogue_rows(const unsigned char *stage, const uint2 (&g4)[4], const float (&nw)[4],
+                                              float rms_eps, void *out, size_t HD, int h, int tok0, int L, int w,
+                                              int lane) {
+    const int j = epi_unit(lane);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int r = epi_token(w, s, lane);
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + r * 512 + ((j ^ (r & 31)) << 4));
+        float q = v[0] * v[0];
+        q = __builtin_fmaf(v[1], v[1], q);
+        q = __builtin_fmaf(v[2], v[2], q);
+        q = __builtin_fmaf(v[3], v[3], q);
+        q = token_sum(q);
+        const float rinv = __builtin_amdgcn_rsqf(q * (1.0f / kD) + rms_eps);
+        const float gg[4] = {__uint_as_float(g4[s].x << 16), __uint_as_float(g4[s].x & 0xffff0000u),
+                             __uint_as_float(g4[s].y << 16), __uint_as_float(g4[s].y & 0xffff0000u)};
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = sigm(gg[i]) * (v[i] * rinv * nw[i]);
+        if (r < L) store_out4(out, (size_t)(tok0 + r) * HD + (size_t)h * kD + 4 * j, y[0], y[1], y[2], y[3], kBf16);
+    }
+}
+
 // kBf16: the output buffer holds bf16 (round to nearest even), else fp32
 template <bool kBf16>
 __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) {
@@ -146,29 +226,28 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                     S[P][x][i] = S0 ? S0[key * kD + 16 * w + lr] : 0.0f;
                 }
     }
-    float nw[4];  // the RMSNorm weight of this lane's output columns 16w + 4lg + i
+    float nw[4];  // the RMSNorm weight of this lane's epilogue values 4j .. 4j+3
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nw[i] = a.norm_w[16 * w + 4 * lg + i];
+    for (int i = 0; i < 4; ++i) nw[i] = a.norm_w[4 * epi_unit(lane) + i];
 
     // Part `part` (0..3) of record c: operand pieces 8j + w for the part's j into an LDS
     // buffer, and one of the wave's four U' tiles into registers.  c is clamped to the last
     // record, so the request past it is a harmless reload, and every wave issues the same
-    // number of loads on every path.  (A CU streams about 21 B per cycle from memory, so a
-    // record takes most of a chunk to arrive; its four parts are issued between the
-    // chunk's products, so that no wave waits long to issue a load while the others
-    // compute.)
-    auto request = [&](auto part_c, lds_void *dst_base, int c, f32x4 (&Un)[2][2]) {
+    // number of loads on every path.  Parts 0 and 1 hold pieces 32 .. 76 (P, K_end, E),
+    // parts 2 and 3 pieces 0 .. 31 (W, Q~), whose place holds the staged O of the previous
+    // chunk until its epilogue has read it.
+    auto request = [&](auto part_c, auto parity, int c, f32x4 (&Un)[2][2]) {
         constexpr int part = decltype(part_c)::value;
-        constexpr int j0 = part == 0 ? 0 : (part == 1 ? 3 : (part == 2 ? 6 : 8));
-        constexpr int j1 = part == 0 ? 3 : (part == 1 ? 6 : (part == 2 ? 8 : kPiecesPerWave));
+        constexpr int BP = decltype(parity)::value;  // the buffer filled
+        constexpr int j0 = part == 0 ? 4 : (part == 1 ? 7 : (part == 2 ? 0 : 2));
+        constexpr int j1 = part == 0 ? 7 : (part == 1 ? kPiecesPerWave : (part == 2 ? 2 : 4));
         const unsigned char *rec = rec0 + (size_t)min(c, nrec - 1) * rec_stride;
 #pragma unroll
         for (int j = j0; j < j1; ++j) {
             const int piece = min(8 * j + w, RecS::kPieces - 1);
-            __builtin_amdgcn_global_load_lds(rec + piece * REC_PIECE + lane * 16,
-                                             (lds_void *)((__attribute__((address_space(3))) unsigned char *)dst_base +
-                                                          piece * REC_PIECE),
-                                             16, 0, 0);
+            unsigned char *dst = part >= 2 ? (BP ? carry_lo1 : carry_lo0) + piece * REC_PIECE
+                                           : (BP ? carry_hi1 : carry_hi0) + (piece - kLoPieces) * REC_PIECE;
+            __builtin_amdgcn_global_load_lds(rec + piece * REC_PIECE + lane * 16, (lds_void *)dst, 16, 0, 0);
         }
         constexpr int tp = part >> 1, x = part & 1;
         Un[tp][x] = *reinterpret_cast<const f32x4 *>(rec + RecS::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
@@ -179,21 +258,23 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
     using P3 = std::integral_constant<int, 3>;
 
     f32x4 Unext[2][2] = {};
-    f32x4 oprev[4] = {};  // the previous chunk's O^T tiles, normalised one chunk later
-    uint2 gprev[4] = {};  // and its output-gate logits
+    uint2 gprev[4] = {};  // the previous chunk's output-gate logits
 
-    // one chunk; the buffer parity B is a compile-time constant
+    // one chunk; the buffer parity B is a compile-time constant.  Chunk c's O is staged in
+    // pieces 0 .. 31 of its own buffer (W and Q~ are dead once every wave has its O) and
+    // normalised and stored early in chunk c + 1, whose stores then have a whole chunk to
+    // drain before the next barrier waits for them.
     auto chunk = [&](auto parity, int c) {
         constexpr int B = decltype(parity)::value;
-        const unsigned char *cur = B ? carry_buf1 : carry_buf0;
-        lds_void *nxt_lds = B ? (lds_void *)carry_buf0 : (lds_void *)carry_buf1;
-        float *part = carry_part[B];
-        const float *part_prev = carry_part[B ^ 1];
+        using Nxt = std::integral_constant<int, B ^ 1>;
+        const unsigned char *cur_lo = B ? carry_lo1 : carry_lo0;
+        const unsigned char *cur_hi = B ? carry_hi1 : carry_hi0;
+        const unsigned char *prv_lo = B ? carry_lo0 : carry_lo1;  // chunk c - 1's staged O
         const int c0 = c * kChunk;
         const int L = min(kChunk, T - c0);
 
-        // this chunk's pieces (every wave's) are in `cur`; nobody reads `nxt` any more;
-        // the previous chunk's partial sums are published
+        // this chunk's pieces (every wave's) are in `cur`; nobody reads `prv` but the
+        // epilogue; the previous chunk's O is staged in it
         barrier_all_mem();
 
         f32x4 U[2][2];
@@ -201,17 +282,20 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
         for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
             for (int x = 0; x < 2; ++x) U[tp][x] = Unext[tp][x];
-        request(P0{}, nxt_lds, c + 1, Unext);
+        request(P0{}, Nxt{}, c + 1, Unext);
 
         // the previous chunk's epilogue (a full chunk: only the last can be partial)
         if (c > 0)
-            gated_rms_store<kBf16, false>(oprev, gprev, part_prev, nw, a.c.rms_eps, a.out, HD, h, t0 + c0 - kChunk,
-                                          kChunk, 0, w, lr, lg);
+            epilogue_rows<kBf16>(prv_lo, gprev, nw, a.c.rms_eps, a.out, HD, h, t0 + c0 - kChunk, kChunk, w, lane);
         uint2 g4[4];
-        load_gate4(g4, a.g, HD, h, t0 + c0, L, w, lr, lg);
-        request(P1{}, nxt_lds, c + 1, Unext);
+        load_gate_rows(g4, a.g, HD, h, t0 + c0, L, w, lane);
+        request(P1{}, Nxt{}, c + 1, Unext);
 
-        auto opnd = [&](int piece) { return *reinterpret_cast<const bf16x8 *>(cur + piece * REC_PIECE + lane * 16); };
+        auto opnd = [&](int piece) {
+            const unsigned char *p = piece < kLoPieces ? cur_lo + piece * REC_PIECE
+                                                       : cur_hi + (piece - kLoPieces) * REC_PIECE;
+            return *reinterpret_cast<const bf16x8 *>(p + lane * 16);
+        };
 
         bf16x8 Sh[4];  // S0 as the B operand of key contractions
 #pragma unroll
@@ -230,7 +314,9 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                 for (int P = 0; P < 4; ++P) ws = mma(opnd(RecS::w(tp, x, P)), Sh[P], ws);
                 U[tp][x] -= ws;
             }
-        request(P2{}, nxt_lds, c + 1, Unext);
+        // every wave's epilogue has read the staged O: pieces 0 .. 31 of `prv` may be loaded
+        lds_barrier();
+        request(P2{}, Nxt{}, c + 1, Unext);
         bf16x8 Uh[2], Ul[2];  // U as the B operand of token contractions, hi/lo [tp]
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
@@ -256,10 +342,12 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
             }
             o[tt] = acc;
         }
-        request(P3{}, nxt_lds, c + 1, Unext);
-        rms_partials(o, part, w, lr, lg);
+        request(P3{}, Nxt{}, c + 1, Unext);
+        // every wave is done with W and Q~: O goes into their place
+        lds_barrier();
+        stage_o(cur_lo, o, w, lr, lg);
         // S = Diag(e^{G_end}) S0 + K_end^T U
-        const float *sE = reinterpret_cast<const float *>(cur + RecS::kE * REC_PIECE);
+        const float *sE = reinterpret_cast<const float *>(cur_hi + (RecS::kE - kLoPieces) * REC_PIECE);
 #pragma unroll
         for (int P = 0; P < 4; ++P)
 #pragma unroll
@@ -276,27 +364,25 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                 S[P][x] = acc;
             }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            oprev[tt] = o[tt];
-            gprev[tt] = g4[tt];
-        }
+        for (int s = 0; s < 4; ++s) gprev[s] = g4[s];
     };
 
     if (nrec > 0) {
-        request(P0{}, (lds_void *)carry_buf0, 0, Unext);
-        request(P1{}, (lds_void *)carry_buf0, 0, Unext);
-        request(P2{}, (lds_void *)carry_buf0, 0, Unext);
-        request(P3{}, (lds_void *)carry_buf0, 0, Unext);
+        using B0 = std::integral_constant<int, 0>;
+        request(P0{}, B0{}, 0, Unext);
+        request(P1{}, B0{}, 0, Unext);
+        request(P2{}, B0{}, 0, Unext);
+        request(P3{}, B0{}, 0, Unext);
         for (int c = 0; c < nrec; c += 2) {
             chunk(std::integral_constant<int, 0>{}, c);
             if (c + 1 < nrec) chunk(std::integral_constant<int, 1>{}, c + 1);
         }
         // the last chunk's epilogue; the wait also drains the reload requested past the
-        // last record before the workgroup's LDS is released
+        // last record (into the other buffer) and publishes the staged O
         barrier_all_mem();
         const int cl = nrec - 1;
-        gated_rms_store<kBf16, false>(oprev, gprev, carry_part[cl & 1], nw, a.c.rms_eps, a.out, HD, h,
-                                      t0 + cl * kChunk, min(kChunk, T - cl * kChunk), 0, w, lr, lg);
+        epilogue_rows<kBf16>((cl & 1) ? carry_lo1 : carry_lo0, gprev, nw, a.c.rms_eps, a.out, HD, h,
+                             t0 + cl * kChunk, min(kChunk, T - cl * kChunk), w, lane);
     }
 
     carry_finish(a, S, seq, h, t0, t1);

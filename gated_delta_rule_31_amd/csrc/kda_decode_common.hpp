@@ -1,12 +1,11 @@
-// kda_decode_common.hpp -- the per-token arithmetic of the two decode kernels
-// (kda_decode.hip: one token; kda_decode_multi.hip: several tokens per launch).  Both
-// evaluate each step of a token with these functions, so that n tokens of the
-// multi-token kernel give the bits of n one-token calls.  Not part of the public ABI.
+// kda_decode_common.hpp -- the per-token arithmetic of the decode kernels (kda_decode.hip:
+// one token; kda_decode_multi.hip: the conv, gate and norm steps of several tokens per
+// launch).  Not part of the public ABI.
 //
 // Floating-point contraction is off from here to the end of the including file, and every
 // fused multiply-add is written out (fmaf): left to the compiler, the choice of which
 // product of a*b + c*d to fuse depends on the surrounding code and on register pressure,
-// and so could differ between the two kernels.
+// and so could differ between kernels that share these steps.
 #pragma once
 
 #include "kda_device.hpp"

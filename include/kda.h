@@ -214,8 +214,11 @@ kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int
  * the state is read once, carried through the tokens, and written once.  This is the
  * decode step for several known tokens (speculative verification, or a short chunk of
  * a prompt against a resident state); each token follows the header comment "KDA
- * per-head recurrence" (page "colibri/c/kimi_k3.c") exactly as kda_decode_step does,
- * and n tokens here give the bits of n kda_decode_step calls on the same tokens.
+ * per-head recurrence" (page "colibri/c/kimi_k3.c").  Tokens are evaluated in blocks of
+ * eight in the chunk form of that recurrence (the same terms summed in another order), so
+ * n tokens here agree with n kda_decode_step calls to fp32 rounding (about 1e-6 relative),
+ * not bit for bit; the final conv windows are exact.  A call with n_tokens = a repeats,
+ * bit for bit, the outputs of the first a tokens of a call with more tokens.
  *
  * Verify and roll back (the engine's multi-token verify and rollback are not
  * implemented on the pages; this is this library's form of it): call with

@@ -1,8 +1,10 @@
 """GPU parity of kda_decode_multi (several known tokens per sequence in one call) against
 the fp64 oracle (max relative error 1e-4 per (sequence, head) slice, as for one-token
-decode), bit-for-bit agreement with the same number of kda_decode_step calls, and the
+decode), agreement with the same number of kda_decode_step calls to fp32 rounding (the
+multi-token kernel evaluates blocks of eight tokens in the chunk form of the recurrence,
+the same terms summed in another order: 2e-5 relative per slice, windows exact), and the
 verify / roll-back use: out-of-place candidates, then an in-place commit of the
-accepted prefix."""
+accepted prefix, whose outputs are the candidates' bits."""
 import numpy as np
 import pytest
 import torch
@@ -14,6 +16,15 @@ from tests.parity import DECODE_REL_TOL, DecodeRun, decode_oracle, slice_rel, t
 pytestmark = pytest.mark.gpu
 
 D = 128
+MULTI_VS_STEPS_REL = 2e-5  # block form against token-by-token fp32, per (sequence, head) slice
+
+
+def _rel(x: torch.Tensor, r: torch.Tensor) -> float:
+    """max over (..., D) slices of max|x - r| / max|r|"""
+    x = x.double().reshape(-1, D)
+    r = r.double().reshape(-1, D)
+    den = r.abs().amax(dim=1).clamp_min(1e-30)
+    return float(((x - r).abs().amax(dim=1) / den).max())
 
 
 class MultiRun:
@@ -80,16 +91,19 @@ def test_per_sequence_counts_against_oracle(device):
     assert worst <= DECODE_REL_TOL, worst
 
 
-def test_in_place_equals_single_steps_bitwise(device):
-    case = ki.decode_case(311, 5, 6, 6, "multi-vs-steps")
-    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=6", flush=True)
-    mr = MultiRun(case, 6, device)
+@pytest.mark.parametrize("T", [6, 8, 11, 17])
+def test_in_place_agrees_with_single_steps(device, T):
+    case = ki.decode_case(311, 5, 6, T, f"multi-vs-steps-{T}")
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T={T}", flush=True)
+    mr = MultiRun(case, T, device)
     state, conv = mr.state0.clone(), mr.conv0.clone()
     out = mr.call(state, conv)
-    outs, st, cst = _single_steps(case, 6, device)
-    for i in range(6):
-        assert torch.equal(out[:, i], outs[i]), i
-    assert torch.equal(state, st) and torch.equal(conv, cst)
+    outs, st, cst = _single_steps(case, T, device)
+    worst = max(_rel(out[:, i], outs[i]) for i in range(T))
+    worst = max(worst, _rel(state, st))
+    print(f"[decode-multi] {case.name}: max rel diff against single steps {worst:.3e}", flush=True)
+    assert worst <= MULTI_VS_STEPS_REL, worst
+    assert torch.equal(conv, cst)
 
 
 def test_verify_then_commit_accepted_prefix(device):
@@ -105,8 +119,14 @@ def test_verify_then_commit_accepted_prefix(device):
     for b, a in enumerate(accepted):
         outs, st, cst = _single_steps(case, a, device) if a else ([], mr.state0, mr.conv0)
         for i in range(a):
-            assert torch.equal(out[b, i], outs[i][b]) and torch.equal(spec_out[b, i], outs[i][b])
-        assert torch.equal(state[b], st[b]) and torch.equal(conv[b], cst[b])
+            assert torch.equal(out[b, i], spec_out[b, i])  # the commit repeats the candidates' bits
+            assert _rel(out[b, i], outs[i][b]) <= MULTI_VS_STEPS_REL
+        assert torch.isnan(out[b, a:]).all()
+        if a == 0:
+            assert torch.equal(state[b], mr.state0[b]) and torch.equal(conv[b], mr.conv0[b])
+        else:
+            assert _rel(state[b], st[b]) <= MULTI_VS_STEPS_REL
+            assert torch.equal(conv[b], cst[b])
     # a fully accepted sequence ends where the candidates ended
     assert torch.equal(state[0], spec_s[0]) and torch.equal(conv[0], spec_c[0])
 
@@ -118,9 +138,9 @@ def test_k3_shape_four_tokens(device):
     state, conv = mr.state0.clone(), mr.conv0.clone()
     out = mr.call(state, conv)
     outs, st, cst = _single_steps(case, 4, device)
-    assert torch.equal(state, st) and torch.equal(conv, cst)
+    assert _rel(state, st) <= MULTI_VS_STEPS_REL and torch.equal(conv, cst)
     for i in range(4):
-        assert torch.equal(out[:, i], outs[i])
+        assert _rel(out[:, i], outs[i]) <= MULTI_VS_STEPS_REL
     rng = np.random.default_rng(313)
     pairs = [(0, 0), (63, 95)] + [(int(b), int(h)) for b, h in zip(rng.integers(0, 64, 10), rng.integers(0, 96, 10))]
     ref = decode_oracle(case, pairs, 4)
@@ -136,8 +156,9 @@ def test_k3_shape_four_tokens(device):
 
 def test_pool_verify_and_commit_matches_dense(device):
     """kda_decode_multi_slots over a pool: candidates into a second pool, then the accepted
-    prefixes committed in place; every applied row and entry equals the dense call's bits,
-    and a row aimed past the pool leaves everything untouched."""
+    prefixes committed in place; every applied output row equals the dense call's bits,
+    the committed entries agree with single steps, and a row aimed past the pool leaves
+    everything untouched."""
     case = ki.decode_case(314, 3, 4, 5, "multi-slots")
     B, H, T, P = case.B, case.H, 5, 6
     home = [4, 0, 2]
@@ -167,8 +188,56 @@ def test_pool_verify_and_commit_matches_dense(device):
         a = int(accepted[bi])
         assert torch.equal(out2[bi, :a], dense_out[bi, :a]) and torch.isnan(out2[bi, a:]).all(), bi
         outs, st, cst = _single_steps(case, a, device) if a else ([], mr.state0, mr.conv0)
-        assert torch.equal(pool_s[e], st[bi]) and torch.equal(pool_c[e], cst[bi]), bi
+        if a == 0:
+            assert torch.equal(pool_s[e], st[bi]), bi
+        else:
+            assert _rel(pool_s[e], st[bi]) <= MULTI_VS_STEPS_REL, bi
+        assert torch.equal(pool_c[e], cst[bi]), bi
     assert torch.isnan(out[3]).all() and torch.isnan(out2[3]).all()
     for e in set(range(P)) - set(home):
         assert torch.equal(pool_s[e], before_s[e]) and torch.equal(pool_c[e], before_c[e]), e
         assert (cand_s[e] == 0).all() and (cand_c[e] == 0).all(), e
+
+
+@pytest.mark.parametrize("regime", ["strongest-decay", "no-decay-beta-one", "mixed"])
+def test_extreme_gates_against_oracle(device, regime):
+    """The block form at the gates' extremes: the strongest decay (the cumulative log decay
+    of a block reaches -40, the bound of its e^{+-G} factors), no decay with beta = 1 (the
+    plain delta rule, where the block's triangular solve is least damped), and a mix."""
+    import oracle
+    from tests.parity import oracle_cfg
+    T = 19
+    case = ki.decode_case(315, 3, 4, T, f"multi-{regime}")
+    mr = MultiRun(case, T, device)
+    steps = [case.step(i) for i in range(T)]
+    x = {nm: np.ascontiguousarray(np.stack([getattr(s, nm) for s in steps], axis=1)) for nm in "qkvzbg"}
+    rng = np.random.default_rng(315)
+    if regime == "strongest-decay":
+        x["z"][...] = 40.0
+        x["b"][...] = 30.0
+    elif regime == "no-decay-beta-one":
+        x["z"][...] = -300.0
+        x["b"][...] = 30.0
+    else:
+        x["z"][...] = rng.choice([-300.0, 40.0, 0.0], size=x["z"].shape)
+        x["b"][...] = rng.choice([-30.0, 30.0, 0.0], size=x["b"].shape)
+    mr.xs[3] = t(x["z"].astype(np.float32), device)
+    mr.xs[4] = t(x["b"].astype(np.float32), device)
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T={T}", flush=True)
+    state, conv = mr.state0.clone(), mr.conv0.clone()
+    out = mr.call(state, conv).cpu().numpy().reshape(case.B, T, case.H, D)
+    st = state.cpu().numpy()
+    B, H = case.B, case.H
+    flat = {nm: x[nm].reshape(B * T, -1) for nm in x}
+    p = case.params
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle.forward(oracle_cfg(), np.arange(B + 1) * T, flat["q"], flat["k"], flat["v"], flat["z"], flat["b"],
+                         flat["g"], p.conv_w, p.A_log, p.dt_bias, p.norm_w, case.state, case.conv_state, pairs=pairs)
+    worst = 0.0
+    for (b, h) in pairs:
+        r = ref[(b, h)]
+        for i in range(T):
+            worst = max(worst, slice_rel(out[b, i, h], r.out[i]))
+        worst = max(worst, slice_rel(st[b, h], r.state))
+    print(f"[decode-multi] {case.name}: max rel err {worst:.3e}", flush=True)
+    assert worst <= DECODE_REL_TOL, worst

@@ -89,7 +89,9 @@ def prefill_bytes(N: int, B: int, H: int, initial: bool, out_bytes: int = 4) -> 
 # (sha256 of the listed files, concatenated in order), so a figure is never reported
 # for a kernel that changed after the counters were taken.
 
-DECODE_SRCS = ["kda_decode.hip", "kda_decode_common.hpp"]
+# (each list covers the kernel file and every header it includes)
+DECODE_SRCS = ["kda_decode.hip", "kda_decode_common.hpp", "kda_device.hpp", "kda_internal.hpp"]
+DECODE_MULTI_SRCS = ["kda_decode_multi.hip", "kda_decode_common.hpp", "kda_device.hpp", "kda_internal.hpp"]
 PREFILL_SRCS = ["kda_prefill.hip", "kda_carry.hip", "kda_device.hpp", "kda_internal.hpp"]
 
 
@@ -343,10 +345,18 @@ def bench_decode_multi(args, dev, T: int):
     torch.cuda.synchronize()
     kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
     alg = decode_multi_bytes(B, H, T)
-    return {"workload": f"kda-decode-multi-64seq-96head-{T}tok", "tokens": T,
-            "kernel_avg_us": round(kern_ms * 1e3, 2), "us_per_token": round(kern_ms * 1e3 / T, 2),
-            "tokens_per_s": round(B * T / (kern_ms * 1e-3), 1), "alg_bytes_per_launch": alg,
-            "hbm_frac": round(alg / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    res = {"workload": f"kda-decode-multi-64seq-96head-{T}tok", "tokens": T,
+           "kernel_avg_us": round(kern_ms * 1e3, 2), "us_per_token": round(kern_ms * 1e3 / T, 2),
+           "tokens_per_s": round(B * T / (kern_ms * 1e-3), 1), "alg_bytes_per_launch": alg,
+           "hbm_frac": round(alg / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if T == 8:
+        # HBM bytes and busy fractions from the rocprofv3 summary of this leg, while its
+        # kernel sources are the ones measured
+        prof = profile_values("decode_multi_kernel_64seq_96head_8tok", DECODE_MULTI_SRCS)
+        res["traffic"] = prof.get("hbm_bytes_per_call")
+        res["mfma_busy_frac"] = prof.get("mfma_busy_frac")
+        res["valu_issue_frac"] = prof.get("valu_issue_frac")
+    return res
 
 
 def bench_decode_slots(args, dev):
@@ -647,8 +657,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--prefill-path", choices=["auto", "fused", "chunked"], default="auto",
                     help="prefill work layout (auto: the library's estimate of the faster one)")
-    ap.add_argument("--only", choices=["all", "decode-cfg4", "decode-cfg1", "decode-multi", "decode-slots",
-                                       "prefill-cfg2", "prefill-cfg3", "prefill-gate-proj", "copy"],
+    ap.add_argument("--only", choices=["all", "decode-cfg4", "decode-cfg1", "decode-multi", "decode-multi-8",
+                                       "decode-slots", "prefill-cfg2", "prefill-cfg3", "prefill-gate-proj", "copy"],
                     default="all", help="run one part only (counter runs under rocprofv3 use this)")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
@@ -670,6 +680,7 @@ def main():
                   "decode-cfg1": lambda: bench_decode_cfg1(args, dev),
                   "decode-slots": lambda: bench_decode_slots(args, dev),
                   "decode-multi": lambda: [bench_decode_multi(args, dev, T) for T in (4, 8)],
+                  "decode-multi-8": lambda: bench_decode_multi(args, dev, 8),
                   "prefill-cfg2": lambda: bench_prefill(args, dev, "cfg2"),
                   "prefill-cfg3": lambda: bench_prefill(args, dev, "cfg3"),
                   "prefill-gate-proj": lambda: bench_prefill_gate_proj(args, dev)}

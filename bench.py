@@ -308,9 +308,10 @@ def bench_decode_cfg1(args, dev):
             "traffic": prof.get("hbm_bytes_per_launch")}
 
 
-def bench_decode_multi(args, dev, T: int):
+def bench_decode_multi(args, dev, T: int, form: int = 0):
     """T known tokens per sequence in one kda_decode_multi call, 64 sequences x 96 heads,
-    in place, three state sets rotated as in the one-token leg."""
+    in place, three state sets rotated as in the one-token leg; form: the call's
+    decode_multi_form (0: blocks of eight tokens, the default; 1: token by token)."""
     import torch
 
     import kda_inputs as ki
@@ -318,7 +319,7 @@ def bench_decode_multi(args, dev, T: int):
 
     case = ki.case1_decode()
     B, H = case.B, case.H
-    cfg = kda.KdaConfig(num_heads=H)
+    cfg = kda.KdaConfig(num_heads=H, decode_multi_form=form)
     p = case.params
     tt = _tt(dev)
     conv_w, A_log, dt_bias, norm_w = tt(p.conv_w), tt(p.A_log), tt(p.dt_bias), tt(p.norm_w)
@@ -345,11 +346,12 @@ def bench_decode_multi(args, dev, T: int):
     torch.cuda.synchronize()
     kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
     alg = decode_multi_bytes(B, H, T)
-    res = {"workload": f"kda-decode-multi-64seq-96head-{T}tok", "tokens": T,
+    res = {"workload": f"kda-decode-multi-64seq-96head-{T}tok" + ("-sequential" if form else ""), "tokens": T,
+           "form": "sequential" if form else "block",
            "kernel_avg_us": round(kern_ms * 1e3, 2), "us_per_token": round(kern_ms * 1e3 / T, 2),
            "tokens_per_s": round(B * T / (kern_ms * 1e-3), 1), "alg_bytes_per_launch": alg,
            "hbm_frac": round(alg / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    if T == 8:
+    if T == 8 and not form:
         # HBM bytes and busy fractions from the rocprofv3 summary of this leg, while its
         # kernel sources are the ones measured
         prof = profile_values("decode_multi_kernel_64seq_96head_8tok", DECODE_MULTI_SRCS)
@@ -679,7 +681,8 @@ def main():
                   "decode-cfg4": lambda: bench_decode_cfg4(args, dev),
                   "decode-cfg1": lambda: bench_decode_cfg1(args, dev),
                   "decode-slots": lambda: bench_decode_slots(args, dev),
-                  "decode-multi": lambda: [bench_decode_multi(args, dev, T) for T in (4, 8)],
+                  "decode-multi": lambda: [bench_decode_multi(args, dev, T) for T in (4, 8)]
+                                          + [bench_decode_multi(args, dev, 8, form=1)],
                   "decode-multi-8": lambda: bench_decode_multi(args, dev, 8),
                   "prefill-cfg2": lambda: bench_prefill(args, dev, "cfg2"),
                   "prefill-cfg3": lambda: bench_prefill(args, dev, "cfg3"),
@@ -695,7 +698,7 @@ def main():
         dec1 = bench_decode_cfg1(args, dev)
         log(f"decode cfg1: {dec1}")
         log("decode_multi: 64 seq x 96 heads, 4 and 8 tokens per call")
-        multi = [bench_decode_multi(args, dev, T) for T in (4, 8)]
+        multi = [bench_decode_multi(args, dev, T) for T in (4, 8)] + [bench_decode_multi(args, dev, 8, form=1)]
         log(f"decode_multi: {multi}")
         log("decode_slots: 64 rows of a 192-entry pool x 96 heads")
         slots = bench_decode_slots(args, dev)

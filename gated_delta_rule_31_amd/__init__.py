@@ -18,14 +18,14 @@ __all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_
            "kda_prefill", "kda_prefill_gate_proj", "kda_prefill_noalloc", "kda_prefill_workspace_bytes",
            "kda_state_copy", "KdaError",
            "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED",
-           "PRECISION_STANDARD", "PRECISION_HIGH"]
+           "PRECISION_STANDARD", "PRECISION_HIGH", "MULTI_BLOCK", "MULTI_SEQUENTIAL"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi",
                     "kda_decode_multi_slots", "kda_prefill", "kda_prefill_gate_proj", "kda_prefill_noalloc",
                     "kda_prefill_workspace_bytes",
                     "kda_state_copy", "kda_status_str", "kda_abi_version")
-ABI_VERSION = 8
+ABI_VERSION = 9
 HEAD_DIM = 128
 CONV = 4
 RANK = 128  # rank of the low-rank decay projection (kda_prefill_gate_proj)
@@ -43,6 +43,7 @@ class _CConfig(ctypes.Structure):
         ("prefill_path", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
         ("precision", ctypes.c_int32),
+        ("decode_multi_form", ctypes.c_int32),
     ]
 
 # kda_config.prefill_path values
@@ -52,6 +53,9 @@ PREFILL_CHUNKED = 2  # chunk records in parallel, then the carry; needs a worksp
 # kda_config.precision values (kda_prefill)
 PRECISION_STANDARD = 0  # bf16 MFMA operands, the decisive ones split hi + lo
 PRECISION_HIGH = 1      # every MFMA operand of the chunk algebra split hi + lo
+# kda_config.decode_multi_form values (kda_decode_multi)
+MULTI_BLOCK = 0       # blocks of eight tokens in the chunk form; fp32 rounding of single steps
+MULTI_SEQUENTIAL = 1  # token by token: the bits of the same number of single steps
 
 
 @dataclass
@@ -66,13 +70,14 @@ class KdaConfig:
     prefill_path: int = PREFILL_AUTO
     out_dtype: torch.dtype = torch.float32  # or torch.bfloat16: element type of the outputs
     precision: int = PRECISION_STANDARD     # kda_prefill operand precision
+    decode_multi_form: int = MULTI_BLOCK    # kda_decode_multi evaluation form
 
     def _c(self) -> _CConfig:
         if self.out_dtype not in (torch.float32, torch.bfloat16):
             raise ValueError(f"out_dtype must be torch.float32 or torch.bfloat16, not {self.out_dtype}")
         return _CConfig(self.num_heads, self.head_dim, self.conv_size, self.gate_lower_bound, self.l2_eps,
                         self.rms_eps, self.q_scale, self.prefill_path, 1 if self.out_dtype == torch.bfloat16 else 0,
-                        self.precision)
+                        self.precision, self.decode_multi_form)
 
 
 class KdaError(RuntimeError):

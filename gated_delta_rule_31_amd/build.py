@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_decode_multi.hip", "kda_prefill.hip", "kda_carry.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_decode_multi.hip", "kda_decode_multi_seq.hip", "kda_prefill.hip",
+           "kda_carry.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -68,6 +68,8 @@ kda_status check_config(const kda_config *cfg, kda::MixerConsts *out) {
         return KDA_ERR_BAD_CONFIG;
     if (cfg->out_dtype != KDA_OUT_F32 && cfg->out_dtype != KDA_OUT_BF16) return KDA_ERR_BAD_CONFIG;
     if (cfg->precision != KDA_PRECISION_STANDARD && cfg->precision != KDA_PRECISION_HIGH) return KDA_ERR_BAD_CONFIG;
+    if (cfg->decode_multi_form != KDA_MULTI_BLOCK && cfg->decode_multi_form != KDA_MULTI_SEQUENTIAL)
+        return KDA_ERR_BAD_CONFIG;
     out->H = cfg->num_heads;
     out->gate_lower_bound = cfg->gate_lower_bound;
     out->l2_eps = cfg->l2_eps;
@@ -75,6 +77,7 @@ kda_status check_config(const kda_config *cfg, kda::MixerConsts *out) {
     out->q_scale = cfg->q_scale > 0.0f ? cfg->q_scale : 1.0f / sqrtf((float)kda::kD);
     out->out_bf16 = cfg->out_dtype == KDA_OUT_BF16;
     out->precise = cfg->precision == KDA_PRECISION_HIGH;
+    out->multi_seq = cfg->decode_multi_form == KDA_MULTI_SEQUENTIAL;
     return KDA_OK;
 }
 
@@ -199,6 +202,7 @@ kda_config kda_config_default(void) {
     c.prefill_path = KDA_PREFILL_AUTO;
     c.out_dtype = KDA_OUT_F32;
     c.precision = KDA_PRECISION_STANDARD;
+    c.decode_multi_form = KDA_MULTI_BLOCK;
     return c;
 }
 
@@ -276,7 +280,9 @@ kda_status decode_multi(const kda_config *cfg, int32_t batch, int32_t tokens, co
     a.out = out;
     a.slots = pooled ? slots : nullptr;
     a.pool = pool_size;
-    return kda::launch_decode_multi(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    const hipError_t e = a.c.multi_seq ? kda::launch_decode_multi_seq(a, static_cast<hipStream_t>(stream))
+                                       : kda::launch_decode_multi(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 // ---- the scratch array of kda_prefill_noalloc ----

@@ -21,6 +21,7 @@ struct MixerConsts {
     float q_scale;
     int out_bf16;  // the output buffers hold bf16 (round to nearest even), else fp32
     int precise;   // prefill: every MFMA operand of the chunk algebra split into bf16 hi + lo
+    int multi_seq; // decode_multi: token by token (the bits of one-token calls), else blocks
 };
 
 // Four consecutive output values at element i (a multiple of 4) of an fp32 or bf16
@@ -162,6 +163,8 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeMultiArgs &a, hipStream_t stream);
+// the token-by-token form (kda_decode_multi_seq.hip)
+hipError_t launch_decode_multi_seq(const DecodeMultiArgs &a, hipStream_t stream);
 // the whole prefill in the chosen layout (kda_prefill.hip); the chunked layout's last
 // launch, the carry, is in kda_carry.hip
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);

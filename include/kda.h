@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 8
+#define KDA_ABI_VERSION 9
 
 typedef enum {
     KDA_OK = 0,
@@ -95,7 +95,18 @@ typedef struct {
     int32_t prefill_path;   /* KDA_PREFILL_AUTO, _FUSED or _CHUNKED (kda_prefill only) */
     int32_t out_dtype;      /* KDA_OUT_F32 or KDA_OUT_BF16: element type of every `out` */
     int32_t precision;      /* KDA_PRECISION_STANDARD or _HIGH (kda_prefill only) */
+    int32_t decode_multi_form; /* KDA_MULTI_BLOCK or _SEQUENTIAL (kda_decode_multi only) */
 } kda_config;
+
+/* How kda_decode_multi evaluates its tokens (both fp32, the same recurrence):
+ *   KDA_MULTI_BLOCK       blocks of eight tokens in the chunk form of the recurrence, with
+ *                         the state products on fp32 MFMAs; agrees with the same number
+ *                         of kda_decode_step calls to fp32 rounding (about 3e-6
+ *                         relative), not bit for bit.  About 1.6x faster at 8 tokens.
+ *   KDA_MULTI_SEQUENTIAL  token by token with kda_decode_step's arithmetic in the same
+ *                         order: n tokens give the bits of n kda_decode_step calls. */
+#define KDA_MULTI_BLOCK 0
+#define KDA_MULTI_SEQUENTIAL 1
 
 /* Operand precision of kda_prefill's chunked algebra (decode is fp32 throughout).
  *   KDA_PRECISION_STANDARD  bf16 MFMA operands with fp32 accumulation, the operands that
@@ -214,11 +225,14 @@ kda_status kda_decode_step_slots(const kda_config *cfg, int32_t batch, const int
  * the state is read once, carried through the tokens, and written once.  This is the
  * decode step for several known tokens (speculative verification, or a short chunk of
  * a prompt against a resident state); each token follows the header comment "KDA
- * per-head recurrence" (page "colibri/c/kimi_k3.c").  Tokens are evaluated in blocks of
- * eight in the chunk form of that recurrence (the same terms summed in another order), so
- * n tokens here agree with n kda_decode_step calls to fp32 rounding (about 1e-6 relative),
- * not bit for bit; the final conv windows are exact.  A call with n_tokens = a repeats,
- * bit for bit, the outputs of the first a tokens of a call with more tokens.
+ * per-head recurrence" (page "colibri/c/kimi_k3.c").  cfg->decode_multi_form picks how:
+ * KDA_MULTI_BLOCK (default) evaluates blocks of eight tokens in the chunk form of that
+ * recurrence (the same terms summed in another order), so n tokens agree with n
+ * kda_decode_step calls to fp32 rounding (about 3e-6 relative), not bit for bit, and a
+ * call with n_tokens = a repeats, bit for bit, the outputs of the first a tokens of a
+ * call with more tokens; KDA_MULTI_SEQUENTIAL runs kda_decode_step's arithmetic token by
+ * token, so n tokens give the bits of n kda_decode_step calls.  The final conv windows
+ * are exact either way.
  *
  * Verify and roll back (the engine's multi-token verify and rollback are not
  * implemented on the pages; this is this library's form of it): call with

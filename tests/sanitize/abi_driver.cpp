@@ -11,6 +11,7 @@ namespace kda {
 static int reached = 0;
 hipError_t launch_decode(const DecodeArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
 hipError_t launch_decode_multi(const DecodeMultiArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
+hipError_t launch_decode_multi_seq(const DecodeMultiArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
 hipError_t launch_prefill(const PrefillArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
 hipError_t launch_carry(const PrefillArgs &, hipStream_t) { ++reached; return hipErrorInvalidValue; }
 }  // namespace kda

@@ -410,6 +410,12 @@ def test_precision_flag():
     assert _ws(_cfg(prefill_path=1, precision=1), 1, 8192) == 0
 
 
+def test_decode_multi_form_flag():
+    assert kda.lib().kda_config_default().decode_multi_form == 0  # blocks of eight tokens
+    assert _decode(_cfg(decode_multi_form=2), 1) == BAD_CONFIG
+    assert _prefill(_cfg(decode_multi_form=-1), 1, 8) == BAD_CONFIG
+
+
 def _gate_proj(cfg, B, N, ptrs=None, stride=0, ws=None, ws_bytes=0):
     # cu, q, k, v, f, w_fb, b, g, conv_w, A_log, dt_bias, norm_w, init_state, init_conv, out, final_state,
     # final_conv

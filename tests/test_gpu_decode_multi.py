@@ -1,10 +1,11 @@
 """GPU parity of kda_decode_multi (several known tokens per sequence in one call) against
 the fp64 oracle (max relative error 1e-4 per (sequence, head) slice, as for one-token
-decode), agreement with the same number of kda_decode_step calls to fp32 rounding (the
-multi-token kernel evaluates blocks of eight tokens in the chunk form of the recurrence,
-the same terms summed in another order: 2e-5 relative per slice, windows exact), and the
-verify / roll-back use: out-of-place candidates, then an in-place commit of the
-accepted prefix, whose outputs are the candidates' bits."""
+decode), in both evaluation forms: the default block form (blocks of eight tokens in the
+chunk form of the recurrence, the same terms summed in another order) agrees with the
+same number of kda_decode_step calls to fp32 rounding (2e-5 relative per slice, windows
+exact); the sequential form gives their bits.  Also the verify / roll-back use:
+out-of-place candidates, then an in-place commit of the accepted prefix, whose outputs
+are the candidates' bits."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +17,8 @@ from tests.parity import DECODE_REL_TOL, DecodeRun, decode_oracle, slice_rel, t
 pytestmark = pytest.mark.gpu
 
 D = 128
+BLOCK, SEQUENTIAL = 0, 1  # kda_config.decode_multi_form
+FORMS = [pytest.param(BLOCK, id="block"), pytest.param(SEQUENTIAL, id="sequential")]
 MULTI_VS_STEPS_REL = 2e-5  # block form against token-by-token fp32, per (sequence, head) slice
 
 
@@ -30,9 +33,9 @@ def _rel(x: torch.Tensor, r: torch.Tensor) -> float:
 class MultiRun:
     """A decode case's first T tokens as [B, T, ...] inputs on the GPU."""
 
-    def __init__(self, case: ki.DecodeCase, T: int, dev):
+    def __init__(self, case: ki.DecodeCase, T: int, dev, form: int = BLOCK):
         self.case, self.T, self.dev = case, T, dev
-        self.cfg = kda.KdaConfig(num_heads=case.H)
+        self.cfg = kda.KdaConfig(num_heads=case.H, decode_multi_form=form)
         p = case.params
         self.prm = [t(p.conv_w, dev), t(p.A_log, dev), t(p.dt_bias, dev), t(p.norm_w, dev)]
         steps = [case.step(i) for i in range(T)]
@@ -62,11 +65,12 @@ def _window(cst, b, h, H):
     return np.stack([cst[b, blk * H * D + h * D: blk * H * D + (h + 1) * D] for blk in range(3)])
 
 
-def test_per_sequence_counts_against_oracle(device):
+@pytest.mark.parametrize("form", FORMS)
+def test_per_sequence_counts_against_oracle(device, form):
     case = ki.decode_case(310, 4, 4, 8, "multi-counts")
     n = [8, 3, 0, 1]
-    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=8 n={n}", flush=True)
-    mr = MultiRun(case, 8, device)
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=8 n={n} form={form}", flush=True)
+    mr = MultiRun(case, 8, device, form)
     s_out, c_out = torch.empty_like(mr.state0), torch.empty_like(mr.conv0)
     state_in, conv_in = mr.state0.clone(), mr.conv0.clone()
     out = mr.call(state_in, conv_in, s_out, c_out, n_tokens=n).cpu().numpy().reshape(case.B, 8, case.H, D)
@@ -106,11 +110,12 @@ def test_in_place_agrees_with_single_steps(device, T):
     assert torch.equal(conv, cst)
 
 
-def test_verify_then_commit_accepted_prefix(device):
+@pytest.mark.parametrize("form", FORMS)
+def test_verify_then_commit_accepted_prefix(device, form):
     case = ki.decode_case(312, 3, 4, 6, "multi-verify")
     accepted = [6, 2, 0]
-    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=6 accepted={accepted}", flush=True)
-    mr = MultiRun(case, 6, device)
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T=6 accepted={accepted} form={form}", flush=True)
+    mr = MultiRun(case, 6, device, form)
     state, conv = mr.state0.clone(), mr.conv0.clone()
     spec_s, spec_c = torch.empty_like(state), torch.empty_like(conv)
     spec_out = mr.call(state, conv, spec_s, spec_c)  # candidates; `state` is the snapshot
@@ -120,15 +125,33 @@ def test_verify_then_commit_accepted_prefix(device):
         outs, st, cst = _single_steps(case, a, device) if a else ([], mr.state0, mr.conv0)
         for i in range(a):
             assert torch.equal(out[b, i], spec_out[b, i])  # the commit repeats the candidates' bits
-            assert _rel(out[b, i], outs[i][b]) <= MULTI_VS_STEPS_REL
+            if form == SEQUENTIAL:
+                assert torch.equal(out[b, i], outs[i][b])
+            else:
+                assert _rel(out[b, i], outs[i][b]) <= MULTI_VS_STEPS_REL
         assert torch.isnan(out[b, a:]).all()
         if a == 0:
             assert torch.equal(state[b], mr.state0[b]) and torch.equal(conv[b], mr.conv0[b])
+        elif form == SEQUENTIAL:
+            assert torch.equal(state[b], st[b]) and torch.equal(conv[b], cst[b])
         else:
             assert _rel(state[b], st[b]) <= MULTI_VS_STEPS_REL
             assert torch.equal(conv[b], cst[b])
     # a fully accepted sequence ends where the candidates ended
     assert torch.equal(state[0], spec_s[0]) and torch.equal(conv[0], spec_c[0])
+
+
+@pytest.mark.parametrize("T", [6, 11])
+def test_sequential_form_equals_single_steps_bitwise(device, T):
+    case = ki.decode_case(311, 5, 6, T, f"multi-seq-vs-steps-{T}")
+    print(f"[decode-multi] {case.name} B={case.B} H={case.H} T={T} sequential", flush=True)
+    mr = MultiRun(case, T, device, SEQUENTIAL)
+    state, conv = mr.state0.clone(), mr.conv0.clone()
+    out = mr.call(state, conv)
+    outs, st, cst = _single_steps(case, T, device)
+    for i in range(T):
+        assert torch.equal(out[:, i], outs[i]), i
+    assert torch.equal(state, st) and torch.equal(conv, cst)
 
 
 def test_k3_shape_four_tokens(device):

@@ -4,6 +4,7 @@ same inputs, and the error metrics the tolerances are stated in.
 Metrics (per (sequence, head) slice):
   rel  = max|x - r| / max|r|          -- "max relative error" (decode: 1e-4; prefill states: 5e-3)
   abs  = max|x - r|                   -- "max abs error" (prefill outputs: 2e-2)
+  elem = max |x - r| / max(|r|, 1e-3 max|r|)  -- elementwise, reported beside them
 """
 from __future__ import annotations
 
@@ -25,6 +26,17 @@ def slice_rel(x: np.ndarray, r: np.ndarray) -> float:
     r = np.asarray(r, np.float64)
     den = np.max(np.abs(r))
     return float(np.max(np.abs(x - r)) / den) if den > 0 else float(np.max(np.abs(x)))
+
+
+def elem_rel(x: np.ndarray, r: np.ndarray) -> float:
+    """The elementwise relative error reported beside slice_rel (no bound is stated for it):
+    max |x - r| / max(|r|, 1e-3 max|r|) over the slice."""
+    x = np.asarray(x, np.float64)
+    r = np.asarray(r, np.float64)
+    floor = 1e-3 * np.max(np.abs(r))
+    if floor == 0:
+        return float(np.max(np.abs(x)))
+    return float(np.max(np.abs(x - r) / np.maximum(np.abs(r), floor)))
 
 
 def t(a, dev, dtype=None):

@@ -95,7 +95,7 @@ def test_per_sequence_counts_against_oracle(device, form):
     assert worst <= DECODE_REL_TOL, worst
 
 
-@pytest.mark.parametrize("T", [6, 8, 11, 17])
+@pytest.mark.parametrize("T", [1, 6, 8, 11, 17, 40])
 def test_in_place_agrees_with_single_steps(device, T):
     case = ki.decode_case(311, 5, 6, T, f"multi-vs-steps-{T}")
     print(f"[decode-multi] {case.name} B={case.B} H={case.H} T={T}", flush=True)

@@ -90,6 +90,7 @@ struct PrefillPlan {
     int path;
     int64_t nchunk_cap, nseg_cap;
     int seg_chunks;
+    bool carry_split;  // chunked: the two-workgroup carry (standard precision, B*H <= 128)
     size_t table_bytes, workspace_bytes;
 };
 // max_workspace >= 0: the workspace is a fixed array of that many bytes; the automatic
@@ -102,6 +103,12 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     const int seg_chunks = kda::seg_chunks_for(B, N, H);
     const int64_t segs = kda::seg_cap(B, cap, seg_chunks);
     const bool chunked_fits = cap * H <= kda::kMaxPrefillUnits && segs * H <= kda::kMaxPrefillUnits;
+    const bool precise = cfg->precision == KDA_PRECISION_HIGH;
+    const bool split = !precise && B * H <= kda::kSplitCarryMaxUnits;
+    // chunk_start and seg_start, then (split carry) the RMS-sum exchange words
+    const size_t table_bytes =
+        (size_t)((8 * (B + 1) + 255) / 256 * 256) + (split ? (size_t)(B * H * kda::kSplitXchgBytes) : 0);
+    const size_t chunked_bytes = table_bytes + (size_t)cap * (size_t)H * (size_t)kda::rec_bytes(precise);
     int path = cfg->prefill_path;
     if (path == kda::kPathAuto) {
         path = kda::kPathFused;
@@ -109,11 +116,10 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
             const double rounds = (double)((B * H + kda::kComputeUnits - 1) / kda::kComputeUnits);
             const double chunks = (double)((N + 64 * B - 1) / (64 * B));  // mean length, rounded up
             const double fused = rounds * chunks * kda::kFusedChunkUs;
-            const double chunked =
-                (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits + rounds * chunks * kda::kCarryChunkUs;
-            const size_t need = (size_t)((8 * (B + 1) + 255) / 256 * 256) +
-                                (size_t)cap * (size_t)H * (size_t)kda::rec_bytes(cfg->precision == KDA_PRECISION_HIGH);
-            if (chunked < fused && (max_workspace < 0 || need <= (size_t)max_workspace)) path = kda::kPathChunked;
+            const double chunked = (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits +
+                                   (split ? chunks * kda::kSplitCarryChunkUs : rounds * chunks * kda::kCarryChunkUs);
+            if (chunked < fused && (max_workspace < 0 || chunked_bytes <= (size_t)max_workspace))
+                path = kda::kPathChunked;
         }
     }
     if (path != kda::kPathFused && path != kda::kPathChunked) return false;
@@ -122,11 +128,9 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     plan->nchunk_cap = cap;
     plan->nseg_cap = segs;
     plan->seg_chunks = seg_chunks;
-    plan->table_bytes = (size_t)((8 * (B + 1) + 255) / 256 * 256);  // chunk_start, seg_start
-    plan->workspace_bytes =
-        path == kda::kPathFused ? 0
-                                : plan->table_bytes + (size_t)cap * (size_t)H *
-                                                          (size_t)kda::rec_bytes(cfg->precision == KDA_PRECISION_HIGH);
+    plan->carry_split = path == kda::kPathChunked && split;
+    plan->table_bytes = table_bytes;
+    plan->workspace_bytes = path == kda::kPathFused ? 0 : chunked_bytes;
     return true;
 }
 
@@ -322,7 +326,7 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
                         const float *initial_conv_state, void *out, float *final_state, float *final_conv_state,
                         void *workspace, size_t workspace_bytes, bool static_scratch, void *stream,
                         bool gate_proj = false, const uint16_t *f = nullptr, const uint16_t *w_fb = nullptr) {
-    kda::PrefillArgs a;
+    kda::PrefillArgs a = {};
     kda_status st = check_config(cfg, &a.c);
     if (st != KDA_OK) return st;
     if (cfg->prefill_path < kda::kPathAuto || cfg->prefill_path > kda::kPathChunked) return KDA_ERR_BAD_CONFIG;
@@ -385,6 +389,9 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
     a.chunk_start = chunked ? static_cast<int32_t *>(workspace) : nullptr;
     a.seg_start = chunked ? static_cast<int32_t *>(workspace) + (num_seqs + 1) : nullptr;
     a.records = chunked ? static_cast<unsigned char *>(workspace) + plan.table_bytes : nullptr;
+    a.xchg = plan.carry_split ? reinterpret_cast<unsigned long long *>(static_cast<unsigned char *>(workspace) +
+                                                                       (8 * (num_seqs + 1) + 255) / 256 * 256)
+                              : nullptr;
     a.cu_seqlens = cu_seqlens;
     a.q = q; a.k = k; a.v = v; a.z = gate_proj ? nullptr : z; a.b = b; a.g = g;
     a.f = gate_proj ? f : nullptr;

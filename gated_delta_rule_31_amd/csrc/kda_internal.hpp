@@ -99,6 +99,13 @@ constexpr int kComputeUnits = 256;
 constexpr double kFusedChunkUs = 17.6;
 constexpr double kRecordUs = 17.0;
 constexpr double kCarryChunkUs = 5.9;
+// The split carry (kda_carry.hip) runs two 4-wave workgroups per (sequence, head), each on
+// its own compute unit and resident together, so it is used for B*H <= 128; its rounds
+// term is then 1 and its per-chunk cost kSplitCarryChunkUs.
+constexpr int64_t kSplitCarryMaxUnits = kComputeUnits / 2;
+constexpr double kSplitCarryChunkUs = 5.2;
+// exchange bytes per (sequence, head) of the split carry: 2 halves x 4 slots x 64 x 8
+constexpr int64_t kSplitXchgBytes = 2 * 4 * kChunk * 8;
 
 // Bytes of one chunk record (the layout is in kda_device.hpp); multiples of 256.  The
 // high-precision record also holds the lo parts of W and Q~.
@@ -149,6 +156,10 @@ struct PrefillArgs {
     int32_t *chunk_start;     // chunked plan: [B+1] first record row of each sequence
     int32_t *seg_start;       // chunked plan: [B+1] first segment of each sequence
     unsigned char *records;   // chunked plan: [nchunk_cap][H] records
+    // chunked plan with the split carry (two workgroups per (sequence, head), B*H <=
+    // kSplitCarryMaxUnits): [B*H][2 halves][4 slots][64 tokens] exchange words of the RMS
+    // sums, zeroed by the chunk table kernel; null otherwise
+    unsigned long long *xchg;
     const int32_t *cu_seqlens;
     const uint16_t *q, *k, *v, *z, *b, *g;
     size_t qkv_ld;  // elements between consecutive token rows of q, k, v (>= H*D)

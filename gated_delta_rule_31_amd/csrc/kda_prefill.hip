@@ -1123,6 +1123,12 @@ __device__ long long block_scan(long long *part, long long v) {
 __global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs a) {
     __shared__ long long part[kTableThreads];
     const int tid = threadIdx.x;
+    // the split carry's exchange words start at zero (no tag matches a chunk)
+    if (a.xchg) {
+        const size_t n = (size_t)a.B * a.c.H * (kSplitXchgBytes / 16);
+        uint4 *x = reinterpret_cast<uint4 *>(a.xchg);
+        for (size_t i = tid; i < n; i += kTableThreads) x[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     const long long cap = a.nchunk_cap;
     long long carry_c = 0, carry_s = 0;  // records and segments of the tiles before
     for (int base = 0; base < a.B; base += kTableThreads) {

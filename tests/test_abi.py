@@ -124,9 +124,14 @@ def _ws(cfg, B, N):
 def test_prefill_path_selection_and_workspace_size():
     # fused: no workspace
     assert _ws(_cfg(prefill_path=1), 1, 8192) == 0
-    # chunked: 2(B+1) int32 padded to 256 bytes, then floor(N/64) + B records per head
-    assert _ws(_cfg(prefill_path=2, num_heads=96), 1, 8192) == 256 + (128 + 1) * 96 * REC_BYTES
+    # chunked: 2(B+1) int32 padded to 256 bytes, for B*H <= 128 in standard precision the
+    # split carry's exchange words (4096 bytes per sequence-head), then floor(N/64) + B
+    # records per head
+    assert _ws(_cfg(prefill_path=2, num_heads=96), 1, 8192) == 256 + 96 * 4096 + (128 + 1) * 96 * REC_BYTES
     assert _ws(_cfg(prefill_path=2, num_heads=4), 100, 1000) == 1024 + (15 + 100) * 4 * REC_BYTES
+    assert _ws(_cfg(prefill_path=2, num_heads=64), 2, 128) == 256 + 128 * 4096 + (2 + 2) * 64 * REC_BYTES
+    assert _ws(_cfg(prefill_path=2, num_heads=43), 3, 128) == 256 + (2 + 3) * 43 * REC_BYTES
+    assert _ws(_cfg(prefill_path=2, num_heads=96, precision=1), 1, 8192) == 256 + (128 + 1) * 96 * 144384
     # auto: the layout the time estimate prefers; these are the measured winners on MI355X
     # for equal sequences of 4096 tokens (fused fills whole rounds of 256 workgroups)
     chunked = lambda B, N: _ws(_cfg(num_heads=96), B, N) == _ws(_cfg(prefill_path=2, num_heads=96), B, N) > 0

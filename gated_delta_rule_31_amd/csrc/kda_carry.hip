@@ -307,16 +307,18 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
                                  S[P][1][0], S[P][1][1], S[P][1][2], S[P][1][3]};
             Sh[P] = to_bf8(v8);
         }
-        // U = U' - W S0
+        // U = U' - W S0.  The products issue their MFMAs round-robin over independent
+        // accumulators (each still takes its terms in the same order: the same bits), so
+        // that no MFMA waits for the one before it on the same accumulator.
+        {
+            f32x4 ws[4] = {};  // [tp][x]
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
+            for (int P = 0; P < 4; ++P)
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < 4; ++i) ws[i] = mma(opnd(RecS::w(i >> 1, i & 1, P)), Sh[P], ws[i]);
 #pragma unroll
-                for (int P = 0; P < 4; ++P) ws = mma(opnd(RecS::w(tp, x, P)), Sh[P], ws);
-                U[tp][x] -= ws;
-            }
+            for (int i = 0; i < 4; ++i) U[i >> 1][i & 1] -= ws[i];
+        }
         // every wave's epilogue has read the staged O: pieces 0 .. 31 of `prv` may be loaded
         lds_barrier();
         request(P2{}, Nxt{}, c + 1, Unext);
@@ -328,22 +330,25 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
             split8(v8, Uh[tp], Ul[tp]);
         }
         // O^T = S0^T Q~^T + U^T P^T
-        f32x4 o[4];
+        f32x4 o[4] = {};
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int P = 0; P < 4; ++P)
 #pragma unroll
-            for (int P = 0; P < 4; ++P) acc = mma(Sh[P], opnd(RecS::q(tt, P)), acc);
+            for (int tt = 0; tt < 4; ++tt) o[tt] = mma(Sh[P], opnd(RecS::q(tt, P)), o[tt]);
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                if (tp > (tt >> 1)) continue;  // P is lower triangular
-                const bf16x8 Ph = opnd(RecS::p(tt, tp, 0));
-                const bf16x8 Pl = opnd(RecS::p(tt, tp, 1));
-                acc = mma(Uh[tp], Ph, acc);
-                acc = mma(Uh[tp], Pl, acc);
-                acc = mma(Ul[tp], Ph, acc);
+        for (int tp = 0; tp < 2; ++tp) {  // P is lower triangular: tt >= 2 tp
+            bf16x8 Ph[4], Pl[4];
+#pragma unroll
+            for (int tt = 2 * tp; tt < 4; ++tt) {
+                Ph[tt] = opnd(RecS::p(tt, tp, 0));
+                Pl[tt] = opnd(RecS::p(tt, tp, 1));
             }
-            o[tt] = acc;
+#pragma unroll
+            for (int tt = 2 * tp; tt < 4; ++tt) o[tt] = mma(Uh[tp], Ph[tt], o[tt]);
+#pragma unroll
+            for (int tt = 2 * tp; tt < 4; ++tt) o[tt] = mma(Uh[tp], Pl[tt], o[tt]);
+#pragma unroll
+            for (int tt = 2 * tp; tt < 4; ++tt) o[tt] = mma(Ul[tp], Ph[tt], o[tt]);
         }
         request(P3{}, Nxt{}, c + 1, Unext);
         // every wave is done with W and Q~: O goes into their place
@@ -354,17 +359,24 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
 #pragma unroll
         for (int P = 0; P < 4; ++P)
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                f32x4 acc = S[P][x] * *reinterpret_cast<const f32x4 *>(sE + 32 * P + 8 * lg + 4 * x);
+            for (int x = 0; x < 2; ++x) S[P][x] = S[P][x] * *reinterpret_cast<const f32x4 *>(sE + 32 * P + 8 * lg + 4 * x);
+        // (two groups of four accumulators (P, x) = (2g + n / 2, n % 2))
 #pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    const bf16x8 Kh = opnd(RecS::k(P, x, tp, 0));
-                    const bf16x8 Kl = opnd(RecS::k(P, x, tp, 1));
-                    acc = mma(Kh, Uh[tp], acc);
-                    acc = mma(Kl, Uh[tp], acc);
-                    acc = mma(Kh, Ul[tp], acc);
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                bf16x8 Kh[4], Kl[4];
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    Kh[n] = opnd(RecS::k(2 * g + (n >> 1), n & 1, tp, 0));
+                    Kl[n] = opnd(RecS::k(2 * g + (n >> 1), n & 1, tp, 1));
                 }
-                S[P][x] = acc;
+#pragma unroll
+                for (int n = 0; n < 4; ++n) S[2 * g + (n >> 1)][n & 1] = mma(Kh[n], Uh[tp], S[2 * g + (n >> 1)][n & 1]);
+#pragma unroll
+                for (int n = 0; n < 4; ++n) S[2 * g + (n >> 1)][n & 1] = mma(Kl[n], Uh[tp], S[2 * g + (n >> 1)][n & 1]);
+#pragma unroll
+                for (int n = 0; n < 4; ++n) S[2 * g + (n >> 1)][n & 1] = mma(Kh[n], Ul[tp], S[2 * g + (n >> 1)][n & 1]);
             }
 #pragma unroll
         for (int s = 0; s < 4; ++s) gprev[s] = g4[s];

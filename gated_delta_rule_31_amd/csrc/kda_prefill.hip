@@ -970,25 +970,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 else
                     Sh[P] = to_bf8(v8);
             }
-            // U = U' - W S0
+            // U = U' - W S0.  The state-side products issue their MFMAs round-robin over
+            // independent accumulators, so that no MFMA waits for the one before it on the
+            // same accumulator; each accumulator still takes its terms in the same order.
+            {
+                f32x4 ws[4] = {};  // [tp][x]
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
+                for (int P = 0; P < 4; ++P)
 #pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int trow = 32 * tp + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                    f32x4 ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int P = 0; P < 4; ++P) {
+                    for (int i = 0; i < 4; ++i) {
+                        const int trow = 32 * (i >> 1) + 8 * (lr >> 2) + 4 * (i & 1) + (lr & 3);
                         const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sW + swi128(trow, 32 * P + 8 * lg));
-                        ws = mma(A8, Sh[P], ws);
+                        ws[i] = mma(A8, Sh[P], ws[i]);
                         if constexpr (kPrecise) {
                             const bf16x8 A8l = *reinterpret_cast<const bf16x8 *>(sWLo + swi128(trow, 32 * P + 8 * lg));
-                            ws = mma(A8, Sl[P], ws);
-                            ws = mma(A8l, Sh[P], ws);
+                            ws[i] = mma(A8, Sl[P], ws[i]);
+                            ws[i] = mma(A8l, Sh[P], ws[i]);
                         }
                     }
-                    U[tp][x] -= ws;
-                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) U[i >> 1][i & 1] -= ws[i];
+            }
             bf16x8 Uh[2], Ul[2];  // [tp]
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp) {
@@ -998,48 +1000,59 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             }
             // O^T = S0^T Q~^T + U^T P^T
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int P = 0; P < 4; ++P) {
-                    const bf16x8 B8 = *reinterpret_cast<const bf16x8 *>(sQe + sw128(16 * tt + lr, 32 * P + 8 * lg));
-                    acc = mma(Sh[P], B8, acc);
-                    if constexpr (kPrecise) {
-                        const bf16x8 B8l = *reinterpret_cast<const bf16x8 *>(sQeLo + sw128(16 * tt + lr, 32 * P + 8 * lg));
-                        acc = mma(Sh[P], B8l, acc);
-                        acc = mma(Sl[P], B8, acc);
-                    }
-                }
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    if (tp > (tt >> 1)) continue;  // P is lower triangular
-                    const bf16x8 Ph = *reinterpret_cast<const bf16x8 *>(sPh + sw64(16 * tt + lr, 32 * tp + 8 * lg));
-                    const bf16x8 Pl = *reinterpret_cast<const bf16x8 *>(sPl + sw64(16 * tt + lr, 32 * tp + 8 * lg));
-                    acc = mma(Uh[tp], Ph, acc);
-                    acc = mma(Uh[tp], Pl, acc);
-                    acc = mma(Ul[tp], Ph, acc);
-                }
-                o[tt] = acc;
-            }
-            rms_partials(o, sRms, w, lr, lg);
-            // S = Diag(e^{G_end}) S0 + K_end^T U
+            for (int tt = 0; tt < 4; ++tt) o[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int P = 0; P < 4; ++P)
 #pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int krow = 32 * P + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                    f32x4 acc = S[P][x];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] *= sExpEnd[32 * P + 8 * lg + 4 * x + i];
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp) {
-                        const bf16x8 Kh = *reinterpret_cast<const bf16x8 *>(sKeHi + swi64(krow, 32 * tp + 8 * lg));
-                        const bf16x8 Kl = *reinterpret_cast<const bf16x8 *>(sKeLo + swi64(krow, 32 * tp + 8 * lg));
-                        acc = mma(Kh, Uh[tp], acc);
-                        acc = mma(Kl, Uh[tp], acc);
-                        acc = mma(Kh, Ul[tp], acc);
+                for (int tt = 0; tt < 4; ++tt) {
+                    const bf16x8 B8 = *reinterpret_cast<const bf16x8 *>(sQe + sw128(16 * tt + lr, 32 * P + 8 * lg));
+                    o[tt] = mma(Sh[P], B8, o[tt]);
+                    if constexpr (kPrecise) {
+                        const bf16x8 B8l = *reinterpret_cast<const bf16x8 *>(sQeLo + sw128(16 * tt + lr, 32 * P + 8 * lg));
+                        o[tt] = mma(Sh[P], B8l, o[tt]);
+                        o[tt] = mma(Sl[P], B8, o[tt]);
                     }
-                    S[P][x] = acc;
+                }
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {  // P is lower triangular: tt >= 2 tp
+                bf16x8 Ph[4], Pl[4];
+#pragma unroll
+                for (int tt = 2 * tp; tt < 4; ++tt) {
+                    Ph[tt] = *reinterpret_cast<const bf16x8 *>(sPh + sw64(16 * tt + lr, 32 * tp + 8 * lg));
+                    Pl[tt] = *reinterpret_cast<const bf16x8 *>(sPl + sw64(16 * tt + lr, 32 * tp + 8 * lg));
+                }
+#pragma unroll
+                for (int tt = 2 * tp; tt < 4; ++tt) o[tt] = mma(Uh[tp], Ph[tt], o[tt]);
+#pragma unroll
+                for (int tt = 2 * tp; tt < 4; ++tt) o[tt] = mma(Uh[tp], Pl[tt], o[tt]);
+#pragma unroll
+                for (int tt = 2 * tp; tt < 4; ++tt) o[tt] = mma(Ul[tp], Ph[tt], o[tt]);
+            }
+            rms_partials(o, sRms, w, lr, lg);
+            // S = Diag(e^{G_end}) S0 + K_end^T U, in two groups of four accumulators
+#pragma unroll
+            for (int P = 0; P < 4; ++P)
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[P][x][i] *= sExpEnd[32 * P + 8 * lg + 4 * x + i];
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    bf16x8 Kh[4], Kl[4];  // accumulators (P, x) = (2g + n / 2, n % 2)
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) {
+                        const int krow = 32 * (2 * g + (n >> 1)) + 8 * (lr >> 2) + 4 * (n & 1) + (lr & 3);
+                        Kh[n] = *reinterpret_cast<const bf16x8 *>(sKeHi + swi64(krow, 32 * tp + 8 * lg));
+                        Kl[n] = *reinterpret_cast<const bf16x8 *>(sKeLo + swi64(krow, 32 * tp + 8 * lg));
+                    }
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) S[2 * g + (n >> 1)][n & 1] = mma(Kh[n], Uh[tp], S[2 * g + (n >> 1)][n & 1]);
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) S[2 * g + (n >> 1)][n & 1] = mma(Kl[n], Uh[tp], S[2 * g + (n >> 1)][n & 1]);
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) S[2 * g + (n >> 1)][n & 1] = mma(Kh[n], Ul[tp], S[2 * g + (n >> 1)][n & 1]);
                 }
         }
         lds_barrier();

@@ -234,15 +234,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     __bf16 *sQeLo = sQe + 64 * 128;                                     // (kPrecise) its lo part
     __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + M.tb);              // [64][64]
     __bf16 *sTbLo = sTb + 64 * 64;                                      // (kPrecise) its lo part
+    // (decay sums in log2 units: G below is the natural-log decay times log2(e))
     float *sTot = reinterpret_cast<float *>(smem + OFF_TAB);  // [4][128] per-sub-chunk gk sums
-    float *sRef = sTot + 512;                                  // [5][128] r_0..r_3, G_end
-    float *sPair = sRef + 640;                                 // [6][128] e^{r_I - r_J}, J < I
+    float *sPair = sTot + 512 + 640;                           // [6][128] e^{r_I - r_J}, J < I
     float *sExpRef = sPair + 768;                              // [4][128] e^{r_I}
     float *sEndRef = sExpRef + 512;                            // [4][128] e^{G_end - r_I}
     float *sExpEnd = sEndRef + 512;                            // [128]    e^{G_end}
     float *sNorm = sExpEnd + 128;                              // [2 halves][q,k][64] sums of squares
     float *sConvW = reinterpret_cast<float *>(smem + OFF_CW);  // [3][128][4] taps, oldest first
-    float *sDtb = reinterpret_cast<float *>(smem + OFF_DTB);   // [128] dt_bias
+    float *sDtb = reinterpret_cast<float *>(smem + OFF_DTB);   // [128] -exp(A_log) log2(e) dt_bias
     float *sNw = reinterpret_cast<float *>(smem + OFF_NW);     // [128] RMSNorm weight
 
     const int H = a.c.H;
@@ -278,10 +278,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     t1 = min(max(t1, t0), N);
     const int T = t1 - t0;
 
-    const float gmin = a.c.gate_lower_bound;
-    const float rate = __expf(a.A_log[h]);
-    const float qscale = a.c.q_scale;
-    const float l2eps = a.c.l2_eps;
+    // The decay gate gk = gmin sigmoid(exp(A_log) (z + dt_bias)) is formed in log2 units:
+    // 1 / (1 + 2^(z zr + dtb')) with zr = -exp(A_log) log2(e) and dtb' = zr dt_bias (one FMA),
+    // scaled by gmin log2(e), so that every e^x of the chunk algebra below is one exp2.
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float gmin2 = a.c.gate_lower_bound * kLog2e;
+    const float zr = -__expf(a.A_log[h]) * kLog2e;
+    // SiLU in the same units: the conv taps are staged times -log2(e), so that a conv output
+    // y' = -log2(e) y gives sigmoid(y) = 1 / (1 + 2^y') and u' = y' sigmoid(y) =
+    // -log2(e) SiLU(y) with no multiply.  The L2 norms of q and k absorb the factor (the
+    // eps scaled by log2(e)^2, the sign by negated scales); v's is folded into beta.
+    constexpr float kLn2 = 0.6931471805599453f;
+    const float qscale = -a.c.q_scale;
+    const float l2eps = a.c.l2_eps * (kLog2e * kLog2e);
     const size_t conv_seq = (size_t)seq * 3 * HD * 3;  // this sequence's conv windows
 
     // ---- the state: S[P][x][i] = S[key 32P + 8lg + 4x + i][value 16w + lr] ----
@@ -308,9 +317,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     for (int i = threadIdx.x; i < 3 * kD; i += kThreads) {
         const int blk = i >> 7, c = i & 127;
         const size_t ch = (size_t)blk * HD + (size_t)h * kD + c;
-        *reinterpret_cast<float4 *>(sConvW + i * 4) = *reinterpret_cast<const float4 *>(a.conv_w + ch * 4);
+        *reinterpret_cast<float4 *>(sConvW + i * 4) = *reinterpret_cast<const float4 *>(a.conv_w + ch * 4) * -kLog2e;
         if (i < kD) {
-            sDtb[i] = a.dt_bias[(size_t)h * kD + i];
+            sDtb[i] = zr * a.dt_bias[(size_t)h * kD + i];
             if (!kChunked) sNw[i] = a.norm_w[i];
         }
         if (cbeg == 0) {
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             const int cbase = 64 * half + 16 * lg;      // first of this lane's 16 channels
             beta = valid ? sigm(ld.b) : 0.0f;
 
-            // SiLU(ShortConv4(x)) of the 8 channels cbase + 8pc .. +7 of block blk.  Tokens
+            // -log2(e) SiLU(ShortConv4(x)) of the 8 channels cbase + 8pc .. +7 of block blk.  Tokens
             // past the sequence end (t >= L) get finite values of no effect: their beta and
             // decay gate are zero, so their rows of W, U' and U are exactly zero and their
             // rows of A are masked; only their own output rows (never stored) see them.
@@ -468,8 +477,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                         y[j] = cw[j].x * xr[0][j] + cw[j].y * xr[1][j] + cw[j].z * xr[2][j] + cw[j].w * xr[3][j];
                 }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) u[j] = y[j] * sigm(y[j]);
+                for (int j = 0; j < 8; ++j) u[j] = y[j] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y[j]));
             };
+            const float vscale = beta * -kLn2;  // beta v = vscale u'
             // v: beta * v, hi/lo, transposed into sVt
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
@@ -477,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 conv_piece(2, pc, u);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float bv = beta * u[j];
+                    const float bv = vscale * u[j];
                     const __bf16 hi = (__bf16)bv;
                     sVtHi[sw64(cbase + 8 * pc + j, t)] = hi;
                     sVtLo[sw64(cbase + 8 * pc + j, t)] = (__bf16)(bv - (float)hi);
@@ -529,8 +539,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     for (int i = 0; i < 4; ++i) zf[4 * m + i] = acc[i];
                 }
             }
-            // decay gate gk = gmin * sigmoid(exp(A_log) * (z + dt_bias)) and its cumulative
-            // sum over the sub-chunk's 16 tokens (= G_t - r_sub)
+            // decay gate gk (log2 units, see above) and its cumulative sum over the
+            // sub-chunk's 16 tokens (= G_t - r_sub)
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 float zz[8], dtb[8];
@@ -543,7 +553,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 lds_read8(sDtb + cbase + 8 * pc, dtb);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float g = valid ? gmin * sigm(rate * (zz[j] + dtb[j])) : 0.f;
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(zz[j], zr, dtb[j]));
+                    const float g = valid ? gmin2 * __builtin_amdgcn_rcpf(1.0f + e) : 0.f;
                     gs[8 * pc + j] = row_scan16(g);
                 }
             }
@@ -570,18 +581,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 r[4] = r[3] + sTot[384 + c];
                 if (tid < 128) {
 #pragma unroll
-                    for (int I = 0; I < 5; ++I) sRef[I * 128 + c] = r[I];
-#pragma unroll
                     for (int I = 0; I < 4; ++I) {
-                        sExpRef[I * 128 + c] = __expf(r[I]);
-                        sEndRef[I * 128 + c] = __expf(r[4] - r[I]);
+                        sExpRef[I * 128 + c] = __builtin_amdgcn_exp2f(r[I]);
+                        sEndRef[I * 128 + c] = __builtin_amdgcn_exp2f(r[4] - r[I]);
                     }
-                    sExpEnd[c] = __expf(r[4]);
+                    sExpEnd[c] = __builtin_amdgcn_exp2f(r[4]);
                 } else {
 #pragma unroll
                     for (int I = 1; I < 4; ++I)
 #pragma unroll
-                        for (int J = 0; J < I; ++J) sPair[pair_index(I, J) * 128 + c] = __expf(r[I] - r[J]);
+                        for (int J = 0; J < I; ++J)
+                            sPair[pair_index(I, J) * 128 + c] = __builtin_amdgcn_exp2f(r[I] - r[J]);
                 }
             }
         }
@@ -591,11 +601,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             const float ssq = sNorm[t] + sNorm[128 + t];
             const float ssk = sNorm[64 + t] + sNorm[192 + t];
             const float inv_q = qscale / sqrtf(ssq + l2eps);
-            const float inv_k = 1.0f / sqrtf(ssk + l2eps);
+            const float inv_k = -1.0f / sqrtf(ssk + l2eps);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float rf = __expf(gs[j]);
-                const float cf = __expf(-gs[j]);
+                const float rf = __builtin_amdgcn_exp2f(gs[j]);
+                const float cf = __builtin_amdgcn_exp2f(-gs[j]);
                 const float kh = uk[j] * inv_k;
                 qr[j] = uq[j] * inv_q * rf;
                 kr[j] = kh * rf;

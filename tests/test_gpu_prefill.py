@@ -204,7 +204,8 @@ def _no_decay_full_beta(T: int, H: int, seed: int):
 
 
 @pytest.mark.xfail(reason="standard precision: with no decay every bf16 operand rounding persists in the state; "
-                          "measured 2.0e-2 output abs error at T = 1024 and 2.6e-2 at 8192 (bound 2e-2). "
+                          "measured 1.9e-2 to 2.3e-2 output abs error at T = 1024 and 2.7e-2 to 3.2e-2 at 8192 "
+                          "(bound 2e-2; the spread is the rounding of different kernel builds). "
                           "KDA_PRECISION_HIGH holds it at 9e-5 (tests/test_gpu_prefill_precise.py)",
                    strict=False)
 @pytest.mark.parametrize("path", PATHS)

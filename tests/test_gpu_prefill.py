@@ -134,6 +134,21 @@ def test_layouts_agree_bitwise_long_segments(device, lengths):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("B,H,lengths", [(2, 64, [65, 128]), (3, 43, [129, 1, 70])], ids=["BH128-split", "BH129-one"])
+def test_carry_forms_agree_bitwise(device, B, H, lengths):
+    """The chunked layout carries B*H <= 128 (sequence, head) pairs with two workgroups per
+    pair (each owning 64 value columns, exchanging the RMS sums of every output row) and
+    larger batches with one workgroup per pair; either form gives the fused kernel's bits.
+    The first case sits at the limit of the split form (2 x 64 pairs, two-chunk sequences:
+    the exchange's first chunks and last two epilogues), the second one pair past it."""
+    case = ki.prefill_case(128 + B, H, lengths, True, f"carry-forms-{B}x{H}")
+    assert case.B * case.H == (128 if B == 2 else 129)
+    a = prefill_gpu(case, device, path=PATH_FUSED)
+    b = prefill_gpu(case, device, path=PATH_CHUNKED)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_packing_invariance(device, path):
     """Each sequence of a packed batch gives what it gives alone."""

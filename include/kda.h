@@ -134,8 +134,10 @@ typedef struct {
  *                        chunk; no workspace.  Fills the GPU when B*H is large.
  *   KDA_PREFILL_CHUNKED  one workgroup per (64-token chunk, head) computes the chunk's
  *                        state-independent products into the workspace, then one
- *                        workgroup per (sequence, head) carries the state through them.
- *                        Fills the GPU when B*H is small (a few long sequences).
+ *                        workgroup per (sequence, head) carries the state through them
+ *                        (two, each owning half the value columns, when B*H <= 128 in
+ *                        the standard precision).  Fills the GPU when B*H is small (a
+ *                        few long sequences).
  *   KDA_PREFILL_AUTO     the one an estimate of both times on MI355X predicts faster,
  *                        from B, H and N (the sequences taken as equal in length): CHUNKED
  *                        for a few long sequences (e.g. B*H = 96 or 288 units), FUSED when
@@ -409,9 +411,11 @@ kda_status kda_prefill_noalloc(const kda_config *cfg, int32_t num_seqs, int32_t 
 
 /* Device scratch kda_prefill needs for these sizes with cfg->prefill_path and
  * cfg->precision: 0 for the fused layout; for the chunked one a table of 2(B+1) int32
- * (padded to 256 bytes) and one record per (chunk, head) (111,616 bytes, or 144,384 with
- * KDA_PRECISION_HIGH) for floor(N/64) + B chunks (the most that B sequences of N tokens in
- * total can need).  Returns 0 for arguments kda_prefill would reject. */
+ * (padded to 256 bytes), for B*H <= 128 in the standard precision 4,096 bytes per
+ * (sequence, head) for the two-workgroup carry's row sums, and one record per (chunk,
+ * head) (111,616 bytes, or 144,384 with KDA_PRECISION_HIGH) for floor(N/64) + B chunks
+ * (the most that B sequences of N tokens in total can need).  Returns 0 for arguments
+ * kda_prefill would reject. */
 size_t kda_prefill_workspace_bytes(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens);
 
 /*

@@ -8,6 +8,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "kda.h"
@@ -319,6 +320,10 @@ kda_status device_scratch(void **out) {
 
 // kda_prefill, and (static_scratch) kda_prefill_noalloc: the workspace is then this
 // device's scratch array, looked up after every argument check has passed
+// kda_test_split_carry's settings, read by every prefill call
+std::atomic<int32_t> split_publish{1};
+std::atomic<int32_t> split_max_polls{0};
+
 kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_tokens, const int32_t *cu_seqlens,
                         const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t qkv_row_stride,
                         const uint16_t *z, const uint16_t *b, const uint16_t *g, const float *conv_w,
@@ -392,6 +397,8 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
     a.xchg = plan.carry_split ? reinterpret_cast<unsigned long long *>(static_cast<unsigned char *>(workspace) +
                                                                        (8 * (num_seqs + 1) + 255) / 256 * 256)
                               : nullptr;
+    a.xchg_publish = split_publish.load();
+    a.xchg_max_polls = split_max_polls.load();
     a.cu_seqlens = cu_seqlens;
     a.q = q; a.k = k; a.v = v; a.z = gate_proj ? nullptr : z; a.b = b; a.g = g;
     a.f = gate_proj ? f : nullptr;
@@ -519,6 +526,11 @@ kda_status kda_state_copy(const kda_config *cfg, int32_t n, const float *src_sta
         if (sc != dc && hipMemcpyAsync(dc, sc, conv_bytes, hipMemcpyDefault, s) != hipSuccess) return KDA_ERR_LAUNCH;
     }
     return KDA_OK;
+}
+
+void kda_test_split_carry(int32_t publish, int32_t max_polls) {
+    split_publish.store(publish != 0 ? 1 : 0);
+    split_max_polls.store(max_polls > 0 ? max_polls : 0);
 }
 
 const char *kda_status_str(kda_status s) {

@@ -423,16 +423,17 @@ __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel(PrefillArgs a) 
 // their check waits for nothing) and used in chunk c + 2.  A half rewrites slot c % 4
 // (with chunk c + 4) only after it has seen the other half's sums of chunk c + 2, which the
 // other half published after it had read chunk c's: no slot is overwritten before it is
-// read.  The
-// wait is bounded (about a second); a half that times out writes NaN for the chunk's
-// outputs instead of hanging.  Both workgroups of a pair must be resident together: the
+// read.  The wait is bounded (2^20 polls, about a second): a wave that times out writes
+// NaN for that chunk's outputs and for every later one, without waiting again, so a
+// missing partner costs one bounded wait, not one per chunk.  Both workgroups of a pair
+// must be resident together: the
 // host launches this form only when every workgroup of the grid has its own compute unit,
 // and the workgroup ids of a pair (16q + x and 16q + 8 + x) fall on the same XCD, so the
 // second read of each record is an L2 hit.
 constexpr int kSplitThreads = 256;
 constexpr int kSplitPiecesPerWave = (RecS::kPieces + 3) / 4;  // 20 (the last ones repeat piece 76)
 constexpr int kSplitSlots = 4;
-constexpr int kSplitMaxPolls = 1 << 23;
+constexpr int kSplitMaxPolls = 1 << 20;
 static_assert(kSplitXchgBytes == 2 * kSplitSlots * kChunk * 8, "exchange area");
 
 // Epilogue lanes: unit u (values 4u .. 4u+3 of the half) from lane bits 0, 1, 4, 5 (so the
@@ -473,7 +474,7 @@ __device__ __forceinline__ void split_poll(unsigned long long (&x)[4], const uns
 // The first half of the epilogue of chunk cp: the staged values and the half's sums of
 // squares, published for the other half.
 __device__ __forceinline__ void split_epi_sums(const unsigned char *stage, SplitEpi &e, unsigned long long *mine,
-                                               int cp, int w, int lane) {
+                                               int cp, int w, int lane, bool publish) {
     const int u = split_unit(lane);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -488,7 +489,7 @@ __device__ __forceinline__ void split_epi_sums(const unsigned char *stage, Split
         q = add_xor16(q);
         e.part[s] = add_xor32(q);
     }
-    if (u == 0) {
+    if (u == 0 && publish) {
         const unsigned long long tag = (unsigned long long)(unsigned)(cp + 1) << 32;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -499,10 +500,12 @@ __device__ __forceinline__ void split_epi_sums(const unsigned char *stage, Split
 
 // The second half: the other half's sums of chunk cp (x from split_poll; polled again,
 // bounded, if not there yet), then out = sigmoid(g) * RMSNorm(O) for the wave's tokens r < L.
+// dead: this wave has timed out before (wave-uniform); it then takes NaN at once.
 template <bool kBf16>
 __device__ __forceinline__ void split_epi_store(const SplitEpi &e, unsigned long long (&x)[4], const float (&nw)[4],
                                                 const unsigned long long *other, int cp, float rms_eps, void *out,
-                                                size_t col0, size_t HD, int tok0, int L, int w, int lane) {
+                                                size_t col0, size_t HD, int tok0, int L, int w, int lane,
+                                                int max_polls, bool &dead) {
     const unsigned tag = (unsigned)(cp + 1);
     auto arrived = [&]() {
         bool ok = true;
@@ -513,15 +516,18 @@ __device__ __forceinline__ void split_epi_store(const SplitEpi &e, unsigned long
     // (the first check stays out of the retry loop, whose reloads would make it wait for
     //  every load in flight)
     if (!arrived()) {
-        for (int tries = 0;; ++tries) {
-            if (tries >= kSplitMaxPolls) {  // the other half never published: NaN, no hang
-#pragma unroll
-                for (int s = 0; s < 4; ++s) x[s] = ((unsigned long long)tag << 32) | 0x7fc00000u;
+        for (int tries = 0; !dead; ++tries) {
+            if (tries >= max_polls) {
+                dead = true;  // the other half never published
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
             split_poll(x, other, cp, w, lane);
             if (arrived()) break;
+        }
+        if (dead) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) x[s] = ((unsigned long long)tag << 32) | 0x7fc00000u;
         }
     }
     const int u = split_unit(lane);
@@ -619,6 +625,9 @@ __global__ __launch_bounds__(kSplitThreads, 1) void carry_split_kernel(PrefillAr
     uint2 gprev[4] = {};  // the previous chunk's output-gate logits of this lane's values
     SplitEpi pend = {};   // the epilogue of the chunk before that, awaiting the other half's sums
     unsigned long long px[4] = {};  // the other half's words for `pend`, loaded at the previous chunk's end
+    bool dead = false;              // this wave timed out waiting for the other half (wave-uniform)
+    const bool publish = a.xchg_publish != 0;
+    const int max_polls = a.xchg_max_polls > 0 ? a.xchg_max_polls : kSplitMaxPolls;
 
     auto chunk = [&](auto parity, int c) {
         constexpr int B = decltype(parity)::value;
@@ -639,7 +648,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void carry_split_kernel(PrefillAr
         // chunk c - 1's sums of squares, published for the other half
         SplitEpi cur;
         if (c > 0) {
-            split_epi_sums(prv_lo, cur, mine, c - 1, w, lane);
+            split_epi_sums(prv_lo, cur, mine, c - 1, w, lane, publish);
 #pragma unroll
             for (int s = 0; s < 4; ++s) cur.g[s] = gprev[s];
         }
@@ -687,7 +696,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void carry_split_kernel(PrefillAr
         // chunk c - 2's outputs (a full chunk: only the last can be partial)
         if (c > 1)
             split_epi_store<kBf16>(pend, px, nw, other, c - 2, a.c.rms_eps, a.out, col0, HD, t0 + c0 - 2 * kChunk,
-                                   kChunk, w, lane);
+                                   kChunk, w, lane, max_polls, dead);
         if (c > 0) pend = cur;
         // every wave has read the staged O: pieces 0 .. 31 of `prv` may be loaded
         lds_barrier();
@@ -770,15 +779,15 @@ __global__ __launch_bounds__(kSplitThreads, 1) void carry_split_kernel(PrefillAr
         barrier_all_mem();
         const int cl = nrec - 1;
         SplitEpi last;
-        split_epi_sums((cl & 1) ? carry_lo1 : carry_lo0, last, mine, cl, w, lane);
+        split_epi_sums((cl & 1) ? carry_lo1 : carry_lo0, last, mine, cl, w, lane, publish);
 #pragma unroll
         for (int s = 0; s < 4; ++s) last.g[s] = gprev[s];
         if (cl > 0)
             split_epi_store<kBf16>(pend, px, nw, other, cl - 1, a.c.rms_eps, a.out, col0, HD,
-                                   t0 + (cl - 1) * kChunk, kChunk, w, lane);
+                                   t0 + (cl - 1) * kChunk, kChunk, w, lane, max_polls, dead);
         split_poll(px, other, cl, w, lane);
         split_epi_store<kBf16>(last, px, nw, other, cl, a.c.rms_eps, a.out, col0, HD, t0 + cl * kChunk,
-                               min(kChunk, T - cl * kChunk), w, lane);
+                               min(kChunk, T - cl * kChunk), w, lane, max_polls, dead);
     }
 
     // half hf writes the conv windows of 192 of the head's 384 channels

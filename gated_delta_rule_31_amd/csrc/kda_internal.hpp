@@ -160,6 +160,8 @@ struct PrefillArgs {
     // kSplitCarryMaxUnits): [B*H][2 halves][4 slots][64 tokens] exchange words of the RMS
     // sums, zeroed by the chunk table kernel; null otherwise
     unsigned long long *xchg;
+    int xchg_publish;    // 1; 0 only under kda_test_split_carry (every wait then times out)
+    int xchg_max_polls;  // polls per wait, 0 = the kernel's bound
     const int32_t *cu_seqlens;
     const uint16_t *q, *k, *v, *z, *b, *g;
     size_t qkv_ld;  // elements between consecutive token rows of q, k, v (>= H*D)

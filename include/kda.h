@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 9
+#define KDA_ABI_VERSION 10
 
 typedef enum {
     KDA_OK = 0,
@@ -452,6 +452,17 @@ kda_status kda_state_copy(const kda_config *cfg, int32_t n,
                           const int32_t *src_slots,
                           float *dst_state, float *dst_conv, int32_t dst_entries,
                           const int32_t *dst_slots, void *stream);
+
+/* Test hook for the bounded wait of the chunked prefill's two-workgroup carry (the form
+ * used for B*H <= 128 in the standard precision, whose two workgroups of a (sequence,
+ * head) pair exchange each output row's RMS sums).  publish = 0 makes both workgroups
+ * skip publishing their sums, so that every wait times out; max_polls > 0 bounds each
+ * wait to that many polls (0: the library's bound, about a second).  A wave that times
+ * out writes NaN for that chunk's outputs and every later chunk's of the call without
+ * waiting again; states and conv windows are unaffected.  Process-wide, read when a
+ * prefill call is made; for tests of that path only.  kda_test_split_carry(1, 0)
+ * restores normal operation. */
+void kda_test_split_carry(int32_t publish, int32_t max_polls);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_str(kda_status s);

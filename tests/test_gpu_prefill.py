@@ -149,6 +149,26 @@ def test_carry_forms_agree_bitwise(device, B, H, lengths):
         assert torch.equal(x, y)
 
 
+def test_split_carry_wait_times_out(device):
+    """The two-workgroup carry's wait for the other half's row sums is bounded: with the
+    publishing switched off from the host (kda_test_split_carry) and a 16-poll bound, the
+    call returns with NaN outputs and the exact final states and windows, and the next call
+    is a normal one again."""
+    import gated_delta_rule_31_amd as kda
+    case = ki.prefill_case(130, 4, [200, 70], True, "split-timeout")
+    ref = prefill_gpu(case, device, path=PATH_CHUNKED)
+    try:
+        kda.kda_test_split_carry(False, 16)
+        got = prefill_gpu(case, device, path=PATH_CHUNKED)
+    finally:
+        kda.kda_test_split_carry(True, 0)
+    assert torch.isnan(got[0]).all()
+    assert torch.equal(got[1], ref[1]) and torch.equal(got[2], ref[2])
+    again = prefill_gpu(case, device, path=PATH_CHUNKED)
+    for x, y in zip(again, ref):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_packing_invariance(device, path):
     """Each sequence of a packed batch gives what it gives alone."""

@@ -115,7 +115,7 @@ typedef struct {
  *                           the fp64 recurrence for gates with decay; with no decay and
  *                           beta -> 1 on every token (the plain delta rule, where no
  *                           rounding is ever forgotten) the output error grows to about
- *                           2e-2 at 1K tokens and 2.6e-2 at 8K.
+ *                           2e-2 at 1K tokens and 3e-2 at 8K.
  *   KDA_PRECISION_HIGH      every MFMA operand of the chunk algebra split into bf16 hi +
  *                           lo (about 16 significant bits each): about 1e-4 in that regime
  *                           too.  Costs more MFMA and VALU work per chunk, and the chunked

@@ -1,8 +1,11 @@
 // kda_carry.hip -- the sequential half of the chunked prefill plan (gfx950).
 //
-// One workgroup of 8 waves per (sequence, head) walks the sequence's chunk records, which
-// the chunk kernel (kda_prefill.hip) wrote, and carries the 128x128 fp32 state in MFMA
-// accumulator registers.  Per chunk, in the notation of the chunk algebra there,
+// The carry walks each (sequence, head)'s chunk records, which the chunk kernel
+// (kda_prefill.hip) wrote, and carries the 128x128 fp32 state in MFMA accumulator
+// registers.  Three forms: carry_kernel (one 8-wave workgroup per pair, described first
+// below), carry_split_kernel (two 4-wave workgroups per pair, each owning half the value
+// columns, for batches with B*H <= 128; described before it) and carry_kernel_precise
+// (the high-precision records).  Per chunk, in the notation of the chunk algebra there,
 //   U = U' - W S0,   O = Q~ S0 + P U,   S_end = Diag(e^{G_end}) S0 + K_end^T U,
 // followed by out = sigmoid(g) * RMSNorm(O) (header comment "KDA per-head recurrence",
 // page "colibri/c/kimi_k3.c").  These are the state-side products of the fused kernel
@@ -19,9 +22,10 @@
 // straight from global memory into LDS with direct-to-LDS loads, double-buffered: the
 // next chunk's pieces are requested in four parts spread over the current chunk (after
 // its opening barrier, after the previous epilogue, after W S0 and after O) and arrive
-// while it computes, without occupying registers or issue slots for LDS writes.  Each chunk-parity buffer is its own LDS array and the loop body is
-// instantiated once per parity, so the compiler can tell the buffer being read from the
-// one being filled and does not wait for the loads in flight.  U' (this wave's 4 KB) is
+// while it computes, without occupying registers or issue slots for LDS writes.  Each
+// chunk-parity buffer is its own LDS array and the loop body is instantiated once per
+// parity, so the compiler can tell the buffer being read from the one being filled and
+// does not wait for the loads in flight.  U' (this wave's 4 KB) is
 // prefetched into registers one chunk ahead.  O is computed transposed, staged in LDS as
 // token rows in the place of W and Q~ (dead by then), and normalised and stored a token per
 // 32 lanes early in the next chunk, so that every gate load and output store covers whole

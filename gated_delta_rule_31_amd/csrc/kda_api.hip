@@ -318,6 +318,25 @@ kda_status device_scratch(void **out) {
     return KDA_OK;
 }
 
+// The current device's compute units, looked up once per device.  The two-workgroup
+// carry needs every workgroup pair resident together, so it runs only where the device
+// has a compute unit for each of its workgroups (one per compute unit by LDS); a device
+// that shows fewer (a partition of the GPU, say) takes the one-workgroup carry instead.
+std::mutex cu_mu;
+int cu_count[kMaxDevices] = {};
+
+int device_compute_units() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::lock_guard<std::mutex> lock(cu_mu);
+    if (!cu_count[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+        cu_count[dev] = n;
+    }
+    return cu_count[dev];
+}
+
 // kda_prefill, and (static_scratch) kda_prefill_noalloc: the workspace is then this
 // device's scratch array, looked up after every argument check has passed
 // kda_test_split_carry's settings, read by every prefill call
@@ -394,9 +413,11 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
     a.chunk_start = chunked ? static_cast<int32_t *>(workspace) : nullptr;
     a.seg_start = chunked ? static_cast<int32_t *>(workspace) + (num_seqs + 1) : nullptr;
     a.records = chunked ? static_cast<unsigned char *>(workspace) + plan.table_bytes : nullptr;
-    a.xchg = plan.carry_split ? reinterpret_cast<unsigned long long *>(static_cast<unsigned char *>(workspace) +
-                                                                       (8 * (num_seqs + 1) + 255) / 256 * 256)
-                              : nullptr;
+    // (the workspace keeps the exchange area either way; an unused one costs nothing)
+    const bool split = plan.carry_split && 2 * (int64_t)num_seqs * cfg->num_heads <= device_compute_units();
+    a.xchg = split ? reinterpret_cast<unsigned long long *>(static_cast<unsigned char *>(workspace) +
+                                                            (8 * (num_seqs + 1) + 255) / 256 * 256)
+                   : nullptr;
     a.xchg_publish = split_publish.load();
     a.xchg_max_polls = split_max_polls.load();
     a.cu_seqlens = cu_seqlens;

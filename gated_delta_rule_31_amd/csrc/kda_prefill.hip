@@ -803,32 +803,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             KDA_LANE_IDS();
             auto column = [&](auto jc) {
                 constexpr int J = decltype(jc)::value;
-                f32x4 R[4];  // R[K] = T_KJ (K > J): rows 16K + 4lg + i, column 16J + lr
+                f32x4 M[4];  // M[I] = A_IJ T_JJ + sum_K A_IK T_KJ, rows 16I + 4lg + i, column 16J + lr
                 float tjj[4];  // T_JJ[4lg + kk][lr]
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) tjj[kk] = sT[(16 * J + 4 * lg + kk) * F_LD + 16 * J + lr];
+                // Every M[I] starts at once with its A_IJ T_JJ term, and takes A_IK T_KJ as soon as
+                // T_KJ is known; each M[I] still sums its terms in the order K = J, J+1, .., so
+                // the bits are those of one block at a time, with the chains of independent
+                // blocks interleaved.
 #pragma unroll
                 for (int I = J + 1; I < 4; ++I) {
-                    f32x4 M = {0.f, 0.f, 0.f, 0.f};
                     const f32x4 aj = *reinterpret_cast<const f32x4 *>(sA + (16 * I + lr) * F_LD + 16 * J + 4 * lg);
+                    M[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) M = mma_f32(aj[kk], tjj[kk], M);
+                    for (int kk = 0; kk < 4; ++kk) M[I] = mma_f32(aj[kk], tjj[kk], M[I]);
+                }
 #pragma unroll
-                    for (int K = J + 1; K < I; ++K) {
-                        const f32x4 ak4 = *reinterpret_cast<const f32x4 *>(sA + (16 * I + lr) * F_LD + 16 * K + 4 * lg);
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) M = mma_f32(ak4[kk], R[K][kk], M);
-                    }
-                    const f32x4 tii = *reinterpret_cast<const f32x4 *>(sT + (16 * I + lr) * F_LD + 16 * I + 4 * lg);
+                for (int K = J + 1; K < 4; ++K) {
+                    // M[K] is complete: T_KJ = -T_KK M[K]
+                    const f32x4 tkk = *reinterpret_cast<const f32x4 *>(sT + (16 * K + lr) * F_LD + 16 * K + 4 * lg);
                     f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) r = mma_f32(-tii[kk], M[kk], r);
-                    R[I] = r;
+                    for (int kk = 0; kk < 4; ++kk) r = mma_f32(-tkk[kk], M[K][kk], r);
+#pragma unroll
+                    for (int I = K + 1; I < 4; ++I) {
+                        const f32x4 ak4 = *reinterpret_cast<const f32x4 *>(sA + (16 * I + lr) * F_LD + 16 * K + 4 * lg);
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) M[I] = mma_f32(ak4[kk], r[kk], M[I]);
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const __bf16 rh = (__bf16)r[i];
-                        sTb[sw64(16 * I + 4 * lg + i, 16 * J + lr)] = rh;
-                        if constexpr (kPrecise) sTbLo[sw64(16 * I + 4 * lg + i, 16 * J + lr)] = (__bf16)(r[i] - (float)rh);
+                        sTb[sw64(16 * K + 4 * lg + i, 16 * J + lr)] = rh;
+                        if constexpr (kPrecise) sTbLo[sw64(16 * K + 4 * lg + i, 16 * J + lr)] = (__bf16)(r[i] - (float)rh);
                     }
                 }
             };

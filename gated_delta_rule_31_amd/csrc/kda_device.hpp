@@ -73,6 +73,14 @@ __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint
 // sigmoid with the hardware reciprocal (about 1 ulp) instead of an IEEE division
 __device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+// The lo part x - hi of x = hi + lo, rounded to bf16.  The subtraction stays a plain
+// subtraction: fast contraction could otherwise fuse it with the multiply that produced x
+// or not, depending on how the inlining kernel happens to be scheduled, and the lo bits
+// would then differ between kernels that must agree bit for bit.
+__device__ __forceinline__ __bf16 bf16_lo(float x, __bf16 hi) {
+#pragma clang fp contract(off)
+    return (__bf16)(x - (float)hi);
+}
 // x = hi + lo with hi, lo bf16 (hi = RNE(x)); hi*hi' + lo*hi' + hi*lo' then carries about
 // 16 significant bits of each operand through a bf16 MFMA
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
@@ -80,7 +88,7 @@ __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
     for (int j = 0; j < 8; ++j) {
         const __bf16 h = (__bf16)x[j];
         hi[j] = h;
-        lo[j] = (__bf16)(x[j] - (float)h);
+        lo[j] = bf16_lo(x[j], h);
     }
 }
 __device__ __forceinline__ bf16x8 to_bf8(const float *x) {

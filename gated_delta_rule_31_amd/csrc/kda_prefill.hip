@@ -490,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     const float bv = vscale * u[j];
                     const __bf16 hi = (__bf16)bv;
                     sVtHi[sw64(cbase + 8 * pc + j, t)] = hi;
-                    sVtLo[sw64(cbase + 8 * pc + j, t)] = (__bf16)(bv - (float)hi);
+                    sVtLo[sw64(cbase + 8 * pc + j, t)] = bf16_lo(bv, hi);
                 }
             }
             // q, k and their partial sums of squares over this wave's 64 channels
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     const float bw = beta * kr[8 * pc + j] * er;
                     const __bf16 bwh = (__bf16)bw;
                     sWr[sw64(c, t)] = bwh;
-                    if constexpr (kPrecise) sWrLo[sw64(c, t)] = (__bf16)(bw - (float)bwh);
+                    if constexpr (kPrecise) sWrLo[sw64(c, t)] = bf16_lo(bw, bwh);
                     qe[j] = qr[8 * pc + j] * er;
                     ke[8 * pc + j] = cbk[8 * pc + j] * sEndRef[sub * 128 + c];
                 }
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                         }
                         va[i] = x;
                         ph[i] = (__bf16)y;
-                        pl[i] = (__bf16)(y - (float)ph[i]);
+                        pl[i] = bf16_lo(y, ph[i]);
                     }
                     *reinterpret_cast<f32x4 *>(sA + t * F_LD + 16 * J + 4 * lg) = va;
                     *reinterpret_cast<bf16x4 *>(sPh + sw64(t, 16 * J + 4 * lg)) = ph;
@@ -736,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     const int c = 64 * half + 16 * lg + j;
                     const __bf16 hi = (__bf16)ke[j];
                     sKeHi[swi64(c, t)] = hi;
-                    sKeLo[swi64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                    sKeLo[swi64(c, t)] = bf16_lo(ke[j], hi);
                 }
             }
         }
@@ -771,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     sT[(d + tt) * F_LD + d + lr] = x[tt];
                     const __bf16 xh = (__bf16)x[tt];
                     sTb[sw64(d + tt, d + lr)] = xh;
-                    if constexpr (kPrecise) sTbLo[sw64(d + tt, d + lr)] = (__bf16)(x[tt] - (float)xh);
+                    if constexpr (kPrecise) sTbLo[sw64(d + tt, d + lr)] = bf16_lo(x[tt], xh);
                 }
             } else if (w >= 4) {
                 // upper blocks (I < J) of sTb: 6 blocks x 256 values over 256 lanes
@@ -835,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     for (int i = 0; i < 4; ++i) {
                         const __bf16 rh = (__bf16)r[i];
                         sTb[sw64(16 * K + 4 * lg + i, 16 * J + lr)] = rh;
-                        if constexpr (kPrecise) sTbLo[sw64(16 * K + 4 * lg + i, 16 * J + lr)] = (__bf16)(r[i] - (float)rh);
+                        if constexpr (kPrecise) sTbLo[sw64(16 * K + 4 * lg + i, 16 * J + lr)] = bf16_lo(r[i], rh);
                     }
                 }
             };
@@ -864,7 +864,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     const int c = 16 * lg + j;
                     const __bf16 hi = (__bf16)ke[j];
                     sKeHi[swi64(c, t)] = hi;
-                    sKeLo[swi64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                    sKeLo[swi64(c, t)] = bf16_lo(ke[j], hi);
                 }
             }
 #pragma unroll
@@ -887,7 +887,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     w4[i] = (__bf16)acc[i];
-                    if constexpr (kPrecise) w4l[i] = (__bf16)(acc[i] - (float)w4[i]);
+                    if constexpr (kPrecise) w4l[i] = bf16_lo(acc[i], w4[i]);
                 }
                 *reinterpret_cast<bf16x4 *>(sW + swi128(16 * tt + lr, 16 * w + 4 * lg)) = w4;
                 if constexpr (kPrecise) *reinterpret_cast<bf16x4 *>(sWLo + swi128(16 * tt + lr, 16 * w + 4 * lg)) = w4l;
@@ -928,7 +928,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 const int c = 64 * half + 16 * lg + j;
                 const __bf16 hi = (__bf16)ke[j];
                 sKeHi[swi64(c, t)] = hi;
-                sKeLo[swi64(c, t)] = (__bf16)(ke[j] - (float)hi);
+                sKeLo[swi64(c, t)] = bf16_lo(ke[j], hi);
             }
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {

@@ -92,7 +92,7 @@ def prefill_bytes(N: int, B: int, H: int, initial: bool, out_bytes: int = 4) -> 
 # (each list covers the kernel file and every header it includes)
 DECODE_SRCS = ["kda_decode.hip", "kda_decode_common.hpp", "kda_device.hpp", "kda_internal.hpp"]
 DECODE_MULTI_SRCS = ["kda_decode_multi.hip", "kda_decode_common.hpp", "kda_device.hpp", "kda_internal.hpp"]
-PREFILL_SRCS = ["kda_prefill.hip", "kda_carry.hip", "kda_device.hpp", "kda_internal.hpp"]
+PREFILL_SRCS = ["kda_prefill.hip", "kda_carry.hip", "kda_carry.hpp", "kda_device.hpp", "kda_internal.hpp"]
 
 
 def sources_sha256(names) -> str:

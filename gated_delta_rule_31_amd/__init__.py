@@ -16,7 +16,7 @@ import torch
 
 __all__ = ["KdaConfig", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi", "kda_decode_multi_slots",
            "kda_prefill", "kda_prefill_gate_proj", "kda_prefill_noalloc", "kda_prefill_workspace_bytes",
-           "kda_state_copy", "kda_test_split_carry", "KdaError",
+           "kda_state_copy", "kda_test_split_carry", "kda_test_pipeline", "KdaError",
            "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "PREFILL_AUTO", "PREFILL_FUSED", "PREFILL_CHUNKED",
            "PRECISION_STANDARD", "PRECISION_HIGH", "MULTI_BLOCK", "MULTI_SEQUENTIAL"]
 
@@ -24,8 +24,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_config_default", "kda_decode_step", "kda_decode_step_slots", "kda_decode_multi",
                     "kda_decode_multi_slots", "kda_prefill", "kda_prefill_gate_proj", "kda_prefill_noalloc",
                     "kda_prefill_workspace_bytes",
-                    "kda_state_copy", "kda_test_split_carry", "kda_status_str", "kda_abi_version")
-ABI_VERSION = 10
+                    "kda_state_copy", "kda_test_split_carry", "kda_test_pipeline", "kda_status_str",
+                    "kda_abi_version")
+ABI_VERSION = 11
 HEAD_DIM = 128
 CONV = 4
 RANK = 128  # rank of the low-rank decay projection (kda_prefill_gate_proj)
@@ -123,6 +124,8 @@ def _load() -> ctypes.CDLL:
                                   ctypes.c_int32, vp, vp])
     L.kda_test_split_carry.restype = None
     L.kda_test_split_carry.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    L.kda_test_pipeline.restype = None
+    L.kda_test_pipeline.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     L.kda_status_str.restype = ctypes.c_char_p
     L.kda_status_str.argtypes = [ctypes.c_int]
     L.kda_abi_version.restype = ctypes.c_int32
@@ -458,3 +461,11 @@ def kda_test_split_carry(publish: bool, max_polls: int = 0) -> None:
     max_polls polls (0: the library's bound) and the outputs become NaN; the states stay
     exact.  Process-wide; kda_test_split_carry(True) restores normal operation."""
     _lib.kda_test_split_carry(1 if publish else 0, int(max_polls))
+
+
+def kda_test_pipeline(mode: int = 0, publish: bool = True, max_polls: int = 0) -> None:
+    """Test hook of the chunked prefill whose carries run in the chunk workgroups' launch
+    (kda.h, kda_test_pipeline): mode 0 the library's choice, 1 never that form, 2 wherever
+    it can run; publish=False makes every carry's wait for a record time out (NaN outputs
+    and NaN final states).  Process-wide; kda_test_pipeline() restores normal operation."""
+    _lib.kda_test_pipeline(int(mode), 1 if publish else 0, int(max_polls))

@@ -8,7 +8,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <mutex>
 
 #include "kda.h"
@@ -92,8 +94,30 @@ struct PrefillPlan {
     int64_t nchunk_cap, nseg_cap;
     int seg_chunks;
     bool carry_split;  // chunked: the two-workgroup carry (standard precision, B*H <= 128)
+    bool pipe;         // chunked: the carries in the chunk kernel's launch (one sequence)
+    size_t ready_off;  // pipe: byte offset of the ready words in the workspace
     size_t table_bytes, workspace_bytes;
 };
+
+// kda_test_pipeline's settings, read by every prefill call: mode 0 = the plan's choice,
+// 1 = never pipelined, 2 = pipelined wherever it can be
+std::atomic<int32_t> pipe_mode{0};
+std::atomic<int32_t> pipe_publish{1};
+std::atomic<int32_t> pipe_max_polls{0};
+
+// The time model of the pipelined plan (kda_internal.hpp): its time and the number of
+// chunk-heads whose workgroups start before the carries, for I chunk-heads, R chunks per
+// sequence, C compute units and NC carries.
+struct PipeModel {
+    double us, lead_chunk_heads;
+};
+PipeModel pipe_model(double I, double R, double C, double NC) {
+    const double ratio = kda::kPipeCarryChunkUs / kda::kRecordUs;
+    const double lead = std::max(0.0, I - R * ratio * (C - NC));
+    const double start = lead * kda::kRecordUs / C;
+    const double rest = (I - lead) * kda::kRecordUs / (C - NC);  // chunk-heads after the carries start
+    return {start + std::max(R * kda::kPipeCarryChunkUs, rest), lead};
+}
 // max_workspace >= 0: the workspace is a fixed array of that many bytes; the automatic
 // choice then takes the chunked layout only if its workspace fits (else fused, which
 // needs none).
@@ -105,20 +129,34 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     const int64_t segs = kda::seg_cap(B, cap, seg_chunks);
     const bool chunked_fits = cap * H <= kda::kMaxPrefillUnits && segs * H <= kda::kMaxPrefillUnits;
     const bool precise = cfg->precision == KDA_PRECISION_HIGH;
-    const bool split = !precise && B * H <= kda::kSplitCarryMaxUnits;
-    // chunk_start and seg_start, then (split carry) the RMS-sum exchange words
-    const size_t table_bytes =
-        (size_t)((8 * (B + 1) + 255) / 256 * 256) + (split ? (size_t)(B * H * kda::kSplitXchgBytes) : 0);
+    const bool split_ok = !precise && B * H <= kda::kSplitCarryMaxUnits;
+    const double rounds = (double)((B * H + kda::kComputeUnits - 1) / kda::kComputeUnits);
+    const double chunks = B > 0 ? (double)((N + 64 * B - 1) / (64 * B)) : 0.0;  // mean length, rounded up
+    const double records_us = (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits;
+    const double serial_us =
+        records_us + (split_ok ? chunks * kda::kSplitCarryChunkUs : rounds * chunks * kda::kCarryChunkUs);
+    // the pipelined plan: one sequence, standard precision, at most half the compute units
+    // for the carries; taken where its model beats the serial one (mode 0)
+    const int32_t mode = pipe_mode.load();
+    const int64_t pipe_segs = kda::seg_cap(B, cap, kda::kPipeSegChunks);
+    bool pipe = mode != 1 && B == 1 && !precise && B * H <= kda::kPipeMaxUnits && N > 0 &&
+                chunked_fits && pipe_segs * H + B * H <= kda::kMaxPrefillUnits;
+    if (pipe && mode == 0)
+        pipe = pipe_model((double)cap * (double)H, chunks, kda::kComputeUnits, (double)(B * H)).us < serial_us;
+    const bool split = split_ok && !pipe;
+    // chunk_start and seg_start, then the RMS-sum exchange words (split carry) or the
+    // records' ready words (pipelined)
+    const size_t base_bytes = (size_t)((8 * (B + 1) + 255) / 256 * 256);
+    const size_t ready_bytes = pipe ? (size_t)((cap * H * 4 + 255) / 256 * 256) : 0;
+    const size_t table_bytes = base_bytes + (split ? (size_t)(B * H * kda::kSplitXchgBytes) : 0) + ready_bytes;
     const size_t chunked_bytes = table_bytes + (size_t)cap * (size_t)H * (size_t)kda::rec_bytes(precise);
     int path = cfg->prefill_path;
     if (path == kda::kPathAuto) {
         path = kda::kPathFused;
         if (chunked_fits && B > 0) {
-            const double rounds = (double)((B * H + kda::kComputeUnits - 1) / kda::kComputeUnits);
-            const double chunks = (double)((N + 64 * B - 1) / (64 * B));  // mean length, rounded up
             const double fused = rounds * chunks * kda::kFusedChunkUs;
-            const double chunked = (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits +
-                                   (split ? chunks * kda::kSplitCarryChunkUs : rounds * chunks * kda::kCarryChunkUs);
+            const double chunked =
+                pipe ? pipe_model((double)cap * (double)H, chunks, kda::kComputeUnits, (double)(B * H)).us : serial_us;
             if (chunked < fused && (max_workspace < 0 || chunked_bytes <= (size_t)max_workspace))
                 path = kda::kPathChunked;
         }
@@ -127,9 +165,11 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     if (path == kda::kPathChunked && !chunked_fits) return false;
     plan->path = path;
     plan->nchunk_cap = cap;
-    plan->nseg_cap = segs;
-    plan->seg_chunks = seg_chunks;
+    plan->nseg_cap = pipe ? pipe_segs : segs;
+    plan->seg_chunks = pipe ? kda::kPipeSegChunks : seg_chunks;
     plan->carry_split = path == kda::kPathChunked && split;
+    plan->pipe = path == kda::kPathChunked && pipe;
+    plan->ready_off = base_bytes;
     plan->table_bytes = table_bytes;
     plan->workspace_bytes = path == kda::kPathFused ? 0 : chunked_bytes;
     return true;
@@ -420,6 +460,21 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
                    : nullptr;
     a.xchg_publish = split_publish.load();
     a.xchg_max_polls = split_max_polls.load();
+    // the pipelined plan, where the device keeps at least half its compute units for the
+    // chunk workgroups (else the serial one-workgroup carry on the same workspace)
+    const int cus = device_compute_units();
+    const int64_t pairs = (int64_t)num_seqs * cfg->num_heads;
+    const bool pipe = plan.pipe && 2 * pairs <= cus;
+    a.ready = pipe ? reinterpret_cast<unsigned *>(static_cast<unsigned char *>(workspace) + plan.ready_off) : nullptr;
+    a.pipe_units = pipe ? (int)pairs : 0;
+    a.pipe_first = 0;
+    if (pipe) {
+        const double chunks = (double)((total_tokens + kda::kChunk - 1) / kda::kChunk);
+        const double lead = pipe_model(chunks * cfg->num_heads, chunks, cus, (double)pairs).lead_chunk_heads;
+        a.pipe_first = (int)std::min((double)plan.nseg_cap * cfg->num_heads, std::floor(lead / plan.seg_chunks));
+    }
+    a.ready_publish = pipe_publish.load();
+    a.ready_max_polls = pipe_max_polls.load();
     a.cu_seqlens = cu_seqlens;
     a.q = q; a.k = k; a.v = v; a.z = gate_proj ? nullptr : z; a.b = b; a.g = g;
     a.f = gate_proj ? f : nullptr;
@@ -552,6 +607,12 @@ kda_status kda_state_copy(const kda_config *cfg, int32_t n, const float *src_sta
 void kda_test_split_carry(int32_t publish, int32_t max_polls) {
     split_publish.store(publish != 0 ? 1 : 0);
     split_max_polls.store(max_polls > 0 ? max_polls : 0);
+}
+
+void kda_test_pipeline(int32_t mode, int32_t publish, int32_t max_polls) {
+    pipe_mode.store(mode == 1 || mode == 2 ? mode : 0);
+    pipe_publish.store(publish != 0 ? 1 : 0);
+    pipe_max_polls.store(max_polls > 0 ? max_polls : 0);
 }
 
 const char *kda_status_str(kda_status s) {

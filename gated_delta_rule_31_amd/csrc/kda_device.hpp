@@ -116,6 +116,17 @@ __device__ __forceinline__ void lds_write8(float *p, const float *x) {
     *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 
+// The cache-policy operand of the load builtins for a device-scope (sc1) access: it does
+// not return a copy that one XCD's caches hold, so it sees what another workgroup of the
+// same launch made visible at device scope.
+constexpr int kCpolSc1 = 16;
+// Word 3 of a raw buffer resource (stride 0, byte-addressed, range-checked against its
+// size) on gfx9-family chips such as gfx950.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// The s_waitcnt operand (gfx9 encoding) of vmcnt(0) alone: expcnt 7 and lgkmcnt 15 wait
+// for nothing.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ---- workgroup order of the per-(sequence, head) prefill kernels ----
 // Workgroups start in id order as compute units free up, so in a batch of unequal
 // sequences the last long ones would run alone at the end.  For batches of up to

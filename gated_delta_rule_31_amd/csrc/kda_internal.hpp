@@ -107,6 +107,27 @@ constexpr double kSplitCarryChunkUs = 5.2;
 // exchange bytes per (sequence, head) of the split carry: 2 halves x 4 slots x 64 x 8
 constexpr int64_t kSplitXchgBytes = 2 * 4 * kChunk * 8;
 
+// The pipelined chunked plan (kda_prefill.hip) puts the B*H one-workgroup carries into
+// the chunk kernel's grid after its first pipe_first workgroups, so that they start once
+// those finish and then follow the records as the rest are written.  It is used for one
+// sequence with B*H <= (compute units) / 2, so that the chunk workgroups keep at least half
+// the compute units.  The carries should start late enough never to wait: with p the time
+// of a chunk-head on one compute unit (kRecordUs), r a carry's time per chunk
+// (kPipeCarryChunkUs), I chunk-heads, R chunks per sequence, C compute units and B*H carries,
+// the workgroups that start before them cover I - R (r / p) (C - B*H) chunk-heads, the
+// work that C - B*H compute units finish while a carry walks its R chunks.  The plan's
+// time is then that start plus R r.  Beside the chunk workgroups a carry walks a chunk in
+// about 6.4 of the model's microseconds (kPipeCarryChunkUs; 5.9 us measured on MI355X,
+// where it takes 4.9 alone).  The chunk workgroups of this plan take segments of
+// kPipeSegChunks chunks: a row of records is complete only when every head's segment is,
+// so long segments would make the carries wait for whole rows (measured on 1 x 8192
+// tokens x 96 heads: 1.14 ms with 4 or 8 chunks, 1.21 ms with 16).  A carry waits for a
+// record at most kReadyMaxPolls polls.
+constexpr double kPipeCarryChunkUs = 6.4;
+constexpr int kPipeSegChunks = 4;
+constexpr int kReadyMaxPolls = 1 << 20;
+constexpr int64_t kPipeMaxUnits = kComputeUnits / 2;
+
 // Bytes of one chunk record (the layout is in kda_device.hpp); multiples of 256.  The
 // high-precision record also holds the lo parts of W and Q~.
 constexpr int kRecBytes = 111616;
@@ -162,6 +183,14 @@ struct PrefillArgs {
     unsigned long long *xchg;
     int xchg_publish;    // 1; 0 only under kda_test_split_carry (every wait then times out)
     int xchg_max_polls;  // polls per wait, 0 = the kernel's bound
+    // chunked plan, pipelined: the chunk kernel's grid also holds the B*H one-workgroup
+    // carries (grid indices pipe_first .. pipe_first + pipe_units - 1), which read each
+    // record once its word in `ready` ([nchunk_cap][H], zeroed by the chunk table kernel)
+    // is set; null and 0 otherwise
+    unsigned *ready;
+    int pipe_first, pipe_units;
+    int ready_publish;    // 1; 0 only under kda_test_pipeline (every wait then times out)
+    int ready_max_polls;  // polls per wait, 0 = the kernel's bound
     const int32_t *cu_seqlens;
     const uint16_t *q, *k, *v, *z, *b, *g;
     size_t qkv_ld;  // elements between consecutive token rows of q, k, v (>= H*D)

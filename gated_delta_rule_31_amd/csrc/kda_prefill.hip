@@ -44,6 +44,7 @@
 
 #include <type_traits>
 
+#include "kda_carry.hpp"
 #include "kda_device.hpp"
 
 namespace kda {
@@ -212,8 +213,13 @@ __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, 
 // kGateProj: the decay logits are z = W_fb f (a.f, a.w_fb) instead of a.z: each chunk
 // stages the head's 128 rows of W_fb in LDS and phase 1 forms its 64 x 128 logits with
 // MFMAs, laid out as the gate computation wants them (see phase 1).
-template <bool kChunked, bool kPrecise, bool kGateProj>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+// kPipe (with the chunked, standard-precision forms only): the pipelined plan, whose carries
+// run in the same launch; each chunk's record is announced in a.ready once every wave's
+// stores of it have completed.  bid: the workgroup's segment-major index (sg * H + h),
+// or (sequence order) * H + h in the fused plan.
+template <bool kChunked, bool kPrecise, bool kGateProj, bool kPipe = false>
+__device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid) {
+    static_assert(!kPipe || (kChunked && !kPrecise), "the pipelined plan's form");
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr LdsMap M = kPrecise ? kMapPrecise : kMapStd;
     using R = Rec<kPrecise>;
@@ -251,8 +257,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // rec0: record row of the sequence's first chunk (chunked plan)
     int seq, h, cbeg, nrec = 0, rec0 = 0;
     if constexpr (kChunked) {
-        const int sg = blockIdx.x / H;
-        h = blockIdx.x - sg * H;
+        const int sg = bid / H;
+        h = bid - sg * H;
         if (sg >= a.seg_start[a.B]) return;  // past the batch's last segment (uniform)
         // the sequence owning segment sg: seg_start[lo] <= sg < seg_start[hi]
         int lo = 0, hi = a.B;
@@ -265,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         nrec = a.chunk_start[seq + 1] - rec0;  // ceil(T / 64) for a valid batch
         cbeg = (sg - a.seg_start[seq]) * a.seg_chunks * kChunk;
     } else {
-        const int r = blockIdx.x / H;
-        h = blockIdx.x - r * H;
+        const int r = bid / H;
+        h = bid - r * H;
         // (region 1 is free until the first chunk's operand rows)
         seq = seq_longest_first(a.cu_seqlens, a.B, N, r, reinterpret_cast<int *>(smem + OFF_R1));
         cbeg = 0;
@@ -390,6 +396,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
 
     const int cend = kChunked ? min(min(cbeg + a.seg_chunks * kChunk, nrec * kChunk), T) : T;
+    // kPipe: chunk cc's record is complete (every wave has waited for its own device-scope
+    // stores of it, then a barrier): its ready word, a device-scope store
+    auto publish_ready = [&](int cc) {
+        if constexpr (kPipe) {
+            if (threadIdx.x == 0 && a.ready_publish)
+                __hip_atomic_store(a.ready + (size_t)(rec0 + cc / kChunk) * H + h, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
     // (inside the chunk loop every cross-wave dependency goes through LDS, so its
     //  barriers wait for LDS traffic only: the next chunk's loads and this chunk's output
     //  stores stay in flight across them)
@@ -564,7 +579,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 lds_write8(sTot + sub * 128 + cbase + 8, gs + 8);
             }
         }
+        // kPipe: the previous chunk's record stores were issued a whole phase ago, and no
+        // other global access is in flight here: wait for them, so that the barrier orders
+        // every wave's stores before the ready word
+        if constexpr (kPipe)
+            if (c0 > cbeg) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         lds_barrier();
+        if (c0 > cbeg) publish_ready(c0 - kChunk);
 
         // ---- per-chunk channel tables (threads 0..255), and this lane's operand rows ----
         float qr[16], kr[16], cbk[16];  // q e^{G-r}, k e^{G-r}, k e^{r-G} of the normalised q, k
@@ -943,11 +964,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             KDA_LANE_IDS();
             const int lane = tid_ & 63;
             unsigned char *rec = a.records + ((size_t)(rec0 + c0 / kChunk) * H + h) * R::kBytes;
+            // kPipe: device-scope (sc1) stores, written through to where the carries' device-
+            // scope loads read them, on any XCD; no cache needs writing back before the ready word
+            auto put = [&](int off, const u32x4 &v) {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, __builtin_amdgcn_make_buffer_rsrc(rec, 0, R::kBytes, kBufferRsrcWord3), off, 0, kCpolSc1);
+            };
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-                for (int x = 0; x < 2; ++x)
-                    *reinterpret_cast<f32x4 *>(rec + R::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16) = U[tp][x];
+                for (int x = 0; x < 2; ++x) {
+                    const int off = R::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16;
+                    if constexpr (kPipe)
+                        put(off, __builtin_bit_cast(u32x4, U[tp][x]));
+                    else
+                        *reinterpret_cast<f32x4 *>(rec + off) = U[tp][x];
+                }
             // the operand pieces, in the order the carry reads them: piece 8j + w is copied
             // by wave w, lane l taking the 16 bytes lane l of a carry wave reads (source
             // offsets computed once, before the chunk loop)
@@ -958,7 +990,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 const uint32_t off = ((rec_src[j >> 1] >> (16 * (j & 1))) & 0xffffu) << 4;
                 u32x4 v = *reinterpret_cast<const u32x4 *>(smem + off);
                 if (piece == R::kE && lane >= 32) v = u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4 *>(rec + piece * REC_PIECE + lane * 16) = v;
+                if constexpr (kPipe)
+                    put(piece * REC_PIECE + lane * 16, v);
+                else
+                    *reinterpret_cast<u32x4 *>(rec + piece * REC_PIECE + lane * 16) = v;
             }
             lds_barrier();  // LDS is rewritten by the next chunk
             continue;
@@ -1090,7 +1125,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         lds_barrier();  // LDS is rewritten by the next chunk
     }
 
-    if constexpr (kChunked) return;  // the carry kernel writes the final state and windows
+    if constexpr (kChunked) {
+        // the last chunk's ready word (kPipe); the carry writes the final state and windows
+        if constexpr (kPipe) {
+            if (cend > cbeg) {
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                lds_barrier();
+                publish_ready(cbeg + (cend - cbeg - 1) / kChunk * kChunk);
+            }
+        }
+        return;
+    }
 
     // ---- final state ----
     {
@@ -1127,6 +1172,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 
 #undef KDA_LANE_IDS
 
+template <bool kChunked, bool kPrecise, bool kGateProj>
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+    prefill_body<kChunked, kPrecise, kGateProj>(a, (int)blockIdx.x);
+}
+
+// ---- the pipelined chunked plan: chunk workgroups and carries in one launch ----
+// Grid indices pipe_first .. pipe_first + pipe_units - 1 are the one-workgroup carries of
+// pairs 0 .. B*H - 1 (kda_carry.hpp, following the ready words); the others are the chunk
+// workgroups of the segment-major order, the carries' indices skipped.  Workgroups start
+// in index order as compute units free up, so the carries start once the first pipe_first
+// chunk workgroups are under way and never hold more compute units than the host allows;
+// the chunk workgroups never wait, so every record is written whatever the carries do.
+// The carry's record buffers take the first 154 KB of the same dynamic LDS.
+template <bool kBf16, bool kGateProj>
+__global__ __launch_bounds__(kThreads, 1) void prefill_pipe_kernel(PrefillArgs a) {
+    static_assert(kThreads == kCarryThreads, "one block size for both roles");
+    static_assert(2 * (kLoPieces + kHiPieces) * REC_PIECE <= kLdsBytes, "the carry's buffers");
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int b = (int)blockIdx.x;
+    if (b >= a.pipe_first && b < a.pipe_first + a.pipe_units) {
+        const int pair = b - a.pipe_first;
+        carry_body<kBf16, true>(a, pair / a.c.H, pair % a.c.H, smem, smem + kLoPieces * REC_PIECE,
+                                smem + (kLoPieces + kHiPieces) * REC_PIECE,
+                                smem + (2 * kLoPieces + kHiPieces) * REC_PIECE);
+        return;
+    }
+    prefill_body<true, false, kGateProj, true>(a, b < a.pipe_first ? b : b - a.pipe_units);
+}
+
 // ---- the chunked plan's tables ----
 // Sequence s owns record rows chunk_start[s] .. chunk_start[s+1]-1, one per chunk of 64
 // tokens (a partial last chunk included), in order, and chunk-kernel segments
@@ -1157,6 +1231,12 @@ __global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs 
     if (a.xchg) {
         const size_t n = (size_t)a.B * a.c.H * (kSplitXchgBytes / 16);
         uint4 *x = reinterpret_cast<uint4 *>(a.xchg);
+        for (size_t i = tid; i < n; i += kTableThreads) x[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // the pipelined plan's ready words start at zero
+    if (a.ready) {
+        const size_t n = ((size_t)a.nchunk_cap * a.c.H + 3) / 4;
+        uint4 *x = reinterpret_cast<uint4 *>(a.ready);
         for (size_t i = tid; i < n; i += kTableThreads) x[i] = make_uint4(0u, 0u, 0u, 0u);
     }
     const long long cap = a.nchunk_cap;
@@ -1210,6 +1290,15 @@ hipError_t launch_prefill_kernel(const PrefillArgs &a, size_t blocks, hipStream_
               : launch_prefill_kernel_t<kChunked, false, false>(a, blocks, stream);
 }
 
+template <bool kBf16, bool kGateProj>
+hipError_t launch_pipe_t(const PrefillArgs &a, size_t blocks, hipStream_t stream) {
+    const void *fn = reinterpret_cast<const void *>(&prefill_pipe_kernel<kBf16, kGateProj>);
+    static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (attr != hipSuccess) return attr;
+    void *args[] = {const_cast<PrefillArgs *>(&a)};
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, kLdsBytes, stream);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
@@ -1218,6 +1307,13 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&chunk_table_kernel), dim3(1), dim3(kTableThreads),
                                    args, 0, stream);
     if (e != hipSuccess) return e;
+    if (a.ready) {
+        const bool gp = a.w_fb != nullptr;
+        const size_t blocks = (size_t)a.nseg_cap * a.c.H + (size_t)a.pipe_units;
+        if (a.c.out_bf16)
+            return gp ? launch_pipe_t<true, true>(a, blocks, stream) : launch_pipe_t<true, false>(a, blocks, stream);
+        return gp ? launch_pipe_t<false, true>(a, blocks, stream) : launch_pipe_t<false, false>(a, blocks, stream);
+    }
     e = launch_prefill_kernel<true>(a, (size_t)a.nseg_cap * a.c.H, stream);
     if (e != hipSuccess) return e;
     return launch_carry(a, stream);

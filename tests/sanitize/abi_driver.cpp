@@ -68,7 +68,8 @@ int main() {
            KDA_ERR_BAD_SHAPE);
     EXPECT(kda_prefill(&c, 0, 0, I, Hh, Hh, Hh, 0, Hh, Hh, Hh, F, F, F, F, nullptr, nullptr, F, F, F, nullptr, 0, nullptr),
            KDA_OK);
-    if (kda_prefill_workspace_bytes(&c, 1, 8192) != (size_t)256 + 96 * 4096 + (size_t)(128 + 1) * 96 * 111616) {
+    // one sequence: the ready words of the records (129 x 96 words, padded to 256 bytes)
+    if (kda_prefill_workspace_bytes(&c, 1, 8192) != (size_t)256 + 49664 + (size_t)(128 + 1) * 96 * 111616) {
         printf("unexpected workspace size %zu\n", kda_prefill_workspace_bytes(&c, 1, 8192));
         ++failures;
     }

@@ -124,10 +124,23 @@ def _ws(cfg, B, N):
 def test_prefill_path_selection_and_workspace_size():
     # fused: no workspace
     assert _ws(_cfg(prefill_path=1), 1, 8192) == 0
-    # chunked: 2(B+1) int32 padded to 256 bytes, for B*H <= 128 in standard precision the
-    # split carry's exchange words (4096 bytes per sequence-head), then floor(N/64) + B
-    # records per head
-    assert _ws(_cfg(prefill_path=2, num_heads=96), 1, 8192) == 256 + 96 * 4096 + (128 + 1) * 96 * REC_BYTES
+    # chunked: 2(B+1) int32 padded to 256 bytes; for one sequence where the carries run in
+    # the chunk workgroups' launch, a ready word per (chunk, head) padded to 256 bytes;
+    # otherwise, for B*H <= 128 in standard precision, the split carry's exchange words
+    # (4096 bytes per sequence-head); then floor(N/64) + B records per head
+    ready = lambda n: (n * 4 + 255) // 256 * 256
+    assert _ws(_cfg(prefill_path=2, num_heads=96), 1, 8192) == 256 + ready(129 * 96) + (128 + 1) * 96 * REC_BYTES
+    try:
+        kda.kda_test_pipeline(1)  # never pipelined: the split carry's layout
+        assert _ws(_cfg(prefill_path=2, num_heads=96), 1, 8192) == 256 + 96 * 4096 + (128 + 1) * 96 * REC_BYTES
+        kda.kda_test_pipeline(2)  # pipelined wherever it can run: one sequence, H <= 128
+        assert _ws(_cfg(prefill_path=2, num_heads=4), 1, 100) == 256 + ready(2 * 4) + (1 + 1) * 4 * REC_BYTES
+        assert _ws(_cfg(prefill_path=2, num_heads=128), 1, 64) == 256 + ready(2 * 128) + 2 * 128 * REC_BYTES
+        assert _ws(_cfg(prefill_path=2, num_heads=129), 1, 64) == 256 + 2 * 129 * REC_BYTES
+        assert _ws(_cfg(prefill_path=2, num_heads=4), 2, 100) == 256 + 8 * 4096 + (1 + 2) * 4 * REC_BYTES
+        assert _ws(_cfg(prefill_path=2, num_heads=4, precision=1), 1, 100) == 256 + (1 + 1) * 4 * 144384
+    finally:
+        kda.kda_test_pipeline(0)
     assert _ws(_cfg(prefill_path=2, num_heads=4), 100, 1000) == 1024 + (15 + 100) * 4 * REC_BYTES
     assert _ws(_cfg(prefill_path=2, num_heads=64), 2, 128) == 256 + 128 * 4096 + (2 + 2) * 64 * REC_BYTES
     assert _ws(_cfg(prefill_path=2, num_heads=43), 3, 128) == 256 + (2 + 3) * 43 * REC_BYTES

@@ -169,6 +169,75 @@ def test_split_carry_wait_times_out(device):
         assert torch.equal(x, y)
 
 
+# one sequence: (heads, length) for the pipelined form (carries in the chunk workgroups'
+# launch): many chunks, a ragged tail, a single partial chunk, the largest H it takes on
+# 256 compute units, one head
+PIPE_CASES = [(32, 8192), (96, 1000), (4, 65), (128, 3000), (1, 321)]
+
+
+@pytest.mark.parametrize("H,T", PIPE_CASES)
+def test_pipelined_carry_agrees_bitwise(device, H, T):
+    """One sequence with the carries running in the chunk workgroups' launch, each reading
+    a record once its ready word is set, gives the bits of the serial carry and of the
+    fused kernel: outputs, final states and windows."""
+    import gated_delta_rule_31_amd as kda
+    case = ki.prefill_case(140 + H, H, [T], True, f"pipe-{H}x{T}")
+    fused = prefill_gpu(case, device, path=PATH_FUSED)
+    try:
+        kda.kda_test_pipeline(1)
+        serial = prefill_gpu(case, device, path=PATH_CHUNKED)
+        kda.kda_test_pipeline(2)
+        piped = prefill_gpu(case, device, path=PATH_CHUNKED)
+    finally:
+        kda.kda_test_pipeline(0)
+    for x, y, z in zip(fused, serial, piped):
+        assert torch.equal(x, y)
+        assert torch.equal(x, z)
+
+
+def test_pipelined_reuses_workspace(device):
+    """Two different batches through the pipelined form in one workspace, back to back and
+    again: each call gives the fused kernel's bits, so no carry reads a record the call
+    before left there."""
+    import gated_delta_rule_31_amd as kda
+    cases = [ki.prefill_case(160 + i, 16, [T], True, f"pipe-ws-{i}") for i, T in enumerate((2000, 1500))]
+    refs = [prefill_gpu(c, device, path=PATH_FUSED) for c in cases]
+    try:
+        kda.kda_test_pipeline(2)
+        cfg = kda.KdaConfig(num_heads=16, prefill_path=PATH_CHUNKED)
+        ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, 1, 2000), dtype=torch.uint8, device=device)
+        for c, ref in [(cases[0], refs[0]), (cases[1], refs[1]), (cases[0], refs[0])]:
+            p = c.params
+            got = kda.kda_prefill(cfg, t(c.cu_seqlens.astype(np.int32), device), *[t(getattr(c.x, n), device) for n in "qkvzbg"],
+                                  t(p.conv_w, device), t(p.A_log, device), t(p.dt_bias, device), t(p.norm_w, device),
+                                  t(c.initial_state, device), t(c.initial_conv_state, device), workspace=ws)
+            torch.cuda.synchronize()
+            for x, y in zip(got, ref):
+                assert torch.equal(x, y)
+    finally:
+        kda.kda_test_pipeline(0)
+
+
+def test_pipelined_wait_times_out(device):
+    """The pipelined carries' wait for a record is bounded: with the ready words never
+    published (kda_test_pipeline) and a 16-poll bound, the call returns with NaN outputs
+    and NaN final states, the windows exact, and the next call is a normal one again."""
+    import gated_delta_rule_31_amd as kda
+    case = ki.prefill_case(170, 4, [300], True, "pipe-timeout")
+    ref = prefill_gpu(case, device, path=PATH_FUSED)
+    try:
+        kda.kda_test_pipeline(2, False, 16)
+        got = prefill_gpu(case, device, path=PATH_CHUNKED)
+        kda.kda_test_pipeline(2)
+        again = prefill_gpu(case, device, path=PATH_CHUNKED)
+    finally:
+        kda.kda_test_pipeline(0)
+    assert torch.isnan(got[0]).all() and torch.isnan(got[1]).all()
+    assert torch.equal(got[2], ref[2])
+    for x, y in zip(again, ref):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_packing_invariance(device, path):
     """Each sequence of a packed batch gives what it gives alone."""

@@ -176,9 +176,9 @@ __device__ __forceinline__ f32x4 load_f32x4_agent(const void *p) {
 // a.ready[row][h] is set, and every read of a record is a device-scope (sc1) load.  The
 // ready word of the record after next is loaded at each chunk's start and checked at the
 // next one, where the opening barrier has waited for it, so a record that is already
-// written costs no wait.  The wait is bounded: a wave that times out sets its columns of
-// the state to NaN (so every later output and its part of the final state are NaN) and
-// stops waiting.
+// written costs no wait.  The wait is bounded (kReadyMaxPolls polls, a few seconds): a wave
+// that times out sets its columns of the state to NaN (so every later output and its part
+// of the final state are NaN) and stops waiting.
 template <bool kBf16, bool kFollow>
 __device__ __forceinline__ void carry_body(const PrefillArgs &a, int seq, int h, unsigned char *__restrict__ lo0,
                                            unsigned char *__restrict__ hi0, unsigned char *__restrict__ lo1,
@@ -277,7 +277,12 @@ __device__ __forceinline__ void carry_body(const PrefillArgs &a, int seq, int h,
                         for (int x = 0; x < 2; ++x) S[P][x] = f32x4{nan, nan, nan, nan};
                     return;
                 }
-                __builtin_amdgcn_s_sleep(4);
+                // short sleeps while the record is likely close, then long ones: the bound
+                // is then several seconds, not one
+                if (n < kReadyShortPolls)
+                    __builtin_amdgcn_s_sleep(4);
+                else
+                    __builtin_amdgcn_s_sleep(127);
             }
         }
     };

@@ -122,10 +122,13 @@ constexpr int64_t kSplitXchgBytes = 2 * 4 * kChunk * 8;
 // kPipeSegChunks chunks: a row of records is complete only when every head's segment is,
 // so long segments would make the carries wait for whole rows (measured on 1 x 8192
 // tokens x 96 heads: 1.14 ms with 4 or 8 chunks, 1.21 ms with 16).  A carry waits for a
-// record at most kReadyMaxPolls polls.
+// record at most kReadyMaxPolls polls: the first kReadyShortPolls about a microsecond
+// apart, the rest about five (so a few seconds in all, which also covers chunk workgroups
+// held off the GPU for a while by other streams' work).
 constexpr double kPipeCarryChunkUs = 6.4;
 constexpr int kPipeSegChunks = 4;
 constexpr int kReadyMaxPolls = 1 << 20;
+constexpr int kReadyShortPolls = 1 << 12;
 constexpr int64_t kPipeMaxUnits = kComputeUnits / 2;
 
 // Bytes of one chunk record (the layout is in kda_device.hpp); multiples of 256.  The

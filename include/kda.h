@@ -141,7 +141,10 @@ typedef struct {
  *                        precision, where the device has at least 2*H compute units
  *                        and an estimate predicts it faster, the
  *                        carries run in the same launch as the chunk workgroups and
- *                        follow the records as they are written (same bits).
+ *                        follow the records as they are written (same bits).  A carry
+ *                        waits for a record a few seconds at most; if other work on
+ *                        the device kept the chunk workgroups from running that long,
+ *                        the outputs and final states of the call would be NaN.
  *   KDA_PREFILL_AUTO     the one an estimate of both times on MI355X predicts faster,
  *                        from B, H and N (the sequences taken as equal in length): CHUNKED
  *                        for a few long sequences (e.g. B*H = 96 or 288 units), FUSED when
@@ -477,7 +480,7 @@ void kda_test_split_carry(int32_t publish, int32_t max_polls);
  * before kda_prefill_workspace_bytes sizes the workspace, so query the size after
  * setting it.  publish = 0 makes the chunk workgroups skip the ready words, so that every
  * carry's wait times out; max_polls > 0 bounds each wait to that many polls (0: the
- * library's bound, about a second).  A wave that times out sets its columns of the state
+ * library's bound, a few seconds).  A wave that times out sets its columns of the state
  * to NaN, so every later output and those columns of the final state are NaN, and does
  * not wait again.  Process-wide, read when a prefill call or a workspace query is made;
  * for tests only.  kda_test_pipeline(0, 1, 0) restores normal operation. */

@@ -53,9 +53,9 @@ namespace {
 constexpr int kThreads = 512;
 
 // ---- LDS map (bytes).  Regions are reused once their first tenant is dead. ----
-constexpr int OFF_R1 = 0;        // sCB fp32 [64][132]          -> sKe hi/lo bf16 [128][64] x2
-constexpr int OFF_R2 = 33792;    // sVt hi/lo bf16 [128][64] x2 -> RMS partial sums fp32 [64][8]
-constexpr int OFF_R3 = 66560;    // sWr bf16 [128][64]          (beta k e^G, transposed)
+constexpr int OFF_R1 = 0;        // sCB fp32 [64][132]          -> sKe hi/lo bf16 64 x 128 x2
+constexpr int OFF_R2 = 33792;    // sVt hi/lo bf16 [64][128] x2 -> RMS partial sums fp32 [64][8]
+constexpr int OFF_R3 = 66560;    // sWr bf16 [64][128]          (beta k e^G)
 constexpr int OFF_R4 = 82944;    // sA fp32 [64][68]            -> sW bf16 [64][128]
 constexpr int OFF_R5 = 100352;   // sPh, sPl bf16 [64][64] (P split hi/lo)
 constexpr int OFF_R6 = 117760;   // sT fp32 [64][68]            -> sQe bf16 [64][128]
@@ -136,6 +136,28 @@ __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2
 __device__ __forceinline__ int wave_sub(int w) { return (w >> 2) ? 3 - (w & 3) : (w & 3); }
 // 4 consecutive bf16 of one row of a swizzled tile (8 bytes, one LDS store)
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// ---- token-major operand tiles, read transposed ----
+// beta v, beta k e^G and K_end^T are kept token-major, [64 tokens][128 channels] bf16 in the
+// sw128 layout, so that a lane holding 8 channels of one token writes them with one 16-byte
+// store.  Their MFMAs take them channel-major (8 consecutive tokens of one channel per
+// lane), which ds_read_b64_tr_b16 (gfx950) gives: within each group of 16 lanes, lane 4k + a
+// supplies the address of channels col(a) .. col(a)+3 of token t0 + k, and lane 4a + b
+// receives channel col(a) + b of tokens t0 .. t0+3 (the lane layout measured on the
+// device).  col_a is this lane's col(lane % 4), a multiple of 4; t0 is uniform over the
+// 16-lane group.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr4(const __bf16 *tile, int t0, int col_a) {
+    const int t = t0 + (((int)threadIdx.x >> 2) & 3);
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(const_cast<__bf16 *>(tile) + sw128(t, col_a)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+// the 8 tokens t0 .. t0+7 of the lane's channel: two transposed reads
+__device__ __forceinline__ bf16x8 lds_tr8(const __bf16 *tile, int t0, int col_a) {
+    const bf16x4 x = lds_tr4(tile, t0, col_a), y = lds_tr4(tile, t0 + 4, col_a);
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // Lane coordinates, re-derived at the start of every phase from an opaque copy of the
 // thread id.  Without this the compiler hoists every lane-dependent LDS address of the
@@ -224,11 +246,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
     constexpr LdsMap M = kPrecise ? kMapPrecise : kMapStd;
     using R = Rec<kPrecise>;
     float *sCB = reinterpret_cast<float *>(smem + M.cb);                // [64][132] k e^{r - G}
-    __bf16 *sKeHi = reinterpret_cast<__bf16 *>(smem + M.ke);            // [128][64] K_end^T
+    __bf16 *sKeHi = reinterpret_cast<__bf16 *>(smem + M.ke);            // K_end (see store_ke)
     __bf16 *sKeLo = sKeHi + 128 * 64;
-    __bf16 *sVtHi = reinterpret_cast<__bf16 *>(smem + M.vt);            // [128][64] (beta v)^T
+    __bf16 *sVtHi = reinterpret_cast<__bf16 *>(smem + M.vt);            // [64][128] beta v, read transposed
     __bf16 *sVtLo = sVtHi + 128 * 64;
-    __bf16 *sWr = reinterpret_cast<__bf16 *>(smem + M.wr);              // [128][64] (beta k e^G)^T
+    __bf16 *sWr = reinterpret_cast<__bf16 *>(smem + M.wr);              // [64][128] beta k e^G, read transposed
     __bf16 *sWrLo = sWr + 128 * 64;                                     // (kPrecise) its lo part
     float *sA = reinterpret_cast<float *>(smem + M.a);                  // [64][68]
     __bf16 *sW = reinterpret_cast<__bf16 *>(smem + M.w);                // [64][128]
@@ -240,6 +262,28 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
     __bf16 *sQeLo = sQe + 64 * 128;                                     // (kPrecise) its lo part
     __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + M.tb);              // [64][64]
     __bf16 *sTbLo = sTb + 64 * 64;                                      // (kPrecise) its lo part
+    // K_end (hi/lo) of token t, channels cb .. cb+15.  The chunked plan keeps it token-major
+    // (16-byte stores; its record copy reads it transposed, once); the fused plan, whose
+    // state update reads it 32 times a chunk, keeps K_end^T channel-major (swi64: 16-byte
+    // operand reads, 2-byte stores).
+    auto store_ke = [&](const float *ke16, int t, int cb) {
+        if constexpr (kChunked) {
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc) {
+                bf16x8 kh, kl;
+                split8(ke16 + 8 * pc, kh, kl);
+                *reinterpret_cast<bf16x8 *>(sKeHi + sw128(t, cb + 8 * pc)) = kh;
+                *reinterpret_cast<bf16x8 *>(sKeLo + sw128(t, cb + 8 * pc)) = kl;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const __bf16 hi = (__bf16)ke16[j];
+                sKeHi[swi64(cb + j, t)] = hi;
+                sKeLo[swi64(cb + j, t)] = bf16_lo(ke16[j], hi);
+            }
+        }
+    };
     // (decay sums in log2 units: G below is the natural-log decay times log2(e))
     float *sTot = reinterpret_cast<float *>(smem + OFF_TAB);  // [4][128] per-sub-chunk gk sums
     float *sPair = sTot + 512 + 640;                           // [6][128] e^{r_I - r_J}, J < I
@@ -382,10 +426,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
                 const int tt = sl < 2 ? sl : (sl + 2) >> 1, tp = sl < 2 ? 0 : (sl & 1);
                 off = M.ph + hl * 64 * 64 * 2 + 2 * sw64(16 * tt + lr, 32 * tp + 8 * lg);  // P hi / lo
             } else if (piece < R::kE) {
-                const int q = piece - R::kK;
-                const int hl = q & 1, tp = (q >> 1) & 1, x = (q >> 2) & 1, P = q >> 3;
-                const int krow = 32 * P + 8 * (lr >> 2) + 4 * x + (lr & 3);
-                off = M.ke + hl * 128 * 64 * 2 + 2 * swi64(krow, 32 * tp + 8 * lg);  // K_end^T hi / lo
+                off = 0;  // K_end^T: read transposed in the copy loop
             } else if (piece == R::kE) {
                 off = OFF_TAB + (512 + 640 + 768 + 512 + 512) * 4 + 16 * min(lane, 31);  // e^{G_end}
             }
@@ -495,18 +536,17 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
                 for (int j = 0; j < 8; ++j) u[j] = y[j] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y[j]));
             };
             const float vscale = beta * -kLn2;  // beta v = vscale u'
-            // v: beta * v, hi/lo, transposed into sVt
+            // v: beta * v, hi/lo, into the token-major sVt
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
-                float u[8];
+                float u[8], bv[8];
                 conv_piece(2, pc, u);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float bv = vscale * u[j];
-                    const __bf16 hi = (__bf16)bv;
-                    sVtHi[sw64(cbase + 8 * pc + j, t)] = hi;
-                    sVtLo[sw64(cbase + 8 * pc + j, t)] = bf16_lo(bv, hi);
-                }
+                for (int j = 0; j < 8; ++j) bv[j] = vscale * u[j];
+                bf16x8 hi, lo;
+                split8(bv, hi, lo);
+                *reinterpret_cast<bf16x8 *>(sVtHi + sw128(t, cbase + 8 * pc)) = hi;
+                *reinterpret_cast<bf16x8 *>(sVtLo + sw128(t, cbase + 8 * pc)) = lo;
             }
             // q, k and their partial sums of squares over this wave's 64 channels
             float ssq = 0.f, ssk = 0.f;
@@ -646,17 +686,22 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
             const int cbase = 64 * half + 16 * lg;
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
-                float qe[8];
+                float qe[8], bw[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int c = cbase + 8 * pc + j;
                     const float er = sExpRef[sub * 128 + c];
-                    const float bw = beta * kr[8 * pc + j] * er;
-                    const __bf16 bwh = (__bf16)bw;
-                    sWr[sw64(c, t)] = bwh;
-                    if constexpr (kPrecise) sWrLo[sw64(c, t)] = bf16_lo(bw, bwh);
+                    bw[j] = beta * kr[8 * pc + j] * er;
                     qe[j] = qr[8 * pc + j] * er;
                     ke[8 * pc + j] = cbk[8 * pc + j] * sEndRef[sub * 128 + c];
+                }
+                if constexpr (kPrecise) {
+                    bf16x8 bh, bl;
+                    split8(bw, bh, bl);
+                    *reinterpret_cast<bf16x8 *>(sWr + sw128(t, cbase + 8 * pc)) = bh;
+                    *reinterpret_cast<bf16x8 *>(sWrLo + sw128(t, cbase + 8 * pc)) = bl;
+                } else {
+                    *reinterpret_cast<bf16x8 *>(sWr + sw128(t, cbase + 8 * pc)) = to_bf8(bw);
                 }
                 if constexpr (kPrecise) {
                     split8(qe, qe8[pc], qel[pc]);
@@ -752,13 +797,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
             // sCB is dead: K_end^T, hi/lo, into region 1 (channel half 1 now, half 0 in
             // phase 4; the precise mode writes both halves after phase 4)
             if (!kPrecise && half == 1) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int c = 64 * half + 16 * lg + j;
-                    const __bf16 hi = (__bf16)ke[j];
-                    sKeHi[swi64(c, t)] = hi;
-                    sKeLo[swi64(c, t)] = bf16_lo(ke[j], hi);
-                }
+                store_ke(ke, t, 64 * half + 16 * lg);
             }
         }
         lds_barrier();
@@ -880,13 +919,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
             KDA_LANE_IDS();
             // K_end^T of channel half 0 (its LDS writes issue beside this phase's MFMAs)
             if (!kPrecise && half == 0) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int c = 16 * lg + j;
-                    const __bf16 hi = (__bf16)ke[j];
-                    sKeHi[swi64(c, t)] = hi;
-                    sKeLo[swi64(c, t)] = bf16_lo(ke[j], hi);
-                }
+                store_ke(ke, t, 16 * lg);
             }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
@@ -895,11 +928,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
                 for (int ks = 0; ks < 2; ++ks) {
                     if (ks == 1 && tt < 2) continue;  // T is lower triangular
                     const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sTb + sw64(16 * tt + lr, 32 * ks + 8 * lg));
-                    const bf16x8 B8 = *reinterpret_cast<const bf16x8 *>(sWr + sw64(16 * w + lr, 32 * ks + 8 * lg));
+                    const bf16x8 B8 = lds_tr8(sWr, 32 * ks + 8 * lg, 16 * w + 4 * (lr & 3));
                     acc = mma(B8, A8, acc);  // W^T tile: keys 16w + 4lg + i of token 16tt + lr
                     if constexpr (kPrecise) {
                         const bf16x8 A8l = *reinterpret_cast<const bf16x8 *>(sTbLo + sw64(16 * tt + lr, 32 * ks + 8 * lg));
-                        const bf16x8 B8l = *reinterpret_cast<const bf16x8 *>(sWrLo + sw64(16 * w + lr, 32 * ks + 8 * lg));
+                        const bf16x8 B8l = lds_tr8(sWrLo, 32 * ks + 8 * lg, 16 * w + 4 * (lr & 3));
                         acc = mma(B8, A8l, acc);
                         acc = mma(B8l, A8, acc);
                     }
@@ -913,7 +946,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
                 *reinterpret_cast<bf16x4 *>(sW + swi128(16 * tt + lr, 16 * w + 4 * lg)) = w4;
                 if constexpr (kPrecise) *reinterpret_cast<bf16x4 *>(sWLo + swi128(16 * tt + lr, 16 * w + 4 * lg)) = w4l;
             }
-            const int vrow = 16 * w + lr;
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
@@ -924,8 +956,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
                     for (int ks = 0; ks < 2; ++ks) {
                         if (ks > tp) continue;
                         const bf16x8 A8 = *reinterpret_cast<const bf16x8 *>(sTb + sw64(trow, 32 * ks + 8 * lg));
-                        const bf16x8 Bh = *reinterpret_cast<const bf16x8 *>(sVtHi + sw64(vrow, 32 * ks + 8 * lg));
-                        const bf16x8 Bl = *reinterpret_cast<const bf16x8 *>(sVtLo + sw64(vrow, 32 * ks + 8 * lg));
+                        const bf16x8 Bh = lds_tr8(sVtHi, 32 * ks + 8 * lg, 16 * w + 4 * (lr & 3));
+                        const bf16x8 Bl = lds_tr8(sVtLo, 32 * ks + 8 * lg, 16 * w + 4 * (lr & 3));
                         acc = mma(A8, Bh, acc);
                         acc = mma(A8, Bl, acc);
                         if constexpr (kPrecise) {
@@ -944,13 +976,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
         if constexpr (kPrecise) {
             // beta v and beta k e^G are dead: K_end^T hi/lo and Q~ hi/lo from registers
             KDA_LANE_IDS();
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int c = 64 * half + 16 * lg + j;
-                const __bf16 hi = (__bf16)ke[j];
-                sKeHi[swi64(c, t)] = hi;
-                sKeLo[swi64(c, t)] = bf16_lo(ke[j], hi);
-            }
+            store_ke(ke, t, 64 * half + 16 * lg);
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 *reinterpret_cast<bf16x8 *>(sQe + sw128(t, 64 * half + 16 * lg + 8 * pc)) = qe8[pc];
@@ -987,8 +1013,17 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
             for (int j = 0; j < kPPW; ++j) {
                 const int piece = 8 * j + w;
                 if (piece >= R::kPieces) break;  // (uniform)
-                const uint32_t off = ((rec_src[j >> 1] >> (16 * (j & 1))) & 0xffffu) << 4;
-                u32x4 v = *reinterpret_cast<const u32x4 *>(smem + off);
+                u32x4 v;
+                if (piece >= R::kK && piece < R::kE) {
+                    // K_end^T hi / lo: key rows 32P + 8(lr/4) + 4x + lr%4, tokens 32tp + 8lg ..
+                    const int q = piece - R::kK;
+                    const int hl = q & 1, tp = (q >> 1) & 1, x = (q >> 2) & 1, P = q >> 3;
+                    v = __builtin_bit_cast(u32x4, lds_tr8(hl ? sKeLo : sKeHi, 32 * tp + 8 * lg,
+                                                          32 * P + 4 * x + 8 * (lr & 3)));
+                } else {
+                    const uint32_t off = ((rec_src[j >> 1] >> (16 * (j & 1))) & 0xffffu) << 4;
+                    v = *reinterpret_cast<const u32x4 *>(smem + off);
+                }
                 if (piece == R::kE && lane >= 32) v = u32x4{0u, 0u, 0u, 0u};
                 if constexpr (kPipe)
                     put(piece * REC_PIECE + lane * 16, v);

@@ -117,15 +117,17 @@ constexpr int64_t kSplitXchgBytes = 2 * 4 * kChunk * 8;
 // the workgroups that start before them cover I - R (r / p) (C - B*H) chunk-heads, the
 // work that C - B*H compute units finish while a carry walks its R chunks.  The plan's
 // time is then that start plus R r.  Beside the chunk workgroups a carry walks a chunk in
-// about 6.4 of the model's microseconds (kPipeCarryChunkUs; 5.9 us measured on MI355X,
-// where it takes 4.9 alone).  The chunk workgroups of this plan take segments of
+// about 5.0-5.9 us on MI355X (4.9 alone); kPipeCarryChunkUs = 5.9 model microseconds (the
+// model's chunk-head takes 17.0 for about 15.7 measured) puts the start where a sweep of
+// it was fastest on 1 x 8192 x 96: a carry that starts early only waits, one that starts
+// late lengthens the call.  The chunk workgroups of this plan take segments of
 // kPipeSegChunks chunks: a row of records is complete only when every head's segment is,
 // so long segments would make the carries wait for whole rows (measured on 1 x 8192
 // tokens x 96 heads: 1.14 ms with 4 or 8 chunks, 1.21 ms with 16).  A carry waits for a
 // record at most kReadyMaxPolls polls: the first kReadyShortPolls about a microsecond
 // apart, the rest about five (so a few seconds in all, which also covers chunk workgroups
 // held off the GPU for a while by other streams' work).
-constexpr double kPipeCarryChunkUs = 6.4;
+constexpr double kPipeCarryChunkUs = 5.9;
 constexpr int kPipeSegChunks = 4;
 constexpr int kReadyMaxPolls = 1 << 20;
 constexpr int kReadyShortPolls = 1 << 12;

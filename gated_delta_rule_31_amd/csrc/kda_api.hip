@@ -94,8 +94,9 @@ struct PrefillPlan {
     int64_t nchunk_cap, nseg_cap;
     int seg_chunks;
     bool carry_split;  // chunked: the two-workgroup carry (standard precision, B*H <= 128)
-    bool pipe;         // chunked: the carries in the chunk kernel's launch (one sequence)
+    bool pipe;         // chunked: the carries in the chunk kernel's launch
     size_t ready_off;  // pipe: byte offset of the ready words in the workspace
+    size_t items_off;  // pipe with B > 1: byte offset of the row-major segment order
     size_t table_bytes, workspace_bytes;
 };
 
@@ -139,7 +140,7 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     // for the carries; taken where its model beats the serial one (mode 0)
     const int32_t mode = pipe_mode.load();
     const int64_t pipe_segs = kda::seg_cap(B, cap, kda::kPipeSegChunks);
-    bool pipe = mode != 1 && B == 1 && !precise && B * H <= kda::kPipeMaxUnits && N > 0 &&
+    bool pipe = mode != 1 && B >= 1 && !precise && B * H <= kda::kPipeMaxUnits && N > 0 &&
                 chunked_fits && pipe_segs * H + B * H <= kda::kMaxPrefillUnits;
     if (pipe && mode == 0)
         pipe = pipe_model((double)cap * (double)H, chunks, kda::kComputeUnits, (double)(B * H)).us < serial_us;
@@ -148,7 +149,9 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     // records' ready words (pipelined)
     const size_t base_bytes = (size_t)((8 * (B + 1) + 255) / 256 * 256);
     const size_t ready_bytes = pipe ? (size_t)((cap * H * 4 + 255) / 256 * 256) : 0;
-    const size_t table_bytes = base_bytes + (split ? (size_t)(B * H * kda::kSplitXchgBytes) : 0) + ready_bytes;
+    const size_t items_bytes = pipe && B > 1 ? (size_t)((pipe_segs * 4 + 255) / 256 * 256) : 0;
+    const size_t table_bytes =
+        base_bytes + (split ? (size_t)(B * H * kda::kSplitXchgBytes) : 0) + ready_bytes + items_bytes;
     const size_t chunked_bytes = table_bytes + (size_t)cap * (size_t)H * (size_t)kda::rec_bytes(precise);
     int path = cfg->prefill_path;
     if (path == kda::kPathAuto) {
@@ -170,6 +173,7 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     plan->carry_split = path == kda::kPathChunked && split;
     plan->pipe = path == kda::kPathChunked && pipe;
     plan->ready_off = base_bytes;
+    plan->items_off = base_bytes + ready_bytes;
     plan->table_bytes = table_bytes;
     plan->workspace_bytes = path == kda::kPathFused ? 0 : chunked_bytes;
     return true;
@@ -466,11 +470,16 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
     const int64_t pairs = (int64_t)num_seqs * cfg->num_heads;
     const bool pipe = plan.pipe && 2 * pairs <= cus;
     a.ready = pipe ? reinterpret_cast<unsigned *>(static_cast<unsigned char *>(workspace) + plan.ready_off) : nullptr;
+    a.item_sg = pipe && num_seqs > 1
+                    ? reinterpret_cast<int32_t *>(static_cast<unsigned char *>(workspace) + plan.items_off)
+                    : nullptr;
     a.pipe_units = pipe ? (int)pairs : 0;
     a.pipe_first = 0;
     if (pipe) {
-        const double chunks = (double)((total_tokens + kda::kChunk - 1) / kda::kChunk);
-        const double lead = pipe_model(chunks * cfg->num_heads, chunks, cus, (double)pairs).lead_chunk_heads;
+        // (the sequences taken as equal in length, as in the plan)
+        const double chunks = (double)((total_tokens + kda::kChunk * num_seqs - 1) / (kda::kChunk * num_seqs));
+        const double lead =
+            pipe_model((double)plan.nchunk_cap * cfg->num_heads, chunks, cus, (double)pairs).lead_chunk_heads;
         a.pipe_first = (int)std::min((double)plan.nseg_cap * cfg->num_heads, std::floor(lead / plan.seg_chunks));
     }
     a.ready_publish = pipe_publish.load();

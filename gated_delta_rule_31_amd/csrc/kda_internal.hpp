@@ -109,9 +109,9 @@ constexpr int64_t kSplitXchgBytes = 2 * 4 * kChunk * 8;
 
 // The pipelined chunked plan (kda_prefill.hip) puts the B*H one-workgroup carries into
 // the chunk kernel's grid after its first pipe_first workgroups, so that they start once
-// those finish and then follow the records as the rest are written.  It is used for one
-// sequence with B*H <= (compute units) / 2, so that the chunk workgroups keep at least half
-// the compute units.  The carries should start late enough never to wait: with p the time
+// those finish and then follow the records as the rest are written.  It is used for
+// B*H <= (compute units) / 2, so that the chunk workgroups keep at least half the compute
+// units; with several sequences the chunk workgroups take the segments row by row.  The carries should start late enough never to wait: with p the time
 // of a chunk-head on one compute unit (kRecordUs), r a carry's time per chunk
 // (kPipeCarryChunkUs), I chunk-heads, R chunks per sequence, C compute units and B*H carries,
 // the workgroups that start before them cover I - R (r / p) (C - B*H) chunk-heads, the
@@ -193,6 +193,7 @@ struct PrefillArgs {
     // record once its word in `ready` ([nchunk_cap][H], zeroed by the chunk table kernel)
     // is set; null and 0 otherwise
     unsigned *ready;
+    int32_t *item_sg;  // pipelined, B > 1: [nseg_cap] segments in row-major order; null otherwise
     int pipe_first, pipe_units;
     int ready_publish;    // 1; 0 only under kda_test_pipeline (every wait then times out)
     int ready_max_polls;  // polls per wait, 0 = the kernel's bound

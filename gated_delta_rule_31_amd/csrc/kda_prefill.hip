@@ -301,9 +301,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
     // rec0: record row of the sequence's first chunk (chunked plan)
     int seq, h, cbeg, nrec = 0, rec0 = 0;
     if constexpr (kChunked) {
-        const int sg = bid / H;
+        int sg = bid / H;
         h = bid - sg * H;
         if (sg >= a.seg_start[a.B]) return;  // past the batch's last segment (uniform)
+        if constexpr (kPipe)
+            if (a.item_sg) sg = a.item_sg[sg];  // several sequences: row-major order
         // the sequence owning segment sg: seg_start[lo] <= sg < seg_start[hi]
         int lo = 0, hi = a.B;
         while (hi - lo > 1) {
@@ -1261,6 +1263,7 @@ __device__ long long block_scan(long long *part, long long v) {
 
 __global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs a) {
     __shared__ long long part[kTableThreads];
+    __shared__ int seq_first[kTableThreads], seq_nseg[kTableThreads];  // (item table: B <= kTableThreads)
     const int tid = threadIdx.x;
     // the split carry's exchange words start at zero (no tag matches a chunk)
     if (a.xchg) {
@@ -1294,6 +1297,10 @@ __global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs 
         if (s < a.B) {
             a.chunk_start[s] = (int)lo;
             a.seg_start[s] = (int)(carry_s + incl_s - nseg);
+            if (base == 0) {
+                seq_first[s] = (int)(carry_s + incl_s - nseg);
+                seq_nseg[s] = (int)nseg;
+            }
         }
         carry_c += tile;
         carry_s += tile_s;
@@ -1302,6 +1309,29 @@ __global__ __launch_bounds__(kTableThreads) void chunk_table_kernel(PrefillArgs 
     if (tid == 0) {
         a.chunk_start[a.B] = (int)min(carry_c, cap);
         a.seg_start[a.B] = (int)carry_s;
+    }
+    // The pipelined plan over several sequences takes the segments row by row: row j of
+    // every sequence (in sequence order) before row j + 1, so that the sequences' records,
+    // which their carries read in order, advance together.  item_sg[i] is the segment of
+    // row-major position i: segment j of sequence s sits after the sum over sequences t of
+    // min(n_t, j) segments of the rows before and after the sequences t < s with n_t > j.
+    if (a.item_sg && a.B <= kTableThreads) {
+        __syncthreads();
+        const int total = (int)carry_s;
+        for (int sg = tid; sg < total; sg += kTableThreads) {
+            int lo = 0, hi = a.B;  // the sequence owning sg: the last with seq_first <= sg
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (seq_first[mid] <= sg) lo = mid; else hi = mid;
+            }
+            const int j = sg - seq_first[lo];
+            int idx = 0;
+            for (int t = 0; t < a.B; ++t) {
+                const int n = seq_nseg[t];
+                idx += min(n, j) + ((t < lo && n > j) ? 1 : 0);
+            }
+            a.item_sg[idx] = sg;
+        }
     }
 }
 

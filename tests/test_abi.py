@@ -137,12 +137,17 @@ def test_prefill_path_selection_and_workspace_size():
         assert _ws(_cfg(prefill_path=2, num_heads=4), 1, 100) == 256 + ready(2 * 4) + (1 + 1) * 4 * REC_BYTES
         assert _ws(_cfg(prefill_path=2, num_heads=128), 1, 64) == 256 + ready(2 * 128) + 2 * 128 * REC_BYTES
         assert _ws(_cfg(prefill_path=2, num_heads=129), 1, 64) == 256 + 2 * 129 * REC_BYTES
-        assert _ws(_cfg(prefill_path=2, num_heads=4), 2, 100) == 256 + 8 * 4096 + (1 + 2) * 4 * REC_BYTES
+        assert _ws(_cfg(prefill_path=2, num_heads=4), 2, 100) == 256 + 256 + 256 + (1 + 2) * 4 * REC_BYTES
+        # three sequences of 300 tokens: 7 record rows; 32 heads: ready words, the order of the
+        # 4 segments (4-chunk segments); 64 heads: B*H = 192 takes neither that form nor the split
+        assert _ws(_cfg(prefill_path=2, num_heads=32), 3, 300) == 256 + 1024 + 256 + 7 * 32 * REC_BYTES
+        assert _ws(_cfg(prefill_path=2, num_heads=64), 3, 300) == 256 + 7 * 64 * REC_BYTES
         assert _ws(_cfg(prefill_path=2, num_heads=4, precision=1), 1, 100) == 256 + (1 + 1) * 4 * 144384
     finally:
         kda.kda_test_pipeline(0)
     assert _ws(_cfg(prefill_path=2, num_heads=4), 100, 1000) == 1024 + (15 + 100) * 4 * REC_BYTES
-    assert _ws(_cfg(prefill_path=2, num_heads=64), 2, 128) == 256 + 128 * 4096 + (2 + 2) * 64 * REC_BYTES
+    # (two sequences of 64 heads: the pipelined plan, with the segments' row-major order)
+    assert _ws(_cfg(prefill_path=2, num_heads=64), 2, 128) == 256 + 1024 + 256 + (2 + 2) * 64 * REC_BYTES
     assert _ws(_cfg(prefill_path=2, num_heads=43), 3, 128) == 256 + (2 + 3) * 43 * REC_BYTES
     assert _ws(_cfg(prefill_path=2, num_heads=96, precision=1), 1, 8192) == 256 + (128 + 1) * 96 * 144384
     # auto: the layout the time estimate prefers; these are the measured winners on MI355X

@@ -195,6 +195,29 @@ def test_pipelined_carry_agrees_bitwise(device, H, T):
         assert torch.equal(x, z)
 
 
+# several sequences (B*H <= 128): the chunk workgroups take the segments row by row
+PIPE_VARLEN = [(16, [700, 0, 1, 2000, 65]), (32, [1500, 1500, 1500]), (64, [3000, 100])]
+
+
+@pytest.mark.parametrize("H,lengths", PIPE_VARLEN)
+def test_pipelined_varlen_agrees_bitwise(device, H, lengths):
+    """Several sequences through the pipelined form (empty, 1-token and ragged ones among
+    them) give the bits of the serial carry and of the fused kernel."""
+    import gated_delta_rule_31_amd as kda
+    case = ki.prefill_case(180 + H, H, lengths, True, f"pipe-varlen-{H}")
+    fused = prefill_gpu(case, device, path=PATH_FUSED)
+    try:
+        kda.kda_test_pipeline(1)
+        serial = prefill_gpu(case, device, path=PATH_CHUNKED)
+        kda.kda_test_pipeline(2)
+        piped = prefill_gpu(case, device, path=PATH_CHUNKED)
+    finally:
+        kda.kda_test_pipeline(0)
+    for x, y, z in zip(fused, serial, piped):
+        assert torch.equal(x, y)
+        assert torch.equal(x, z)
+
+
 def test_pipelined_reuses_workspace(device):
     """Two different batches through the pipelined form in one workspace, back to back and
     again: each call gives the fused kernel's bits, so no carry reads a record the call

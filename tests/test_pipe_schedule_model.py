@@ -112,3 +112,21 @@ def test_carries_on_every_compute_unit_can_stall():
     rng = random.Random(7)
     cus = XCDS * 2
     assert not _simulate(cus, cus, 4, 2, 0, cus, rng)
+
+
+def _row_major_index(nseg, s, j):
+    """The position the chunk table kernel gives segment j of sequence s (nseg: segments per
+    sequence): the rows before it, then the sequences before s that reach row j."""
+    return sum(min(n, j) for n in nseg) + sum(1 for t in range(s) if nseg[t] > j)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_row_major_segment_order(seed):
+    # the kernel's formula is a bijection onto the segments in row-major order: row j of
+    # every sequence (in sequence order) before row j + 1, empty sequences skipped
+    rng = random.Random(seed)
+    nseg = [rng.choice([0, 0, 1, 2, 3, 5, 8]) for _ in range(rng.randint(1, 12))]
+    expect = [(s, j) for j in range(max(nseg)) for s in range(len(nseg)) if j < nseg[s]]
+    got = sorted(((_row_major_index(nseg, s, j), (s, j)) for s in range(len(nseg)) for j in range(nseg[s])))
+    assert [i for i, _ in got] == list(range(len(expect)))
+    assert [sj for _, sj in got] == expect

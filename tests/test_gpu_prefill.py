@@ -141,10 +141,15 @@ def test_carry_forms_agree_bitwise(device, B, H, lengths):
     larger batches with one workgroup per pair; either form gives the fused kernel's bits.
     The first case sits at the limit of the split form (2 x 64 pairs, two-chunk sequences:
     the exchange's first chunks and last two epilogues), the second one pair past it."""
+    import gated_delta_rule_31_amd as kda
     case = ki.prefill_case(128 + B, H, lengths, True, f"carry-forms-{B}x{H}")
     assert case.B * case.H == (128 if B == 2 else 129)
     a = prefill_gpu(case, device, path=PATH_FUSED)
-    b = prefill_gpu(case, device, path=PATH_CHUNKED)
+    try:
+        kda.kda_test_pipeline(1)  # the serial carries (not the pipelined form)
+        b = prefill_gpu(case, device, path=PATH_CHUNKED)
+    finally:
+        kda.kda_test_pipeline(0)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
@@ -156,15 +161,18 @@ def test_split_carry_wait_times_out(device):
     is a normal one again."""
     import gated_delta_rule_31_amd as kda
     case = ki.prefill_case(130, 4, [200, 70], True, "split-timeout")
-    ref = prefill_gpu(case, device, path=PATH_CHUNKED)
     try:
+        kda.kda_test_pipeline(1)  # the split carry (not the pipelined form)
+        ref = prefill_gpu(case, device, path=PATH_CHUNKED)
         kda.kda_test_split_carry(False, 16)
         got = prefill_gpu(case, device, path=PATH_CHUNKED)
+        kda.kda_test_split_carry(True, 0)
+        again = prefill_gpu(case, device, path=PATH_CHUNKED)
     finally:
         kda.kda_test_split_carry(True, 0)
+        kda.kda_test_pipeline(0)
     assert torch.isnan(got[0]).all()
     assert torch.equal(got[1], ref[1]) and torch.equal(got[2], ref[2])
-    again = prefill_gpu(case, device, path=PATH_CHUNKED)
     for x, y in zip(again, ref):
         assert torch.equal(x, y)
 

@@ -136,8 +136,8 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     const double records_us = (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits;
     const double serial_us =
         records_us + (split_ok ? chunks * kda::kSplitCarryChunkUs : rounds * chunks * kda::kCarryChunkUs);
-    // the pipelined plan: one sequence, standard precision, at most half the compute units
-    // for the carries; taken where its model beats the serial one (mode 0)
+    // the pipelined plan: standard precision, B*H <= 128 (at most half the compute units
+    // for the carries); taken where its model beats the serial one (mode 0)
     const int32_t mode = pipe_mode.load();
     const int64_t pipe_segs = kda::seg_cap(B, cap, kda::kPipeSegChunks);
     bool pipe = mode != 1 && B >= 1 && !precise && B * H <= kda::kPipeMaxUnits && N > 0 &&

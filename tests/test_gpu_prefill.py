@@ -226,6 +226,28 @@ def test_pipelined_varlen_agrees_bitwise(device, H, lengths):
         assert torch.equal(x, z)
 
 
+@pytest.mark.parametrize("seed", [302, 307, 309, 317, 318, 321])
+def test_pipelined_random_batches_agree_bitwise(device, seed):
+    """Random batches through the pipelined form (1 to 6 sequences of 0 to 3000 tokens,
+    B*H <= 128) give the fused kernel's bits."""
+    import gated_delta_rule_31_amd as kda
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 7))
+    H = int(rng.integers(1, 128 // B + 1))
+    lengths = [int(x) for x in rng.choice([0, 1, 2, 63, 64, 65, 300, 1000, 3000], size=B)]
+    if sum(lengths) == 0:
+        lengths[0] = 129
+    case = ki.prefill_case(seed, H, lengths, True, f"pipe-random-{seed}")
+    fused = prefill_gpu(case, device, path=PATH_FUSED)
+    try:
+        kda.kda_test_pipeline(2)
+        piped = prefill_gpu(case, device, path=PATH_CHUNKED)
+    finally:
+        kda.kda_test_pipeline(0)
+    for x, y in zip(fused, piped):
+        assert torch.equal(x, y)
+
+
 def test_pipelined_reuses_workspace(device):
     """Two different batches through the pipelined form in one workspace, back to back and
     again: each call gives the fused kernel's bits, so no carry reads a record the call

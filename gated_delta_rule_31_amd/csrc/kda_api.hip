@@ -108,16 +108,21 @@ std::atomic<int32_t> pipe_max_polls{0};
 
 // The time model of the pipelined plan (kda_internal.hpp): its time and the number of
 // chunk-heads whose workgroups start before the carries, for I chunk-heads, R chunks per
-// sequence, C compute units and NC carries.
+// sequence, C compute units and NC carries, in the standard or high-precision mode.
 struct PipeModel {
     double us, lead_chunk_heads;
 };
-PipeModel pipe_model(double I, double R, double C, double NC) {
-    const double ratio = kda::kPipeCarryChunkUs / kda::kRecordUs;
-    const double lead = std::max(0.0, I - R * ratio * (C - NC));
-    const double start = lead * kda::kRecordUs / C;
-    const double rest = (I - lead) * kda::kRecordUs / (C - NC);  // chunk-heads after the carries start
-    return {start + std::max(R * kda::kPipeCarryChunkUs, rest), lead};
+PipeModel pipe_model(double I, double R, double C, double NC, bool precise) {
+    const double p = precise ? kda::kRecordUsPrecise : kda::kRecordUs;
+    const double r = precise ? kda::kPipeCarryChunkUsPrecise : kda::kPipeCarryChunkUs;
+    const double r_alone = precise ? kda::kCarryChunkUsPrecise : kda::kCarryChunkUs;
+    const double lead = std::max(0.0, I - R * (r / p) * (C - NC));
+    const double start = lead * p / C;
+    const double rest = (I - lead) * p / (C - NC);  // chunk-heads after the carries start
+    // (with lead > 0, R r = rest; with lead = 0 the carries walk rest / r chunks beside the
+    // chunk workgroups and the others alone)
+    const double carry = R * r <= rest ? rest : rest + (R - rest / r) * r_alone;
+    return {start + carry, lead};
 }
 // max_workspace >= 0: the workspace is a fixed array of that many bytes; the automatic
 // choice then takes the chunked layout only if its workspace fits (else fused, which
@@ -133,17 +138,20 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     const bool split_ok = !precise && B * H <= kda::kSplitCarryMaxUnits;
     const double rounds = (double)((B * H + kda::kComputeUnits - 1) / kda::kComputeUnits);
     const double chunks = B > 0 ? (double)((N + 64 * B - 1) / (64 * B)) : 0.0;  // mean length, rounded up
-    const double records_us = (double)cap * (double)H * kda::kRecordUs / kda::kComputeUnits;
+    const double records_us =
+        (double)cap * (double)H * (precise ? kda::kRecordUsPrecise : kda::kRecordUs) / kda::kComputeUnits;
     const double serial_us =
-        records_us + (split_ok ? chunks * kda::kSplitCarryChunkUs : rounds * chunks * kda::kCarryChunkUs);
-    // the pipelined plan: standard precision, B*H <= 128 (at most half the compute units
-    // for the carries); taken where its model beats the serial one (mode 0)
+        records_us + (split_ok ? chunks * kda::kSplitCarryChunkUs
+                               : rounds * chunks * (precise ? kda::kCarryChunkUsPrecise : kda::kCarryChunkUs));
+    // the pipelined plan: B*H <= 128 (at most half the compute units for the carries);
+    // taken where its model beats the serial one (mode 0)
     const int32_t mode = pipe_mode.load();
     const int64_t pipe_segs = kda::seg_cap(B, cap, kda::kPipeSegChunks);
-    bool pipe = mode != 1 && B >= 1 && !precise && B * H <= kda::kPipeMaxUnits && N > 0 &&
-                chunked_fits && pipe_segs * H + B * H <= kda::kMaxPrefillUnits;
+    bool pipe = mode != 1 && B >= 1 && B * H <= kda::kPipeMaxUnits && N > 0 && chunked_fits &&
+                pipe_segs * H + B * H <= kda::kMaxPrefillUnits;
     if (pipe && mode == 0)
-        pipe = pipe_model((double)cap * (double)H, chunks, kda::kComputeUnits, (double)(B * H)).us < serial_us;
+        pipe = pipe_model((double)cap * (double)H, chunks, kda::kComputeUnits, (double)(B * H), precise).us <
+               serial_us;
     const bool split = split_ok && !pipe;
     // chunk_start and seg_start, then the RMS-sum exchange words (split carry) or the
     // records' ready words (pipelined)
@@ -157,9 +165,10 @@ bool plan_prefill(const kda_config *cfg, int64_t B, int64_t N, PrefillPlan *plan
     if (path == kda::kPathAuto) {
         path = kda::kPathFused;
         if (chunked_fits && B > 0) {
-            const double fused = rounds * chunks * kda::kFusedChunkUs;
+            const double fused = rounds * chunks * (precise ? kda::kFusedChunkUsPrecise : kda::kFusedChunkUs);
             const double chunked =
-                pipe ? pipe_model((double)cap * (double)H, chunks, kda::kComputeUnits, (double)(B * H)).us : serial_us;
+                pipe ? pipe_model((double)cap * (double)H, chunks, kda::kComputeUnits, (double)(B * H), precise).us
+                     : serial_us;
             if (chunked < fused && (max_workspace < 0 || chunked_bytes <= (size_t)max_workspace))
                 path = kda::kPathChunked;
         }
@@ -479,7 +488,8 @@ kda_status prefill_impl(const kda_config *cfg, int32_t num_seqs, int32_t total_t
         // (the sequences taken as equal in length, as in the plan)
         const double chunks = (double)((total_tokens + kda::kChunk * num_seqs - 1) / (kda::kChunk * num_seqs));
         const double lead =
-            pipe_model((double)plan.nchunk_cap * cfg->num_heads, chunks, cus, (double)pairs).lead_chunk_heads;
+            pipe_model((double)plan.nchunk_cap * cfg->num_heads, chunks, cus, (double)pairs, cfg->precision == KDA_PRECISION_HIGH)
+                .lead_chunk_heads;
         a.pipe_first = (int)std::min((double)plan.nseg_cap * cfg->num_heads, std::floor(lead / plan.seg_chunks));
     }
     a.ready_publish = pipe_publish.load();

@@ -450,163 +450,12 @@ __global__ __launch_bounds__(kSplitThreads, 1) void carry_split_kernel(PrefillAr
     carry_finish(a, S, seq, h, t0, t1, 4 * hf, kSplitThreads, 192 * hf, 192 * hf + 192);
 }
 
-// The high-precision carry (records of the precise chunk kernel): the same products with
-// every operand split into bf16 hi + lo, W S0 and Q~ S0 included.  Its 109-piece record does
-// not fit twice in the LDS, so one buffer holds the current chunk's pieces and the next
-// chunk's are requested once every wave is done with them; their latency overlaps the
-// chunk's epilogue only.
+// kBf16: the output buffer holds bf16 (round to nearest even), else fp32
 template <bool kBf16>
 __global__ __launch_bounds__(kCarryThreads, 1) void carry_kernel_precise(PrefillArgs a) {
     const int H = a.c.H;
-    const int N = a.N;
-    const int h = blockIdx.x % H;
-    const int seq = seq_longest_first(a.cu_seqlens, a.B, N, blockIdx.x / H, carry_order);
-    const size_t HD = (size_t)H * kD;
-    int t0 = a.cu_seqlens[seq];
-    int t1 = a.cu_seqlens[seq + 1];
-    t0 = min(max(t0, 0), N);
-    t1 = min(max(t1, t0), N);
-    const int T = t1 - t0;
-    const int r0 = a.chunk_start[seq];
-    const int nrec = a.chunk_start[seq + 1] - r0;  // ceil(T / 64) for a valid batch
-    const size_t rec_stride = (size_t)H * RecP::kBytes;
-    const unsigned char *rec0 = a.records + ((size_t)r0 * H + h) * RecP::kBytes;
-
-    const int tid = (int)threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int lr = tid & 15;
-    const int lg = (tid >> 4) & 3;
-
-    f32x4 S[4][2];  // S[P][x][i] = S[key 32P + 8lg + 4x + i][value 16w + lr]
-    {
-        const float *S0 = a.initial_state ? a.initial_state + ((size_t)seq * H + h) * kD * kD : nullptr;
-#pragma unroll
-        for (int P = 0; P < 4; ++P)
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = 32 * P + 8 * lg + 4 * x + i;
-                    S[P][x][i] = S0 ? S0[key * kD + 16 * w + lr] : 0.0f;
-                }
-    }
-    float nw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nw[i] = a.norm_w[16 * w + 4 * lg + i];
-
-    auto request = [&](int c, f32x4 (&Un)[2][2]) {
-        const unsigned char *rec = rec0 + (size_t)c * rec_stride;
-#pragma unroll
-        for (int j = 0; j < kPiecesPerWaveP; ++j) {
-            const int piece = min(8 * j + w, RecP::kPieces - 1);
-            __builtin_amdgcn_global_load_lds(rec + piece * REC_PIECE + lane * 16,
-                                             (lds_void *)((__attribute__((address_space(3))) unsigned char *)carry_pbuf +
-                                                          piece * REC_PIECE),
-                                             16, 0, 0);
-        }
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-                Un[tp][x] = *reinterpret_cast<const f32x4 *>(rec + RecP::kU + (((w * 2 + tp) * 2 + x) * 64 + lane) * 16);
-    };
-    auto opnd = [&](int piece) {
-        return *reinterpret_cast<const bf16x8 *>(carry_pbuf + piece * REC_PIECE + lane * 16);
-    };
-
-    f32x4 Unext[2][2] = {};
-    if (nrec > 0) request(0, Unext);
-    for (int c = 0; c < nrec; ++c) {
-        const int c0 = c * kChunk;
-        const int L = min(kChunk, T - c0);
-        barrier_all_mem();  // chunk c's pieces are in the buffer; the last epilogue is done
-        f32x4 U[2][2];
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-            for (int x = 0; x < 2; ++x) U[tp][x] = Unext[tp][x];
-        uint2 g4[4];
-        load_gate4(g4, a.g, HD, h, t0 + c0, L, w, lr, lg);
-
-        bf16x8 Sh[4], Sl[4];
-#pragma unroll
-        for (int P = 0; P < 4; ++P) {
-            const float v8[8] = {S[P][0][0], S[P][0][1], S[P][0][2], S[P][0][3],
-                                 S[P][1][0], S[P][1][1], S[P][1][2], S[P][1][3]};
-            split8(v8, Sh[P], Sl[P]);
-        }
-        // U = U' - W S0
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                f32x4 ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int P = 0; P < 4; ++P) {
-                    const bf16x8 Wh = opnd(RecP::w(tp, x, P, 0));
-                    const bf16x8 Wl = opnd(RecP::w(tp, x, P, 1));
-                    ws = mma(Wh, Sh[P], ws);
-                    ws = mma(Wh, Sl[P], ws);
-                    ws = mma(Wl, Sh[P], ws);
-                }
-                U[tp][x] -= ws;
-            }
-        bf16x8 Uh[2], Ul[2];
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-            const float v8[8] = {U[tp][0][0], U[tp][0][1], U[tp][0][2], U[tp][0][3],
-                                 U[tp][1][0], U[tp][1][1], U[tp][1][2], U[tp][1][3]};
-            split8(v8, Uh[tp], Ul[tp]);
-        }
-        // O^T = S0^T Q~^T + U^T P^T
-        f32x4 o[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int P = 0; P < 4; ++P) {
-                const bf16x8 Qh = opnd(RecP::q(tt, P, 0));
-                const bf16x8 Ql = opnd(RecP::q(tt, P, 1));
-                acc = mma(Sh[P], Qh, acc);
-                acc = mma(Sh[P], Ql, acc);
-                acc = mma(Sl[P], Qh, acc);
-            }
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                if (tp > (tt >> 1)) continue;  // P is lower triangular
-                const bf16x8 Ph = opnd(RecP::p(tt, tp, 0));
-                const bf16x8 Pl = opnd(RecP::p(tt, tp, 1));
-                acc = mma(Uh[tp], Ph, acc);
-                acc = mma(Uh[tp], Pl, acc);
-                acc = mma(Ul[tp], Ph, acc);
-            }
-            o[tt] = acc;
-        }
-        rms_partials(o, carry_ppart, w, lr, lg);
-        // S = Diag(e^{G_end}) S0 + K_end^T U
-        const float *sE = reinterpret_cast<const float *>(carry_pbuf + RecP::kE * REC_PIECE);
-#pragma unroll
-        for (int P = 0; P < 4; ++P)
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                f32x4 acc = S[P][x] * *reinterpret_cast<const f32x4 *>(sE + 32 * P + 8 * lg + 4 * x);
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    const bf16x8 Kh = opnd(RecP::k(P, x, tp, 0));
-                    const bf16x8 Kl = opnd(RecP::k(P, x, tp, 1));
-                    acc = mma(Kh, Uh[tp], acc);
-                    acc = mma(Kl, Uh[tp], acc);
-                    acc = mma(Kh, Ul[tp], acc);
-                }
-                S[P][x] = acc;
-            }
-        lds_barrier();  // every wave is done with the buffer and has published its sums
-        if (c + 1 < nrec) request(c + 1, Unext);
-        gated_rms_store<kBf16, false>(o, g4, carry_ppart, nw, a.c.rms_eps, a.out, HD, h, t0 + c0, L, 0, w, lr, lg);
-    }
-    barrier_all_mem();  // the last epilogue's reads of the sums are done before the LDS is released
-    carry_finish(a, S, seq, h, t0, t1);
+    const int seq = seq_longest_first(a.cu_seqlens, a.B, a.N, blockIdx.x / H, carry_order);
+    carry_body_precise<kBf16, false>(a, seq, blockIdx.x % H, carry_pbuf, carry_ppart);
 }
 
 }  // namespace

@@ -99,6 +99,11 @@ constexpr int kComputeUnits = 256;
 constexpr double kFusedChunkUs = 17.6;
 constexpr double kRecordUs = 17.0;
 constexpr double kCarryChunkUs = 5.9;
+// the same three costs in the high-precision mode (every operand split into hi + lo;
+// measured on 1 x 8192 tokens x 96 heads: fused 2.43 ms, chunk kernel 805 us, carry 1019 us)
+constexpr double kFusedChunkUsPrecise = 19.0;
+constexpr double kRecordUsPrecise = 18.0;
+constexpr double kCarryChunkUsPrecise = 8.0;
 // The split carry (kda_carry.hip) runs two 4-wave workgroups per (sequence, head), each on
 // its own compute unit and resident together, so it is used for B*H <= 128; its rounds
 // term is then 1 and its per-chunk cost kSplitCarryChunkUs.
@@ -128,6 +133,11 @@ constexpr int64_t kSplitXchgBytes = 2 * 4 * kChunk * 8;
 // apart, the rest about five (so a few seconds in all, which also covers chunk workgroups
 // held off the GPU for a while by other streams' work).
 constexpr double kPipeCarryChunkUs = 5.9;
+// The high-precision carry walks a chunk in about 11 us beside the chunk workgroups and 8
+// alone, slower than the records arrive: its start point comes out at the grid's start
+// (on 1 x 8192 x 96, a start after 0, 250 and 1,000 chunk workgroups took 1.44, 1.48 and
+// 1.57 ms), and after the last record it walks at kCarryChunkUsPrecise.
+constexpr double kPipeCarryChunkUsPrecise = 11.0;
 constexpr int kPipeSegChunks = 4;
 constexpr int kReadyMaxPolls = 1 << 20;
 constexpr int kReadyShortPolls = 1 << 12;

@@ -235,13 +235,13 @@ __device__ __forceinline__ void load_chunk(ChunkLoads &r, const PrefillArgs &a, 
 // kGateProj: the decay logits are z = W_fb f (a.f, a.w_fb) instead of a.z: each chunk
 // stages the head's 128 rows of W_fb in LDS and phase 1 forms its 64 x 128 logits with
 // MFMAs, laid out as the gate computation wants them (see phase 1).
-// kPipe (with the chunked, standard-precision forms only): the pipelined plan, whose carries
-// run in the same launch; each chunk's record is announced in a.ready once every wave's
+// kPipe (with the chunked forms only): the pipelined plan, whose carries run in the same
+// launch; each chunk's record is announced in a.ready once every wave's
 // stores of it have completed.  bid: the workgroup's segment-major index (sg * H + h),
 // or (sequence order) * H + h in the fused plan.
 template <bool kChunked, bool kPrecise, bool kGateProj, bool kPipe = false>
 __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid) {
-    static_assert(!kPipe || (kChunked && !kPrecise), "the pipelined plan's form");
+    static_assert(!kPipe || kChunked, "the pipelined plan's form");
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr LdsMap M = kPrecise ? kMapPrecise : kMapStd;
     using R = Rec<kPrecise>;
@@ -1221,21 +1221,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 // in index order as compute units free up, so the carries start once the first pipe_first
 // chunk workgroups are under way and never hold more compute units than the host allows;
 // the chunk workgroups never wait, so every record is written whatever the carries do.
-// The carry's record buffers take the first 154 KB of the same dynamic LDS.
-template <bool kBf16, bool kGateProj>
+// The carry's record buffers take the first 154 KB (high precision: 111 KB) of the same
+// dynamic LDS.
+template <bool kBf16, bool kPrecise, bool kGateProj>
 __global__ __launch_bounds__(kThreads, 1) void prefill_pipe_kernel(PrefillArgs a) {
     static_assert(kThreads == kCarryThreads, "one block size for both roles");
     static_assert(2 * (kLoPieces + kHiPieces) * REC_PIECE <= kLdsBytes, "the carry's buffers");
+    static_assert(RecP::kPieces * REC_PIECE + kChunk * 8 * 4 <= kLdsBytes, "the precise carry's buffers");
     extern __shared__ __align__(16) unsigned char smem[];
     const int b = (int)blockIdx.x;
     if (b >= a.pipe_first && b < a.pipe_first + a.pipe_units) {
         const int pair = b - a.pipe_first;
-        carry_body<kBf16, true>(a, pair / a.c.H, pair % a.c.H, smem, smem + kLoPieces * REC_PIECE,
-                                smem + (kLoPieces + kHiPieces) * REC_PIECE,
-                                smem + (2 * kLoPieces + kHiPieces) * REC_PIECE);
+        if constexpr (kPrecise)
+            carry_body_precise<kBf16, true>(a, pair / a.c.H, pair % a.c.H, smem,
+                                            reinterpret_cast<float *>(smem + RecP::kPieces * REC_PIECE));
+        else
+            carry_body<kBf16, true>(a, pair / a.c.H, pair % a.c.H, smem, smem + kLoPieces * REC_PIECE,
+                                    smem + (kLoPieces + kHiPieces) * REC_PIECE,
+                                    smem + (2 * kLoPieces + kHiPieces) * REC_PIECE);
         return;
     }
-    prefill_body<true, false, kGateProj, true>(a, b < a.pipe_first ? b : b - a.pipe_units);
+    prefill_body<true, kPrecise, kGateProj, true>(a, b < a.pipe_first ? b : b - a.pipe_units);
 }
 
 // ---- the chunked plan's tables ----
@@ -1355,9 +1361,9 @@ hipError_t launch_prefill_kernel(const PrefillArgs &a, size_t blocks, hipStream_
               : launch_prefill_kernel_t<kChunked, false, false>(a, blocks, stream);
 }
 
-template <bool kBf16, bool kGateProj>
+template <bool kBf16, bool kPrecise, bool kGateProj>
 hipError_t launch_pipe_t(const PrefillArgs &a, size_t blocks, hipStream_t stream) {
-    const void *fn = reinterpret_cast<const void *>(&prefill_pipe_kernel<kBf16, kGateProj>);
+    const void *fn = reinterpret_cast<const void *>(&prefill_pipe_kernel<kBf16, kPrecise, kGateProj>);
     static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (attr != hipSuccess) return attr;
     void *args[] = {const_cast<PrefillArgs *>(&a)};
@@ -1375,9 +1381,18 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     if (a.ready) {
         const bool gp = a.w_fb != nullptr;
         const size_t blocks = (size_t)a.nseg_cap * a.c.H + (size_t)a.pipe_units;
+        if (a.c.precise) {
+            if (a.c.out_bf16)
+                return gp ? launch_pipe_t<true, true, true>(a, blocks, stream)
+                          : launch_pipe_t<true, true, false>(a, blocks, stream);
+            return gp ? launch_pipe_t<false, true, true>(a, blocks, stream)
+                      : launch_pipe_t<false, true, false>(a, blocks, stream);
+        }
         if (a.c.out_bf16)
-            return gp ? launch_pipe_t<true, true>(a, blocks, stream) : launch_pipe_t<true, false>(a, blocks, stream);
-        return gp ? launch_pipe_t<false, true>(a, blocks, stream) : launch_pipe_t<false, false>(a, blocks, stream);
+            return gp ? launch_pipe_t<true, false, true>(a, blocks, stream)
+                      : launch_pipe_t<true, false, false>(a, blocks, stream);
+        return gp ? launch_pipe_t<false, false, true>(a, blocks, stream)
+                  : launch_pipe_t<false, false, false>(a, blocks, stream);
     }
     e = launch_prefill_kernel<true>(a, (size_t)a.nseg_cap * a.c.H, stream);
     if (e != hipSuccess) return e;

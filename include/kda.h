@@ -137,8 +137,8 @@ typedef struct {
  *                        workgroup per (sequence, head) carries the state through them
  *                        (two, each owning half the value columns, when B*H <= 128 in
  *                        the standard precision).  Fills the GPU when B*H is small (a
- *                        few long sequences).  For B*H <= 128 in the standard
- *                        precision, where the device has at least 2*B*H compute units
+ *                        few long sequences).  For B*H <= 128 (either precision),
+ *                        where the device has at least 2*B*H compute units
  *                        and an estimate predicts it faster, the
  *                        carries run in the same launch as the chunk workgroups and
  *                        follow the records as they are written (same bits).  A carry
@@ -418,8 +418,8 @@ kda_status kda_prefill_noalloc(const kda_config *cfg, int32_t num_seqs, int32_t 
 
 /* Device scratch kda_prefill needs for these sizes with cfg->prefill_path and
  * cfg->precision: 0 for the fused layout; for the chunked one a table of 2(B+1) int32
- * (padded to 256 bytes); where the carries run in the chunk workgroups' launch (standard
- * precision, B*H <= 128, when the estimate prefers it), 4 bytes per (chunk, head) of
+ * (padded to 256 bytes); where the carries run in the chunk workgroups' launch (B*H <=
+ * 128, when the estimate prefers it), 4 bytes per (chunk, head) of
  * records' ready words (padded to 256 bytes) and, for B > 1, 4 bytes per chunk-kernel
  * segment of the segments' order (padded to 256 bytes); otherwise, for B*H <= 128 in the
  * standard precision, 4,096 bytes per (sequence, head) for the two-workgroup carry's row
@@ -475,9 +475,9 @@ kda_status kda_state_copy(const kda_config *cfg, int32_t n,
 void kda_test_split_carry(int32_t publish, int32_t max_polls);
 
 /* Test hook for the chunked prefill whose carries run in the chunk workgroups' launch
- * (B*H <= 128 in the standard precision; each carry reads a record once its ready word
- * is set).  mode 0: the library's choice; 1: never that form; 2: that form wherever it
- * can run (standard precision, B*H <= 128, 2*B*H <= compute units), chosen
+ * (B*H <= 128, either precision; each carry reads a record once its ready word is set).
+ * mode 0: the library's choice; 1: never that form; 2: that form wherever it can run
+ * (B*H <= 128, 2*B*H <= compute units), chosen
  * before kda_prefill_workspace_bytes sizes the workspace, so query the size after
  * setting it.  publish = 0 makes the chunk workgroups skip the ready words, so that every
  * carry's wait times out; max_polls > 0 bounds each wait to that many polls (0: the

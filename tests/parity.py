@@ -154,9 +154,10 @@ PRECISION_STANDARD, PRECISION_HIGH = 0, 1
 
 
 def prefill_gpu(case: ki.PrefillCase, dev, in_place: bool = False, path: int = PATH_AUTO,
-                precision: int = PRECISION_STANDARD):
+                precision: int = PRECISION_STANDARD, out_dtype=None):
     import gated_delta_rule_31_amd as kda
-    cfg = kda.KdaConfig(num_heads=case.H, prefill_path=path, precision=precision)
+    cfg = kda.KdaConfig(num_heads=case.H, prefill_path=path, precision=precision,
+                        **({} if out_dtype is None else {"out_dtype": out_dtype}))
     p = case.params
     cu = t(case.cu_seqlens.astype(np.int32), dev)
     xs = [t(getattr(case.x, n), dev) for n in "qkvzbg"]

@@ -142,6 +142,9 @@ def test_prefill_path_selection_and_workspace_size():
         # 4 segments (4-chunk segments); 64 heads: B*H = 192 takes neither that form nor the split
         assert _ws(_cfg(prefill_path=2, num_heads=32), 3, 300) == 256 + 1024 + 256 + 7 * 32 * REC_BYTES
         assert _ws(_cfg(prefill_path=2, num_heads=64), 3, 300) == 256 + 7 * 64 * REC_BYTES
+        # high precision: the pipelined form too (its records are 144,384 bytes)
+        assert _ws(_cfg(prefill_path=2, num_heads=4, precision=1), 1, 100) == 256 + 256 + (1 + 1) * 4 * 144384
+        kda.kda_test_pipeline(1)  # and its serial carry, which has no split form
         assert _ws(_cfg(prefill_path=2, num_heads=4, precision=1), 1, 100) == 256 + (1 + 1) * 4 * 144384
     finally:
         kda.kda_test_pipeline(0)
@@ -149,7 +152,7 @@ def test_prefill_path_selection_and_workspace_size():
     # (two sequences of 64 heads: the pipelined plan, with the segments' row-major order)
     assert _ws(_cfg(prefill_path=2, num_heads=64), 2, 128) == 256 + 1024 + 256 + (2 + 2) * 64 * REC_BYTES
     assert _ws(_cfg(prefill_path=2, num_heads=43), 3, 128) == 256 + (2 + 3) * 43 * REC_BYTES
-    assert _ws(_cfg(prefill_path=2, num_heads=96, precision=1), 1, 8192) == 256 + (128 + 1) * 96 * 144384
+    assert _ws(_cfg(prefill_path=2, num_heads=96, precision=1), 1, 8192) == 256 + ready(129 * 96) + (128 + 1) * 96 * 144384
     # auto: the layout the time estimate prefers; these are the measured winners on MI355X
     # for equal sequences of 4096 tokens (fused fills whole rounds of 256 workgroups)
     chunked = lambda B, N: _ws(_cfg(num_heads=96), B, N) == _ws(_cfg(prefill_path=2, num_heads=96), B, N) > 0
@@ -428,8 +431,10 @@ def test_precision_flag():
     assert kda.lib().kda_config_default().precision == 0
     assert _decode(_cfg(precision=2), 1) == BAD_CONFIG
     assert _prefill(_cfg(precision=-1), 1, 8) == BAD_CONFIG
-    # the high-precision records carry the lo parts of W and Q~: 144,384 bytes each
-    assert _ws(_cfg(prefill_path=2, num_heads=96, precision=1), 1, 8192) == 256 + (128 + 1) * 96 * 144384
+    # the high-precision records carry the lo parts of W and Q~: 144,384 bytes each (one
+    # sequence of 96 heads: the pipelined form, with a ready word per record)
+    ready = (129 * 96 * 4 + 255) // 256 * 256
+    assert _ws(_cfg(prefill_path=2, num_heads=96, precision=1), 1, 8192) == 256 + ready + (128 + 1) * 96 * 144384
     assert _ws(_cfg(prefill_path=1, precision=1), 1, 8192) == 0
 
 

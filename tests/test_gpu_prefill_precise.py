@@ -6,7 +6,10 @@ standard mode (2e-2 abs on outputs, 5e-3 relative on final states, exact windows
   token, the plain delta rule, at 1,024 and 8,192 tokens, on both work layouts;
 - the ordinary cases (single chunk, ragged lengths, varlen with empty and short sequences,
   many sequences, saturated gates, in-place carry) on both layouts;
-- the two layouts bit for bit, and bf16 outputs as the fp32 ones rounded."""
+- the two layouts bit for bit, and bf16 outputs as the fp32 ones rounded;
+- the chunked layout's two carry forms (serial after the chunk kernel, and pipelined in its
+  launch behind the records' ready words) bit for bit against the fused layout, with bf16
+  outputs too, and the pipelined carries' bounded wait."""
 import numpy as np
 import pytest
 import torch
@@ -118,3 +121,59 @@ def test_bf16_outputs_are_the_fp32_outputs_rounded(device, path):
     torch.cuda.synchronize()
     assert torch.equal(got[0], ref[0].to(torch.bfloat16))
     assert torch.equal(got[1], ref[1]) and torch.equal(got[2], ref[2])
+
+
+def _precise_modes(case, device, out_dtype=None):
+    """The fused layout, then the chunked one with the serial and with the pipelined carry
+    (kda_test_pipeline modes 1 and 2)."""
+    import gated_delta_rule_31_amd as kda
+    runs = [prefill_gpu(case, device, path=PATH_FUSED, precision=PRECISION_HIGH, out_dtype=out_dtype)]
+    try:
+        for mode in (1, 2):
+            kda.kda_test_pipeline(mode)
+            runs.append(prefill_gpu(case, device, path=PATH_CHUNKED, precision=PRECISION_HIGH, out_dtype=out_dtype))
+    finally:
+        kda.kda_test_pipeline(0)
+    return runs
+
+
+@pytest.mark.parametrize("H,lengths", [(32, [8192]), (96, [1000]), (4, [65]), (1, [321]), (16, [700, 0, 1, 2000, 65]),
+                                       (32, [1500, 1500, 1500])])
+def test_pipelined_carry_agrees_bitwise(device, H, lengths):
+    """The high-precision carry pipelined in the chunk workgroups' launch gives the bits of
+    its serial form and of the fused kernel (outputs, final states, windows)."""
+    case = ki.prefill_case(430 + H, H, lengths, True, "precise-pipe")
+    print(f"[precise] pipelined B={case.B} N={case.N} H={H}", flush=True)
+    fused, serial, piped = _precise_modes(case, device)
+    for x, y, z in zip(fused, serial, piped):
+        assert torch.equal(x, y)
+        assert torch.equal(x, z)
+
+
+def test_pipelined_bf16_outputs(device):
+    case = ki.prefill_case(436, 8, [900, 77], True, "precise-pipe-bf16")
+    fused, serial, piped = _precise_modes(case, device, out_dtype=torch.bfloat16)
+    assert fused[0].dtype == torch.bfloat16
+    for x, y, z in zip(fused, serial, piped):
+        assert torch.equal(x, y)
+        assert torch.equal(x, z)
+
+
+def test_pipelined_wait_times_out(device):
+    """The high-precision pipelined carries' wait is bounded too: with the ready words never
+    published and a 16-poll bound, the outputs and final states are NaN, the windows exact,
+    and the next call is a normal one."""
+    import gated_delta_rule_31_amd as kda
+    case = ki.prefill_case(437, 4, [300], True, "precise-pipe-timeout")
+    ref = prefill_gpu(case, device, path=PATH_FUSED, precision=PRECISION_HIGH)
+    try:
+        kda.kda_test_pipeline(2, False, 16)
+        got = prefill_gpu(case, device, path=PATH_CHUNKED, precision=PRECISION_HIGH)
+        kda.kda_test_pipeline(2)
+        again = prefill_gpu(case, device, path=PATH_CHUNKED, precision=PRECISION_HIGH)
+    finally:
+        kda.kda_test_pipeline(0)
+    assert torch.isnan(got[0]).all() and torch.isnan(got[1]).all()
+    assert torch.equal(got[2], ref[2])
+    for x, y in zip(again, ref):
+        assert torch.equal(x, y)

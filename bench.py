@@ -415,7 +415,15 @@ PREFILL_WORKLOADS = {
 }
 
 
-def bench_prefill(args, dev, which: str, with_bf16_out: bool = False):
+def prefill_warmup(args) -> int:
+    """Untimed calls before each prefill leg's timed ones.  The GPU comes to each leg from
+    host-side input generation, and its per-call time keeps falling over the first ten to
+    fifteen calls (1.24 -> 1.05 ms on the 8192-token workload), so a leg warms up with at
+    least ten calls."""
+    return max(10, args.warmup)
+
+
+def bench_prefill(args, dev, which: str, with_bf16_out: bool = False, with_precise: bool = False):
     """One kda_prefill call on the workload (inputs resident in HBM, outputs, final states
     and the workspace allocated before the timed calls), the layout the library picks
     unless --prefill-path forces one; HIP events around each of n calls."""
@@ -446,10 +454,11 @@ def bench_prefill(args, dev, which: str, with_bf16_out: bool = False):
     ws_bytes = kda.kda_prefill_workspace_bytes(cfg, B, N)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
-    def timed(c, o):
+    def timed(c, o, w=None):
+        wsp = ws if w is None else w
         call = lambda: kda.kda_prefill(c, cu, *xs, *prm, s0, c0, out=o, final_state=fs, final_conv_state=fcs,
-                                       workspace=ws)
-        for _ in range(max(1, args.warmup // 2)):
+                                       workspace=wsp)
+        for _ in range(prefill_warmup(args)):
             call()
         torch.cuda.synchronize()
         n = args.prefill_steps
@@ -461,7 +470,9 @@ def bench_prefill(args, dev, which: str, with_bf16_out: bool = False):
             ev[i][1].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        return (t1 - t0) * 1e3 / n, float(np.mean([s.elapsed_time(e) for s, e in ev]))
+        per = [s.elapsed_time(e) for s, e in ev]
+        log(f"prefill {which}: per-call ms {[round(x, 4) for x in per]}")
+        return (t1 - t0) * 1e3 / n, float(np.mean(per))
 
     ms, kern_ms = timed(cfg, out)
     flops = prefill_flops(lengths, H)
@@ -488,6 +499,16 @@ def bench_prefill(args, dev, which: str, with_bf16_out: bool = False):
         byts16 = prefill_bytes(N, B, H, initial=initial, out_bytes=2)
         res["bf16_out"] = {"ms_per_call": round(ms16, 4), "tokens_per_s": round(N / (ms16 * 1e-3), 1),
                            "alg_bytes": byts16, "hbm_frac": round(byts16 / (ms16 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if with_precise:
+        # the opt-in high-precision mode (every MFMA operand of the chunk algebra split hi + lo),
+        # same workload, with its own workspace (larger chunk records)
+        cfgp = kda.KdaConfig(num_heads=H, prefill_path=path, precision=kda.PRECISION_HIGH)
+        wsp_bytes = kda.kda_prefill_workspace_bytes(cfgp, B, N)
+        wsp = torch.empty(wsp_bytes, dtype=torch.uint8, device=dev) if wsp_bytes else None
+        _, msp = timed(cfgp, out, wsp)
+        res["precision_high"] = {"ms_per_call": round(msp, 4), "tokens_per_s": round(N / (msp * 1e-3), 1),
+                                 "workspace_bytes": wsp_bytes, "vs_standard": round(msp / kern_ms, 3),
+                                 "hbm_frac": round(byts / (msp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return res
 
 
@@ -519,7 +540,7 @@ def bench_prefill_gate_proj(args, dev):
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     call = lambda: kda.kda_prefill_gate_proj(cfg, cu, xs["q"], xs["k"], xs["v"], fd, wd, xs["b"], xs["g"], *prm,
                                              None, None, out=out, final_state=fs, final_conv_state=fcs, workspace=ws)
-    for _ in range(max(1, args.warmup // 2)):
+    for _ in range(prefill_warmup(args)):
         call()
     torch.cuda.synchronize()
     n = args.prefill_steps
@@ -656,7 +677,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=32, help="timed decode steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=10, help="timed calls of each prefill leg")
     ap.add_argument("--prefill-path", choices=["auto", "fused", "chunked"], default="auto",
                     help="prefill work layout (auto: the library's estimate of the faster one)")
     ap.add_argument("--only", choices=["all", "decode-cfg4", "decode-cfg1", "decode-multi", "decode-multi-8",
@@ -706,7 +727,7 @@ def main():
         pre2 = pre3 = None
         if not args.skip_prefill:
             log("prefill: 1 x 8192 tokens x 96 heads")
-            pre2 = bench_prefill(args, dev, "cfg2", with_bf16_out=True)
+            pre2 = bench_prefill(args, dev, "cfg2", with_bf16_out=True, with_precise=True)
             log(f"prefill cfg2: {pre2}")
             log("prefill: 16 varlen sequences x 96 heads")
             pre3 = bench_prefill(args, dev, "cfg3")

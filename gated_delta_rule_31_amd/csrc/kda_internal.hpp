@@ -116,23 +116,25 @@ constexpr int64_t kSplitXchgBytes = 2 * 4 * kChunk * 8;
 // the chunk kernel's grid after its first pipe_first workgroups, so that they start once
 // those finish and then follow the records as the rest are written.  It is used for
 // B*H <= (compute units) / 2, so that the chunk workgroups keep at least half the compute
-// units; with several sequences the chunk workgroups take the segments row by row.  The carries should start late enough never to wait: with p the time
+// units; with several sequences the chunk workgroups take the segments row by row.  The
+// carries should start late enough never to wait: with p the time
 // of a chunk-head on one compute unit (kRecordUs), r a carry's time per chunk
 // (kPipeCarryChunkUs), I chunk-heads, R chunks per sequence, C compute units and B*H carries,
 // the workgroups that start before them cover I - R (r / p) (C - B*H) chunk-heads, the
 // work that C - B*H compute units finish while a carry walks its R chunks.  The plan's
 // time is then that start plus R r.  Beside the chunk workgroups a carry walks a chunk in
-// about 5.0-5.9 us on MI355X (4.9 alone); kPipeCarryChunkUs = 5.9 model microseconds (the
+// about 5.0-5.9 us on MI355X (4.9 alone); kPipeCarryChunkUs = 6.4 model microseconds (the
 // model's chunk-head takes 17.0 for about 15.7 measured) puts the start where a sweep of
-// it was fastest on 1 x 8192 x 96: a carry that starts early only waits, one that starts
-// late lengthens the call.  The chunk workgroups of this plan take segments of
+// it was fastest on 1 x 8192 x 96 with the GPU warmed up by ten earlier calls (4.9 to 7.6:
+// 6.4 fastest, 5.9 2% slower, 7.2 3% slower): a carry that starts early only waits, one
+// that starts late lengthens the call.  The chunk workgroups of this plan take segments of
 // kPipeSegChunks chunks: a row of records is complete only when every head's segment is,
 // so long segments would make the carries wait for whole rows (measured on 1 x 8192
 // tokens x 96 heads: 1.14 ms with 4 or 8 chunks, 1.21 ms with 16).  A carry waits for a
 // record at most kReadyMaxPolls polls: the first kReadyShortPolls about a microsecond
 // apart, the rest about five (so a few seconds in all, which also covers chunk workgroups
 // held off the GPU for a while by other streams' work).
-constexpr double kPipeCarryChunkUs = 5.9;
+constexpr double kPipeCarryChunkUs = 6.4;
 // The high-precision carry walks a chunk in about 11 us beside the chunk workgroups and 8
 // alone, slower than the records arrive: its start point comes out at the grid's start
 // (on 1 x 8192 x 96, a start after 0, 250 and 1,000 chunk workgroups took 1.44, 1.48 and
